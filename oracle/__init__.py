@@ -1,0 +1,173 @@
+"""CPU oracle for masked grouped-query softmax attention (fp64).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU
+baseline leg import this package; the product path (the HIP library and its
+Python binding) never does, and shares no code with it.
+
+``fwd`` and ``bwd`` call the plain fp64 C definition in ``gqa_oracle.c``.
+``online.chunked_fwd`` is a separate numpy model of the chunked
+online-softmax recurrence, used only to cross-check the plain definition.
+
+Inputs are torch bf16 CPU tensors (or numpy uint16 bit patterns) in the
+layout q/dO [B,K,G,T,H], k/v [B,K,S,H], segment ids int32 [B,T]/[B,S],
+explicit mask bool [B,T,S].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gqa_oracle.c")
+_LIB = os.path.join(_HERE, "libgqa_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP). Returns the library path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.oracle_fwd_rows.restype = ctypes.c_int
+        lib.oracle_fwd_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_int,
+                                        I64, P, P, P]
+        lib.oracle_bwd_rows.restype = ctypes.c_int
+        lib.oracle_bwd_rows.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_int,
+                                        I64, P, P, P, I64, P, P, P]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def _bits(x):
+    """bf16 tensor / uint16 array -> contiguous numpy uint16 bit patterns."""
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.uint16
+        return np.ascontiguousarray(x)
+    import torch
+    assert x.dtype == torch.bfloat16, x.dtype
+    return np.ascontiguousarray(x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def _i32(x):
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        return np.ascontiguousarray(x, dtype=np.int32)
+    return np.ascontiguousarray(x.detach().cpu().numpy().astype(np.int32))
+
+
+def _u8(x):
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        return np.ascontiguousarray(x.astype(np.uint8))
+    return np.ascontiguousarray(x.detach().cpu().numpy().astype(np.uint8))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows(rows):
+    if rows is None:
+        return None
+    return np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+
+
+def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None):
+    """Plain fp64 attention. Returns (O, lse) as float64 numpy arrays.
+
+    rows=None: O has q's shape and lse q's shape minus H.
+    rows given (flat indices into [B,K,G,T]): O is [len(rows), H], lse [len(rows)].
+    """
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    B, K, G, T, H = qb.shape
+    S = kb.shape[2]
+    assert kb.shape == (B, K, S, H) and vb.shape == kb.shape
+    qs, ks, mk = _i32(q_seg), _i32(kv_seg), _u8(mask)
+    if mk is not None:
+        assert mk.shape == (B, T, S)
+    r = _rows(rows)
+    n = B * K * G * T if r is None else len(r)
+    o = np.empty((n, H), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load().oracle_fwd_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(qs), _ptr(ks), _ptr(mk),
+                                 B, K, G, T, S, H, int(bool(causal)), n, _ptr(r), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_fwd_rows failed with code %d" % rc)
+    if r is None:
+        return o.reshape(B, K, G, T, H), lse.reshape(B, K, G, T)
+    return o, lse
+
+
+def bwd(q, k, v, do, *, causal=False, q_seg=None, kv_seg=None, mask=None, qrows=None, kvrows=None,
+        want_dq=True, want_dkv=True):
+    """Plain fp64 gradients of sum(O * dO). Returns dict with dq, dk, dv, D.
+
+    Full tensors when the row lists are None, else [n, H] arrays for the
+    listed rows (qrows index [B,K,G,T], kvrows index [B,K,S])."""
+    qb, kb, vb, db = _bits(q), _bits(k), _bits(v), _bits(do)
+    B, K, G, T, H = qb.shape
+    S = kb.shape[2]
+    assert db.shape == qb.shape
+    qs, ks, mk = _i32(q_seg), _i32(kv_seg), _u8(mask)
+    qr, kr = _rows(qrows), _rows(kvrows)
+    nq = (B * K * G * T if qr is None else len(qr)) if want_dq else 0
+    nkv = (B * K * S if kr is None else len(kr)) if want_dkv else 0
+    if not want_dq:
+        qr = np.zeros(0, dtype=np.int64)
+    if not want_dkv:
+        kr = np.zeros(0, dtype=np.int64)
+    dq = np.empty((max(nq, 1), H), dtype=np.float64)
+    dd = np.empty((max(nq, 1),), dtype=np.float64)
+    dk = np.empty((max(nkv, 1), H), dtype=np.float64)
+    dv = np.empty((max(nkv, 1), H), dtype=np.float64)
+    rc = _load().oracle_bwd_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(db), _ptr(qs), _ptr(ks), _ptr(mk),
+                                 B, K, G, T, S, H, int(bool(causal)),
+                                 nq, _ptr(qr), _ptr(dq) if nq else None, _ptr(dd) if nq else None,
+                                 nkv, _ptr(kr), _ptr(dk) if nkv else None, _ptr(dv) if nkv else None)
+    if rc != 0:
+        raise ValueError("oracle_bwd_rows failed with code %d" % rc)
+    out = {}
+    if want_dq:
+        dq, dd = dq[:nq], dd[:nq]
+        if qrows is None:
+            dq, dd = dq.reshape(B, K, G, T, H), dd.reshape(B, K, G, T)
+        out["dq"], out["D"] = dq, dd
+    if want_dkv:
+        dk, dv = dk[:nkv], dv[:nkv]
+        if kvrows is None:
+            dk, dv = dk.reshape(B, K, S, H), dv.reshape(B, K, S, H)
+        out["dk"], out["dv"] = dk, dv
+    return out
+
+
+if __name__ == "__main__":
+    print(build(force=True), file=sys.stderr)

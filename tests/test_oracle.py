@@ -1,0 +1,330 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other
+than its own formula -- a library routine (torch fp64 SDPA / autograd), a
+closed form, an invariant, an independent formulation, or the chunked
+recurrence of danielwatson6.github.io/fa ("Chunked attention").
+
+Plausible oracle mistakes and the tests that catch them:
+  wrong contraction index / transposed operand -> torch SDPA, brute force
+  missing max-shift or wrong normaliser        -> rows-sum-to-1, brute force
+  causal off by one (s < t vs s <= t)          -> causal row 0, prefix means
+  segment compare wrong                        -> explicit mask, per-segment runs
+  wrong kv head for a query head (GQA)         -> MHA-with-repeats, SDPA
+  backward sign / missing D term               -> torch autograd, invariants
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import online
+from workloads import make_qkv, make_segment_ids
+
+
+def bits(x):
+    return x.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def f64(x):
+    return x.to(torch.float64)
+
+
+def explicit_mask(B, T, S, causal, q_seg=None, kv_seg=None):
+    m = torch.ones(B, T, S, dtype=torch.bool)
+    if causal:
+        m &= torch.arange(S)[None, :] <= torch.arange(T)[:, None]
+    if q_seg is not None:
+        m &= q_seg[:, :, None] == kv_seg[:, None, :]
+    return m
+
+
+def sdpa_reference(q, k, v, mask):
+    """torch fp64 SDPA with scale 1 on K/V repeated per query head (GQA -> MHA)."""
+    B, K, G, T, H = q.shape
+    S = k.shape[2]
+    qh = f64(q).reshape(B, K * G, T, H)
+    kh = f64(k).repeat_interleave(G, dim=1)
+    vh = f64(v).repeat_interleave(G, dim=1)
+    am = mask[:, None, :, :].expand(B, K * G, T, S)
+    o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=am, scale=1.0)
+    logits = torch.matmul(qh, kh.transpose(-1, -2).contiguous())
+    logits = logits.masked_fill(~am, -math.inf)
+    lse = torch.logsumexp(logits, dim=-1)
+    return o.reshape(B, K, G, T, H).numpy(), lse.reshape(B, K, G, T).numpy()
+
+
+CASES = [
+    # B, K, G, T, S, H, causal, segments
+    (1, 1, 1, 5, 5, 4, False, False),
+    (2, 2, 3, 7, 7, 8, True, False),
+    (1, 2, 2, 9, 13, 16, False, False),
+    (2, 1, 4, 16, 16, 32, True, True),
+    (1, 3, 2, 33, 33, 64, True, False),
+    (2, 2, 2, 40, 40, 128, True, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_fwd_matches_torch_sdpa_fp64(case):
+    B, K, G, T, S, H, causal, segs = case
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=11 + T)
+    q_seg = kv_seg = None
+    if segs:
+        q_seg = make_segment_ids(B, T, seed=T, lo=1, hi=6)
+        kv_seg = q_seg.clone()
+    o, lse = oracle.fwd(q, k, v, causal=causal, q_seg=q_seg, kv_seg=kv_seg)
+    ref_o, ref_lse = sdpa_reference(q, k, v, explicit_mask(B, T, S, causal, q_seg, kv_seg))
+    np.testing.assert_allclose(o, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_fwd_brute_force_without_max_shift():
+    """Independent formulation: O = sum e^l v / sum e^l with exactly rounded
+    sums (math.fsum) and no max subtraction, on a tiny problem."""
+    B, K, G, T, S, H = 2, 2, 3, 6, 8, 4
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=3)
+    qf, kf, vf = f64(q).numpy(), f64(k).numpy(), f64(v).numpy()
+    for causal in (False, True):
+        o, lse = oracle.fwd(q, k, v, causal=causal)
+        for b in range(B):
+            for kk in range(K):
+                for g in range(G):
+                    for t in range(T):
+                        ss = [s for s in range(S) if (not causal or s <= t)]
+                        e = [math.exp(math.fsum(qf[b, kk, g, t, h] * kf[b, kk, s, h] for h in range(H))) for s in ss]
+                        z = math.fsum(e)
+                        for h in range(H):
+                            num = math.fsum(e[i] * vf[b, kk, s, h] for i, s in enumerate(ss))
+                            assert abs(o[b, kk, g, t, h] - num / z) < 1e-13
+                        assert abs(lse[b, kk, g, t] - math.log(z)) < 1e-13
+
+
+@pytest.mark.parametrize("causal,segs", [(False, False), (True, False), (True, True), (False, True)])
+def test_rows_of_p_sum_to_one(causal, segs):
+    """With v[s] = e_s (one-hot, S <= H), O[t] is the weight row P[t, :]."""
+    B, K, G, T, H = 2, 1, 2, 24, 32
+    S = T
+    q, k, _ = make_qkv(B, K, G, T, S, H, seed=5)
+    v = torch.zeros(B, K, S, H, dtype=torch.bfloat16)
+    for s in range(S):
+        v[:, :, s, s] = 1.0
+    q_seg = kv_seg = None
+    if segs:
+        q_seg = make_segment_ids(B, T, seed=7, lo=2, hi=9)
+        kv_seg = q_seg.clone()
+    o, _ = oracle.fwd(q, k, v, causal=causal, q_seg=q_seg, kv_seg=kv_seg)
+    P = o[..., :S]
+    assert np.all(P >= 0)
+    np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-12)
+    m = explicit_mask(B, T, S, causal, q_seg, kv_seg).numpy()
+    assert np.all(P[~np.broadcast_to(m[:, None, None], P.shape)] == 0)
+
+
+def test_constant_v_gives_constant_output():
+    B, K, G, T, S, H = 1, 2, 2, 20, 20, 16
+    q, k, _ = make_qkv(B, K, G, T, S, H, seed=9)
+    c = torch.linspace(-2, 2, H).to(torch.bfloat16)
+    v = c.expand(B, K, S, H).contiguous()
+    for causal in (False, True):
+        o, _ = oracle.fwd(q, k, v, causal=causal)
+        np.testing.assert_allclose(o, np.broadcast_to(f64(c).numpy(), o.shape), atol=1e-12)
+
+
+def test_causal_row_zero_is_v0_and_segment_starts():
+    B, K, G, T, H = 2, 2, 2, 48, 16
+    q, k, v = make_qkv(B, K, G, T, T, H, seed=13)
+    o, lse = oracle.fwd(q, k, v, causal=True)
+    assert np.array_equal(o[:, :, :, 0, :], np.broadcast_to(f64(v).numpy()[:, :, None, 0, :], o[:, :, :, 0, :].shape))
+    seg = make_segment_ids(B, T, seed=1, lo=3, hi=11)
+    o, _ = oracle.fwd(q, k, v, causal=True, q_seg=seg, kv_seg=seg)
+    vf = f64(v).numpy()
+    for b in range(B):
+        starts = [0] + [t for t in range(1, T) if seg[b, t] != seg[b, t - 1]]
+        for t in starts:
+            assert np.array_equal(o[b, :, :, t, :], np.broadcast_to(vf[b, :, None, t, :], o[b, :, :, t, :].shape))
+
+
+def test_zero_q_gives_prefix_means():
+    B, K, G, T, H = 1, 2, 3, 30, 8
+    _, k, v = make_qkv(B, K, G, T, T, H, seed=17)
+    q = torch.zeros(B, K, G, T, H, dtype=torch.bfloat16)
+    vf = f64(v).numpy()
+    o, lse = oracle.fwd(q, k, v, causal=True)
+    for t in range(T):
+        np.testing.assert_allclose(o[:, :, :, t, :], np.broadcast_to(vf[:, :, None, : t + 1].mean(axis=3), o[:, :, :, t, :].shape), atol=1e-13)
+        np.testing.assert_allclose(lse[..., t], math.log(t + 1), atol=1e-13)
+    o, lse = oracle.fwd(q, k, v, causal=False)
+    np.testing.assert_allclose(o, np.broadcast_to(vf.mean(axis=2)[:, :, None, None, :], o.shape), atol=1e-13)
+    np.testing.assert_allclose(lse, math.log(T), atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    B, K, G, T, S, H = 2, 2, 3, 12, 12, 16
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=19)
+    o, lse = oracle.fwd(q, k, v, causal=True)
+    q_m = q.reshape(B, K * G, 1, T, H)
+    k_m = k.repeat_interleave(G, dim=1)
+    v_m = v.repeat_interleave(G, dim=1)
+    o_m, lse_m = oracle.fwd(q_m, k_m, v_m, causal=True)
+    np.testing.assert_array_equal(o, o_m.reshape(o.shape))
+    np.testing.assert_array_equal(lse, lse_m.reshape(lse.shape))
+    # permuting query heads permutes outputs
+    perm = torch.tensor([2, 0, 1])
+    o_p, _ = oracle.fwd(q[:, :, perm].contiguous(), k, v, causal=True)
+    np.testing.assert_array_equal(o_p, o[:, :, perm.numpy()])
+
+
+def test_segments_equal_explicit_mask_and_per_segment_runs():
+    B, K, G, T, H = 3, 2, 2, 64, 16
+    q, k, v = make_qkv(B, K, G, T, T, H, seed=23)
+    seg = make_segment_ids(B, T, seed=29, lo=4, hi=20)
+    o, lse = oracle.fwd(q, k, v, causal=True, q_seg=seg, kv_seg=seg)
+    m = explicit_mask(B, T, T, True, seg, seg)
+    o_m, lse_m = oracle.fwd(q, k, v, mask=m)
+    np.testing.assert_array_equal(o, o_m)
+    np.testing.assert_array_equal(lse, lse_m)
+    for b in range(B):
+        ids = seg[b]
+        for sid in torch.unique(ids).tolist():
+            idx = (ids == sid).nonzero().flatten()
+            a, e = int(idx[0]), int(idx[-1]) + 1
+            o_s, lse_s = oracle.fwd(q[b:b + 1, :, :, a:e].contiguous(), k[b:b + 1, :, a:e].contiguous(),
+                                    v[b:b + 1, :, a:e].contiguous(), causal=True)
+            np.testing.assert_allclose(o[b:b + 1, :, :, a:e], o_s, atol=1e-14)
+            np.testing.assert_allclose(lse[b:b + 1, :, :, a:e], lse_s, atol=1e-14)
+
+
+def test_causal_row_equals_noncausal_prefix():
+    B, K, G, T, H = 1, 1, 2, 40, 16
+    q, k, v = make_qkv(B, K, G, T, T, H, seed=31)
+    o, lse = oracle.fwd(q, k, v, causal=True)
+    for t in (0, 1, 17, 39):
+        o_t, lse_t = oracle.fwd(q[:, :, :, t:t + 1].contiguous(), k[:, :, :t + 1].contiguous(),
+                                v[:, :, :t + 1].contiguous(), causal=False)
+        np.testing.assert_allclose(o[:, :, :, t:t + 1], o_t, atol=1e-14)
+        np.testing.assert_allclose(lse[:, :, :, t:t + 1], lse_t, atol=1e-14)
+
+
+@pytest.mark.parametrize("bkv", [1, 3, 16, 64, 100])
+def test_chunked_recurrence_equals_plain_definition(bkv):
+    B, K, G, T, S, H = 2, 2, 2, 50, 50, 32
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=37)
+    seg = make_segment_ids(B, T, seed=41, lo=5, hi=30)
+    for causal, segs in ((False, False), (True, False), (True, True)):
+        kw = dict(q_seg=seg, kv_seg=seg) if segs else {}
+        o, lse = oracle.fwd(q, k, v, causal=causal, **kw)
+        o_c, lse_c = online.chunked_fwd(bits(q), bits(k), bits(v), bkv=bkv, causal=causal,
+                                        q_seg=seg.numpy() if segs else None,
+                                        kv_seg=seg.numpy() if segs else None)
+        np.testing.assert_allclose(o_c, o, atol=1e-12)
+        np.testing.assert_allclose(lse_c, lse, atol=1e-12)
+
+
+def test_large_logits_stay_finite_and_approach_hard_max():
+    """The max-free chunked form overflows for large logits; the definition
+    with the maximum subtracted must not (same page, "Chunked attention")."""
+    B, K, G, T, S, H = 1, 1, 2, 16, 16, 64
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=43, q_scale=100.0)
+    o, lse = oracle.fwd(q, k, v, causal=False)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    logits = np.einsum("bkgth,bksh->bkgts", f64(q).numpy(), f64(k).numpy())
+    srt = np.sort(logits, axis=-1)
+    am = logits.argmax(-1)
+    vf = f64(v).numpy()
+    for g in range(G):
+        for t in range(T):
+            if srt[0, 0, g, t, -1] - srt[0, 0, g, t, -2] > 60:
+                np.testing.assert_allclose(o[0, 0, g, t], vf[0, 0, am[0, 0, g, t]], atol=1e-12)
+    np.testing.assert_allclose(lse, logits.max(-1) + np.log(np.exp(logits - logits.max(-1, keepdims=True)).sum(-1)), atol=1e-9)
+
+
+def test_fully_masked_row_convention():
+    """Segments whose q id never appears among kv ids: O = 0, lse = -inf."""
+    B, K, G, T, H = 1, 1, 1, 8, 8
+    q, k, v = make_qkv(B, K, G, T, T, H, seed=47)
+    q_seg = torch.tensor([[0, 0, 5, 5, 1, 1, 1, 1]], dtype=torch.int32)
+    kv_seg = torch.tensor([[0, 0, 0, 0, 1, 1, 1, 1]], dtype=torch.int32)
+    o, lse = oracle.fwd(q, k, v, causal=False, q_seg=q_seg, kv_seg=kv_seg)
+    assert np.all(o[0, 0, 0, 2:4] == 0) and np.all(np.isneginf(lse[0, 0, 0, 2:4]))
+    assert np.all(np.isfinite(lse[0, 0, 0, [0, 1, 4, 5, 6, 7]]))
+
+
+def test_row_selection_matches_full():
+    B, K, G, T, S, H = 2, 2, 2, 10, 12, 8
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=53)
+    o, lse = oracle.fwd(q, k, v, causal=True)
+    rows = [0, 5, 17, 39, 79]
+    o_r, lse_r = oracle.fwd(q, k, v, causal=True, rows=rows)
+    np.testing.assert_array_equal(o_r, o.reshape(-1, H)[rows])
+    np.testing.assert_array_equal(lse_r, lse.reshape(-1)[rows])
+
+
+# ---------------------------------------------------------------- backward
+
+def autograd_reference(q, k, v, do, mask):
+    B, K, G, T, H = q.shape
+    S = k.shape[2]
+    qh = f64(q).reshape(B, K * G, T, H).requires_grad_(True)
+    k64 = f64(k).requires_grad_(True)
+    v64 = f64(v).requires_grad_(True)
+    am = mask[:, None].expand(B, K * G, T, S)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qh, k64.repeat_interleave(G, dim=1), v64.repeat_interleave(G, dim=1), attn_mask=am, scale=1.0)
+    (o * f64(do).reshape(B, K * G, T, H)).sum().backward()
+    return qh.grad.reshape(B, K, G, T, H).numpy(), k64.grad.numpy(), v64.grad.numpy()
+
+
+@pytest.mark.parametrize("case", [
+    (1, 1, 2, 8, 8, 8, False, False),
+    (2, 2, 2, 16, 16, 16, True, False),
+    (2, 1, 3, 24, 24, 32, True, True),
+    (1, 2, 2, 12, 20, 16, False, False),
+])
+def test_bwd_matches_torch_autograd_fp64(case):
+    B, K, G, T, S, H, causal, segs = case
+    q, k, v, do = make_qkv(B, K, G, T, S, H, seed=59 + T, with_do=True)
+    q_seg = kv_seg = None
+    if segs:
+        q_seg = make_segment_ids(B, T, seed=61, lo=3, hi=9)
+        kv_seg = q_seg.clone()
+    g = oracle.bwd(q, k, v, do, causal=causal, q_seg=q_seg, kv_seg=kv_seg)
+    dq, dk, dv = autograd_reference(q, k, v, do, explicit_mask(B, T, S, causal, q_seg, kv_seg))
+    np.testing.assert_allclose(g["dq"], dq, atol=1e-11)
+    np.testing.assert_allclose(g["dk"], dk, atol=1e-11)
+    np.testing.assert_allclose(g["dv"], dv, atol=1e-11)
+
+
+def test_bwd_invariants_and_rows():
+    B, K, G, T, H = 2, 2, 2, 32, 16
+    q, k, v, do = make_qkv(B, K, G, T, T, H, seed=67, with_do=True)
+    g = oracle.bwd(q, k, v, do, causal=True)
+    # a row-constant logit shift is a no-op -> sum_s dS[t, s] = 0 -> sum_s dK = 0
+    np.testing.assert_allclose(g["dk"].sum(axis=2), 0.0, atol=1e-10)
+    # rows of P sum to 1 -> sum_s dV[s] = sum_{g,t} dO[g,t]
+    np.testing.assert_allclose(g["dv"].sum(axis=2), f64(do).numpy().sum(axis=(2, 3)), atol=1e-10)
+    # D = rowsum(dO * O)
+    o, _ = oracle.fwd(q, k, v, causal=True)
+    np.testing.assert_allclose(g["D"], (o * f64(do).numpy()).sum(-1), atol=1e-12)
+    # selected rows equal the full result
+    qrows, kvrows = [1, 40, 127], [0, 33, 127]
+    gs = oracle.bwd(q, k, v, do, causal=True, qrows=qrows, kvrows=kvrows)
+    np.testing.assert_allclose(gs["dq"], g["dq"].reshape(-1, H)[qrows], atol=1e-14)
+    np.testing.assert_allclose(gs["dk"], g["dk"].reshape(-1, H)[kvrows], atol=1e-14)
+    np.testing.assert_allclose(gs["dv"], g["dv"].reshape(-1, H)[kvrows], atol=1e-14)
+
+
+def test_bwd_directional_derivative_in_v_is_exact():
+    """sum(O * dO) is linear in V, so a finite step in V moves it by exactly
+    <dV, step>; the step is a bf16-exact power of two on one element."""
+    B, K, G, T, H = 1, 1, 2, 12, 8
+    q, k, v, do = make_qkv(B, K, G, T, T, H, seed=71, with_do=True)
+    g = oracle.bwd(q, k, v, do, causal=True)
+    f0 = (oracle.fwd(q, k, v, causal=True)[0] * f64(do).numpy()).sum()
+    for s, h in ((0, 0), (5, 3), (11, 7)):
+        v2 = v.clone()
+        v2[0, 0, s, h] = v2[0, 0, s, h] + 2.0 ** -3
+        if f64(v2)[0, 0, s, h] - f64(v)[0, 0, s, h] != 2.0 ** -3:
+            continue
+        f1 = (oracle.fwd(q, k, v2, causal=True)[0] * f64(do).numpy()).sum()
+        assert abs((f1 - f0) / 2.0 ** -3 - g["dv"][0, 0, s, h]) < 1e-10
