@@ -1,0 +1,176 @@
+"""Python binding of libgqa_attn.so, the fused grouped-query flash-attention
+library for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/gqa_attn.h. PyTorch provides
+device memory and the current stream; there is no CPU or PyTorch fallback --
+if the library is missing or fails, these functions raise.
+
+Layouts: q, o, dO [B, K, G, T, H] bf16 (q pre-multiplied by H^-1/2);
+k, v [B, K, S, H] bf16; lse [B, K, G, T] fp32; q_seg [B, T] and
+kv_seg [B, S] int32; gradients fp32 in the layouts of their inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
+
+GQA_ATTN_OK = 0
+GQA_ATTN_ERR_NULL = 1
+GQA_ATTN_ERR_SHAPE = 2
+GQA_ATTN_ERR_HEADDIM = 3
+GQA_ATTN_ERR_ALIGN = 4
+GQA_ATTN_ERR_SEGMENTS = 5
+GQA_ATTN_ERR_WORKSPACE = 6
+GQA_ATTN_ERR_HIP = 7
+
+EXPORTED_SYMBOLS = (
+    "attn_fwd", "attn_check_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_check_bwd",
+    "attn_strerror", "attn_last_hip_error",
+)
+
+_lib = None
+
+
+class GqaAttnError(ValueError):
+    """A nonzero return code of the C library."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = attn_strerror(code)
+        if code == GQA_ATTN_ERR_HIP:
+            msg += " (hipError %d)" % attn_last_hip_error()
+        super().__init__("%s: %s [code %d]" % (where, msg, code))
+
+
+def load_library():
+    """Load libgqa_attn.so (built by grouped_query_attention_flash_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgqa_attn.so is not built (%s); run `python -m grouped_query_attention_flash_amd.build`"
+                           % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.attn_fwd.restype = I
+    lib.attn_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.attn_check_fwd.restype = I
+    lib.attn_check_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I]
+    lib.attn_bwd_workspace_bytes.restype = SZ
+    lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_bwd.restype = I
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, SZ, P]
+    lib.attn_check_bwd.restype = I
+    lib.attn_check_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, SZ]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_strerror.argtypes = [I]
+    lib.attn_last_hip_error.restype = I
+    lib.attn_last_hip_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def attn_strerror(code: int) -> str:
+    return load_library().attn_strerror(int(code)).decode()
+
+
+def attn_last_hip_error() -> int:
+    return int(load_library().attn_last_hip_error())
+
+
+def attn_bwd_workspace_bytes(B: int, K: int, G: int, T: int, S: int, H: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, K, G, T, S, H))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor):
+    if q.dim() != 5 or k.dim() != 4:
+        raise ValueError("q must be [B,K,G,T,H] and k, v [B,K,S,H]")
+    B, K, G, T, H = q.shape
+    if k.shape[0] != B or k.shape[1] != K or k.shape[3] != H:
+        raise ValueError("k shape %s does not match q shape %s" % (tuple(k.shape), tuple(q.shape)))
+    return B, K, G, T, k.shape[2], H
+
+
+def _check_tensor(name, t, dtype, shape=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+             q_seg: Optional[torch.Tensor] = None, kv_seg: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward pass on the current stream. Returns (o, lse)."""
+    B, K, G, T, S, H = _dims(q, k)
+    _check_tensor("q", q, torch.bfloat16)
+    _check_tensor("k", k, torch.bfloat16)
+    _check_tensor("v", v, torch.bfloat16, k.shape)
+    if (q_seg is None) != (kv_seg is None):
+        raise GqaAttnError(GQA_ATTN_ERR_SEGMENTS, "attn_fwd")
+    if q_seg is not None:
+        _check_tensor("q_seg", q_seg, torch.int32, (B, T))
+        _check_tensor("kv_seg", kv_seg, torch.int32, (B, S))
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, torch.bfloat16, q.shape)
+    if lse is None and want_lse:
+        lse = torch.empty(B, K, G, T, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, (B, K, G, T))
+    rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg), _ptr(kv_seg),
+                                 B, K, G, T, S, H, int(bool(causal)), _stream_handle(q.device))
+    if rc != GQA_ATTN_OK:
+        raise GqaAttnError(rc, "attn_fwd")
+    return out, lse
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             do: torch.Tensor, *, causal: bool = False, q_seg: Optional[torch.Tensor] = None,
+             kv_seg: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """Backward pass on the current stream. Returns (dq, dk, dv) in fp32."""
+    B, K, G, T, S, H = _dims(q, k)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, t, torch.bfloat16)
+    _check_tensor("lse", lse, torch.float32, (B, K, G, T))
+    if (q_seg is None) != (kv_seg is None):
+        raise GqaAttnError(GQA_ATTN_ERR_SEGMENTS, "attn_bwd")
+    dev = q.device
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev) if dv is None else dv
+    _check_tensor("dq", dq, torch.float32, q.shape)
+    _check_tensor("dk", dk, torch.float32, k.shape)
+    _check_tensor("dv", dv, torch.float32, k.shape)
+    wsb = attn_bwd_workspace_bytes(B, K, G, T, S, H)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    rc = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(q_seg), _ptr(kv_seg), B, K, G, T, S, H, int(bool(causal)),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream_handle(dev))
+    if rc != GQA_ATTN_OK:
+        raise GqaAttnError(rc, "attn_bwd")
+    return dq, dk, dv

@@ -1,0 +1,143 @@
+// C ABI of the library: argument validation, tile selection and launch.
+// The declarations and their contracts are in include/gqa_attn.h.
+#include "gqa_attn.h"
+#include "gqa_launch.h"
+
+#include <climits>
+#include <cstdint>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_common(const void *q, const void *k, const void *v, const void *o,
+                 const int32_t *q_seg, const int32_t *kv_seg,
+                 int B, int K, int G, int T, int S, int H) {
+    if (!q || !k || !v || !o) return GQA_ATTN_ERR_NULL;
+    if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return GQA_ATTN_ERR_SHAPE;
+    // 32-bit grid and per-(b, kv head) element offsets must not overflow
+    const long long q_slice = (long long)G * T * H, kv_slice = (long long)S * H;
+    if (q_slice >= INT_MAX || kv_slice >= INT_MAX) return GQA_ATTN_ERR_SHAPE;
+    if ((long long)B * K * G * ((long long)T + 31) >= INT_MAX) return GQA_ATTN_ERR_SHAPE;
+    if (H != 64 && H != 128 && H != 256) return GQA_ATTN_ERR_HEADDIM;
+    if ((q_seg == nullptr) != (kv_seg == nullptr)) return GQA_ATTN_ERR_SEGMENTS;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GQA_ATTN_ERR_ALIGN;
+    if (q_seg && (!aligned(q_seg, 4) || !aligned(kv_seg, 4))) return GQA_ATTN_ERR_ALIGN;
+    return GQA_ATTN_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return GQA_ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal) {
+    (void)causal;
+    int rc = check_common(q, k, v, o, q_seg, kv_seg, B, K, G, T, S, H);
+    if (rc) return rc;
+    if (lse && !aligned(lse, 4)) return GQA_ATTN_ERR_ALIGN;
+    return GQA_ATTN_OK;
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             const int32_t *q_seg, const int32_t *kv_seg,
+             int B, int K, int G, int T, int S, int H, int causal, void *stream) {
+    int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal);
+    if (rc) return rc;
+    const gqa::FwdConfig cfg = gqa::fwd_config(G, T, H);
+    gqa::FwdArgs a;
+    a.q = (const __bf16 *)q;
+    a.k = (const __bf16 *)k;
+    a.v = (const __bf16 *)v;
+    a.o = (__bf16 *)o;
+    a.lse = lse;
+    a.q_seg = q_seg;
+    a.kv_seg = kv_seg;
+    a.B = B, a.K = K, a.G = G, a.T = T, a.S = S;
+    a.causal = causal ? 1 : 0;
+    a.gw = cfg.gw;
+    a.bq = cfg.bq;
+    a.n_gsplit = G / cfg.gw;
+    a.n_qblocks = (T + cfg.bq - 1) / cfg.bq;
+    hipError_t e = gqa::launch_fwd(a, H, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return GQA_ATTN_OK;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int K, int G, int T, int S, int H) {
+    (void)H;
+    if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return 0;
+    return round256(sizeof(float) * (size_t)B * K * G * T);
+}
+
+int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dO, const float *dq, const float *dk, const float *dv,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal,
+                   const void *workspace, size_t workspace_bytes) {
+    (void)causal;
+    int rc = check_common(q, k, v, o, q_seg, kv_seg, B, K, G, T, S, H);
+    if (rc) return rc;
+    if (!lse || !dO || !dq || !dk || !dv) return GQA_ATTN_ERR_NULL;
+    if (!aligned(lse, 16) || !aligned(dO, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return GQA_ATTN_ERR_ALIGN;
+    if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, K, G, T, S, H)) return GQA_ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return GQA_ATTN_ERR_ALIGN;
+    return GQA_ATTN_OK;
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dO, float *dq, float *dk, float *dv,
+             const int32_t *q_seg, const int32_t *kv_seg,
+             int B, int K, int G, int T, int S, int H, int causal,
+             void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = attn_check_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal,
+                            workspace, workspace_bytes);
+    if (rc) return rc;
+    gqa::BwdArgs a;
+    a.q = (const __bf16 *)q;
+    a.k = (const __bf16 *)k;
+    a.v = (const __bf16 *)v;
+    a.o = (const __bf16 *)o;
+    a.dout = (const __bf16 *)dO;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = (float *)workspace;
+    a.q_seg = q_seg;
+    a.kv_seg = kv_seg;
+    a.B = B, a.K = K, a.G = G, a.T = T, a.S = S;
+    a.causal = causal ? 1 : 0;
+    hipError_t e = gqa::launch_bwd(a, H, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return GQA_ATTN_OK;
+}
+
+const char *attn_strerror(int code) {
+    switch (code) {
+        case GQA_ATTN_OK: return "success";
+        case GQA_ATTN_ERR_NULL: return "a required pointer is NULL";
+        case GQA_ATTN_ERR_SHAPE: return "invalid sizes: B, K, G, T, S must be >= 1 and each tensor slice < 2^31 elements";
+        case GQA_ATTN_ERR_HEADDIM: return "unsupported head dimension H (supported: 64, 128, 256)";
+        case GQA_ATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte alignment, segment ids 4-byte)";
+        case GQA_ATTN_ERR_SEGMENTS: return "q_seg and kv_seg must both be given or both be NULL";
+        case GQA_ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
+        case GQA_ATTN_ERR_HIP: return "a HIP launch failed (see attn_last_hip_error)";
+        default: return "unknown error code";
+    }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,314 @@
+// Fused grouped-query flash attention, forward pass, for gfx950 (MI355X).
+//
+// Method (danielwatson6.github.io/fa): "Chunked attention" gives the
+// numerically stable scan over key chunks -- a running row maximum m, a
+// running denominator and an output carry rescaled by exp(m_old - m_new) --
+// and "Optimizing the kernel" fuses the key loop into one kernel whose carries
+// never leave the chip and whose output is written once, in bf16. Masks are
+// generated lazily (apple/axlearn PR 845): causal and segment-id visibility
+// are evaluated from indices, and whole key tiles that no query of a block
+// can see are never visited.
+//
+// Work decomposition. One workgroup owns one (batch b, kv head k, group of
+// gw query heads, block of bq queries) unit: gw*bq query rows, 32 per wave.
+// All gw heads of the unit read the same K/V tiles (the page's kernel sees
+// the G axis inside each (b, kv head) program), so every K/V tile is staged
+// into LDS once per workgroup and consumed by all of its waves.
+//
+// Per wave, per key tile of BKV keys:
+//   S^T = K_tile Q^T  : bf16 MFMA 32x32x16, K from LDS (A operand),
+//                       Q^T resident in registers (B operand)
+//   each lane owns one query column of S^T (its half of the keys; the other
+//   half sits in lane ^ 32), so the row max and row sum are in-lane plus one
+//   cross-half exchange
+//   P = exp2(S*log2e - m), carries rescaled by exp2(m_old - m_new)
+//   O^T += V_tile^T P^T : bf16 MFMA, P^T straight from the S^T registers
+//                         (B operand), V^T via the LDS transpose read
+#include "gqa_device.h"
+#include "gqa_launch.h"
+
+#include <climits>
+#include <cmath>
+
+namespace gqa {
+
+template <int H, int BKV, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
+    constexpr int CPR = H / 8;        // 16-byte chunks per K/V row
+    constexpr int KSTEPS = H / 16;    // k-steps of the QK^T contraction
+    constexpr int MB = BKV / 32;      // 32-key blocks per tile
+    constexpr int HB = H / 32;        // 32-wide h blocks of O^T
+    constexpr int PK = BKV / 16;      // k-steps of the PV contraction
+    constexpr int NT = NW * 64;
+    constexpr int TILE_CHUNKS = BKV * CPR;
+    static_assert((2 * TILE_CHUNKS) % NT == 0, "tile load must split evenly");
+    constexpr int LOADS = 2 * TILE_CHUNKS / NT;
+    static_assert(TILE_CHUNKS % NT == 0, "K and V loads must not share a step");
+
+    __shared__ __attribute__((aligned(16))) __bf16 sk[BKV * H];
+    __shared__ __attribute__((aligned(16))) __bf16 sv[BKV * H];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, c = lane >> 5;
+
+    // ---- work unit; causal blocks are issued heaviest (last query block) first
+    const int units = a.B * a.K * a.n_gsplit;
+    int qb = blockIdx.x / units;
+    if (a.causal) qb = a.n_qblocks - 1 - qb;
+    const int u = blockIdx.x % units;
+    const int gs = u % a.n_gsplit;
+    const int kh = (u / a.n_gsplit) % a.K;
+    const int b = u / (a.n_gsplit * a.K);
+    const int t0 = qb * a.bq;
+    const int T = a.T, S = a.S;
+
+    // ---- this lane's query row (column n of the wave's S^T tile)
+    const int rows_wg = a.gw * a.bq;
+    const int rho = wave * 32 + n;
+    const bool row_in_wg = rho < rows_wg;
+    const int g = gs * a.gw + (row_in_wg ? rho / a.bq : 0);
+    const int t = t0 + (row_in_wg ? rho % a.bq : 0);
+    const bool q_valid = row_in_wg && t < T;
+    const bool wave_active = wave * 32 < rows_wg;
+    const int tmin_w = t0 + (a.bq >= 32 ? (wave * 32) % a.bq : 0);
+    const int tmax_w = tmin_w + (a.bq >= 32 ? 31 : a.bq - 1);
+
+    const size_t bk = (size_t)b * a.K + kh;
+    const size_t qrow_off = ((bk * a.G + g) * (size_t)T + t) * H;
+
+    // Q^T operand: lane (n, c), k-step ks holds q[t][16ks + 8c .. +7]
+    bf16x8 qf[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++) {
+        if (q_valid)
+            qf[ks] = *(const bf16x8 *)(a.q + qrow_off + 16 * ks + 8 * c);
+        else
+            qf[ks] = bf16x8{};
+    }
+
+    const __bf16 *kbase = a.k + bk * (size_t)S * H;
+    const __bf16 *vbase = a.v + bk * (size_t)S * H;
+
+    // ---- segment ids: this lane's query id and the workgroup / wave id ranges
+    const bool segs = a.q_seg != nullptr;
+    const int32_t *kvs = segs ? a.kv_seg + (size_t)b * S : nullptr;
+    int my_qid = 0, wg_qmin = INT_MAX, wg_qmax = INT_MIN, w_qmin = INT_MAX, w_qmax = INT_MIN;
+    if (segs) {
+        const int32_t *qs = a.q_seg + (size_t)b * T;
+        int lo = INT_MAX, hi = INT_MIN;
+        for (int i = lane; i < a.bq; i += 64) {
+            if (t0 + i < T) {
+                int id = qs[t0 + i];
+                lo = min(lo, id);
+                hi = max(hi, id);
+            }
+        }
+        wg_qmin = wave_min_i(lo);
+        wg_qmax = wave_max_i(hi);
+        my_qid = q_valid ? qs[t] : 0;
+        w_qmin = wave_min_i(q_valid ? my_qid : INT_MAX);
+        w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
+    }
+
+    // ---- key-tile range: causal stops at the block's last query
+    const int n_tiles = (S + BKV - 1) / BKV;
+    int j_end = n_tiles;
+    if (a.causal) j_end = min(j_end, (min(t0 + a.bq, T) - 1) / BKV + 1);
+
+    // kv-id range of tile j (wave-uniform; every wave computes the same value)
+    auto tile_ids = [&](int j, int &kmin, int &kmax) {
+        const int s = j * BKV + lane;
+        int id = 0;
+        const bool ok = lane < BKV && s < S;
+        if (ok) id = kvs[s];
+        kmin = wave_min_i(ok ? id : INT_MAX);
+        kmax = wave_max_i(ok ? id : INT_MIN);
+    };
+    // next tile at or after j that some query of the workgroup can see
+    auto next_tile = [&](int j) {
+        if (!segs) return j;
+        for (; j < j_end; j++) {
+            int kmin, kmax;
+            tile_ids(j, kmin, kmax);
+            if (!(kmax < wg_qmin || kmin > wg_qmax)) break;
+        }
+        return j;
+    };
+
+    i32x4 pre[LOADS];
+    auto load_tile = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < LOADS; i++) {
+            const int ci = tid + i * NT;
+            const int tensor = ci / TILE_CHUNKS;
+            const int cc = ci % TILE_CHUNKS;
+            const int r = cc / CPR, ch = cc % CPR;
+            const int s = j * BKV + r;
+            const __bf16 *src = (tensor ? vbase : kbase) + (size_t)s * H + ch * 8;
+            pre[i] = s < S ? *(const i32x4 *)src : i32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < LOADS; i++) {
+            const int ci = tid + i * NT;
+            const int tensor = ci / TILE_CHUNKS;
+            const int cc = ci % TILE_CHUNKS;
+            const int r = cc / CPR, ch = cc % CPR;
+            __bf16 *dst = (tensor ? sv : sk) + r * H + ((ch ^ swz<CPR>(r)) << 3);
+            *(i32x4 *)dst = pre[i];
+        }
+    };
+
+    f32x16 oacc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++) oacc[hb] = f32x16{};
+    float m_run = -INFINITY;  // running max, log2 units
+    float l_run = 0.f;        // running denominator
+
+    int j = next_tile(0);
+    if (j < j_end) load_tile(j);
+    while (j < j_end) {
+        __syncthreads();  // every wave is done reading the previous tile
+        store_tile();
+        __syncthreads();
+        const int jn = next_tile(j + 1);
+        if (jn < j_end) load_tile(jn);  // in flight while tile j is computed
+
+        const int s0 = j * BKV;
+        bool run = wave_active && !(a.causal && s0 > tmax_w);
+        bool seg_mask = false;
+        if (run && segs) {
+            int kmin, kmax;
+            tile_ids(j, kmin, kmax);
+            if (kmax < w_qmin || kmin > w_qmax) run = false;
+            seg_mask = !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
+        }
+        if (run) {
+            // ---- S^T = K Q^T
+            f32x16 sacc[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++) {
+                sacc[mb] = f32x16{};
+                const int r = 32 * mb + n;
+                const __bf16 *krow = sk + r * H;
+                const int sw = swz<CPR>(r);
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ks++) {
+                    const bf16x8 kf = *(const bf16x8 *)(krow + (((2 * ks + c) ^ sw) << 3));
+                    sacc[mb] = mfma32x32x16(kf, qf[ks], sacc[mb]);
+                }
+            }
+            // ---- lazy mask: only tiles that cross the diagonal, the key tail or a segment edge
+            const bool need_mask = (a.causal && s0 + BKV - 1 > tmin_w) || (s0 + BKV > S) || seg_mask;
+            if (need_mask) {
+#pragma unroll
+                for (int mb = 0; mb < MB; mb++) {
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int s = s0 + 32 * mb + acc_row(r, c);
+                        bool vis = s < S && !(a.causal && s > t);
+                        if (segs && vis) vis = kvs[s] == my_qid;
+                        if (!vis) sacc[mb][r] = -INFINITY;
+                    }
+                }
+            }
+            // ---- online softmax (log2 domain)
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) mx = fmaxf(mx, sacc[mb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx * kLog2e);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float corr = exp2_fast(m_run - m_use);
+            float rs = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const float p = exp2_fast(__builtin_fmaf(sacc[mb][r], kLog2e, -m_use));
+                    sacc[mb][r] = p;
+                    rs += p;
+                }
+            rs += __shfl_xor(rs, 32);
+            l_run = l_run * corr + rs;
+            m_run = m_new;
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
+
+            // ---- O^T += V^T P^T
+            const int gi = lane & 15, hh = (lane >> 4) & 1;
+#pragma unroll
+            for (int kk = 0; kk < PK; kk++) {
+                bf16x8 pf;
+#pragma unroll
+                for (int e = 0; e < 8; e++) pf[e] = (__bf16)sacc[kk >> 1][8 * (kk & 1) + e];
+#pragma unroll
+                for (int hb = 0; hb < HB; hb++) {
+                    const int hcol = 32 * hb + 16 * hh + 4 * (gi & 3);
+                    const int ch = hcol >> 3, within = hcol & 7;
+                    const int r0 = 16 * kk + 4 * c + (gi >> 2);
+                    const int r1 = r0 + 8;
+                    const s16x4 lo = lds_read_tr16(sv + r0 * H + ((ch ^ swz<CPR>(r0)) << 3) + within);
+                    const s16x4 hi = lds_read_tr16(sv + r1 * H + ((ch ^ swz<CPR>(r1)) << 3) + within);
+                    oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf, oacc[hb]);
+                }
+            }
+        }
+        j = jn;
+    }
+
+    // ---- finalize: O = acc / l in bf16, lse = ln(sum exp(logits))
+    if (q_valid) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        __bf16 *orow = a.o + qrow_off;
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                bf16x4 val;
+#pragma unroll
+                for (int e = 0; e < 4; e++) val[e] = (__bf16)(oacc[hb][4 * q4 + e] * inv);
+                *(bf16x4 *)(orow + 32 * hb + 8 * q4 + 4 * c) = val;
+            }
+        if (c == 0 && a.lse)
+            a.lse[(bk * a.G + g) * (size_t)T + t] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    }
+}
+
+template <int H, int BKV, int NW>
+static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
+    const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks);
+    hipLaunchKernelGGL((attn_fwd_kernel<H, BKV, NW>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+FwdConfig fwd_config(int G, int T, int H) {
+    // 32 query rows per wave. H <= 128: 8 waves (2 per SIMD, <= 256 registers
+    // each). H = 256: the O^T carry alone is 128 registers per lane, so 4 waves
+    // (1 per SIMD, up to 512 registers). gw query heads (the largest divisor of
+    // G that is <= the wave count) share each K/V tile.
+    FwdConfig cfg;
+    cfg.nw = (H == 256) ? 4 : 8;
+    cfg.bkv = (H == 256) ? 32 : 64;
+    int gw = 1;
+    for (int d = 1; d <= cfg.nw && d <= G; d++)
+        if (G % d == 0) gw = d;
+    cfg.gw = gw;
+    cfg.bq = 32 * (cfg.nw / gw);
+    (void)T;
+    return cfg;
+}
+
+hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
+    switch (H) {
+        case 64: return launch_fwd_t<64, 64, 8>(a, stream);
+        case 128: return launch_fwd_t<128, 64, 8>(a, stream);
+        case 256: return launch_fwd_t<256, 32, 4>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gqa

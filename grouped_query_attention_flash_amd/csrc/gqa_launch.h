@@ -1,0 +1,42 @@
+// Host-visible kernel argument blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+struct FwdArgs {
+    const __bf16 *q, *k, *v;
+    __bf16 *o;
+    float *lse;                      // may be null
+    const int32_t *q_seg, *kv_seg;   // both null or both set
+    int B, K, G, T, S;
+    int causal;
+    int gw;         // query heads per workgroup (divides G)
+    int bq;         // queries per workgroup; gw * bq is a multiple of 32
+    int n_gsplit;   // G / gw
+    int n_qblocks;  // ceil(T / bq)
+};
+
+struct FwdConfig {
+    int nw, gw, bq, bkv;
+};
+
+// Tile configuration for a shape (pure host function).
+FwdConfig fwd_config(int G, int T, int H);
+hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream);
+
+struct BwdArgs {
+    const __bf16 *q, *k, *v, *o, *dout;
+    const float *lse;
+    float *dq, *dk, *dv;
+    float *delta;                    // workspace: D = rowsum(dO * O), [B,K,G,T]
+    const int32_t *q_seg, *kv_seg;
+    int B, K, G, T, S;
+    int causal;
+};
+
+hipError_t launch_bwd(const BwdArgs &a, int H, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,124 @@
+/*
+ * gqa_attn.h -- C ABI of the fused grouped-query flash-attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Notation follows danielwatson6.github.io/fa, section "Notation":
+ *   B batch, T queries, S keys/values, K kv heads, G query heads per kv head,
+ *   H head dimension.
+ * Layouts (row-major, contiguous, H innermost):
+ *   q, o, dO, dq : [B, K, G, T, H]   (query head k*G + g reads kv head k)
+ *   k, v, dk, dv : [B, K, S, H]
+ *   lse          : [B, K, G, T] fp32
+ *   q_seg        : [B, T] int32,  kv_seg : [B, S] int32
+ *
+ * What is computed (same page, attn_naive in "What is wrong with naive
+ * attention?", and the fused kernel of "Optimizing the kernel"):
+ *   O[t,:] = sum_s softmax_s(q[t,:].k[s,:] + mask[t,s]) v[s,:]
+ * with no further scaling: q must arrive pre-multiplied by H^-1/2.
+ * bf16 inputs, fp32 accumulation, bf16 output (the page's kernel writes its
+ * output in the input dtype). The T x S weights are never stored.
+ * Masks are generated lazily, never materialised:
+ *   causal (apple/axlearn PR 845, lazy causal mask): key s visible to query t
+ *     iff s <= t (top-left aligned when T != S);
+ *   segments (fjformer Pallas flash-attention docs, SegmentIds): key s visible
+ *     to query t iff q_seg[b,t] == kv_seg[b,s]; combined with causal by AND.
+ * A query row that sees no key gets O = 0 and lse = -inf.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or retains them. It holds no state.
+ *   - Tensor pointers must be 16-byte aligned (128-bit loads); int32 segment
+ *     arrays 4-byte aligned.
+ *   - Arguments are validated on the host BEFORE anything is enqueued; on a
+ *     nonzero return nothing has been launched and no output is written.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL =
+ *     the default stream) without any host synchronisation.
+ *   - Returns 0 on success or a positive GQA_ATTN_ERR_* code.
+ *   - Thread-safe: concurrent calls on different streams are independent.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    GQA_ATTN_OK = 0,
+    GQA_ATTN_ERR_NULL = 1,      /* a required pointer is NULL                    */
+    GQA_ATTN_ERR_SHAPE = 2,     /* B,K,G,T,S < 1, or a tensor too large (>2^31 elements per (b,k) slice) */
+    GQA_ATTN_ERR_HEADDIM = 3,   /* H not in {64, 128, 256}                       */
+    GQA_ATTN_ERR_ALIGN = 4,     /* a pointer is not 16-byte (4 for ids) aligned  */
+    GQA_ATTN_ERR_SEGMENTS = 5,  /* exactly one of q_seg / kv_seg given           */
+    GQA_ATTN_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required       */
+    GQA_ATTN_ERR_HIP = 7        /* a HIP launch failed: see gqa_attn_last_hip_error */
+};
+
+/* Forward pass (danielwatson6.github.io/fa, "Optimizing the kernel": the fused
+ * two-axis kernel with the output carry kept on chip; its running max and sum
+ * follow the numerically stable scan of "Chunked attention").
+ *   q        bf16 [B,K,G,T,H], pre-scaled by H^-1/2
+ *   k, v     bf16 [B,K,S,H]
+ *   o        bf16 [B,K,G,T,H]  (written)
+ *   lse      fp32 [B,K,G,T]    (written: natural-log logsumexp of each row's
+ *            visible logits, the residual the backward needs), or NULL
+ *   q_seg    int32 [B,T] and kv_seg int32 [B,S]: both or neither (NULL)
+ *   causal   0 or 1
+ * Errors: NULL q/k/v/o -> ERR_NULL; bad sizes -> ERR_SHAPE; H -> ERR_HEADDIM;
+ * alignment -> ERR_ALIGN; one segment array -> ERR_SEGMENTS; launch -> ERR_HIP. */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             const int32_t *q_seg, const int32_t *kv_seg,
+             int B, int K, int G, int T, int S, int H, int causal, void *stream);
+
+/* Host-only validation of attn_fwd's arguments (pointer values are checked for
+ * NULL and alignment but never dereferenced). Same return codes. */
+int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal);
+
+/* Bytes of device workspace attn_bwd needs for these sizes (the per-row
+ * D = rowsum(dO * O) vector, fp32 [B,K,G,T], rounded up to 256 bytes).
+ * Returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int K, int G, int T, int S, int H);
+
+/* Backward pass: gradients of sum(O * dO) with respect to the pre-scaled q,
+ * and k, v. The weights are recomputed from the saved lse (the role splash
+ * attention's save_residuals plays on the danielwatson6.github.io/fa page);
+ * dK/dV and dQ are computed by separate kernels, as the separate *_dkv and
+ * *_dq block sizes of the fjformer BlockSizes dataclass suggest.
+ *   q, k, v, o, dO   bf16, layouts above; o and lse from attn_fwd on the
+ *                    same inputs
+ *   lse              fp32 [B,K,G,T] (required)
+ *   dq               fp32 [B,K,G,T,H] (written)
+ *   dk, dv           fp32 [B,K,S,H]   (written; summed over the G query heads)
+ *   workspace        device buffer of at least attn_bwd_workspace_bytes(),
+ *                    16-byte aligned, owned by the caller, contents ignored
+ * Errors as attn_fwd, plus ERR_NULL for lse/dO/dq/dk/dv and ERR_WORKSPACE. */
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dO, float *dq, float *dk, float *dv,
+             const int32_t *q_seg, const int32_t *kv_seg,
+             int B, int K, int G, int T, int S, int H, int causal,
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only validation of attn_bwd's arguments. Same return codes. */
+int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dO, const float *dq, const float *dk, const float *dv,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal,
+                   const void *workspace, size_t workspace_bytes);
+
+/* Static, NUL-terminated description of a return code. Never NULL. */
+const char *attn_strerror(int code);
+
+/* The hipError_t behind the calling thread's most recent GQA_ATTN_ERR_HIP
+ * (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

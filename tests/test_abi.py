@@ -1,0 +1,99 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+declared in include/gqa_attn.h, and its host-side validation returns the
+documented codes. No compute entry point is called here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_query_attention_flash_amd as gqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+A16 = 0x10000  # a fake, 16-byte aligned, never dereferenced address
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", src)))
+
+
+def test_header_declarations_match_binding_list():
+    assert declared_functions() == sorted(gqa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gqa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def check_fwd(q=A16, k=A16, v=A16, o=A16, lse=None, qs=None, ks=None,
+              B=1, K=1, G=4, T=64, S=64, H=128, causal=1):
+    P = ctypes.c_void_p
+    return gqa.load_library().attn_check_fwd(P(q), P(k), P(v), P(o), P(lse), P(qs), P(ks),
+                                             B, K, G, T, S, H, causal)
+
+
+def check_bwd(ws=A16, wsb=None, B=1, K=1, G=4, T=64, S=64, H=128, dq=A16, lse=A16, qs=None, ks=None, o=A16):
+    P = ctypes.c_void_p
+    if wsb is None:
+        wsb = gqa.attn_bwd_workspace_bytes(B, K, G, T, S, H)
+    return gqa.load_library().attn_check_bwd(P(A16), P(A16), P(A16), P(o), P(lse), P(A16), P(dq), P(A16),
+                                             P(A16), P(qs), P(ks), B, K, G, T, S, H, 1, P(ws), wsb)
+
+
+def test_check_fwd_codes():
+    assert check_fwd() == gqa.GQA_ATTN_OK
+    assert check_fwd(lse=A16, qs=A16, ks=A16) == gqa.GQA_ATTN_OK
+    assert check_fwd(q=None) == gqa.GQA_ATTN_ERR_NULL
+    assert check_fwd(o=None) == gqa.GQA_ATTN_ERR_NULL
+    for bad in (dict(B=0), dict(K=0), dict(G=0), dict(T=0), dict(S=-1)):
+        assert check_fwd(**bad) == gqa.GQA_ATTN_ERR_SHAPE, bad
+    assert check_fwd(G=1 << 12, T=1 << 20) == gqa.GQA_ATTN_ERR_SHAPE  # slice >= 2^31 elements
+    for h in (0, 32, 96, 129, 512):
+        assert check_fwd(H=h) == gqa.GQA_ATTN_ERR_HEADDIM, h
+    for h in (64, 128, 256):
+        assert check_fwd(H=h) == gqa.GQA_ATTN_OK
+    assert check_fwd(qs=A16) == gqa.GQA_ATTN_ERR_SEGMENTS
+    assert check_fwd(ks=A16) == gqa.GQA_ATTN_ERR_SEGMENTS
+    assert check_fwd(q=A16 + 8) == gqa.GQA_ATTN_ERR_ALIGN
+    assert check_fwd(v=A16 + 2) == gqa.GQA_ATTN_ERR_ALIGN
+    assert check_fwd(qs=A16 + 2, ks=A16) == gqa.GQA_ATTN_ERR_ALIGN
+    assert check_fwd(qs=A16 + 4, ks=A16 + 4) == gqa.GQA_ATTN_OK
+    # ragged sizes are accepted
+    assert check_fwd(T=77, S=1031) == gqa.GQA_ATTN_OK
+
+
+def test_check_bwd_codes_and_workspace():
+    assert gqa.attn_bwd_workspace_bytes(1, 8, 4, 8192, 8192, 128) == 4 * 8 * 4 * 8192
+    assert gqa.attn_bwd_workspace_bytes(1, 1, 1, 3, 3, 128) == 256
+    assert gqa.attn_bwd_workspace_bytes(0, 1, 1, 3, 3, 128) == 0
+    assert check_bwd() == gqa.GQA_ATTN_OK
+    assert check_bwd(lse=None) == gqa.GQA_ATTN_ERR_NULL
+    assert check_bwd(dq=None) == gqa.GQA_ATTN_ERR_NULL
+    assert check_bwd(ws=None) == gqa.GQA_ATTN_ERR_WORKSPACE
+    assert check_bwd(wsb=16) == gqa.GQA_ATTN_ERR_WORKSPACE
+    assert check_bwd(ws=A16 + 4) == gqa.GQA_ATTN_ERR_ALIGN
+    assert check_bwd(H=96) == gqa.GQA_ATTN_ERR_HEADDIM
+    assert check_bwd(qs=A16) == gqa.GQA_ATTN_ERR_SEGMENTS
+
+
+def test_strerror_and_hip_error():
+    for code in range(0, 8):
+        s = gqa.attn_strerror(code)
+        assert s and s != "unknown error code"
+    assert gqa.attn_strerror(99) == "unknown error code"
+    assert gqa.attn_last_hip_error() == 0
+
+
+def test_python_binding_rejects_before_calling():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gqa.attn_fwd(q, k, k)  # CPU tensors are refused; nothing is launched
