@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GQA flash-attention forward on one MI355X.
+
+Workload: causal grouped-query attention forward, B=1, K=8 kv heads, G=4
+(32 query heads), T=S=8192, H=128, bf16 inputs ~ N(0,1) (q pre-scaled by
+H^-1/2), synthetic and seeded. One step = one attn_fwd call over the whole
+batch; inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line. `value` is forward TFLOP/s with causal FLOPs counted
+as the executed half, 4*B*K*G*T*S*H/2. `roofline` compares the forward
+kernel's average launch time (HIP events on the launch stream) with the
+MI355X dense bf16 MFMA peak; `cpu_baseline` times the CPU oracle on a
+bounded random sample of the same workload's query rows on the host cores.
+A second leg times the backward (dQ, dK, dV from the saved lse) on the same
+tensors and reports it under "backward".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_BF16_DENSE_TFLOPS = 2500.0   # published dense bf16 MFMA peak
+MI355X_HBM_GBPS = 8000.0            # published HBM3E bandwidth
+METRIC = "attention TFLOP/s (fwd, causal) at 1 GPU; % of bf16 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_b1_k8_g4_t8192_h128_traffic.json")
+FWD_SOURCES = ["grouped_query_attention_flash_amd/csrc/attn_fwd.hip",
+               "grouped_query_attention_flash_amd/csrc/gqa_device.h"]
+
+
+def kernel_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    missing or taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_digest") != kernel_digest(FWD_SOURCES):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per launch
+
+
+def cpu_baseline(inp, w, o_gpu, target_s=12.0):
+    """Time the fp64 oracle on random query rows of the workload (host cores)."""
+    import numpy as np
+    import oracle
+    from workloads import attention_flops
+
+    threads = oracle.max_threads()
+    rng = np.random.default_rng(12345)
+    total_rows = w.B * w.K * w.G * w.T
+    # calibrate on a small sample, then size the timed sample to ~target_s
+    n = 2048
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t0 = time.perf_counter()
+    oracle.fwd(inp["q"], inp["k"], inp["v"], causal=w.causal, rows=rows)
+    per_row = (time.perf_counter() - t0) / n
+    n = int(min(total_rows, max(n, target_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t0 = time.perf_counter()
+    ref_o, _ = oracle.fwd(inp["q"], inp["k"], inp["v"], causal=w.causal, rows=rows)
+    elapsed = time.perf_counter() - t0
+    t = rows % w.T
+    visible = (t + 1) if w.causal else np.full_like(t, w.S)
+    flops = float(4.0 * w.H * visible.sum())
+    got = o_gpu.reshape(-1, w.H)[rows].float().cpu().numpy()
+    err = float(np.abs(got - ref_o).max())
+    rel = float(np.linalg.norm(got - ref_o) / np.linalg.norm(ref_o))
+    full = attention_flops(w.B, w.K, w.G, w.T, w.S, w.H, w.causal)
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d random query rows of the workload (%.3g of its FLOPs), fp64 oracle, %.1f s" % (
+            n, flops / full, elapsed),
+        "sample_max_abs_vs_gpu": err,
+        "sample_rel_l2_vs_gpu": rel,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (--gpus %d refused)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import grouped_query_attention_flash_amd as gqa
+    from workloads import HEADLINE, attention_flops, make_qkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = HEADLINE
+    q, k, v, do = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=True)
+    inp_cpu = {"q": q, "k": k, "v": v}
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o = torch.empty_like(qd)
+    lse = torch.empty(w.B, w.K, w.G, w.T, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        gqa.attn_fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse)
+
+    ms = time_launches(step, args.steps, args.warmup)
+    flops = attention_flops(w.B, w.K, w.G, w.T, w.S, w.H, w.causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    fwd_bytes = 2 * (qd.numel() + kd.numel() + vd.numel() + o.numel()) + 4 * lse.numel()
+
+    result = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, q pre-scaled by H^-1/2)",
+        "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
+                   "causal": w.causal, "mask": "lazy causal"},
+        "pct_of_peak": 100.0 * tflops / MI355X_BF16_DENSE_TFLOPS,
+        "roofline": {
+            "kernel": "attn_fwd_kernel<128,64,8>",
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MI355X_BF16_DENSE_TFLOPS,
+            "traffic": measured_traffic(),
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_hbm_bytes_per_launch": fwd_bytes,
+        },
+    }
+
+    if not args.no_backward:
+        ws = torch.empty(gqa.attn_bwd_workspace_bytes(w.B, w.K, w.G, w.T, w.S, w.H), dtype=torch.uint8, device=dev)
+        dq = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(kd.shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(vd.shape, dtype=torch.float32, device=dev)
+        step()
+
+        def bstep():
+            gqa.attn_bwd(qd, kd, vd, o, lse, dod, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+        try:
+            bms = time_launches(bstep, max(5, args.steps // 2), max(2, args.warmup // 2))
+            bflops = 2.5 * flops
+            result["backward"] = {"ms": bms, "tflops": bflops / (bms * 1e-3) / 1e12,
+                                  "flops_convention": "2.5x forward (5 matmuls per visible pair)",
+                                  "fwd_plus_bwd_tflops": 3.5 * flops / ((ms + bms) * 1e-3) / 1e12}
+        except gqa.GqaAttnError as e:
+            result["backward"] = {"error": str(e)}
+
+    if not args.no_cpu_baseline:
+        step()
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline(inp_cpu, w, o, target_s=12.0)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
