@@ -150,10 +150,14 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              kv_seg: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
              dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None):
-    """Backward pass on the current stream. Returns (dq, dk, dv) in fp32."""
+    """Backward pass on the current stream. Returns (dq, dk, dv) in fp32.
+
+    `o` (the forward output) may be None: the library does not read it."""
     B, K, G, T, S, H = _dims(q, k)
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
         _check_tensor(name, t, torch.bfloat16)
+    if o is not None:
+        _check_tensor("o", o, torch.bfloat16, q.shape)
     _check_tensor("lse", lse, torch.float32, (B, K, G, T))
     if (q_seg is None) != (kv_seg is None):
         raise GqaAttnError(GQA_ATTN_ERR_SEGMENTS, "attn_bwd")

@@ -86,9 +86,10 @@ int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, c
                    int B, int K, int G, int T, int S, int H, int causal,
                    const void *workspace, size_t workspace_bytes) {
     (void)causal;
-    int rc = check_common(q, k, v, o, q_seg, kv_seg, B, K, G, T, S, H);
+    int rc = check_common(q, k, v, dq, q_seg, kv_seg, B, K, G, T, S, H);
     if (rc) return rc;
     if (!lse || !dO || !dq || !dk || !dv) return GQA_ATTN_ERR_NULL;
+    if (o && !aligned(o, 16)) return GQA_ATTN_ERR_ALIGN;
     if (!aligned(lse, 16) || !aligned(dO, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
         return GQA_ATTN_ERR_ALIGN;
     if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, K, G, T, S, H)) return GQA_ATTN_ERR_WORKSPACE;

@@ -1,13 +1,558 @@
-// Backward pass kernels (gfx950). Placeholder until the kernels land.
+// Fused grouped-query flash attention, backward pass, for gfx950 (MI355X).
+//
+// The pages give no backward math; this is the standard calculus of softmax
+// attention, recomputing the weights from the forward's saved logsumexp
+// (the residual that splash attention's save_residuals option keeps,
+// danielwatson6.github.io/fa, "Our first kernel"), split into a dK/dV
+// kernel and a dQ kernel as the separate *_dkv and *_dq block sizes of the
+// fjformer BlockSizes dataclass do:
+//   P  = exp(S - lse),  S = q.k (no scale)
+//   dP = dO V^T,  D = rowsum(P * dP)                          (bwd_dq<DELTA>)
+//   dS = P * (dP - D)
+//   dV = sum_{g,t} P^T dO,  dK = sum_{g,t} dS^T Q             (bwd_dkv)
+//   dQ = dS K                                                 (bwd_dq)
+// All contractions run on the 32x32x16 bf16 MFMA with fp32 accumulation;
+// P and dS are rounded to bf16 as MFMA operands, except that dS enters the
+// dQ product as a bf16 hi + lo pair. Gradients are written in fp32. The G-sum of dK/dV stays inside one workgroup: no atomics, and the
+// result is deterministic.
+//
+// D equals rowsum(dO * O) in exact arithmetic, but the forward's O carries
+// the rounding of P to bf16 in its PV product; D taken from it moves dQ by
+// up to ~1e-1 on early causal rows (where |dS| ~ 10). D is therefore summed
+// in fp32 from the recomputed weights, in a pass of its own over K and V.
+#include "gqa_device.h"
 #include "gqa_launch.h"
+
+#include <climits>
+#include <cmath>
 
 namespace gqa {
 
+// ---------------------------------------------------------------------------
+// dK, dV. One workgroup per (b, kv head, block of 32*NW keys); wave w owns
+// keys [s0 + 32w, s0 + 32w + 32). The workgroup walks every query head g
+// and every query tile of BQ = 32 rows that can see its keys; Q, dO, lse
+// and D of the tile are staged in LDS and shared by the waves.
+//
+// Per wave and query tile (M = queries, N = the wave's 32 keys):
+//   S  = Q K^T    A: Q rows (LDS)         B: K^T (registers)
+//   dP = dO V^T   A: dO rows (LDS)        B: V^T (registers)
+//   lane (n, c) holds key n and the 16 queries acc_row(r, c) of S, P, dP, dS
+//   dV^T += dO^T P   A: dO^T (LDS transpose read)   B: P  (registers, bf16)
+//   dK^T += Q^T dS   A: Q^T  (LDS transpose read)   B: dS (registers, bf16)
+template <int H, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_kblocks) {
+    constexpr int BQ = 32;
+    constexpr int CPR = H / 8;
+    constexpr int KSTEPS = H / 16;
+    constexpr int HB = H / 32;
+    constexpr int NT = NW * 64;
+    constexpr int TILE_CHUNKS = BQ * CPR;                 // per tensor (Q or dO)
+    constexpr int LOADS = (2 * TILE_CHUNKS + NT - 1) / NT;
+
+    __shared__ __attribute__((aligned(16))) __bf16 sq[BQ * H];
+    __shared__ __attribute__((aligned(16))) __bf16 sdo[BQ * H];
+    __shared__ __attribute__((aligned(16))) float slse[BQ];  // lse * log2(e); +inf for empty rows
+    __shared__ __attribute__((aligned(16))) float sdel[BQ];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, c = lane >> 5;
+    const int T = a.T, S = a.S, G = a.G;
+
+    // heaviest first: with causal masking the first key blocks see the most queries
+    const int units = a.B * a.K;
+    const int kb_idx = blockIdx.x / units;
+    const int u = blockIdx.x % units;
+    const int kh = u % a.K, b = u / a.K;
+    const int s0_wg = kb_idx * 32 * NW;
+    const int s_w = s0_wg + 32 * wave;      // first key of this wave
+    const int s = s_w + n;                   // this lane's key
+    const bool k_valid = s < S;
+    const bool wave_active = s_w < S;
+    const size_t bk = (size_t)b * a.K + kh;
+
+    // K^T and V^T operands (B operands): lane (n, c), k-step ks holds row s, h = 16ks + 8c .. +7
+    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    {
+        const __bf16 *krow = a.k + (bk * S + s) * H;
+        const __bf16 *vrow = a.v + (bk * S + s) * H;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            kf[ks] = k_valid ? *(const bf16x8 *)(krow + 16 * ks + 8 * c) : bf16x8{};
+            vf[ks] = k_valid ? *(const bf16x8 *)(vrow + 16 * ks + 8 * c) : bf16x8{};
+        }
+    }
+
+    const bool segs = a.q_seg != nullptr;
+    const int32_t *qsb = segs ? a.q_seg + (size_t)b * T : nullptr;
+    int my_kid = 0, wg_kmin = INT_MAX, wg_kmax = INT_MIN, w_kmin = INT_MAX, w_kmax = INT_MIN;
+    if (segs) {
+        const int32_t *kvs = a.kv_seg + (size_t)b * S;
+        int lo = INT_MAX, hi = INT_MIN;
+        for (int i = lane; i < 32 * NW; i += 64) {
+            if (s0_wg + i < S) {
+                const int id = kvs[s0_wg + i];
+                lo = min(lo, id);
+                hi = max(hi, id);
+            }
+        }
+        wg_kmin = wave_min_i(lo);
+        wg_kmax = wave_max_i(hi);
+        my_kid = k_valid ? kvs[s] : 0;
+        w_kmin = wave_min_i(k_valid ? my_kid : INT_MAX);
+        w_kmax = wave_max_i(k_valid ? my_kid : INT_MIN);
+    }
+
+    // query tiles: causal -> only tiles holding some t >= s0_wg
+    const int n_qt = (T + BQ - 1) / BQ;
+    const int qt_begin = a.causal ? min(n_qt, s0_wg / BQ) : 0;
+    const int n_steps = G * (n_qt - qt_begin);  // (g, query tile) pairs, g outer
+
+    auto q_ids = [&](int qt, int &qmin, int &qmax) {
+        const int t = qt * BQ + lane;
+        const bool ok = lane < BQ && t < T;
+        const int id = ok ? qsb[t] : 0;
+        qmin = wave_min_i(ok ? id : INT_MAX);
+        qmax = wave_max_i(ok ? id : INT_MIN);
+    };
+    auto next_step = [&](int st) {
+        if (!segs) return st;
+        for (; st < n_steps; st++) {
+            int qmin, qmax;
+            q_ids(qt_begin + st % (n_qt - qt_begin), qmin, qmax);
+            if (!(qmax < wg_kmin || qmin > wg_kmax)) break;
+        }
+        return st;
+    };
+
+    i32x4 pre[LOADS];
+    float pre_lse = 0.f, pre_del = 0.f;
+    auto load_step = [&](int st) {
+        const int g = st / (n_qt - qt_begin);
+        const int t0 = (qt_begin + st % (n_qt - qt_begin)) * BQ;
+        const size_t rowbase = (bk * G + g) * (size_t)T;
+#pragma unroll
+        for (int i = 0; i < LOADS; i++) {
+            const int ci = tid + i * NT;
+            if (ci < 2 * TILE_CHUNKS) {
+                const int tensor = ci / TILE_CHUNKS;
+                const int cc = ci % TILE_CHUNKS;
+                const int r = cc / CPR, ch = cc % CPR;
+                const int t = t0 + r;
+                const __bf16 *src = (tensor ? a.dout : a.q) + (rowbase + t) * H + ch * 8;
+                pre[i] = t < T ? *(const i32x4 *)src : i32x4{0, 0, 0, 0};
+            }
+        }
+        if (tid < BQ) {
+            const int t = t0 + tid;
+            float l = INFINITY, d = 0.f;
+            if (t < T) {
+                l = a.lse[rowbase + t];
+                l = (l == -INFINITY) ? INFINITY : l * kLog2e;  // empty row: every P is 0
+                d = a.delta[rowbase + t];
+            }
+            pre_lse = l;
+            pre_del = d;
+        }
+    };
+    auto store_step = [&]() {
+#pragma unroll
+        for (int i = 0; i < LOADS; i++) {
+            const int ci = tid + i * NT;
+            if (ci < 2 * TILE_CHUNKS) {
+                const int tensor = ci / TILE_CHUNKS;
+                const int cc = ci % TILE_CHUNKS;
+                const int r = cc / CPR, ch = cc % CPR;
+                *(i32x4 *)((tensor ? sdo : sq) + r * H + ((ch ^ swz<CPR>(r)) << 3)) = pre[i];
+            }
+        }
+        if (tid < BQ) {
+            slse[tid] = pre_lse;
+            sdel[tid] = pre_del;
+        }
+    };
+
+    f32x16 dv_acc[HB], dk_acc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++) {
+        dv_acc[hb] = f32x16{};
+        dk_acc[hb] = f32x16{};
+    }
+
+    int st = next_step(0);
+    if (st < n_steps) load_step(st);
+    while (st < n_steps) {
+        __syncthreads();
+        store_step();
+        __syncthreads();
+        const int st_next = next_step(st + 1);
+        if (st_next < n_steps) load_step(st_next);
+
+        const int t0 = (qt_begin + st % (n_qt - qt_begin)) * BQ;
+        bool run = wave_active && !(a.causal && t0 + BQ - 1 < s_w);
+        bool seg_mask = false;
+        if (run && segs) {
+            int qmin, qmax;
+            q_ids(t0 / BQ, qmin, qmax);
+            if (qmax < w_kmin || qmin > w_kmax) run = false;
+            seg_mask = !(w_kmin == w_kmax && qmin == qmax && qmin == w_kmin);
+        }
+        if (run) {
+            // S = Q K^T and dP = dO V^T, both 32 queries x 32 keys
+            f32x16 sacc = f32x16{}, pacc = f32x16{};
+            {
+                const __bf16 *qrow = sq + n * H;
+                const __bf16 *drow = sdo + n * H;
+                const int sw = swz<CPR>(n);
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ks++) {
+                    const int off = ((2 * ks + c) ^ sw) << 3;
+                    sacc = mfma32x32x16(*(const bf16x8 *)(qrow + off), kf[ks], sacc);
+                    pacc = mfma32x32x16(*(const bf16x8 *)(drow + off), vf[ks], pacc);
+                }
+            }
+            const bool need_mask = (a.causal && s_w + 31 > t0) || (s_w + 32 > S) || (t0 + BQ > T) || seg_mask;
+            // P = exp2(S log2e - lse log2e); dS = P (dP - D)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                const int r0 = 8 * q4 + 4 * c;  // queries r0 .. r0+3 of the tile
+                const f32x4 l4 = *(const f32x4 *)(slse + r0);
+                const f32x4 d4 = *(const f32x4 *)(sdel + r0);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = 4 * q4 + e;
+                    float x = sacc[r];
+                    if (need_mask) {
+                        const int t = t0 + r0 + e;
+                        bool vis = k_valid && t < T && !(a.causal && s > t);
+                        if (segs && vis) vis = qsb[t] == my_kid;
+                        if (!vis) x = -INFINITY;
+                    }
+                    const float p = exp2_fast(__builtin_fmaf(x, kLog2e, -l4[e]));
+                    sacc[r] = p;
+                    pacc[r] = p * (pacc[r] - d4[e]);
+                }
+            }
+            // dV^T += dO^T P ; dK^T += Q^T dS   (k = queries, 2 k-steps of 16)
+            const int gi = lane & 15, hh = (lane >> 4) & 1;
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++) {
+                bf16x8 pf, sf;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    pf[e] = (__bf16)sacc[8 * kk + e];
+                    sf[e] = (__bf16)pacc[8 * kk + e];
+                }
+                const int r0 = 16 * kk + 4 * c + (gi >> 2);
+                const int r1 = r0 + 8;
+                const int sw0 = swz<CPR>(r0), sw1 = swz<CPR>(r1);
+#pragma unroll
+                for (int hb = 0; hb < HB; hb++) {
+                    const int hcol = 32 * hb + 16 * hh + 4 * (gi & 3);
+                    const int ch = hcol >> 3, within = hcol & 7;
+                    const int o0 = r0 * H + ((ch ^ sw0) << 3) + within;
+                    const int o1 = r1 * H + ((ch ^ sw1) << 3) + within;
+                    const bf16x8 dot = join_bf16x8(lds_read_tr16(sdo + o0), lds_read_tr16(sdo + o1));
+                    dv_acc[hb] = mfma32x32x16(dot, pf, dv_acc[hb]);
+                    const bf16x8 qt = join_bf16x8(lds_read_tr16(sq + o0), lds_read_tr16(sq + o1));
+                    dk_acc[hb] = mfma32x32x16(qt, sf, dk_acc[hb]);
+                }
+            }
+        }
+        st = st_next;
+    }
+
+    // dK, dV rows (fp32): lane (n, c) holds h = 32hb + acc_row(r, c) of key s
+    if (k_valid) {
+        float *dkrow = a.dk + (bk * S + s) * H;
+        float *dvrow = a.dv + (bk * S + s) * H;
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                const int h = 32 * hb + 8 * q4 + 4 * c;
+                *(f32x4 *)(dkrow + h) = f32x4{dk_acc[hb][4 * q4], dk_acc[hb][4 * q4 + 1], dk_acc[hb][4 * q4 + 2],
+                                              dk_acc[hb][4 * q4 + 3]};
+                *(f32x4 *)(dvrow + h) = f32x4{dv_acc[hb][4 * q4], dv_acc[hb][4 * q4 + 1], dv_acc[hb][4 * q4 + 2],
+                                              dv_acc[hb][4 * q4 + 3]};
+            }
+    }
+    (void)n_kblocks;
+}
+
+// ---------------------------------------------------------------------------
+// dQ. Same decomposition as the forward: one workgroup per (b, kv head,
+// gw heads, bq queries), 32 query rows per wave, K/V tiles in LDS.
+// Per wave and key tile (M = keys, N = the wave's 32 queries):
+//   S^T  = K Q^T    A: K rows (LDS)    B: Q^T (registers)
+//   dP^T = V dO^T   A: V rows (LDS)    B: dO^T (registers)
+//   lane (n, c) holds query n: lse and D are one value per lane
+//   dQ^T += K^T dS^T   A: K^T (LDS transpose read)   B: dS^T (registers, bf16)
+//
+// With DELTA set the kernel only computes D = rowsum(P * dP) in fp32 (the
+// S^T and dP^T products and the weights) and writes it to the workspace.
+template <int H, int BKV, int NW, bool DELTA>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
+                                                              int n_qblocks) {
+    constexpr int CPR = H / 8;
+    constexpr int KSTEPS = H / 16;
+    constexpr int MB = BKV / 32;
+    constexpr int HB = H / 32;
+    constexpr int PK = BKV / 16;
+    constexpr int NT = NW * 64;
+    constexpr int TILE_CHUNKS = BKV * CPR;
+    static_assert(TILE_CHUNKS % NT == 0, "K and V loads must not share a step");
+    constexpr int LOADS = 2 * TILE_CHUNKS / NT;
+
+    __shared__ __attribute__((aligned(16))) __bf16 sk[BKV * H];
+    __shared__ __attribute__((aligned(16))) __bf16 sv[BKV * H];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, c = lane >> 5;
+    const int T = a.T, S = a.S;
+
+    const int units = a.B * a.K * n_gsplit;
+    int qb = blockIdx.x / units;
+    if (a.causal) qb = n_qblocks - 1 - qb;
+    const int u = blockIdx.x % units;
+    const int gs = u % n_gsplit;
+    const int kh = (u / n_gsplit) % a.K;
+    const int b = u / (n_gsplit * a.K);
+    const int t0 = qb * bq;
+
+    const int rows_wg = gw * bq;
+    const int rho = wave * 32 + n;
+    const bool row_in_wg = rho < rows_wg;
+    const int g = gs * gw + (row_in_wg ? rho / bq : 0);
+    const int t = t0 + (row_in_wg ? rho % bq : 0);
+    const bool q_valid = row_in_wg && t < T;
+    const bool wave_active = wave * 32 < rows_wg;
+    const int tmin_w = t0 + (bq >= 32 ? (wave * 32) % bq : 0);
+    const int tmax_w = tmin_w + (bq >= 32 ? 31 : bq - 1);
+
+    const size_t bk = (size_t)b * a.K + kh;
+    const size_t row = (bk * a.G + g) * (size_t)T + t;
+
+    bf16x8 qf[KSTEPS], df[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++) {
+        qf[ks] = q_valid ? *(const bf16x8 *)(a.q + row * H + 16 * ks + 8 * c) : bf16x8{};
+        df[ks] = q_valid ? *(const bf16x8 *)(a.dout + row * H + 16 * ks + 8 * c) : bf16x8{};
+    }
+    float lse2 = INFINITY, dlt = 0.f;
+    if (q_valid) {
+        const float l = a.lse[row];
+        lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        if constexpr (!DELTA) dlt = a.delta[row];
+    }
+    float d_acc = 0.f;  // DELTA: running sum of P * dP over this lane's keys
+
+    const __bf16 *kbase = a.k + bk * (size_t)S * H;
+    const __bf16 *vbase = a.v + bk * (size_t)S * H;
+
+    const bool segs = a.q_seg != nullptr;
+    const int32_t *kvs = segs ? a.kv_seg + (size_t)b * S : nullptr;
+    int my_qid = 0, wg_qmin = INT_MAX, wg_qmax = INT_MIN, w_qmin = INT_MAX, w_qmax = INT_MIN;
+    if (segs) {
+        const int32_t *qs = a.q_seg + (size_t)b * T;
+        int lo = INT_MAX, hi = INT_MIN;
+        for (int i = lane; i < bq; i += 64) {
+            if (t0 + i < T) {
+                const int id = qs[t0 + i];
+                lo = min(lo, id);
+                hi = max(hi, id);
+            }
+        }
+        wg_qmin = wave_min_i(lo);
+        wg_qmax = wave_max_i(hi);
+        my_qid = q_valid ? qs[t] : 0;
+        w_qmin = wave_min_i(q_valid ? my_qid : INT_MAX);
+        w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
+    }
+
+    const int n_tiles = (S + BKV - 1) / BKV;
+    int j_end = n_tiles;
+    if (a.causal) j_end = min(j_end, (min(t0 + bq, T) - 1) / BKV + 1);
+
+    auto tile_ids = [&](int j, int &kmin, int &kmax) {
+        const int ss = j * BKV + lane;
+        const bool ok = lane < BKV && ss < S;
+        const int id = ok ? kvs[ss] : 0;
+        kmin = wave_min_i(ok ? id : INT_MAX);
+        kmax = wave_max_i(ok ? id : INT_MIN);
+    };
+    auto next_tile = [&](int j) {
+        if (!segs) return j;
+        for (; j < j_end; j++) {
+            int kmin, kmax;
+            tile_ids(j, kmin, kmax);
+            if (!(kmax < wg_qmin || kmin > wg_qmax)) break;
+        }
+        return j;
+    };
+
+    i32x4 pre[LOADS];
+    auto load_tile = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < LOADS; i++) {
+            const int ci = tid + i * NT;
+            const int tensor = ci / TILE_CHUNKS;
+            const int cc = ci % TILE_CHUNKS;
+            const int r = cc / CPR, ch = cc % CPR;
+            const int ss = j * BKV + r;
+            const __bf16 *src = (tensor ? vbase : kbase) + (size_t)ss * H + ch * 8;
+            pre[i] = ss < S ? *(const i32x4 *)src : i32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < LOADS; i++) {
+            const int ci = tid + i * NT;
+            const int tensor = ci / TILE_CHUNKS;
+            const int cc = ci % TILE_CHUNKS;
+            const int r = cc / CPR, ch = cc % CPR;
+            *(i32x4 *)((tensor ? sv : sk) + r * H + ((ch ^ swz<CPR>(r)) << 3)) = pre[i];
+        }
+    };
+
+    f32x16 dq_acc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++) dq_acc[hb] = f32x16{};
+
+    int j = next_tile(0);
+    if (j < j_end) load_tile(j);
+    while (j < j_end) {
+        __syncthreads();
+        store_tile();
+        __syncthreads();
+        const int jn = next_tile(j + 1);
+        if (jn < j_end) load_tile(jn);
+
+        const int s0 = j * BKV;
+        bool run = wave_active && !(a.causal && s0 > tmax_w);
+        bool seg_mask = false;
+        if (run && segs) {
+            int kmin, kmax;
+            tile_ids(j, kmin, kmax);
+            if (kmax < w_qmin || kmin > w_qmax) run = false;
+            seg_mask = !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
+        }
+        if (run) {
+            f32x16 sacc[MB], pacc[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++) {
+                sacc[mb] = f32x16{};
+                pacc[mb] = f32x16{};
+                const int r = 32 * mb + n;
+                const int sw = swz<CPR>(r);
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ks++) {
+                    const int off = r * H + (((2 * ks + c) ^ sw) << 3);
+                    sacc[mb] = mfma32x32x16(*(const bf16x8 *)(sk + off), qf[ks], sacc[mb]);
+                    pacc[mb] = mfma32x32x16(*(const bf16x8 *)(sv + off), df[ks], pacc[mb]);
+                }
+            }
+            const bool need_mask = (a.causal && s0 + BKV - 1 > tmin_w) || (s0 + BKV > S) || seg_mask;
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    float x = sacc[mb][r];
+                    if (need_mask) {
+                        const int ss = s0 + 32 * mb + acc_row(r, c);
+                        bool vis = ss < S && !(a.causal && ss > t);
+                        if (segs && vis) vis = kvs[ss] == my_qid;
+                        if (!vis) x = -INFINITY;
+                    }
+                    const float p = exp2_fast(__builtin_fmaf(x, kLog2e, -lse2));
+                    if constexpr (DELTA)
+                        d_acc += p * pacc[mb][r];
+                    else
+                        pacc[mb][r] = p * (pacc[mb][r] - dlt);
+                }
+            if constexpr (DELTA) {
+                j = jn;
+                continue;
+            }
+            // dQ^T += K^T dS^T, with dS^T split into bf16 hi + lo parts: early causal rows
+            // have |dS| of order 10, where one bf16 rounding alone costs ~1e-1 in dQ
+            const int gi = lane & 15, hh = (lane >> 4) & 1;
+#pragma unroll
+            for (int kk = 0; kk < PK; kk++) {
+                bf16x8 sf, sf_lo;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float x = pacc[kk >> 1][8 * (kk & 1) + e];
+                    const __bf16 hi = (__bf16)x;
+                    sf[e] = hi;
+                    sf_lo[e] = (__bf16)(x - (float)hi);
+                }
+                const int r0 = 16 * kk + 4 * c + (gi >> 2);
+                const int r1 = r0 + 8;
+                const int sw0 = swz<CPR>(r0), sw1 = swz<CPR>(r1);
+#pragma unroll
+                for (int hb = 0; hb < HB; hb++) {
+                    const int hcol = 32 * hb + 16 * hh + 4 * (gi & 3);
+                    const int ch = hcol >> 3, within = hcol & 7;
+                    const bf16x8 kt = join_bf16x8(lds_read_tr16(sk + r0 * H + ((ch ^ sw0) << 3) + within),
+                                                  lds_read_tr16(sk + r1 * H + ((ch ^ sw1) << 3) + within));
+                    dq_acc[hb] = mfma32x32x16(kt, sf, dq_acc[hb]);
+                    dq_acc[hb] = mfma32x32x16(kt, sf_lo, dq_acc[hb]);
+                }
+            }
+        }
+        j = jn;
+    }
+
+    if constexpr (DELTA) {
+        d_acc += __shfl_xor(d_acc, 32);
+        if (q_valid && c == 0) a.delta[row] = d_acc;
+        return;
+    }
+    if (q_valid) {
+        float *dqrow = a.dq + row * H;
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++)
+                *(f32x4 *)(dqrow + 32 * hb + 8 * q4 + 4 * c) =
+                    f32x4{dq_acc[hb][4 * q4], dq_acc[hb][4 * q4 + 1], dq_acc[hb][4 * q4 + 2], dq_acc[hb][4 * q4 + 3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int H, int NW_DKV, int BKV_DQ, int NW_DQ>
+static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
+    int gw = 1;
+    for (int d = 1; d <= NW_DQ && d <= a.G; d++)
+        if (a.G % d == 0) gw = d;
+    const int bq = 32 * (NW_DQ / gw);
+    const int n_gsplit = a.G / gw;
+    const int n_qblocks = (a.T + bq - 1) / bq;
+    const dim3 qgrid((unsigned)(a.B * a.K * n_gsplit * n_qblocks));
+    // D = rowsum(P * dP), then dQ, then dK / dV (both read D)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<H, BKV_DQ, NW_DQ, true>), qgrid, dim3(NW_DQ * 64), 0, stream, a, gw, bq,
+                       n_gsplit, n_qblocks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<H, BKV_DQ, NW_DQ, false>), qgrid, dim3(NW_DQ * 64), 0, stream, a, gw, bq,
+                       n_gsplit, n_qblocks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int keys_wg = 32 * NW_DKV;
+    const int n_kblocks = (a.S + keys_wg - 1) / keys_wg;
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<H, NW_DKV>), dim3((unsigned)(a.B * a.K * n_kblocks)), dim3(NW_DKV * 64),
+                       0, stream, a, n_kblocks);
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd(const BwdArgs &a, int H, hipStream_t stream) {
-    (void)a;
-    (void)H;
-    (void)stream;
-    return hipErrorNotSupported;
+    switch (H) {
+        case 64: return launch_bwd_t<64, 4, 64, 8>(a, stream);
+        case 128: return launch_bwd_t<128, 4, 32, 8>(a, stream);
+        case 256: return launch_bwd_t<256, 4, 32, 4>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace gqa

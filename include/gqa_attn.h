@@ -80,7 +80,7 @@ int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, c
                    int B, int K, int G, int T, int S, int H, int causal);
 
 /* Bytes of device workspace attn_bwd needs for these sizes (the per-row
- * D = rowsum(dO * O) vector, fp32 [B,K,G,T], rounded up to 256 bytes).
+ * D = sum_s P[t,s] dP[t,s] vector, fp32 [B,K,G,T], rounded up to 256 bytes).
  * Returns 0 for invalid sizes. */
 size_t attn_bwd_workspace_bytes(int B, int K, int G, int T, int S, int H);
 
@@ -89,14 +89,21 @@ size_t attn_bwd_workspace_bytes(int B, int K, int G, int T, int S, int H);
  * attention's save_residuals plays on the danielwatson6.github.io/fa page);
  * dK/dV and dQ are computed by separate kernels, as the separate *_dkv and
  * *_dq block sizes of the fjformer BlockSizes dataclass suggest.
- *   q, k, v, o, dO   bf16, layouts above; o and lse from attn_fwd on the
- *                    same inputs
- *   lse              fp32 [B,K,G,T] (required)
+ *   q, k, v, dO      bf16, layouts above
+ *   o                the forward output, or NULL: it is not read. D =
+ *                    rowsum(dO * O) is instead summed in fp32 as
+ *                    sum_s P dP from the recomputed weights, because the
+ *                    bf16 O carries the forward's bf16 rounding of P and a
+ *                    D taken from it moves dQ by up to ~1e-1 on early
+ *                    causal rows
+ *   lse              fp32 [B,K,G,T] from attn_fwd on the same inputs (required)
  *   dq               fp32 [B,K,G,T,H] (written)
  *   dk, dv           fp32 [B,K,S,H]   (written; summed over the G query heads)
  *   workspace        device buffer of at least attn_bwd_workspace_bytes(),
  *                    16-byte aligned, owned by the caller, contents ignored
- * Errors as attn_fwd, plus ERR_NULL for lse/dO/dq/dk/dv and ERR_WORKSPACE. */
+ * Errors as attn_fwd (with dq in the role of o), plus ERR_NULL for
+ * lse/dO/dq/dk/dv, ERR_ALIGN for a misaligned non-NULL o, and ERR_WORKSPACE.
+ * Enqueues three kernels on `stream`: the D pass, dQ, then dK/dV. */
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
              const void *dO, float *dq, float *dk, float *dv,
              const int32_t *q_seg, const int32_t *kv_seg,

@@ -29,6 +29,16 @@ def assert_close_o(x, ref, what="O"):
     return ma, rl
 
 
+def assert_close_all(pairs):
+    """Check several (name, got, ref) triples and report every failure at once."""
+    errs = []
+    for name, x, ref in pairs:
+        ma, rl = max_abs(x, ref), rel_l2(x, ref)
+        if not (ma <= O_MAX_ABS and rl <= O_REL_L2):
+            errs.append("%s: max-abs %.3e rel-L2 %.3e" % (name, ma, rl))
+    assert not errs, "; ".join(errs)
+
+
 def assert_close_lse(x, ref, what="lse"):
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

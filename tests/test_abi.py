@@ -80,6 +80,8 @@ def test_check_bwd_codes_and_workspace():
     assert check_bwd(wsb=16) == gqa.GQA_ATTN_ERR_WORKSPACE
     assert check_bwd(ws=A16 + 4) == gqa.GQA_ATTN_ERR_ALIGN
     assert check_bwd(H=96) == gqa.GQA_ATTN_ERR_HEADDIM
+    assert check_bwd(o=None) == gqa.GQA_ATTN_OK          # o is not read by the backward
+    assert check_bwd(o=A16 + 2) == gqa.GQA_ATTN_ERR_ALIGN
     assert check_bwd(qs=A16) == gqa.GQA_ATTN_ERR_SEGMENTS
 
 
