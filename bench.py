@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB three times (a known-size "
+                         "reference dispatch for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (--gpus %d refused)"
@@ -192,6 +195,15 @@ def main():
                                   "fwd_plus_bwd_tflops": 3.5 * flops / ((ms + bms) * 1e-3) / 1e12}
         except gqa.GqaAttnError as e:
             result["backward"] = {"error": str(e)}
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
 
     if not args.no_cpu_baseline:
         step()
