@@ -213,38 +213,47 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
                     }
                 }
             }
-            // ---- online softmax (log2 domain)
+            // ---- online softmax (log2 domain), lazy rescale: the reference max m_run
+            // moves only when some row of the wave grew by more than 2^kRescaleLog2.
+            // Keeping a stale reference is an exact re-association (numerator and
+            // denominator carry the same factor); it bounds P by 2^kRescaleLog2.
             float mx = -INFINITY;
 #pragma unroll
             for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) mx = fmaxf(mx, sacc[mb][r]);
+                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[mb][r], sacc[mb][r + 1]));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx * kLog2e);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float corr = exp2_fast(m_run - m_use);
+            const float mt = mx * kLog2e;
+            if (__any(mt > m_run + kRescaleLog2)) {
+                const float m_new = fmaxf(m_run, mt);
+                const float corr = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+                l_run *= corr;
+#pragma unroll
+                for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            // P in bf16 (the PV operand); the row sum stays in fp32 (lse accuracy)
+            bf16x8 pf[PK];
             float rs = 0.f;
 #pragma unroll
-            for (int mb = 0; mb < MB; mb++)
+            for (int kk = 0; kk < PK; kk++) {
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const float p = exp2_fast(__builtin_fmaf(sacc[mb][r], kLog2e, -m_use));
-                    sacc[mb][r] = p;
-                    rs += p;
+                for (int e = 0; e < 8; e += 2) {
+                    const float p0 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e], kLog2e, -m_use));
+                    const float p1 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e + 1], kLog2e, -m_use));
+                    pf[kk][e] = (__bf16)p0;
+                    pf[kk][e + 1] = (__bf16)p1;
+                    rs += p0 + p1;
                 }
+            }
             rs += __shfl_xor(rs, 32);
-            l_run = l_run * corr + rs;
-            m_run = m_new;
-#pragma unroll
-            for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
+            l_run += rs;
 
             // ---- O^T += V^T P^T
             const int gi = lane & 15, hh = (lane >> 4) & 1;
 #pragma unroll
             for (int kk = 0; kk < PK; kk++) {
-                bf16x8 pf;
-#pragma unroll
-                for (int e = 0; e < 8; e++) pf[e] = (__bf16)sacc[kk >> 1][8 * (kk & 1) + e];
 #pragma unroll
                 for (int hb = 0; hb < HB; hb++) {
                     const int hcol = 32 * hb + 16 * hh + 4 * (gi & 3);
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
                     const int r1 = r0 + 8;
                     const s16x4 lo = lds_read_tr16(sv + r0 * H + ((ch ^ swz<CPR>(r0)) << 3) + within);
                     const s16x4 hi = lds_read_tr16(sv + r1 * H + ((ch ^ swz<CPR>(r1)) << 3) + within);
-                    oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf, oacc[hb]);
+                    oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf[kk], oacc[hb]);
                 }
             }
         }

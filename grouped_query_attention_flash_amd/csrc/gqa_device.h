@@ -8,6 +8,7 @@ namespace gqa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -16,6 +17,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
 constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
+// The online softmax moves its reference max only when a row max grows by more
+// than this many powers of two, so unnormalised weights stay below 2^8.
+constexpr float kRescaleLog2 = 8.0f;
 
 // D = A * B + C on a 32x32 fp32 tile, A 32x16 and B 16x32 in bf16.
 // Operand layout (64-wide wave): lane l holds A[l%32][8*(l/32) .. +7] and
