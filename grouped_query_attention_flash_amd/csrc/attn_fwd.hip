@@ -39,16 +39,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     constexpr int MB = BKV / 32;      // 32-key blocks per tile
     constexpr int HB = H / 32;        // 32-wide h blocks of O^T
     constexpr int PK = BKV / 16;      // k-steps of the PV contraction
-    constexpr int NT = NW * 64;
-    constexpr int TILE_CHUNKS = BKV * CPR;
-    static_assert((2 * TILE_CHUNKS) % NT == 0, "tile load must split evenly");
-    constexpr int LOADS = 2 * TILE_CHUNKS / NT;
-    static_assert(TILE_CHUNKS % NT == 0, "K and V loads must not share a step");
+    using L = TileLayout<H, BKV>;
 
-    __shared__ __attribute__((aligned(16))) __bf16 sk[BKV * H];
-    __shared__ __attribute__((aligned(16))) __bf16 sv[BKV * H];
+    // K and V tiles, two buffers each (see the pipeline below), in padded-row
+    // layouts that make every MFMA operand read bank-conflict free.
+    __shared__ __attribute__((aligned(1024))) __bf16 sk0[L::K_ELEMS];
+    __shared__ __attribute__((aligned(1024))) __bf16 sk1[L::K_ELEMS];
+    __shared__ __attribute__((aligned(1024))) __bf16 sv0[L::V_ELEMS];
+    __shared__ __attribute__((aligned(1024))) __bf16 sv1[L::V_ELEMS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, c = lane >> 5;
 
     // ---- work unit; causal blocks are issued heaviest (last query block) first
@@ -86,8 +87,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             qf[ks] = bf16x8{};
     }
 
-    const __bf16 *kbase = a.k + bk * (size_t)S * H;
-    const __bf16 *vbase = a.v + bk * (size_t)S * H;
+    // K and V of this (b, kv head) as bounds-checked buffers: rows past S read as zero
+    const buffer_rsrc krs = make_rsrc(a.k + bk * (size_t)S * H, S * H * 2);
+    const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
 
     // ---- segment ids: this lane's query id and the workgroup / wave id ranges
     const bool segs = a.q_seg != nullptr;
@@ -134,49 +136,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         }
         return j;
     };
-
-    i32x4 pre[LOADS];
-    auto load_tile = [&](int j) {
-#pragma unroll
-        for (int i = 0; i < LOADS; i++) {
-            const int ci = tid + i * NT;
-            const int tensor = ci / TILE_CHUNKS;
-            const int cc = ci % TILE_CHUNKS;
-            const int r = cc / CPR, ch = cc % CPR;
-            const int s = j * BKV + r;
-            const __bf16 *src = (tensor ? vbase : kbase) + (size_t)s * H + ch * 8;
-            pre[i] = s < S ? *(const i32x4 *)src : i32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < LOADS; i++) {
-            const int ci = tid + i * NT;
-            const int tensor = ci / TILE_CHUNKS;
-            const int cc = ci % TILE_CHUNKS;
-            const int r = cc / CPR, ch = cc % CPR;
-            __bf16 *dst = (tensor ? sv : sk) + r * H + ((ch ^ swz<CPR>(r)) << 3);
-            *(i32x4 *)dst = pre[i];
-        }
-    };
-
-    f32x16 oacc[HB];
-#pragma unroll
-    for (int hb = 0; hb < HB; hb++) oacc[hb] = f32x16{};
-    float m_run = -INFINITY;  // running max, log2 units
-    float l_run = 0.f;        // running denominator
-
-    int j = next_tile(0);
-    if (j < j_end) load_tile(j);
-    while (j < j_end) {
-        __syncthreads();  // every wave is done reading the previous tile
-        store_tile();
-        __syncthreads();
-        const int jn = next_tile(j + 1);
-        if (jn < j_end) load_tile(jn);  // in flight while tile j is computed
-
+    // does this wave compute tile j, and does it need an element mask there
+    auto tile_flags = [&](int j, bool &run, bool &mask) {
         const int s0 = j * BKV;
-        bool run = wave_active && !(a.causal && s0 > tmax_w);
+        run = j < j_end && wave_active && !(a.causal && s0 > tmax_w);
         bool seg_mask = false;
         if (run && segs) {
             int kmin, kmax;
@@ -184,89 +147,150 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             if (kmax < w_qmin || kmin > w_qmax) run = false;
             seg_mask = !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
         }
-        if (run) {
-            // ---- S^T = K Q^T
-            f32x16 sacc[MB];
+        mask = (a.causal && s0 + BKV - 1 > tmin_w) || (s0 + BKV > S) || seg_mask;
+    };
+
+    // One tile of K (row stride L::KRS chunks) or V (L::VRS) into LDS, straight
+    // from memory (no registers). Wave load blk writes the 64 consecutive
+    // 16-byte slots blk*64 .. blk*64+63; slot p holds chunk p % RS of key row
+    // p / RS, and the padding slots (chunk >= CPR) repeat the row's last chunk.
+    auto issue_tile = [&](const buffer_rsrc &rs, int j, __bf16 *dst, int RS, int n_blk) {
+        for (int blk = wave; blk < n_blk; blk += NW) {
+            const int p = blk * 64 + lane;
+            const int r = p / RS, ch = min(p % RS, CPR - 1);
+            lds_load16(rs, dst + blk * 512, ((j * BKV + r) * H + ch * 8) * 2);
+        }
+    };
+    auto issue_k = [&](int j, __bf16 *dst) { issue_tile(krs, j, dst, L::KRS, L::K_BLOCKS); };
+    auto issue_v = [&](int j, __bf16 *dst) { issue_tile(vrs, j, dst, L::VRS, L::V_BLOCKS); };
+
+    // S^T = K_tile Q^T for one tile: lane reads row 32mb + n, chunk 2ks + c
+    const int k_lane = n * L::KRS * 8 + c * 8;
+    auto qk = [&](const __bf16 *kt, f32x16 (&sacc)[MB]) {
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) {
+            sacc[mb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ks++) {
+                const bf16x8 kf = *(const bf16x8 *)(kt + k_lane + mb * 32 * L::KRS * 8 + ks * 16);
+                sacc[mb] = mfma32x32x16(kf, qf[ks], sacc[mb]);
+            }
+        }
+    };
+
+    f32x16 oacc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++) oacc[hb] = f32x16{};
+    float m_run = -INFINITY;  // reference max, log2 units
+    float l_run = 0.f;        // running denominator
+
+    const int v_lane = (4 * c + ((lane & 15) >> 2)) * L::VRS * 8 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // mask, online softmax and O^T += V^T P^T for one tile
+    auto softmax_pv = [&](f32x16 (&sacc)[MB], const __bf16 *vt, int s0, bool need_mask) {
+        if (need_mask) {
 #pragma unroll
             for (int mb = 0; mb < MB; mb++) {
-                sacc[mb] = f32x16{};
-                const int r = 32 * mb + n;
-                const __bf16 *krow = sk + r * H;
-                const int sw = swz<CPR>(r);
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ks++) {
-                    const bf16x8 kf = *(const bf16x8 *)(krow + (((2 * ks + c) ^ sw) << 3));
-                    sacc[mb] = mfma32x32x16(kf, qf[ks], sacc[mb]);
-                }
-            }
-            // ---- lazy mask: only tiles that cross the diagonal, the key tail or a segment edge
-            const bool need_mask = (a.causal && s0 + BKV - 1 > tmin_w) || (s0 + BKV > S) || seg_mask;
-            if (need_mask) {
-#pragma unroll
-                for (int mb = 0; mb < MB; mb++) {
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int s = s0 + 32 * mb + acc_row(r, c);
-                        bool vis = s < S && !(a.causal && s > t);
-                        if (segs && vis) vis = kvs[s] == my_qid;
-                        if (!vis) sacc[mb][r] = -INFINITY;
-                    }
-                }
-            }
-            // ---- online softmax (log2 domain), lazy rescale: the reference max m_run
-            // moves only when some row of the wave grew by more than 2^kRescaleLog2.
-            // Keeping a stale reference is an exact re-association (numerator and
-            // denominator carry the same factor); it bounds P by 2^kRescaleLog2.
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mb = 0; mb < MB; mb++)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[mb][r], sacc[mb][r + 1]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mt = mx * kLog2e;
-            if (__any(mt > m_run + kRescaleLog2)) {
-                const float m_new = fmaxf(m_run, mt);
-                const float corr = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
-                l_run *= corr;
-#pragma unroll
-                for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
-                m_run = m_new;
-            }
-            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-            // P in bf16 (the PV operand); the row sum stays in fp32 (lse accuracy)
-            bf16x8 pf[PK];
-            float rs = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < PK; kk++) {
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e], kLog2e, -m_use));
-                    const float p1 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e + 1], kLog2e, -m_use));
-                    pf[kk][e] = (__bf16)p0;
-                    pf[kk][e + 1] = (__bf16)p1;
-                    rs += p0 + p1;
-                }
-            }
-            rs += __shfl_xor(rs, 32);
-            l_run += rs;
-
-            // ---- O^T += V^T P^T
-            const int gi = lane & 15, hh = (lane >> 4) & 1;
-#pragma unroll
-            for (int kk = 0; kk < PK; kk++) {
-#pragma unroll
-                for (int hb = 0; hb < HB; hb++) {
-                    const int hcol = 32 * hb + 16 * hh + 4 * (gi & 3);
-                    const int ch = hcol >> 3, within = hcol & 7;
-                    const int r0 = 16 * kk + 4 * c + (gi >> 2);
-                    const int r1 = r0 + 8;
-                    const s16x4 lo = lds_read_tr16(sv + r0 * H + ((ch ^ swz<CPR>(r0)) << 3) + within);
-                    const s16x4 hi = lds_read_tr16(sv + r1 * H + ((ch ^ swz<CPR>(r1)) << 3) + within);
-                    oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf[kk], oacc[hb]);
+                for (int r = 0; r < 16; r++) {
+                    const int s = s0 + 32 * mb + acc_row(r, c);
+                    bool vis = s < S && !(a.causal && s > t);
+                    if (segs && vis) vis = kvs[s] == my_qid;
+                    if (!vis) sacc[mb][r] = -INFINITY;
                 }
             }
         }
-        j = jn;
+        // Lazy rescale: the reference max m_run moves only when some row of the
+        // wave grew by more than 2^kRescaleLog2. Keeping a stale reference is an
+        // exact re-association (numerator and denominator carry the same factor).
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[mb][r], sacc[mb][r + 1]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = mx * kLog2e;
+        if (__any(mt > m_run + kRescaleLog2)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float corr = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+            l_run *= corr;
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        // P in bf16 (the PV operand); the row sum stays in fp32
+        bf16x8 pf[PK];
+        float rs = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < PK; kk++) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e], kLog2e, -m_use));
+                const float p1 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e + 1], kLog2e, -m_use));
+                pf[kk][e] = (__bf16)p0;
+                pf[kk][e + 1] = (__bf16)p1;
+                rs += p0 + p1;
+            }
+        }
+        rs += __shfl_xor(rs, 32);
+        l_run += rs;
+        // O^T += V^T P^T; V^T from two transpose reads per MFMA. Source lane gi of
+        // each 16-lane group addresses key row 16kk + 8e + 4c + gi/4 at
+        // h = 32hb + 16hh + 4(gi%4), so lane l receives h = 32hb + l%32 for the
+        // four keys 16kk + 8e + 4c + (0..3) -- the keys of its P^T slots.
+#pragma unroll
+        for (int kk = 0; kk < PK; kk++) {
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++) {
+                const __bf16 *vp = vt + v_lane + kk * 16 * L::VRS * 8 + hb * 32;
+                const s16x4 lo = lds_read_tr16(vp);
+                const s16x4 hi = lds_read_tr16(vp + 8 * L::VRS * 8);
+                oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf[kk], oacc[hb]);
+            }
+        }
+    };
+
+    // ---- software pipeline over the visible tiles n_0 < n_1 < ...
+    // Iteration i starts with S^T of n_i in registers, K of n_{i+1} and V of n_i
+    // in LDS. After one barrier (every wave finished iteration i-1) it loads K of
+    // n_{i+2} into the K buffer of n_i and V of n_{i+1} into the V buffer of
+    // n_{i-1}, issues the QK^T MFMAs of n_{i+1} and, while they run, does the
+    // softmax and PV of n_i. Even iterations use (sk0 | sk1, sv0 | sv1), odd ones
+    // the swapped pairs, so S^T buffers alternate without register copies.
+    int j_cur = next_tile(0);
+    int j_nxt = j_cur < j_end ? next_tile(j_cur + 1) : j_end;
+    if (j_cur < j_end) {
+        issue_k(j_cur, sk0);
+        issue_v(j_cur, sv0);
+    }
+    if (j_nxt < j_end) issue_k(j_nxt, sk1);
+    wait_lds_loads();
+    __syncthreads();
+    f32x16 sa[MB], sb[MB];
+    bool run_cur, mask_cur;
+    tile_flags(j_cur, run_cur, mask_cur);
+    if (run_cur) qk(sk0, sa);
+
+    auto iteration = [&](f32x16 (&s_cur)[MB], f32x16 (&s_nxt)[MB], __bf16 *k_cur, __bf16 *k_nxt,
+                         __bf16 *v_cur, __bf16 *v_nxt) {
+        const int j_nn = j_nxt < j_end ? next_tile(j_nxt + 1) : j_end;
+        wait_lds_loads();
+        __syncthreads();
+        if (j_nn < j_end) issue_k(j_nn, k_cur);
+        if (j_nxt < j_end) issue_v(j_nxt, v_nxt);
+        bool run_nxt, mask_nxt;
+        tile_flags(j_nxt, run_nxt, mask_nxt);
+        if (run_nxt) qk(k_nxt, s_nxt);
+        if (run_cur) softmax_pv(s_cur, v_cur, j_cur * BKV, mask_cur);
+        j_cur = j_nxt;
+        j_nxt = j_nn;
+        run_cur = run_nxt;
+        mask_cur = mask_nxt;
+        return j_cur < j_end;
+    };
+    if (j_cur < j_end) {
+        while (iteration(sa, sb, sk0, sk1, sv0, sv1) && iteration(sb, sa, sk1, sk0, sv1, sv0)) {
+        }
     }
 
     // ---- finalize: O = acc / l in bf16, lse = ln(sum exp(logits))

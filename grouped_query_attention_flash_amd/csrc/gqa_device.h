@@ -32,6 +32,24 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b,
 // Row of the 32x32 accumulator tile held by register r of a lane in half c (= lane / 32).
 __device__ __forceinline__ constexpr int acc_row(int r, int c) { return 8 * (r >> 2) + 4 * c + (r & 3); }
 
+// LDS layouts of K and V tiles (BKV key rows of H bf16): rows are padded so
+// that the MFMA operand reads are bank-conflict free on 64 banks x 4 bytes.
+//   K: row stride CPR + 1 chunks of 16 bytes. The A-operand read of 16 lanes
+//      (16 consecutive rows, one chunk) hits 16 distinct 16-byte bank groups.
+//   V: row stride CPR + 4 chunks. A transpose read of 32 lanes covers 4 rows x
+//      64 bytes; rows 4 chunks apart fill the 64 banks exactly once.
+// Sizes are rounded up to whole 1 KiB wave loads.
+template <int H, int BKV>
+struct TileLayout {
+    static constexpr int CPR = H / 8;
+    static constexpr int KRS = CPR + 1;
+    static constexpr int VRS = CPR + 4;
+    static constexpr int K_BLOCKS = (BKV * KRS + 63) / 64;
+    static constexpr int V_BLOCKS = (BKV * VRS + 63) / 64;
+    static constexpr int K_ELEMS = K_BLOCKS * 512;
+    static constexpr int V_ELEMS = V_BLOCKS * 512;
+};
+
 // XOR swizzle of 16-byte chunks inside one LDS row of CPR chunks. Rows
 // r..r+15 (aligned) map one logical chunk to 16 distinct chunk slots, and
 // 4 consecutive rows x 4 consecutive chunks (the transpose-read footprint)
@@ -60,6 +78,31 @@ __device__ __forceinline__ bf16x8 join_bf16x8(const s16x4 &lo, const s16x4 &hi) 
     const i32x4 w = {a[0], a[1], b[0], b[1]};
     return __builtin_bit_cast(bf16x8, w);
 }
+
+// Buffer resource over [base, base + bytes): loads past the end return zeros.
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc;
+// The fields are forced wave-uniform so that the descriptor lives in SGPRs.
+__device__ __forceinline__ buffer_rsrc make_rsrc(const void *base, int bytes) {
+    const uint64_t p = (uint64_t)(size_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void *ub = (void *)(size_t)(((uint64_t)hi << 32) | lo);
+    // 0x00020000: the raw 32-bit data format of gfx9-family buffer descriptors
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS (no registers). The wave's
+// 64 lanes write 1 KiB at dst (wave-uniform): lane l at dst + 16 l bytes.
+// dst is made provably wave-uniform (it is kept in M0).
+__device__ __forceinline__ void lds_load16(const buffer_rsrc &rs, __bf16 *dst, int voffset) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const unsigned addr = (unsigned)(size_t)(lds_void *)dst;
+    lds_void *p = (lds_void *)(size_t)__builtin_amdgcn_readfirstlane(addr);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, p, 16, voffset, 0, 0, 0);
+}
+
+// Wait until this wave's LDS-direct loads have landed (vmcnt = 0 only).
+__device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
