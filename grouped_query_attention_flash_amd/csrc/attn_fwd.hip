@@ -30,6 +30,17 @@
 #include <climits>
 #include <cmath>
 
+// Build-time switches of the forward schedule (defaults are the tuned ones).
+#ifndef GQA_FWD_FASTPATH
+#define GQA_FWD_FASTPATH 1
+#endif
+#ifndef GQA_FWD_SCHED
+#define GQA_FWD_SCHED 0
+#endif
+#ifndef GQA_FWD_BKV128
+#define GQA_FWD_BKV128 64
+#endif
+
 namespace gqa {
 
 template <int H, int BKV, int NW>
@@ -40,6 +51,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     constexpr int HB = H / 32;        // 32-wide h blocks of O^T
     constexpr int PK = BKV / 16;      // k-steps of the PV contraction
     using L = TileLayout<H, BKV>;
+#if GQA_FWD_SCHED
+    // VALU instructions (exp, fma, convert, add) per lane per tile, spread over the
+    // QK^T MFMAs of the next tile
+    constexpr int kValuPerMfma = (MB * 16 * 3 + MB * 8 + MB * KSTEPS - 1) / (MB * KSTEPS);
+#endif
 
     // K and V tiles, two buffers each (see the pipeline below), in padded-row
     // layouts that make every MFMA operand read bank-conflict free.
@@ -154,15 +170,34 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     // from memory (no registers). Wave load blk writes the 64 consecutive
     // 16-byte slots blk*64 .. blk*64+63; slot p holds chunk p % RS of key row
     // p / RS, and the padding slots (chunk >= CPR) repeat the row's last chunk.
-    auto issue_tile = [&](const buffer_rsrc &rs, int j, __bf16 *dst, int RS, int n_blk) {
-        for (int blk = wave; blk < n_blk; blk += NW) {
-            const int p = blk * 64 + lane;
-            const int r = p / RS, ch = min(p % RS, CPR - 1);
-            lds_load16(rs, dst + blk * 512, ((j * BKV + r) * H + ch * 8) * 2);
-        }
+    // This wave issues loads blk = wave, wave + NW, ...; their per-lane byte
+    // offsets within a tile are fixed, and the tile's own offset goes in the
+    // instruction's scalar offset.
+    constexpr int K_PER_WAVE = (L::K_BLOCKS + NW - 1) / NW;
+    constexpr int V_PER_WAVE = (L::V_BLOCKS + NW - 1) / NW;
+    int k_off[K_PER_WAVE], v_off[V_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < K_PER_WAVE; i++) {
+        const int p = (wave + i * NW) * 64 + lane;
+        k_off[i] = ((p / L::KRS) * H + min(p % L::KRS, CPR - 1) * 8) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_WAVE; i++) {
+        const int p = (wave + i * NW) * 64 + lane;
+        v_off[i] = ((p / L::VRS) * H + min(p % L::VRS, CPR - 1) * 8) * 2;
+    }
+    auto issue_k = [&](int j, __bf16 *dst) {
+        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+#pragma unroll
+        for (int i = 0; i < K_PER_WAVE; i++)
+            if (wave + i * NW < L::K_BLOCKS) lds_load16(krs, dst + (wave + i * NW) * 512, k_off[i], tile);
     };
-    auto issue_k = [&](int j, __bf16 *dst) { issue_tile(krs, j, dst, L::KRS, L::K_BLOCKS); };
-    auto issue_v = [&](int j, __bf16 *dst) { issue_tile(vrs, j, dst, L::VRS, L::V_BLOCKS); };
+    auto issue_v = [&](int j, __bf16 *dst) {
+        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+#pragma unroll
+        for (int i = 0; i < V_PER_WAVE; i++)
+            if (wave + i * NW < L::V_BLOCKS) lds_load16(vrs, dst + (wave + i * NW) * 512, v_off[i], tile);
+    };
 
     // S^T = K_tile Q^T for one tile: lane reads row 32mb + n, chunk 2ks + c
     const int k_lane = n * L::KRS * 8 + c * 8;
@@ -182,44 +217,48 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int hb = 0; hb < HB; hb++) oacc[hb] = f32x16{};
     float m_run = -INFINITY;  // reference max, log2 units
-    float l_run = 0.f;        // running denominator
+    float l_run = 0.f;        // running denominator over this lane's half of the keys
 
-    const int v_lane = (4 * c + ((lane & 15) >> 2)) * L::VRS * 8 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    // mask, online softmax and O^T += V^T P^T for one tile
-    auto softmax_pv = [&](f32x16 (&sacc)[MB], const __bf16 *vt, int s0, bool need_mask) {
-        if (need_mask) {
+    // ---- per-tile pieces: lazy mask, row max + rescale, weights, PV
+    auto mask_tile = [&](f32x16 (&sacc)[MB], int s0) {
 #pragma unroll
-            for (int mb = 0; mb < MB; mb++) {
+        for (int mb = 0; mb < MB; mb++) {
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int s = s0 + 32 * mb + acc_row(r, c);
-                    bool vis = s < S && !(a.causal && s > t);
-                    if (segs && vis) vis = kvs[s] == my_qid;
-                    if (!vis) sacc[mb][r] = -INFINITY;
-                }
+            for (int r = 0; r < 16; r++) {
+                const int s = s0 + 32 * mb + acc_row(r, c);
+                bool vis = s < S && !(a.causal && s > t);
+                if (segs && vis) vis = kvs[s] == my_qid;
+                if (!vis) sacc[mb][r] = -INFINITY;
             }
         }
-        // Lazy rescale: the reference max m_run moves only when some row of the
-        // wave grew by more than 2^kRescaleLog2. Keeping a stale reference is an
-        // exact re-association (numerator and denominator carry the same factor).
+    };
+    // Lazy rescale: the reference max m_run moves only when some row of the
+    // wave grew by more than 2^kRescaleLog2. Keeping a stale reference is an
+    // exact re-association (numerator and denominator carry the same factor).
+    // A row's keys are split between lane n and lane n + 32; each checks its
+    // own half, so the common case needs no cross-lane exchange. When some row
+    // must move, both halves take the full row max, so m_run stays identical in
+    // the lane pair. Returns the reference the weights are taken against.
+    auto rowmax_rescale = [&](const f32x16 (&sacc)[MB]) {
         float mx = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[mb][r], sacc[mb][r + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mt = mx * kLog2e;
-        if (__any(mt > m_run + kRescaleLog2)) {
-            const float m_new = fmaxf(m_run, mt);
+        if (__any(mx * kLog2e > m_run + kRescaleLog2)) {
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx * kLog2e);
             const float corr = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
             l_run *= corr;
 #pragma unroll
             for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
             m_run = m_new;
         }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        // P in bf16 (the PV operand); the row sum stays in fp32
-        bf16x8 pf[PK];
+        return (m_run == -INFINITY) ? 0.f : m_run;
+    };
+    // P = exp2(S log2e - m) in bf16 (the PV operand); returns this lane's part
+    // of the fp32 row sum
+    auto weights = [&](const f32x16 (&sacc)[MB], float m_use, bf16x8 (&pf)[PK]) {
         float rs = 0.f;
 #pragma unroll
         for (int kk = 0; kk < PK; kk++) {
@@ -232,12 +271,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
                 rs += p0 + p1;
             }
         }
-        rs += __shfl_xor(rs, 32);
-        l_run += rs;
-        // O^T += V^T P^T; V^T from two transpose reads per MFMA. Source lane gi of
-        // each 16-lane group addresses key row 16kk + 8e + 4c + gi/4 at
-        // h = 32hb + 16hh + 4(gi%4), so lane l receives h = 32hb + l%32 for the
-        // four keys 16kk + 8e + 4c + (0..3) -- the keys of its P^T slots.
+        return rs;
+    };
+    // O^T += V^T P^T; V^T from two transpose reads per MFMA. Source lane gi of
+    // each 16-lane group addresses key row 16kk + 8e + 4c + gi/4 at
+    // h = 32hb + 16hh + 4(gi%4), so lane l receives h = 32hb + l%32 for the
+    // four keys 16kk + 8e + 4c + (0..3) -- the keys of its P^T slots.
+    const int v_lane = (4 * c + ((lane & 15) >> 2)) * L::VRS * 8 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto pv = [&](const bf16x8 (&pf)[PK], const __bf16 *vt) {
 #pragma unroll
         for (int kk = 0; kk < PK; kk++) {
 #pragma unroll
@@ -248,6 +289,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
                 oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf[kk], oacc[hb]);
             }
         }
+    };
+    auto softmax_pv = [&](f32x16 (&sacc)[MB], const __bf16 *vt, int s0, bool need_mask) {
+        if (need_mask) mask_tile(sacc, s0);
+        const float m_use = rowmax_rescale(sacc);
+        bf16x8 pf[PK];
+        l_run += weights(sacc, m_use, pf);
+        pv(pf, vt);
     };
 
     // ---- software pipeline over the visible tiles n_0 < n_1 < ...
@@ -280,8 +328,37 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         if (j_nxt < j_end) issue_v(j_nxt, v_nxt);
         bool run_nxt, mask_nxt;
         tile_flags(j_nxt, run_nxt, mask_nxt);
-        if (run_nxt) qk(k_nxt, s_nxt);
-        if (run_cur) softmax_pv(s_cur, v_cur, j_cur * BKV, mask_cur);
+        if (GQA_FWD_FASTPATH && run_cur && run_nxt && !mask_cur) {
+            // common case, one basic block: the QK^T MFMAs of the next tile are
+            // interleaved with the exponentials of this one, so the matrix pipe
+            // and the VALU work at the same time
+            const float m_use = rowmax_rescale(s_cur);
+            bf16x8 pf[PK];
+            qk(k_nxt, s_nxt);
+            l_run += weights(s_cur, m_use, pf);
+            pv(pf, v_cur);
+            // schedule: K operand reads run two MFMAs ahead; each QK^T MFMA is
+            // followed by a share of the weight computation; then the PV MFMAs
+            // with their V transpose reads two MFMAs ahead
+#if GQA_FWD_SCHED
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < MB * KSTEPS; i++) {
+                if (i + 2 < MB * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < PK * HB; i++) {
+                if (i + 2 < PK * HB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+#endif
+        } else {
+            if (run_nxt) qk(k_nxt, s_nxt);
+            if (run_cur) softmax_pv(s_cur, v_cur, j_cur * BKV, mask_cur);
+        }
         j_cur = j_nxt;
         j_nxt = j_nn;
         run_cur = run_nxt;
@@ -294,6 +371,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     }
 
     // ---- finalize: O = acc / l in bf16, lse = ln(sum exp(logits))
+    l_run += __shfl_xor(l_run, 32);  // the two halves of each row
     if (q_valid) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
         __bf16 *orow = a.o + qrow_off;
@@ -338,7 +416,7 @@ FwdConfig fwd_config(int G, int T, int H) {
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
     switch (H) {
         case 64: return launch_fwd_t<64, 64, 8>(a, stream);
-        case 128: return launch_fwd_t<128, 64, 8>(a, stream);
+        case 128: return launch_fwd_t<128, GQA_FWD_BKV128, 8>(a, stream);
         case 256: return launch_fwd_t<256, 32, 4>(a, stream);
         default: return hipErrorInvalidValue;
     }

@@ -94,11 +94,12 @@ __device__ __forceinline__ buffer_rsrc make_rsrc(const void *base, int bytes) {
 // 16 bytes per lane from a buffer straight into LDS (no registers). The wave's
 // 64 lanes write 1 KiB at dst (wave-uniform): lane l at dst + 16 l bytes.
 // dst is made provably wave-uniform (it is kept in M0).
-__device__ __forceinline__ void lds_load16(const buffer_rsrc &rs, __bf16 *dst, int voffset) {
+// The byte offset is voffset (per lane) + soffset (wave-uniform).
+__device__ __forceinline__ void lds_load16(const buffer_rsrc &rs, __bf16 *dst, int voffset, int soffset = 0) {
     typedef __attribute__((address_space(3))) void lds_void;
     const unsigned addr = (unsigned)(size_t)(lds_void *)dst;
     lds_void *p = (lds_void *)(size_t)__builtin_amdgcn_readfirstlane(addr);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, p, 16, voffset, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, p, 16, voffset, soffset, 0, 0);
 }
 
 // Wait until this wave's LDS-direct loads have landed (vmcnt = 0 only).
