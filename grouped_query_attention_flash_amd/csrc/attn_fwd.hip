@@ -40,11 +40,28 @@
 #ifndef GQA_FWD_BKV128
 #define GQA_FWD_BKV128 64
 #endif
+// waves per workgroup at H = 128 (8: one workgroup per CU; 4: two per CU)
+#ifndef GQA_FWD_NW128
+#define GQA_FWD_NW128 8
+#endif
+// 0: no scheduling fences; 1: fences between pipeline phases; 2: also inside
+// the QK^T and PV loops
+#ifndef GQA_FWD_FENCE
+#define GQA_FWD_FENCE 0
+#endif
+// raise the wave's issue priority while it feeds the matrix pipe
+#ifndef GQA_FWD_PRIO
+#define GQA_FWD_PRIO 1
+#endif
 
 namespace gqa {
 
-template <int H, int BKV, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
+// DENSE: no segment ids, whole key tiles (S % BKV == 0) and, when causal,
+// T == S with one query block per key tile (bq == BKV): only the last tile of
+// a block (its diagonal) needs an element mask, and the key loop has scalar
+// control and a branch-free steady state.
+template <int H, int BKV, int NW, int WAVES_PER_SIMD, bool CAUSAL, bool DENSE>
+__global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdArgs a) {
     constexpr int CPR = H / 8;        // 16-byte chunks per K/V row
     constexpr int KSTEPS = H / 16;    // k-steps of the QK^T contraction
     constexpr int MB = BKV / 32;      // 32-key blocks per tile
@@ -71,7 +88,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     // ---- work unit; causal blocks are issued heaviest (last query block) first
     const int units = a.B * a.K * a.n_gsplit;
     int qb = blockIdx.x / units;
-    if (a.causal) qb = a.n_qblocks - 1 - qb;
+    if (CAUSAL) qb = a.n_qblocks - 1 - qb;
     const int u = blockIdx.x % units;
     const int gs = u % a.n_gsplit;
     const int kh = (u / a.n_gsplit) % a.K;
@@ -108,7 +125,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
 
     // ---- segment ids: this lane's query id and the workgroup / wave id ranges
-    const bool segs = a.q_seg != nullptr;
+    const bool segs = !DENSE && a.q_seg != nullptr;
     const int32_t *kvs = segs ? a.kv_seg + (size_t)b * S : nullptr;
     int my_qid = 0, wg_qmin = INT_MAX, wg_qmax = INT_MIN, w_qmin = INT_MAX, w_qmax = INT_MIN;
     if (segs) {
@@ -131,7 +148,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     // ---- key-tile range: causal stops at the block's last query
     const int n_tiles = (S + BKV - 1) / BKV;
     int j_end = n_tiles;
-    if (a.causal) j_end = min(j_end, (min(t0 + a.bq, T) - 1) / BKV + 1);
+    if (CAUSAL) j_end = min(j_end, (min(t0 + a.bq, T) - 1) / BKV + 1);
 
     // kv-id range of tile j (wave-uniform; every wave computes the same value)
     auto tile_ids = [&](int j, int &kmin, int &kmax) {
@@ -155,7 +172,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     // does this wave compute tile j, and does it need an element mask there
     auto tile_flags = [&](int j, bool &run, bool &mask) {
         const int s0 = j * BKV;
-        run = j < j_end && wave_active && !(a.causal && s0 > tmax_w);
+        run = j < j_end && wave_active && !(CAUSAL && s0 > tmax_w);
         bool seg_mask = false;
         if (run && segs) {
             int kmin, kmax;
@@ -163,7 +180,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             if (kmax < w_qmin || kmin > w_qmax) run = false;
             seg_mask = !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
         }
-        mask = (a.causal && s0 + BKV - 1 > tmin_w) || (s0 + BKV > S) || seg_mask;
+        mask = (CAUSAL && s0 + BKV - 1 > tmin_w) || (s0 + BKV > S) || seg_mask;
     };
 
     // One tile of K (row stride L::KRS chunks) or V (L::VRS) into LDS, straight
@@ -186,17 +203,22 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         const int p = (wave + i * NW) * 64 + lane;
         v_off[i] = ((p / L::VRS) * H + min(p % L::VRS, CPR - 1) * 8) * 2;
     }
-    auto issue_k = [&](int j, __bf16 *dst) {
+    const unsigned wave_slot = wave * 1024;  // this wave's first 1 KiB block
+    auto issue_k = [&](int j, const __bf16 *dst) {
         const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+        const unsigned base = lds_addr(dst) + wave_slot;
 #pragma unroll
         for (int i = 0; i < K_PER_WAVE; i++)
-            if (wave + i * NW < L::K_BLOCKS) lds_load16(krs, dst + (wave + i * NW) * 512, k_off[i], tile);
+            if ((wave + i * NW) * 64 + lane < L::K_BLOCKS * 64)  // whole waves in or out
+                lds_load16(krs, base + i * NW * 1024, k_off[i], tile);
     };
-    auto issue_v = [&](int j, __bf16 *dst) {
+    auto issue_v = [&](int j, const __bf16 *dst) {
         const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+        const unsigned base = lds_addr(dst) + wave_slot;
 #pragma unroll
         for (int i = 0; i < V_PER_WAVE; i++)
-            if (wave + i * NW < L::V_BLOCKS) lds_load16(vrs, dst + (wave + i * NW) * 512, v_off[i], tile);
+            if ((wave + i * NW) * 64 + lane < L::V_BLOCKS * 64)
+                lds_load16(vrs, base + i * NW * 1024, v_off[i], tile);
     };
 
     // S^T = K_tile Q^T for one tile: lane reads row 32mb + n, chunk 2ks + c
@@ -209,6 +231,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             for (int ks = 0; ks < KSTEPS; ks++) {
                 const bf16x8 kf = *(const bf16x8 *)(kt + k_lane + mb * 32 * L::KRS * 8 + ks * 16);
                 sacc[mb] = mfma32x32x16(kf, qf[ks], sacc[mb]);
+                if (GQA_FWD_FENCE >= 2 && ks % 4 == 3) sched_fence();  // at most 4 operand reads in flight
             }
         }
     };
@@ -220,14 +243,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     float l_run = 0.f;        // running denominator over this lane's half of the keys
 
     // ---- per-tile pieces: lazy mask, row max + rescale, weights, PV
+    // Register r of block mb holds key s0 + 32mb + acc_row(r, c); with the lane's
+    // half c folded into one limit, every comparison is against a constant.
     auto mask_tile = [&](f32x16 (&sacc)[MB], int s0) {
+        const int lim = min(CAUSAL ? t : INT_MAX, S - 1) - s0 - 4 * c;  // last visible key offset
 #pragma unroll
         for (int mb = 0; mb < MB; mb++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int s = s0 + 32 * mb + acc_row(r, c);
-                bool vis = s < S && !(a.causal && s > t);
-                if (segs && vis) vis = kvs[s] == my_qid;
+                const int off = 32 * mb + 8 * (r >> 2) + (r & 3);
+                bool vis = off <= lim;
+                if (segs && vis) vis = kvs[s0 + off + 4 * c] == my_qid;
                 if (!vis) sacc[mb][r] = -INFINITY;
             }
         }
@@ -240,11 +266,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     // must move, both halves take the full row max, so m_run stays identical in
     // the lane pair. Returns the reference the weights are taken against.
     auto rowmax_rescale = [&](const f32x16 (&sacc)[MB]) {
-        float mx = -INFINITY;
+        // four independent partial maxima (short dependency chains)
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[mb][r], sacc[mb][r + 1]));
+            for (int r = 0; r < 16; r += 2) m4[(r >> 1) & 3] = fmaxf(m4[(r >> 1) & 3], fmaxf(sacc[mb][r], sacc[mb][r + 1]));
+        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         if (__any(mx * kLog2e > m_run + kRescaleLog2)) {
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float m_new = fmaxf(m_run, mx * kLog2e);
@@ -259,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     // P = exp2(S log2e - m) in bf16 (the PV operand); returns this lane's part
     // of the fp32 row sum
     auto weights = [&](const f32x16 (&sacc)[MB], float m_use, bf16x8 (&pf)[PK]) {
-        float rs = 0.f;
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
         for (int kk = 0; kk < PK; kk++) {
 #pragma unroll
@@ -268,10 +296,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
                 const float p1 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e + 1], kLog2e, -m_use));
                 pf[kk][e] = (__bf16)p0;
                 pf[kk][e + 1] = (__bf16)p1;
-                rs += p0 + p1;
+                rs[e >> 1] += p0 + p1;
             }
         }
-        return rs;
+        return (rs[0] + rs[1]) + (rs[2] + rs[3]);
     };
     // O^T += V^T P^T; V^T from two transpose reads per MFMA. Source lane gi of
     // each 16-lane group addresses key row 16kk + 8e + 4c + gi/4 at
@@ -288,85 +316,144 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
                 const s16x4 hi = lds_read_tr16(vp + 8 * L::VRS * 8);
                 oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf[kk], oacc[hb]);
             }
+            if (GQA_FWD_FENCE >= 2) sched_fence();
         }
     };
-    auto softmax_pv = [&](f32x16 (&sacc)[MB], const __bf16 *vt, int s0, bool need_mask) {
-        if (need_mask) mask_tile(sacc, s0);
+    auto softmax_pv = [&](f32x16 (&sacc)[MB], const __bf16 *vt) {
         const float m_use = rowmax_rescale(sacc);
         bf16x8 pf[PK];
         l_run += weights(sacc, m_use, pf);
         pv(pf, vt);
     };
 
-    // ---- software pipeline over the visible tiles n_0 < n_1 < ...
-    // Iteration i starts with S^T of n_i in registers, K of n_{i+1} and V of n_i
-    // in LDS. After one barrier (every wave finished iteration i-1) it loads K of
-    // n_{i+2} into the K buffer of n_i and V of n_{i+1} into the V buffer of
-    // n_{i-1}, issues the QK^T MFMAs of n_{i+1} and, while they run, does the
-    // softmax and PV of n_i. Even iterations use (sk0 | sk1, sv0 | sv1), odd ones
-    // the swapped pairs, so S^T buffers alternate without register copies.
-    int j_cur = next_tile(0);
-    int j_nxt = j_cur < j_end ? next_tile(j_cur + 1) : j_end;
-    if (j_cur < j_end) {
-        issue_k(j_cur, sk0);
-        issue_v(j_cur, sv0);
-    }
-    if (j_nxt < j_end) issue_k(j_nxt, sk1);
-    wait_lds_loads();
-    __syncthreads();
-    f32x16 sa[MB], sb[MB];
-    bool run_cur, mask_cur;
-    tile_flags(j_cur, run_cur, mask_cur);
-    if (run_cur) qk(sk0, sa);
-
-    auto iteration = [&](f32x16 (&s_cur)[MB], f32x16 (&s_nxt)[MB], __bf16 *k_cur, __bf16 *k_nxt,
-                         __bf16 *v_cur, __bf16 *v_nxt) {
-        const int j_nn = j_nxt < j_end ? next_tile(j_nxt + 1) : j_end;
+    if constexpr (DENSE) {
+        // ---- dense pipeline over tiles 0 .. n_t-1 (same buffer rotation as below)
+        const int n_t = CAUSAL ? qb + 1 : S / BKV;
+        issue_k(0, sk0);
+        issue_v(0, sv0);
+        if (n_t > 1) issue_k(1, sk1);
         wait_lds_loads();
         __syncthreads();
-        if (j_nn < j_end) issue_k(j_nn, k_cur);
-        if (j_nxt < j_end) issue_v(j_nxt, v_nxt);
-        bool run_nxt, mask_nxt;
-        tile_flags(j_nxt, run_nxt, mask_nxt);
-        if (GQA_FWD_FASTPATH && run_cur && run_nxt && !mask_cur) {
-            // common case, one basic block: the QK^T MFMAs of the next tile are
-            // interleaved with the exponentials of this one, so the matrix pipe
-            // and the VALU work at the same time
+        f32x16 sa[MB], sb[MB];
+        qk(sk0, sa);
+        auto step = [&](f32x16 (&s_cur)[MB], f32x16 (&s_nxt)[MB], const __bf16 *k_cur, const __bf16 *k_nxt,
+                        const __bf16 *v_cur, const __bf16 *v_nxt, int i) {
+            wait_lds_loads();
+            __syncthreads();
+            if (i + 2 < n_t) issue_k(i + 2, k_cur);
+            issue_v(i + 1, v_nxt);
             const float m_use = rowmax_rescale(s_cur);
             bf16x8 pf[PK];
+            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
             qk(k_nxt, s_nxt);
             l_run += weights(s_cur, m_use, pf);
             pv(pf, v_cur);
-            // schedule: K operand reads run two MFMAs ahead; each QK^T MFMA is
-            // followed by a share of the weight computation; then the PV MFMAs
-            // with their V transpose reads two MFMAs ahead
-#if GQA_FWD_SCHED
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+        };
+        auto last = [&](f32x16 (&s_cur)[MB], const __bf16 *v_cur) {
+            wait_lds_loads();
+            __syncthreads();
+            if (CAUSAL) mask_tile(s_cur, (n_t - 1) * BKV);
+            softmax_pv(s_cur, v_cur);
+        };
+        // The loop runs whole pairs of steps so that the last tile's S^T always
+        // ends in sa: an odd step count is evened out by one step before the
+        // loop, whose S^T is moved into sa once; the K/V buffer roles then flip,
+        // which only changes (uniform) LDS base pointers.
+        int i = 0;
+        const __bf16 *kA = sk0, *kB = sk1, *vA = sv0, *vB = sv1;
+        if ((n_t - 1) & 1) {
+            step(sa, sb, sk0, sk1, sv0, sv1, i++);
 #pragma unroll
-            for (int i = 0; i < MB * KSTEPS; i++) {
-                if (i + 2 < MB * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < PK * HB; i++) {
-                if (i + 2 < PK * HB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            }
-#endif
-        } else {
-            if (run_nxt) qk(k_nxt, s_nxt);
-            if (run_cur) softmax_pv(s_cur, v_cur, j_cur * BKV, mask_cur);
+            for (int mb = 0; mb < MB; mb++) sa[mb] = sb[mb];
+            kA = sk1;
+            kB = sk0;
+            vA = sv1;
+            vB = sv0;
         }
-        j_cur = j_nxt;
-        j_nxt = j_nn;
-        run_cur = run_nxt;
-        mask_cur = mask_nxt;
-        return j_cur < j_end;
-    };
-    if (j_cur < j_end) {
-        while (iteration(sa, sb, sk0, sk1, sv0, sv1) && iteration(sb, sa, sk1, sk0, sv1, sv0)) {
+        while (i + 1 < n_t) {
+            step(sa, sb, kA, kB, vA, vB, i++);
+            step(sb, sa, kB, kA, vB, vA, i++);
+        }
+        last(sa, vA);
+    } else {
+        // ---- software pipeline over the visible tiles n_0 < n_1 < ...
+        // Iteration i starts with S^T of n_i in registers, K of n_{i+1} and V of n_i
+        // in LDS. After one barrier (every wave finished iteration i-1) it loads K of
+        // n_{i+2} into the K buffer of n_i and V of n_{i+1} into the V buffer of
+        // n_{i-1}, issues the QK^T MFMAs of n_{i+1} and, while they run, does the
+        // softmax and PV of n_i. Even iterations use (sk0 | sk1, sv0 | sv1), odd ones
+        // the swapped pairs, so S^T buffers alternate without register copies.
+        int j_cur = next_tile(0);
+        int j_nxt = j_cur < j_end ? next_tile(j_cur + 1) : j_end;
+        if (j_cur < j_end) {
+            issue_k(j_cur, sk0);
+            issue_v(j_cur, sv0);
+        }
+        if (j_nxt < j_end) issue_k(j_nxt, sk1);
+        wait_lds_loads();
+        __syncthreads();
+        f32x16 sa[MB], sb[MB];
+        bool run_cur, mask_cur;
+        tile_flags(j_cur, run_cur, mask_cur);
+        if (run_cur) qk(sk0, sa);
+
+        auto iteration = [&](f32x16 (&s_cur)[MB], f32x16 (&s_nxt)[MB], __bf16 *k_cur, __bf16 *k_nxt,
+                             __bf16 *v_cur, __bf16 *v_nxt) {
+            if (GQA_FWD_FENCE >= 1) sched_fence();
+            const int j_nn = j_nxt < j_end ? next_tile(j_nxt + 1) : j_end;
+            wait_lds_loads();
+            __syncthreads();
+            if (j_nn < j_end) issue_k(j_nn, k_cur);
+            if (j_nxt < j_end) issue_v(j_nxt, v_nxt);
+            bool run_nxt, mask_nxt;
+            tile_flags(j_nxt, run_nxt, mask_nxt);
+            if (run_cur && mask_cur) mask_tile(s_cur, j_cur * BKV);
+            if (GQA_FWD_FASTPATH && run_cur && run_nxt) {
+                // common case, one basic block: the QK^T MFMAs of the next tile are
+                // interleaved with the exponentials of this one, so the matrix pipe
+                // and the VALU work at the same time
+                const float m_use = rowmax_rescale(s_cur);
+                bf16x8 pf[PK];
+                if (GQA_FWD_FENCE >= 1) sched_fence();
+                if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+                qk(k_nxt, s_nxt);
+                l_run += weights(s_cur, m_use, pf);
+                if (GQA_FWD_FENCE >= 1) sched_fence();
+                pv(pf, v_cur);
+                if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+                if (GQA_FWD_FENCE >= 1) sched_fence();
+                // schedule: K operand reads run two MFMAs ahead; each QK^T MFMA is
+                // followed by a share of the weight computation; then the PV MFMAs
+                // with their V transpose reads two MFMAs ahead
+    #if GQA_FWD_SCHED
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    #pragma unroll
+                for (int i = 0; i < MB * KSTEPS; i++) {
+                    if (i + 2 < MB * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    #pragma unroll
+                for (int i = 0; i < PK * HB; i++) {
+                    if (i + 2 < PK * HB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+    #endif
+            } else {
+                if (run_nxt) qk(k_nxt, s_nxt);
+                if (run_cur) softmax_pv(s_cur, v_cur);
+            }
+            j_cur = j_nxt;
+            j_nxt = j_nn;
+            run_cur = run_nxt;
+            mask_cur = mask_nxt;
+            return j_cur < j_end;
+        };
+        if (j_cur < j_end) {
+            while (iteration(sa, sb, sk0, sk1, sv0, sv1) && iteration(sb, sa, sk1, sk0, sv1, sv0)) {
+            }
         }
     }
 
@@ -389,10 +476,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     }
 }
 
-template <int H, int BKV, int NW>
+template <int H, int BKV, int NW, int WPS>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks);
-    hipLaunchKernelGGL((attn_fwd_kernel<H, BKV, NW>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    const bool all_waves = a.gw * a.bq == 32 * NW;
+    const bool dense = a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
+                       (!a.causal || (a.T == a.S && a.bq == BKV));
+    if (a.causal && dense)
+        hipLaunchKernelGGL((attn_fwd_kernel<H, BKV, NW, WPS, true, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    else if (a.causal)
+        hipLaunchKernelGGL((attn_fwd_kernel<H, BKV, NW, WPS, true, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    else if (dense)
+        hipLaunchKernelGGL((attn_fwd_kernel<H, BKV, NW, WPS, false, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<H, BKV, NW, WPS, false, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -402,7 +499,7 @@ FwdConfig fwd_config(int G, int T, int H) {
     // (1 per SIMD, up to 512 registers). gw query heads (the largest divisor of
     // G that is <= the wave count) share each K/V tile.
     FwdConfig cfg;
-    cfg.nw = (H == 256) ? 4 : 8;
+    cfg.nw = (H == 256) ? 4 : (H == 128 ? GQA_FWD_NW128 : 8);
     cfg.bkv = (H == 256) ? 32 : 64;
     int gw = 1;
     for (int d = 1; d <= cfg.nw && d <= G; d++)
@@ -415,9 +512,9 @@ FwdConfig fwd_config(int G, int T, int H) {
 
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
     switch (H) {
-        case 64: return launch_fwd_t<64, 64, 8>(a, stream);
-        case 128: return launch_fwd_t<128, GQA_FWD_BKV128, 8>(a, stream);
-        case 256: return launch_fwd_t<256, 32, 4>(a, stream);
+        case 64: return launch_fwd_t<64, 64, 8, 2>(a, stream);
+        case 128: return launch_fwd_t<128, GQA_FWD_BKV128, GQA_FWD_NW128, 2>(a, stream);
+        case 256: return launch_fwd_t<256, 32, 4, 1>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -91,19 +91,27 @@ __device__ __forceinline__ buffer_rsrc make_rsrc(const void *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// 32-bit LDS byte address of a __shared__ object.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 // 16 bytes per lane from a buffer straight into LDS (no registers). The wave's
-// 64 lanes write 1 KiB at dst (wave-uniform): lane l at dst + 16 l bytes.
-// dst is made provably wave-uniform (it is kept in M0).
-// The byte offset is voffset (per lane) + soffset (wave-uniform).
-__device__ __forceinline__ void lds_load16(const buffer_rsrc &rs, __bf16 *dst, int voffset, int soffset = 0) {
+// 64 lanes write 1 KiB at LDS byte address dst (wave-uniform, kept in M0):
+// lane l at dst + 16 l. The byte offset in the buffer is voffset (per lane) +
+// soffset (wave-uniform).
+__device__ __forceinline__ void lds_load16(const buffer_rsrc &rs, unsigned dst, int voffset, int soffset) {
     typedef __attribute__((address_space(3))) void lds_void;
-    const unsigned addr = (unsigned)(size_t)(lds_void *)dst;
-    lds_void *p = (lds_void *)(size_t)__builtin_amdgcn_readfirstlane(addr);
+    lds_void *p = (lds_void *)(size_t)__builtin_amdgcn_readfirstlane(dst);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, p, 16, voffset, soffset, 0, 0);
 }
 
 // Wait until this wave's LDS-direct loads have landed (vmcnt = 0 only).
 __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Keep the compiler's scheduler from moving instructions across this point
+// (bounds how far ahead it hoists LDS operand reads, and so register pressure).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
