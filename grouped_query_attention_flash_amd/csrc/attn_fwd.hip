@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         const unsigned base = lds_addr(dst) + wave_slot;
 #pragma unroll
         for (int i = 0; i < K_PER_WAVE; i++)
-            if ((wave + i * NW) * 64 + lane < L::K_BLOCKS * 64)  // whole waves in or out
+            if ((i + 1) * NW <= L::K_BLOCKS || wave + i * NW < L::K_BLOCKS)  // wave-uniform
                 lds_load16(krs, base + i * NW * 1024, k_off[i], tile);
     };
     auto issue_v = [&](int j, const __bf16 *dst) {
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         const unsigned base = lds_addr(dst) + wave_slot;
 #pragma unroll
         for (int i = 0; i < V_PER_WAVE; i++)
-            if ((wave + i * NW) * 64 + lane < L::V_BLOCKS * 64)
+            if ((i + 1) * NW <= L::V_BLOCKS || wave + i * NW < L::V_BLOCKS)
                 lds_load16(vrs, base + i * NW * 1024, v_off[i], tile);
     };
 
@@ -264,24 +264,30 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     // A row's keys are split between lane n and lane n + 32; each checks its
     // own half, so the common case needs no cross-lane exchange. When some row
     // must move, both halves take the full row max, so m_run stays identical in
-    // the lane pair. Returns the reference the weights are taken against.
-    auto rowmax_rescale = [&](const f32x16 (&sacc)[MB]) {
+    // the lane pair.
+    auto tile_max = [&](const f32x16 (&sacc)[MB]) {
         // four independent partial maxima (short dependency chains)
         float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) m4[(r >> 1) & 3] = fmaxf(m4[(r >> 1) & 3], fmaxf(sacc[mb][r], sacc[mb][r + 1]));
-        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        if (__any(mx * kLog2e > m_run + kRescaleLog2)) {
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx * kLog2e);
-            const float corr = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
-            l_run *= corr;
+            for (int r = 0; r < 16; r += 2)
+                m4[(r >> 1) & 3] = max_nan(m4[(r >> 1) & 3], max_nan(sacc[mb][r], sacc[mb][r + 1]));
+        return max_nan(max_nan(m4[0], m4[1]), max_nan(m4[2], m4[3]));
+    };
+    auto rescale = [&](float mx) {
+        mx = max_nan(mx, __shfl_xor(mx, 32));
+        const float m_new = max_nan(m_run, mx * kLog2e);
+        const float corr = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= corr;
 #pragma unroll
-            for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
-            m_run = m_new;
-        }
+        for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
+        m_run = m_new;
+    };
+    // returns the reference the weights are taken against
+    auto rowmax_rescale = [&](const f32x16 (&sacc)[MB]) {
+        const float mx = tile_max(sacc);
+        if (__any(mx * kLog2e > m_run + kRescaleLog2)) rescale(mx);
         return (m_run == -INFINITY) ? 0.f : m_run;
     };
     // P = exp2(S log2e - m) in bf16 (the PV operand); returns this lane's part
@@ -336,17 +342,29 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         __syncthreads();
         f32x16 sa[MB], sb[MB];
         qk(sk0, sa);
+        // Tiles before the diagonal have no masked keys, so the rescale test needs
+        // no row max: every weight is >= 0, and a lane whose weights for the tile
+        // sum to at most 2^kRescaleLog2 has none above that bound. The weights are
+        // computed against the current reference first; only when some lane's sum
+        // exceeds the bound (or is inf / NaN, as on the first tile, where the
+        // reference is -inf) does the wave take the row max, rescale and recompute.
+        // A sum can pass the bound while every weight is below it; the rescale is
+        // exact either way.
         auto step = [&](f32x16 (&s_cur)[MB], f32x16 (&s_nxt)[MB], const __bf16 *k_cur, const __bf16 *k_nxt,
                         const __bf16 *v_cur, const __bf16 *v_nxt, int i) {
             wait_lds_loads();
             __syncthreads();
             if (i + 2 < n_t) issue_k(i + 2, k_cur);
             issue_v(i + 1, v_nxt);
-            const float m_use = rowmax_rescale(s_cur);
             bf16x8 pf[PK];
             if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
             qk(k_nxt, s_nxt);
-            l_run += weights(s_cur, m_use, pf);
+            float ls = weights(s_cur, m_run, pf);
+            if (__any(!(ls <= kRescaleBound))) {
+                rescale(tile_max(s_cur));
+                ls = weights(s_cur, m_run, pf);
+            }
+            l_run += ls;
             pv(pf, v_cur);
             if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
         };

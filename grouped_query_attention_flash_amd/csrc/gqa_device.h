@@ -20,6 +20,7 @@ constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
 // The online softmax moves its reference max only when a row max grows by more
 // than this many powers of two, so unnormalised weights stay below 2^8.
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRescaleBound = 256.0f;  // 2^kRescaleLog2
 
 // D = A * B + C on a 32x32 fp32 tile, A 32x16 and B 16x32 in bf16.
 // Operand layout (64-wide wave): lane l holds A[l%32][8*(l/32) .. +7] and
@@ -114,6 +115,10 @@ __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max that propagates NaN (IEEE 754-2019 maximum): gfx950 has a three-input
+// form of it, and unlike fmaxf it needs no canonicalisation of its inputs.
+__device__ __forceinline__ float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 __device__ __forceinline__ int wave_min_i(int x) {
 #pragma unroll
