@@ -29,6 +29,8 @@
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
+#include <utility>
 
 // Build-time switches of the forward schedule (defaults are the tuned ones).
 #ifndef GQA_FWD_FASTPATH
@@ -36,6 +38,14 @@
 #endif
 #ifndef GQA_FWD_SCHED
 #define GQA_FWD_SCHED 0
+#endif
+// interleave pattern for the dense loop (MFMA / operand reads / VALU)
+#ifndef GQA_FWD_DSCHED
+#define GQA_FWD_DSCHED 1
+#endif
+// LDS operand reads run this many MFMAs ahead in the dense loop
+#ifndef GQA_FWD_PREF
+#define GQA_FWD_PREF 2
 #endif
 #ifndef GQA_FWD_BKV128
 #define GQA_FWD_BKV128 64
@@ -55,6 +65,26 @@
 #endif
 
 namespace gqa {
+
+// Interleave pattern of one dense-loop iteration for the machine scheduler.
+// MFMA slot m: the MFMA, the LDS operand reads of MFMA m + D (one b128 read of
+// K for each of the N_QK QK^T MFMAs, two transpose reads of V for each PV
+// MFMA), then VALU_PER VALU instructions of the weight computation.
+template <int M, int N_QK, int N_MFMA>
+__device__ __forceinline__ void sched_operand_reads() {
+    if constexpr (M < N_MFMA) __builtin_amdgcn_sched_group_barrier(0x100, (M < N_QK) ? 1 : 2, 0);
+}
+template <int M, int N_QK, int N_MFMA, int D, int VALU_PER>
+__device__ __forceinline__ void sched_slot() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    sched_operand_reads<M + D, N_QK, N_MFMA>();
+    __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
+}
+template <int N_QK, int N_MFMA, int D, int VALU_PER, int... P, int... M>
+__device__ __forceinline__ void dense_schedule(std::integer_sequence<int, P...>, std::integer_sequence<int, M...>) {
+    (sched_operand_reads<P, N_QK, N_MFMA>(), ...);
+    (sched_slot<M, N_QK, N_MFMA, D, VALU_PER>(), ...);
+}
 
 // DENSE: no segment ids, whole key tiles (S % BKV == 0) and, when causal,
 // T == S with one query block per key tile (bq == BKV): only the last tile of
@@ -333,67 +363,105 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     };
 
     if constexpr (DENSE) {
-        // ---- dense pipeline over tiles 0 .. n_t-1 (same buffer rotation as below)
+        // ---- dense pipeline over tiles 0 .. n_t-1, two stages deep.
+        // Iteration i (0 <= i < n_t - 1) issues the QK^T MFMAs of tile i+1 and the
+        // PV MFMAs of tile i-1, and between them computes the weights of tile i,
+        // so every MFMA of the iteration has VALU work beside it. Tile i+1's K and
+        // tile i-1's V are read from LDS while K(i+2) and V(i) are being loaded
+        // into the buffers that held K(i) and V(i-2).
+        //
+        // Buffer and register roles alternate between iterations; "A" iterations
+        // (even i) hold S(i) in sa and P(i) in pa and read (kB, vB), "B" iterations
+        // the other halves. The last iteration always runs in the A roles: when
+        // n_t - 1 is odd, its S and the previous P are copied over once and the
+        // buffer pointers are swapped (uniform values).
         const int n_t = CAUSAL ? qb + 1 : S / BKV;
-        issue_k(0, sk0);
-        issue_v(0, sv0);
-        if (n_t > 1) issue_k(1, sk1);
+        f32x16 sa[MB], sb[MB];
+        bf16x8 pa[PK], pb[PK];
+        const __bf16 *kA = sk0, *kB = sk1, *vA = sv0, *vB = sv1;
+        issue_k(0, kA);
+        if (n_t > 1) issue_k(1, kB);
         wait_lds_loads();
         __syncthreads();
-        f32x16 sa[MB], sb[MB];
-        qk(sk0, sa);
-        // Tiles before the diagonal have no masked keys, so the rescale test needs
-        // no row max: every weight is >= 0, and a lane whose weights for the tile
-        // sum to at most 2^kRescaleLog2 has none above that bound. The weights are
-        // computed against the current reference first; only when some lane's sum
-        // exceeds the bound (or is inf / NaN, as on the first tile, where the
-        // reference is -inf) does the wave take the row max, rescale and recompute.
-        // A sum can pass the bound while every weight is below it; the rescale is
-        // exact either way.
-        auto step = [&](f32x16 (&s_cur)[MB], f32x16 (&s_nxt)[MB], const __bf16 *k_cur, const __bf16 *k_nxt,
-                        const __bf16 *v_cur, const __bf16 *v_nxt, int i) {
+        qk(kA, sa);
+
+        // Weights of a tile with no masked key. The rescale test needs no row max:
+        // weights are >= 0, so a lane whose weights sum to at most 2^kRescaleLog2
+        // has none above that bound. Only when some lane's sum exceeds it (or is
+        // inf / NaN, as on the first tile, whose reference is -inf) does the wave
+        // take the row max, rescale and recompute. A sum can pass the bound while
+        // every weight is below it; the rescale is exact either way.
+        auto mid = [&](auto with_pv, f32x16 (&s_cur)[MB], f32x16 (&s_nxt)[MB], const bf16x8 (&p_prev)[PK],
+                       bf16x8 (&p_cur)[PK], const __bf16 *k_rd, const __bf16 *k_ld, const __bf16 *v_rd,
+                       const __bf16 *v_ld, int i) {
             wait_lds_loads();
             __syncthreads();
-            if (i + 2 < n_t) issue_k(i + 2, k_cur);
-            issue_v(i + 1, v_nxt);
-            bf16x8 pf[PK];
+            if (i + 2 < n_t) issue_k(i + 2, k_ld);
+            issue_v(i, v_ld);
             if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
-            qk(k_nxt, s_nxt);
-            float ls = weights(s_cur, m_run, pf);
+            qk(k_rd, s_nxt);
+            if constexpr (decltype(with_pv)::value) pv(p_prev, v_rd);
+            float ls = weights(s_cur, m_run, p_cur);
+#if GQA_FWD_DSCHED
+            constexpr int n_qk = MB * KSTEPS;
+            constexpr int n_mfma = n_qk + (decltype(with_pv)::value ? PK * HB : 0);
+            constexpr int valu_per = (3 * MB * 16 + n_mfma - 1) / n_mfma;
+            dense_schedule<n_qk, n_mfma, GQA_FWD_PREF, valu_per>(std::make_integer_sequence<int, GQA_FWD_PREF>(),
+                                                                std::make_integer_sequence<int, n_mfma>());
+#endif
+            // a rescale in here multiplies O after the PV above has been added:
+            // P(i-1) was taken against the old reference
             if (__any(!(ls <= kRescaleBound))) {
                 rescale(tile_max(s_cur));
-                ls = weights(s_cur, m_run, pf);
+                ls = weights(s_cur, m_run, p_cur);
             }
             l_run += ls;
-            pv(pf, v_cur);
             if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
         };
-        auto last = [&](f32x16 (&s_cur)[MB], const __bf16 *v_cur) {
+        using no_pv = std::integral_constant<bool, false>;
+        using do_pv = std::integral_constant<bool, true>;
+        if (n_t > 1) {
+            mid(no_pv{}, sa, sb, pb, pa, kB, kA, vB, vA, 0);
+            int i = 1;
+            while (i + 1 < n_t - 1) {
+                mid(do_pv{}, sb, sa, pa, pb, kA, kB, vA, vB, i);
+                mid(do_pv{}, sa, sb, pb, pa, kB, kA, vB, vA, i + 1);
+                i += 2;
+            }
+            if (i < n_t - 1) mid(do_pv{}, sb, sa, pa, pb, kA, kB, vA, vB, i++);
+            if (i & 1) {
+#pragma unroll
+                for (int mb = 0; mb < MB; mb++) sa[mb] = sb[mb];
+#pragma unroll
+                for (int kk = 0; kk < PK; kk++) pb[kk] = pa[kk];
+                const __bf16 *t = kA;
+                kA = kB;
+                kB = t;
+                t = vA;
+                vA = vB;
+                vB = t;
+            }
+            // last tile (the diagonal one when causal): PV of the tile before it,
+            // then its own mask, weights and PV
             wait_lds_loads();
             __syncthreads();
-            if (CAUSAL) mask_tile(s_cur, (n_t - 1) * BKV);
-            softmax_pv(s_cur, v_cur);
-        };
-        // The loop runs whole pairs of steps so that the last tile's S^T always
-        // ends in sa: an odd step count is evened out by one step before the
-        // loop, whose S^T is moved into sa once; the K/V buffer roles then flip,
-        // which only changes (uniform) LDS base pointers.
-        int i = 0;
-        const __bf16 *kA = sk0, *kB = sk1, *vA = sv0, *vB = sv1;
-        if ((n_t - 1) & 1) {
-            step(sa, sb, sk0, sk1, sv0, sv1, i++);
-#pragma unroll
-            for (int mb = 0; mb < MB; mb++) sa[mb] = sb[mb];
-            kA = sk1;
-            kB = sk0;
-            vA = sv1;
-            vB = sv0;
+            issue_v(n_t - 1, vA);
+            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+            pv(pb, vB);
+            if (CAUSAL) mask_tile(sa, (n_t - 1) * BKV);
+            const float m_use = rowmax_rescale(sa);
+            l_run += weights(sa, m_use, pa);
+            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+            wait_lds_loads();
+            __syncthreads();
+            pv(pa, vA);
+        } else {
+            issue_v(0, vA);
+            wait_lds_loads();
+            __syncthreads();
+            if (CAUSAL) mask_tile(sa, 0);
+            softmax_pv(sa, vA);
         }
-        while (i + 1 < n_t) {
-            step(sa, sb, kA, kB, vA, vB, i++);
-            step(sb, sa, kB, kA, vB, vA, i++);
-        }
-        last(sa, vA);
     } else {
         // ---- software pipeline over the visible tiles n_0 < n_1 < ...
         // Iteration i starts with S^T of n_i in registers, K of n_{i+1} and V of n_i
