@@ -47,6 +47,10 @@
 #ifndef GQA_FWD_PREF
 #define GQA_FWD_PREF 2
 #endif
+// issue the global-to-LDS loads inside the dense loop's MFMA stream
+#ifndef GQA_FWD_DMASPREAD
+#define GQA_FWD_DMASPREAD 1
+#endif
 #ifndef GQA_FWD_BKV128
 #define GQA_FWD_BKV128 64
 #endif
@@ -234,21 +238,43 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         v_off[i] = ((p / L::VRS) * H + min(p % L::VRS, CPR - 1) * 8) * 2;
     }
     const unsigned wave_slot = wave * 1024;  // this wave's first 1 KiB block
-    auto issue_k = [&](int j, const __bf16 *dst) {
+    // Loads i < K_FULL (V_FULL) are issued by every wave; the rest only by the
+    // first waves (wave-uniform branches).
+    constexpr int K_FULL = L::K_BLOCKS / NW;
+    constexpr int V_FULL = L::V_BLOCKS / NW;
+    auto issue_k_part = [&](int j, const __bf16 *dst, auto full) {
         const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
-        const unsigned base = lds_addr(dst) + wave_slot;
+        char *base = (char *)dst + wave_slot;
 #pragma unroll
-        for (int i = 0; i < K_PER_WAVE; i++)
-            if ((i + 1) * NW <= L::K_BLOCKS || wave + i * NW < L::K_BLOCKS)  // wave-uniform
-                lds_load16(krs, base + i * NW * 1024, k_off[i], tile);
+        for (int i = 0; i < K_PER_WAVE; i++) {
+            if constexpr (decltype(full)::value) {
+                if (i < K_FULL) lds_load16_to(krs, base + i * NW * 1024, k_off[i], tile);
+            } else {
+                if (i >= K_FULL && wave + i * NW < L::K_BLOCKS) lds_load16_to(krs, base + i * NW * 1024, k_off[i], tile);
+            }
+        }
+    };
+    auto issue_v_part = [&](int j, const __bf16 *dst, auto full) {
+        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+        char *base = (char *)dst + wave_slot;
+#pragma unroll
+        for (int i = 0; i < V_PER_WAVE; i++) {
+            if constexpr (decltype(full)::value) {
+                if (i < V_FULL) lds_load16_to(vrs, base + i * NW * 1024, v_off[i], tile);
+            } else {
+                if (i >= V_FULL && wave + i * NW < L::V_BLOCKS) lds_load16_to(vrs, base + i * NW * 1024, v_off[i], tile);
+            }
+        }
+    };
+    using all_waves_t = std::integral_constant<bool, true>;
+    using first_waves_t = std::integral_constant<bool, false>;
+    auto issue_k = [&](int j, const __bf16 *dst) {
+        issue_k_part(j, dst, all_waves_t{});
+        issue_k_part(j, dst, first_waves_t{});
     };
     auto issue_v = [&](int j, const __bf16 *dst) {
-        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
-        const unsigned base = lds_addr(dst) + wave_slot;
-#pragma unroll
-        for (int i = 0; i < V_PER_WAVE; i++)
-            if ((i + 1) * NW <= L::V_BLOCKS || wave + i * NW < L::V_BLOCKS)
-                lds_load16(vrs, base + i * NW * 1024, v_off[i], tile);
+        issue_v_part(j, dst, all_waves_t{});
+        issue_v_part(j, dst, first_waves_t{});
     };
 
     // S^T = K_tile Q^T for one tile: lane reads row 32mb + n, chunk 2ks + c
@@ -396,9 +422,20 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
                        const __bf16 *v_ld, int i) {
             wait_lds_loads();
             __syncthreads();
+#if GQA_FWD_DMASPREAD
+            // the loads every wave issues go into the MFMA stream below (the
+            // scheduler spreads them); K(i+2) past the last tile is a dead load,
+            // or a bounds-checked zero read past the end of K
+            if (i + 2 < n_t) issue_k_part(i + 2, k_ld, first_waves_t{});
+            issue_v_part(i, v_ld, first_waves_t{});
+            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+            issue_k_part(i + 2, k_ld, all_waves_t{});
+            issue_v_part(i, v_ld, all_waves_t{});
+#else
             if (i + 2 < n_t) issue_k(i + 2, k_ld);
             issue_v(i, v_ld);
             if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+#endif
             qk(k_rd, s_nxt);
             if constexpr (decltype(with_pv)::value) pv(p_prev, v_rd);
             float ls = weights(s_cur, m_run, p_cur);
@@ -407,7 +444,7 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
             constexpr int n_mfma = n_qk + (decltype(with_pv)::value ? PK * HB : 0);
             constexpr int valu_per = (3 * MB * 16 + n_mfma - 1) / n_mfma;
             dense_schedule<n_qk, n_mfma, GQA_FWD_PREF, valu_per>(std::make_integer_sequence<int, GQA_FWD_PREF>(),
-                                                                std::make_integer_sequence<int, n_mfma>());
+                                                                        std::make_integer_sequence<int, n_mfma>());
 #endif
             // a rescale in here multiplies O after the PV above has been added:
             // P(i-1) was taken against the old reference

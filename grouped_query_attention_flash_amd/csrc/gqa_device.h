@@ -107,6 +107,14 @@ __device__ __forceinline__ void lds_load16(const buffer_rsrc &rs, unsigned dst, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, p, 16, voffset, soffset, 0, 0);
 }
 
+// The same load with the LDS destination given as a pointer into a __shared__
+// array (plus a wave-uniform offset): the compiler then knows which array the
+// load writes and may move LDS reads of other arrays across it.
+__device__ __forceinline__ void lds_load16_to(const buffer_rsrc &rs, void *dst, int voffset, int soffset) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voffset, soffset, 0, 0);
+}
+
 // Wait until this wave's LDS-direct loads have landed (vmcnt = 0 only).
 __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
