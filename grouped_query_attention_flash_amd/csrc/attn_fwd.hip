@@ -51,6 +51,17 @@
 #ifndef GQA_FWD_DMASPREAD
 #define GQA_FWD_DMASPREAD 1
 #endif
+// dense shapes at H <= 128 run the ping-pong kernel
+#ifndef GQA_FWD_PINGPONG
+#define GQA_FWD_PINGPONG 1
+#endif
+// ping-pong M phase: pinned MFMA / operand-read pattern, reads this many steps ahead
+#ifndef GQA_PP_MSCHED
+#define GQA_PP_MSCHED 1
+#endif
+#ifndef GQA_PP_MPREF
+#define GQA_PP_MPREF 2
+#endif
 #ifndef GQA_FWD_BKV128
 #define GQA_FWD_BKV128 64
 #endif
@@ -599,12 +610,286 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     }
 }
 
+
+
+// Interleave pattern of one M phase of the ping-pong kernel: NX steps of
+// NM MFMAs each (one QK^T and / or one PV MFMA), the LDS operand reads of a
+// step (R reads: one b128 read of K, two transpose reads of V) issued D steps
+// ahead.
+template <int X, int NX, int R>
+__device__ __forceinline__ void sched_m_reads() {
+    if constexpr (X < NX) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+}
+template <int X, int NX, int NM, int R, int D>
+__device__ __forceinline__ void sched_m_step() {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    sched_m_reads<X + D, NX, R>();
+}
+template <int NX, int NM, int R, int D, int... P, int... X>
+__device__ __forceinline__ void m_phase_schedule(std::integer_sequence<int, P...>, std::integer_sequence<int, X...>) {
+    (sched_m_reads<P, NX, R>(), ...);
+    (sched_m_step<X, NX, NM, R, D>(), ...);
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong forward for dense shapes at H <= 128 (the conditions of DENSE
+// above, 8 waves, one workgroup per CU).
+//
+// The two waves of each SIMD take turns: waves 0-3 (group A) and waves 4-7
+// (group B) run the same sequence of phases, B one phase behind A, with a
+// workgroup barrier between phases. A wave alternates
+//   M(i): the QK^T MFMAs of tile i+1 and the PV MFMAs of tile i (MFMA only)
+//   V(i): the weights of tile i (exp / fma / add / convert, VALU only)
+// so while one wave of a SIMD keeps the matrix pipe busy, the other does its
+// softmax beside it, and a wave needs one S^T and one P^T tile of registers.
+//
+// Tiles move through LDS in three slots: slot i % 3 holds K(i+1) and V(i),
+// the operands of M(i). During V(i) group A loads K(i+2) and group B loads
+// V(i+1) into slot (i+1) % 3, whose previous contents (read by M(i-2)) are
+// dead by then. Every wave waits for its own loads at the end of each of its
+// M phases, one barrier before any wave reads them.
+template <int H, int BKV, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
+    constexpr int NG = 4;  // waves per group (8 per workgroup)
+    constexpr int CPR = H / 8;
+    constexpr int KSTEPS = H / 16;
+    constexpr int MB = BKV / 32;
+    constexpr int HB = H / 32;
+    constexpr int PK = BKV / 16;
+    constexpr int NQK = MB * KSTEPS, NPV = PK * HB;
+    static_assert(NQK == NPV, "M phase pairs one QK^T MFMA with one PV MFMA");
+    using L = TileLayout<H, BKV>;
+    constexpr int NSLOT = 3;
+    __shared__ __attribute__((aligned(1024))) __bf16 sk[NSLOT][L::K_ELEMS];
+    __shared__ __attribute__((aligned(1024))) __bf16 sv[NSLOT][L::V_ELEMS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave / NG, gwv = wave % NG;
+    const int n = lane & 31, c = lane >> 5;
+
+    // ---- work unit (causal: heaviest query block first) and this lane's row
+    const int units = a.B * a.K * a.n_gsplit;
+    int qb = blockIdx.x / units;
+    if (CAUSAL) qb = a.n_qblocks - 1 - qb;
+    const int u = blockIdx.x % units;
+    const int gs = u % a.n_gsplit;
+    const int kh = (u / a.n_gsplit) % a.K;
+    const int b = u / (a.n_gsplit * a.K);
+    const int t0 = qb * a.bq;
+    const int T = a.T, S = a.S;
+    const int rho = wave * 32 + n;  // gw * bq == 32 * NW: every row belongs to the unit
+    const int g = gs * a.gw + rho / a.bq;
+    const int t = t0 + rho % a.bq;
+    const bool q_valid = t < T;
+    const size_t bk = (size_t)b * a.K + kh;
+    const size_t qrow_off = ((bk * a.G + g) * (size_t)T + t) * H;
+
+    bf16x8 qf[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++)
+        qf[ks] = q_valid ? *(const bf16x8 *)(a.q + qrow_off + 16 * ks + 8 * c) : bf16x8{};
+
+    const buffer_rsrc krs = make_rsrc(a.k + bk * (size_t)S * H, S * H * 2);
+    const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
+    const int n_t = CAUSAL ? qb + 1 : S / BKV;
+
+    // ---- global -> LDS loads: group A loads K tiles, group B V tiles; wave gwv
+    // of a group issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat
+    // the row's last chunk, as in TileLayout)
+    constexpr int KL = (L::K_BLOCKS + NG - 1) / NG, VL = (L::V_BLOCKS + NG - 1) / NG;
+    constexpr int NL = KL > VL ? KL : VL;
+    const int rs = grp == 0 ? L::KRS : L::VRS;
+    int ld_off[NL];
+#pragma unroll
+    for (int i = 0; i < NL; i++) {
+        const int pslot = (gwv + i * NG) * 64 + lane;
+        ld_off[i] = ((pslot / rs) * H + min(pslot % rs, CPR - 1) * 8) * 2;
+    }
+    auto issue_tile = [&](int j, int slot) {
+        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+        if (grp == 0) {
+#pragma unroll
+            for (int i = 0; i < KL; i++)
+                if (gwv + i * NG < L::K_BLOCKS)
+                    lds_load16_to(krs, (char *)sk[slot] + (gwv + i * NG) * 1024, ld_off[i], tile);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VL; i++)
+                if (gwv + i * NG < L::V_BLOCKS)
+                    lds_load16_to(vrs, (char *)sv[slot] + (gwv + i * NG) * 1024, ld_off[i], tile);
+        }
+    };
+
+    f32x16 sacc[MB];
+    bf16x8 pf[PK];
+    f32x16 oacc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++) oacc[hb] = f32x16{};
+    float m_run = -INFINITY;  // reference max, log2 units (identical in a lane pair)
+    float l_run = 0.f;        // denominator over this lane's half of the keys
+
+    // ---- M phase: QK^T MFMA x and PV MFMA x alternate (independent chains)
+    const int k_lane = n * L::KRS * 8 + c * 8;
+    const int v_lane = (4 * c + ((lane & 15) >> 2)) * L::VRS * 8 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto m_phase = [&](auto do_qk, auto do_pv, int kslot, int vslot) {
+        const __bf16 *kt = sk[kslot];
+        const __bf16 *vt = sv[vslot];
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int x = 0; x < NQK; x++) {
+            if constexpr (decltype(do_qk)::value) {
+                const int mb = x % MB, ks = x / MB;
+                const bf16x8 kf = *(const bf16x8 *)(kt + k_lane + mb * 32 * L::KRS * 8 + ks * 16);
+                sacc[mb] = mfma32x32x16(kf, qf[ks], ks == 0 ? f32x16{} : sacc[mb]);
+            }
+            if constexpr (decltype(do_pv)::value) {
+                const int kk = x / HB, hb = x % HB;
+                const __bf16 *vp = vt + v_lane + kk * 16 * L::VRS * 8 + hb * 32;
+                const s16x4 lo = lds_read_tr16(vp);
+                const s16x4 hi = lds_read_tr16(vp + 8 * L::VRS * 8);
+                oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf[kk], oacc[hb]);
+            }
+        }
+#if GQA_PP_MSCHED
+        constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
+        constexpr int D = GQA_PP_MPREF < NQK ? GQA_PP_MPREF : NQK;
+        m_phase_schedule<NQK, (QK ? 1 : 0) + (PV ? 1 : 0), (QK ? 1 : 0) + (PV ? 2 : 0), D>(
+            std::make_integer_sequence<int, D>(), std::make_integer_sequence<int, NQK>());
+#endif
+        __builtin_amdgcn_s_setprio(0);
+        wait_lds_loads();
+    };
+
+    // ---- V phase pieces (as in the kernel above)
+    auto mask_tile = [&](int s0) {
+        const int lim = min(CAUSAL ? t : INT_MAX, S - 1) - s0 - 4 * c;
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) sacc[mb][r] = -INFINITY;
+    };
+    auto tile_max = [&]() {
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2)
+                m4[(r >> 1) & 3] = max_nan(m4[(r >> 1) & 3], max_nan(sacc[mb][r], sacc[mb][r + 1]));
+        return max_nan(max_nan(m4[0], m4[1]), max_nan(m4[2], m4[3]));
+    };
+    auto rescale = [&](float mx) {
+        mx = max_nan(mx, __shfl_xor(mx, 32));
+        const float m_new = max_nan(m_run, mx * kLog2e);
+        const float corr = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= corr;
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
+        m_run = m_new;
+    };
+    auto weights = [&](float m_use) {
+        float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < PK; kk++) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e], kLog2e, -m_use));
+                const float p1 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e + 1], kLog2e, -m_use));
+                pf[kk][e] = (__bf16)p0;
+                pf[kk][e + 1] = (__bf16)p1;
+                rsum[e >> 1] += p0 + p1;
+            }
+        }
+        return (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+    };
+    // Weights of a tile with no masked key: the rescale test needs no row max
+    // (weights are >= 0, so a lane whose weights sum to at most 2^kRescaleLog2
+    // has none above it); the first tile (reference -inf) always rescales.
+    auto v_phase_open = [&]() {
+        float ls = weights(m_run);
+        if (__any(!(ls <= kRescaleBound))) {
+            rescale(tile_max());
+            ls = weights(m_run);
+        }
+        l_run += ls;
+    };
+    // The diagonal tile: element mask, row max, weights.
+    auto v_phase_masked = [&](int s0) {
+        mask_tile(s0);
+        const float mx = tile_max();
+        if (__any(mx * kLog2e > m_run + kRescaleLog2)) rescale(mx);
+        l_run += weights(m_run == -INFINITY ? 0.f : m_run);
+    };
+
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    // ---- prologue: K(0) -> slot 2, K(1) and V(0) -> slot 0
+    issue_tile(0, grp == 0 ? 2 : 0);
+    if (grp == 0 && n_t > 1) issue_tile(1, 0);
+    wait_lds_loads();
+    __syncthreads();
+
+    if (grp == 1) __syncthreads();  // group B runs one phase behind
+    m_phase(yes{}, no{}, 2, 0);      // M(-1): S^T of tile 0
+    int slot = 0;                    // slot of tile set i: K(i+1), V(i)
+    for (int i = 0; i < n_t - 1; i++) {
+        const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
+        __syncthreads();
+        // V(i)
+        if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
+        v_phase_open();
+        __syncthreads();
+        // M(i)
+        m_phase(yes{}, yes{}, slot, slot);
+        slot = nslot;
+    }
+    // the last tile (the diagonal one when causal): nothing left to load or to
+    // multiply with K
+    __syncthreads();
+    if (CAUSAL)
+        v_phase_masked((n_t - 1) * BKV);
+    else
+        v_phase_open();
+    __syncthreads();
+    m_phase(no{}, yes{}, slot, slot);
+    if (grp == 0) __syncthreads();  // group A's trailing phase
+
+    // ---- finalize
+    l_run += __shfl_xor(l_run, 32);
+    if (q_valid) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        __bf16 *orow = a.o + qrow_off;
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                bf16x4 val;
+#pragma unroll
+                for (int e = 0; e < 4; e++) val[e] = (__bf16)(oacc[hb][4 * q4 + e] * inv);
+                *(bf16x4 *)(orow + 32 * hb + 8 * q4 + 4 * c) = val;
+            }
+        if (c == 0 && a.lse)
+            a.lse[(bk * a.G + g) * (size_t)T + t] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    }
+}
+
 template <int H, int BKV, int NW, int WPS>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks);
     const bool all_waves = a.gw * a.bq == 32 * NW;
     const bool dense = a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
                        (!a.causal || (a.T == a.S && a.bq == BKV));
+    if constexpr (GQA_FWD_PINGPONG && H <= 128 && NW == 8) {
+        if (dense) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+            else
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     if (a.causal && dense)
         hipLaunchKernelGGL((attn_fwd_kernel<H, BKV, NW, WPS, true, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
     else if (a.causal)

@@ -37,6 +37,14 @@ SMALL = [
     (1, 2, 8, 256, 256, 256, True, None),
     (1, 1, 4, 90, 130, 256, False, None),
     (1, 1, 8, 128, 128, 256, True, (10, 60)),
+    # whole key tiles without segment ids (the ping-pong path at H <= 128):
+    # one- and two-tile causal blocks, ragged T with G = 1, 2, 8, longer H = 64
+    (1, 1, 4, 64, 64, 128, True, None),
+    (1, 2, 4, 128, 128, 128, True, None),
+    (1, 1, 2, 100, 192, 128, False, None),
+    (1, 1, 1, 300, 128, 64, False, None),
+    (1, 1, 8, 77, 256, 128, False, None),
+    (2, 1, 4, 384, 384, 64, True, None),
 ]
 
 
