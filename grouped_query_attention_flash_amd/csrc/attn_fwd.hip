@@ -789,19 +789,25 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
         m_run = m_new;
     };
     auto weights = [&](float m_use) {
-        float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+        float w[PK * 8];
 #pragma unroll
-        for (int kk = 0; kk < PK; kk++) {
+        for (int kk = 0; kk < PK; kk++)
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const float p0 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e], kLog2e, -m_use));
-                const float p1 = exp2_fast(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e + 1], kLog2e, -m_use));
-                pf[kk][e] = (__bf16)p0;
-                pf[kk][e + 1] = (__bf16)p1;
-                rsum[e >> 1] += p0 + p1;
-            }
-        }
-        return (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+            for (int e = 0; e < 8; e++) w[kk * 8 + e] = __builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + e], kLog2e, -m_use);
+        sched_fence();
+#pragma unroll
+        for (int j = 0; j < PK * 8; j++) w[j] = exp2_fast(w[j]);
+        sched_fence();
+#pragma unroll
+        for (int kk = 0; kk < PK; kk++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) pf[kk][e] = (__bf16)w[kk * 8 + e];
+        // pairwise tree: short dependency chains for a lone VALU wave
+#pragma unroll
+        for (int n2 = PK * 8 / 2; n2 >= 1; n2 /= 2)
+#pragma unroll
+            for (int j = 0; j < n2; j++) w[j] = w[2 * j] + w[2 * j + 1];
+        return w[0];
     };
     // Weights of a tile with no masked key: the rescale test needs no row max
     // (weights are >= 0, so a lane whose weights sum to at most 2^kRescaleLog2
@@ -829,32 +835,32 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     issue_tile(0, grp == 0 ? 2 : 0);
     if (grp == 0 && n_t > 1) issue_tile(1, 0);
     wait_lds_loads();
-    __syncthreads();
+    barrier_no_drain();
 
-    if (grp == 1) __syncthreads();  // group B runs one phase behind
+    if (grp == 1) barrier_no_drain();  // group B runs one phase behind
     m_phase(yes{}, no{}, 2, 0);      // M(-1): S^T of tile 0
     int slot = 0;                    // slot of tile set i: K(i+1), V(i)
     for (int i = 0; i < n_t - 1; i++) {
         const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
-        __syncthreads();
+        barrier_no_drain();
         // V(i)
         if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
         v_phase_open();
-        __syncthreads();
+        barrier_no_drain();
         // M(i)
         m_phase(yes{}, yes{}, slot, slot);
         slot = nslot;
     }
     // the last tile (the diagonal one when causal): nothing left to load or to
     // multiply with K
-    __syncthreads();
+    barrier_no_drain();
     if (CAUSAL)
         v_phase_masked((n_t - 1) * BKV);
     else
         v_phase_open();
-    __syncthreads();
+    barrier_no_drain();
     m_phase(no{}, yes{}, slot, slot);
-    if (grp == 0) __syncthreads();  // group A's trailing phase
+    if (grp == 0) barrier_no_drain();  // group A's trailing phase
 
     // ---- finalize
     l_run += __shfl_xor(l_run, 32);

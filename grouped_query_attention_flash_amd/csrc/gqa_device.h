@@ -117,6 +117,21 @@ __device__ __forceinline__ void lds_load16_to(const buffer_rsrc &rs, void *dst, 
 
 // Wait until this wave's LDS-direct loads have landed (vmcnt = 0 only).
 __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's vector-memory loads are outstanding (they
+// complete in issue order), i.e. all but the N most recent have landed.
+template <int N>
+__device__ __forceinline__ void wait_lds_loads_but() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the release/acquire fence of __syncthreads(),
+// which would make every wave drain all of its outstanding global-to-LDS
+// loads first. Callers wait themselves (wait_lds_loads_but / wait_lds_loads)
+// for the loads that other waves read after the barrier; LDS operand reads are
+// consumed (waited for) before the barrier. The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_no_drain() { asm volatile("s_barrier" ::: "memory"); }
 
 // Keep the compiler's scheduler from moving instructions across this point
 // (bounds how far ahead it hoists LDS operand reads, and so register pressure).
