@@ -59,6 +59,10 @@
 #ifndef GQA_PP_MSCHED
 #define GQA_PP_MSCHED 1
 #endif
+// ping-pong: O leaves through LDS in coalesced 1 KiB stores
+#ifndef GQA_PP_OSTAGE
+#define GQA_PP_OSTAGE 1
+#endif
 #ifndef GQA_PP_MPREF
 #define GQA_PP_MPREF 2
 #endif
@@ -788,6 +792,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
         for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
         m_run = m_new;
     };
+    // all scaled logits before all exponentials: a lone VALU wave would
+    // otherwise wait on each fma before its exp
     auto weights = [&](float m_use) {
         float w[PK * 8];
 #pragma unroll
@@ -862,10 +868,44 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     m_phase(no{}, yes{}, slot, slot);
     if (grp == 0) barrier_no_drain();  // group A's trailing phase
 
-    // ---- finalize
+    // ---- finalize: O = acc / l in bf16 through LDS, so that the wave's 32 rows
+    // (consecutive queries of one head: 8 KiB contiguous in o) leave in eight
+    // fully coalesced 1 KiB stores; lse = ln(sum exp(logits)).
     l_run += __shfl_xor(l_run, 32);
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#if GQA_PP_OSTAGE
+    // Staging region of this wave: 32 rows of 272 bytes (padded: conflict-free
+    // 8-byte writes), two waves per K slot and the last two in a V slot. Every
+    // K slot and V slot n_t % 3 are dead here: the only phase still running is
+    // group B's last PV, which reads V slot (n_t - 1) % 3, and all loads have
+    // landed (each M phase ends with a wait).
+    constexpr int OROW = H * 2 + 16;
+    static_assert(2 * 32 * OROW <= L::K_ELEMS * 2 && 2 * 32 * OROW <= L::V_ELEMS * 2, "staging fits a slot");
+    char *stage = (wave < 6 ? (char *)sk[wave >> 1] : (char *)sv[n_t % NSLOT]) + (wave & 1) * 32 * OROW;
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+            bf16x4 val;
+#pragma unroll
+            for (int e = 0; e < 4; e++) val[e] = (__bf16)(oacc[hb][4 * q4 + e] * inv);
+            *(bf16x4 *)(stage + n * OROW + (32 * hb + 8 * q4 + 4 * c) * 2) = val;
+        }
+    // rows of this wave: queries t_w .. t_w + 31 of head g (all lanes agree)
+    const int t_w = t - n;
+    __bf16 *orows = a.o + ((bk * a.G + g) * (size_t)T + t_w) * H;
+    constexpr int CPR16 = H / 8;  // 16-byte chunks per row
+#pragma unroll
+    for (int j = 0; j < 32 * CPR16 / 64; j++) {
+        const int idx = j * 64 + lane;
+        const int r = idx / CPR16, ch = idx % CPR16;
+        const bf16x8 val = *(const bf16x8 *)(stage + r * OROW + ch * 16);
+        if (t_w + r < T) *(bf16x8 *)(orows + (size_t)r * H + ch * 8) = val;
+    }
+    if (q_valid && c == 0 && a.lse)
+        a.lse[(bk * a.G + g) * (size_t)T + t] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+#else
     if (q_valid) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
         __bf16 *orow = a.o + qrow_off;
 #pragma unroll
         for (int hb = 0; hb < HB; hb++)
@@ -879,6 +919,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
         if (c == 0 && a.lse)
             a.lse[(bk * a.G + g) * (size_t)T + t] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
     }
+#endif
 }
 
 template <int H, int BKV, int NW, int WPS>
