@@ -25,6 +25,12 @@
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
+
+// pipelined dK/dV kernel for shapes without segment ids at H <= 128
+#ifndef GQA_BWD_DKV2
+#define GQA_BWD_DKV2 1
+#endif
 
 namespace gqa {
 
@@ -260,6 +266,212 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
             }
         }
         st = st_next;
+    }
+
+    // dK, dV rows (fp32): lane (n, c) holds h = 32hb + acc_row(r, c) of key s
+    if (k_valid) {
+        float *dkrow = a.dk + (bk * S + s) * H;
+        float *dvrow = a.dv + (bk * S + s) * H;
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                const int h = 32 * hb + 8 * q4 + 4 * c;
+                *(f32x4 *)(dkrow + h) = f32x4{dk_acc[hb][4 * q4], dk_acc[hb][4 * q4 + 1], dk_acc[hb][4 * q4 + 2],
+                                              dk_acc[hb][4 * q4 + 3]};
+                *(f32x4 *)(dvrow + h) = f32x4{dv_acc[hb][4 * q4], dv_acc[hb][4 * q4 + 1], dv_acc[hb][4 * q4 + 2],
+                                              dv_acc[hb][4 * q4 + 3]};
+            }
+    }
+    (void)n_kblocks;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV for shapes without segment ids at H <= 128: the same products as the
+// kernel above, pipelined. Q, dO, lse and D of each 32-query step go straight
+// from memory into a three-stage LDS ring (no register staging), and
+// iteration i issues the S and dP MFMAs of step i+1 before the dV and dK
+// MFMAs of step i, with step i+1's weights computed beside the latter.
+// One wave per SIMD (up to 512 registers): the overlap is inside the wave.
+//
+// LDS tile layout: the XOR swizzle of the kernel above (row r, 16-byte chunk x
+// stored at position x ^ swz(r)); the loads write 1 KiB per wave instruction
+// lane-linearly, so each lane fetches the global chunk that belongs in its slot.
+template <int H, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_kblocks) {
+    constexpr int NW = 4, BQ = 32;
+    constexpr int CPR = H / 8;
+    constexpr int KSTEPS = H / 16;
+    constexpr int HB = H / 32;
+    constexpr int TILE = BQ * H;                  // bf16 elements of a Q or dO tile
+    constexpr int TBLK = TILE * 2 / 1024;         // its 1 KiB wave loads
+    constexpr int TBW = (TBLK + NW - 1) / NW;     // per wave and tensor
+    constexpr int NSTAGE = 3;
+    static_assert(TBLK % NW == 0, "tile loads spread evenly over the waves");
+    __shared__ __attribute__((aligned(1024))) __bf16 sq[NSTAGE][TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 sdo[NSTAGE][TILE];
+    __shared__ __attribute__((aligned(1024))) float sld[NSTAGE][2][256];  // lse, D (32 used)
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, c = lane >> 5;
+    const int T = a.T, S = a.S, G = a.G;
+
+    const int units = a.B * a.K;
+    const int kb_idx = blockIdx.x / units;  // heaviest (causal) key block first
+    const int u = blockIdx.x % units;
+    const int kh = u % a.K, b = u / a.K;
+    const int s0_wg = kb_idx * 32 * NW;
+    const int s_w = s0_wg + 32 * wave;
+    const int s = s_w + n;
+    const bool k_valid = s < S;
+    const size_t bk = (size_t)b * a.K + kh;
+
+    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    {
+        const __bf16 *krow = a.k + (bk * S + s) * H;
+        const __bf16 *vrow = a.v + (bk * S + s) * H;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            kf[ks] = k_valid ? *(const bf16x8 *)(krow + 16 * ks + 8 * c) : bf16x8{};
+            vf[ks] = k_valid ? *(const bf16x8 *)(vrow + 16 * ks + 8 * c) : bf16x8{};
+        }
+    }
+
+    // steps: (g, query tile) pairs, g outer; causal: tiles holding some t >= s0_wg
+    const int n_qt = (T + BQ - 1) / BQ;
+    const int qt_begin = CAUSAL ? min(n_qt, s0_wg / BQ) : 0;
+    const int nq = n_qt - qt_begin;
+    const int n_steps = G * nq;
+
+    // loads of one step: Q and dO tiles (wave w: blocks w, w + NW, ...), lse (wave 0), D (wave 1)
+    const buffer_rsrc qrs = make_rsrc(a.q + bk * G * (size_t)T * H, G * T * H * 2);
+    const buffer_rsrc drs = make_rsrc(a.dout + bk * G * (size_t)T * H, G * T * H * 2);
+    const buffer_rsrc lrs = make_rsrc(a.lse + bk * G * (size_t)T, G * T * 4);
+    const buffer_rsrc ers = make_rsrc(a.delta + bk * G * (size_t)T, G * T * 4);
+    int t_off[TBW];
+#pragma unroll
+    for (int i = 0; i < TBW; i++) {
+        const int p = (wave + i * NW) * 64 + lane;
+        const int r = p / CPR, x = p % CPR;
+        t_off[i] = (r * H + ((x ^ swz<CPR>(r)) << 3)) * 2;
+    }
+    auto step_pos = [&](int st, int &g, int &t0) {
+        g = st / nq;
+        t0 = (qt_begin + st - g * nq) * BQ;
+    };
+    auto issue_step = [&](int st, int stage) {
+        int g, t0;
+        step_pos(st, g, t0);
+        const int row0 = __builtin_amdgcn_readfirstlane(g * T + t0);
+#pragma unroll
+        for (int i = 0; i < TBW; i++) {
+            lds_load16_to(qrs, (char *)sq[stage] + (wave + i * NW) * 1024, t_off[i], row0 * H * 2);
+            lds_load16_to(drs, (char *)sdo[stage] + (wave + i * NW) * 1024, t_off[i], row0 * H * 2);
+        }
+        // 32 floats of lse / D: lanes 0-7 fetch them, the other lanes repeat
+        // in-range addresses into slots that are not read
+        if (wave == 0) lds_load16_to(lrs, (char *)sld[stage][0], (lane & 7) * 16, row0 * 4);
+        if (wave == 1) lds_load16_to(ers, (char *)sld[stage][1], (lane & 7) * 16, row0 * 4);
+    };
+
+    f32x16 dv_acc[HB], dk_acc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++) {
+        dv_acc[hb] = f32x16{};
+        dk_acc[hb] = f32x16{};
+    }
+
+    // S = Q K^T and dP = dO V^T of a step (32 queries x the wave's 32 keys)
+    const int sw_n = swz<CPR>(n);
+    auto sdp = [&](int stage, f32x16 &sacc, f32x16 &pacc) {
+        const __bf16 *qrow = sq[stage] + n * H;
+        const __bf16 *drow = sdo[stage] + n * H;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            const int off = ((2 * ks + c) ^ sw_n) << 3;
+            sacc = mfma32x32x16(*(const bf16x8 *)(qrow + off), kf[ks], ks == 0 ? f32x16{} : sacc);
+            pacc = mfma32x32x16(*(const bf16x8 *)(drow + off), vf[ks], ks == 0 ? f32x16{} : pacc);
+        }
+    };
+    // P = exp2(S log2e - lse log2e) and dS = P (dP - D), as bf16 MFMA operands
+    // (2 x 8 queries each). Invisible (query, key) pairs get P = 0: with
+    // causal masking a pair is visible iff 0 <= t - s < T - s, otherwise iff
+    // t < T; one unsigned compare per element (a key past S gets bound 0).
+    const unsigned vis_bound = k_valid ? (unsigned)(CAUSAL ? T - s : T) : 0u;
+    auto weights = [&](int stage, int t0, const f32x16 &sacc, const f32x16 &pacc, bf16x8 (&pf)[2], bf16x8 (&sf)[2]) {
+        const int tb = t0 + 4 * c - (CAUSAL ? s : 0);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+            const int r0 = 8 * q4 + 4 * c;
+            const f32x4 l4 = *(const f32x4 *)(&sld[stage][0][r0]);
+            const f32x4 d4 = *(const f32x4 *)(&sld[stage][1][r0]);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = 4 * q4 + e;
+                float p = exp2_fast(__builtin_fmaf(sacc[r], kLog2e, -l4[e] * kLog2e));
+                p = (unsigned)(tb + 8 * q4 + e) < vis_bound ? p : 0.f;
+                pf[r >> 3][r & 7] = (__bf16)p;
+                sf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - d4[e]));
+            }
+        }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS for a step (k = the step's 32 queries)
+    const int gi = lane & 15, hh = (lane >> 4) & 1;
+    auto dvdk = [&](int stage, const bf16x8 (&pf)[2], const bf16x8 (&sf)[2]) {
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+            const int r0 = 16 * kk + 4 * c + (gi >> 2);
+            const int r1 = r0 + 8;
+            const int sw0 = swz<CPR>(r0), sw1 = swz<CPR>(r1);
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++) {
+                const int hcol = 32 * hb + 16 * hh + 4 * (gi & 3);
+                const int ch = hcol >> 3, within = hcol & 7;
+                const int o0 = r0 * H + ((ch ^ sw0) << 3) + within;
+                const int o1 = r1 * H + ((ch ^ sw1) << 3) + within;
+                const bf16x8 dot = join_bf16x8(lds_read_tr16(sdo[stage] + o0), lds_read_tr16(sdo[stage] + o1));
+                dv_acc[hb] = mfma32x32x16(dot, pf[kk], dv_acc[hb]);
+                const bf16x8 qt = join_bf16x8(lds_read_tr16(sq[stage] + o0), lds_read_tr16(sq[stage] + o1));
+                dk_acc[hb] = mfma32x32x16(qt, sf[kk], dk_acc[hb]);
+            }
+        }
+    };
+    if (n_steps > 0) {
+        issue_step(0, 0);
+        if (n_steps > 1) issue_step(1, 1);
+        wait_lds_loads();
+        __syncthreads();
+        f32x16 sa, pa;
+        bf16x8 pfa[2], sfa[2];
+        sdp(0, sa, pa);
+        {
+            int g0, t00;
+            step_pos(0, g0, t00);
+            weights(0, t00, sa, pa, pfa, sfa);
+        }
+        // iteration i: stage i % 3 holds step i (dV / dK now), stage (i+1) % 3
+        // step i+1 (S / dP now); step i+2 is loaded into stage (i+2) % 3, which
+        // held step i-1 (read in the previous iteration). Past the last step the
+        // load is a bounds-checked zero read into a stage that is not read again.
+        int stage = 0;
+        for (int i = 0; i + 1 < n_steps; i++) {
+            const int st1 = stage == NSTAGE - 1 ? 0 : stage + 1;
+            const int st2 = st1 == NSTAGE - 1 ? 0 : st1 + 1;
+            barrier_no_drain();
+            issue_step(i + 2, st2);
+            f32x16 sb, pb;
+            sdp(st1, sb, pb);
+            dvdk(stage, pfa, sfa);
+            int g1, t01;
+            step_pos(i + 1, g1, t01);
+            weights(st1, t01, sb, pb, pfa, sfa);
+            // the loads of step i+2 land before the next barrier
+            wait_lds_loads();
+            stage = st1;
+        }
+        barrier_no_drain();
+        dvdk(stage, pfa, sfa);
     }
 
     // dK, dV rows (fp32): lane (n, c) holds h = 32hb + acc_row(r, c) of key s
@@ -541,8 +753,17 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int keys_wg = 32 * NW_DKV;
     const int n_kblocks = (a.S + keys_wg - 1) / keys_wg;
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<H, NW_DKV>), dim3((unsigned)(a.B * a.K * n_kblocks)), dim3(NW_DKV * 64),
-                       0, stream, a, n_kblocks);
+    const dim3 kgrid((unsigned)(a.B * a.K * n_kblocks));
+    if constexpr (GQA_BWD_DKV2 && H <= 128 && NW_DKV == 4) {
+        if (a.q_seg == nullptr) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_dkv2_kernel<H, true>), kgrid, dim3(256), 0, stream, a, n_kblocks);
+            else
+                hipLaunchKernelGGL((attn_bwd_dkv2_kernel<H, false>), kgrid, dim3(256), 0, stream, a, n_kblocks);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<H, NW_DKV>), kgrid, dim3(NW_DKV * 64), 0, stream, a, n_kblocks);
     return hipGetLastError();
 }
 
