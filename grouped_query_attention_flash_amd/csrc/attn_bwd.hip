@@ -294,20 +294,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
 // MFMAs of step i, with step i+1's weights computed beside the latter.
 // One wave per SIMD (up to 512 registers): the overlap is inside the wave.
 //
-// LDS tile layout: the XOR swizzle of the kernel above (row r, 16-byte chunk x
-// stored at position x ^ swz(r)); the loads write 1 KiB per wave instruction
-// lane-linearly, so each lane fetches the global chunk that belongs in its slot.
+// The loads write 1 KiB per wave instruction lane-linearly into padded-row
+// tiles, each lane fetching the global chunk that belongs in its slot.
 template <int H, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_kblocks) {
     constexpr int NW = 4, BQ = 32;
     constexpr int CPR = H / 8;
     constexpr int KSTEPS = H / 16;
     constexpr int HB = H / 32;
-    constexpr int TILE = BQ * H;                  // bf16 elements of a Q or dO tile
-    constexpr int TBLK = TILE * 2 / 1024;         // its 1 KiB wave loads
+    // Q / dO tiles in LDS: 32 rows of RS = CPR + 3 16-byte chunks (padded rows:
+    // the b128 row reads are conflict-free and the transpose reads 2-way), so
+    // that every operand address is a per-lane base plus an immediate
+    constexpr int RS = CPR + 3;
+    constexpr int TBLK = (BQ * RS + 63) / 64;     // 1 KiB wave loads per tile
+    constexpr int TILE = TBLK * 512;              // bf16 elements per tile buffer
     constexpr int TBW = (TBLK + NW - 1) / NW;     // per wave and tensor
     constexpr int NSTAGE = 3;
-    static_assert(TBLK % NW == 0, "tile loads spread evenly over the waves");
     __shared__ __attribute__((aligned(1024))) __bf16 sq[NSTAGE][TILE];
     __shared__ __attribute__((aligned(1024))) __bf16 sdo[NSTAGE][TILE];
     __shared__ __attribute__((aligned(1024))) float sld[NSTAGE][2][256];  // lse, D (32 used)
@@ -349,12 +351,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_
     const buffer_rsrc drs = make_rsrc(a.dout + bk * G * (size_t)T * H, G * T * H * 2);
     const buffer_rsrc lrs = make_rsrc(a.lse + bk * G * (size_t)T, G * T * 4);
     const buffer_rsrc ers = make_rsrc(a.delta + bk * G * (size_t)T, G * T * 4);
+    // slot p of a tile holds chunk min(p % RS, CPR - 1) of row p / RS (the
+    // padding slots repeat the row's last chunk; rows past 31 are not read)
     int t_off[TBW];
 #pragma unroll
     for (int i = 0; i < TBW; i++) {
         const int p = (wave + i * NW) * 64 + lane;
-        const int r = p / CPR, x = p % CPR;
-        t_off[i] = (r * H + ((x ^ swz<CPR>(r)) << 3)) * 2;
+        t_off[i] = ((p / RS) * H + min(p % RS, CPR - 1) * 8) * 2;
     }
     auto step_pos = [&](int st, int &g, int &t0) {
         g = st / nq;
@@ -366,8 +369,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_
         const int row0 = __builtin_amdgcn_readfirstlane(g * T + t0);
 #pragma unroll
         for (int i = 0; i < TBW; i++) {
-            lds_load16_to(qrs, (char *)sq[stage] + (wave + i * NW) * 1024, t_off[i], row0 * H * 2);
-            lds_load16_to(drs, (char *)sdo[stage] + (wave + i * NW) * 1024, t_off[i], row0 * H * 2);
+            if (wave + i * NW < TBLK) {
+                lds_load16_to(qrs, (char *)sq[stage] + (wave + i * NW) * 1024, t_off[i], row0 * H * 2);
+                lds_load16_to(drs, (char *)sdo[stage] + (wave + i * NW) * 1024, t_off[i], row0 * H * 2);
+            }
         }
         // 32 floats of lse / D: lanes 0-7 fetch them, the other lanes repeat
         // in-range addresses into slots that are not read
@@ -383,15 +388,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_
     }
 
     // S = Q K^T and dP = dO V^T of a step (32 queries x the wave's 32 keys)
-    const int sw_n = swz<CPR>(n);
+    const int row_lane = n * RS * 8 + c * 8;  // row n, chunk c
     auto sdp = [&](int stage, f32x16 &sacc, f32x16 &pacc) {
-        const __bf16 *qrow = sq[stage] + n * H;
-        const __bf16 *drow = sdo[stage] + n * H;
+        const __bf16 *qrow = sq[stage] + row_lane;
+        const __bf16 *drow = sdo[stage] + row_lane;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ks++) {
-            const int off = ((2 * ks + c) ^ sw_n) << 3;
-            sacc = mfma32x32x16(*(const bf16x8 *)(qrow + off), kf[ks], ks == 0 ? f32x16{} : sacc);
-            pacc = mfma32x32x16(*(const bf16x8 *)(drow + off), vf[ks], ks == 0 ? f32x16{} : pacc);
+            sacc = mfma32x32x16(*(const bf16x8 *)(qrow + 16 * ks), kf[ks], ks == 0 ? f32x16{} : sacc);
+            pacc = mfma32x32x16(*(const bf16x8 *)(drow + 16 * ks), vf[ks], ks == 0 ? f32x16{} : pacc);
         }
     };
     // P = exp2(S log2e - lse log2e) and dS = P (dP - D), as bf16 MFMA operands
@@ -418,21 +422,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_
     };
     // dV^T += dO^T P and dK^T += Q^T dS for a step (k = the step's 32 queries)
     const int gi = lane & 15, hh = (lane >> 4) & 1;
+    // transpose reads: lane (gi, hh) of 16-lane group c addresses query row
+    // 16 kk + 4 c + gi / 4 (+ 8 for the upper half) at h = 32 hb + 16 hh + 4 (gi % 4)
+    const int tr_lane = (4 * c + (gi >> 2)) * RS * 8 + 16 * hh + 4 * (gi & 3);
     auto dvdk = [&](int stage, const bf16x8 (&pf)[2], const bf16x8 (&sf)[2]) {
+        const __bf16 *qt_base = sq[stage] + tr_lane;
+        const __bf16 *dt_base = sdo[stage] + tr_lane;
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {
-            const int r0 = 16 * kk + 4 * c + (gi >> 2);
-            const int r1 = r0 + 8;
-            const int sw0 = swz<CPR>(r0), sw1 = swz<CPR>(r1);
 #pragma unroll
             for (int hb = 0; hb < HB; hb++) {
-                const int hcol = 32 * hb + 16 * hh + 4 * (gi & 3);
-                const int ch = hcol >> 3, within = hcol & 7;
-                const int o0 = r0 * H + ((ch ^ sw0) << 3) + within;
-                const int o1 = r1 * H + ((ch ^ sw1) << 3) + within;
-                const bf16x8 dot = join_bf16x8(lds_read_tr16(sdo[stage] + o0), lds_read_tr16(sdo[stage] + o1));
+                const int o0 = 16 * kk * RS * 8 + 32 * hb;
+                const int o1 = o0 + 8 * RS * 8;
+                const bf16x8 dot = join_bf16x8(lds_read_tr16(dt_base + o0), lds_read_tr16(dt_base + o1));
                 dv_acc[hb] = mfma32x32x16(dot, pf[kk], dv_acc[hb]);
-                const bf16x8 qt = join_bf16x8(lds_read_tr16(sq[stage] + o0), lds_read_tr16(sq[stage] + o1));
+                const bf16x8 qt = join_bf16x8(lds_read_tr16(qt_base + o0), lds_read_tr16(qt_base + o1));
                 dk_acc[hb] = mfma32x32x16(qt, sf[kk], dk_acc[hb]);
             }
         }
