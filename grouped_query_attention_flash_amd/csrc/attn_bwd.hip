@@ -26,10 +26,15 @@
 #include <climits>
 #include <cmath>
 #include <type_traits>
+#include <utility>
 
 // pipelined dK/dV kernel for shapes without segment ids at H <= 128
 #ifndef GQA_BWD_DKV2
 #define GQA_BWD_DKV2 1
+#endif
+// its operand reads are issued this many MFMAs ahead of their use
+#ifndef GQA_BWD_DKV_PREF
+#define GQA_BWD_DKV_PREF 6
 #endif
 
 namespace gqa {
@@ -288,16 +293,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
 
 // ---------------------------------------------------------------------------
 // dK, dV for shapes without segment ids at H <= 128: the same products as the
-// kernel above, pipelined. Q, dO, lse and D of each 32-query step go straight
-// from memory into a three-stage LDS ring (no register staging), and
-// iteration i issues the S and dP MFMAs of step i+1 before the dV and dK
-// MFMAs of step i, with step i+1's weights computed beside the latter.
-// One wave per SIMD (up to 512 registers): the overlap is inside the wave.
+// kernel above, software-pipelined three steps deep. Q, dO, lse and D of each
+// 32-query step go straight from memory into a four-stage LDS ring (no
+// register staging); iteration i runs the S and dP MFMAs of step i+2 and the
+// dV and dK MFMAs of step i, and computes the weights of step i+1 (whose S and
+// dP came from the previous iteration) between them, so the VALU work never
+// waits on the MFMAs of its own iteration. One wave per SIMD (up to 512
+// registers): the overlap is inside the wave.
 //
 // The loads write 1 KiB per wave instruction lane-linearly into padded-row
 // tiles, each lane fetching the global chunk that belongs in its slot.
 template <int H, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_kblocks) {
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_bwd_dkv2_kernel(BwdArgs a, int n_kblocks) {
     constexpr int NW = 4, BQ = 32;
     constexpr int CPR = H / 8;
     constexpr int KSTEPS = H / 16;
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_
     constexpr int TBLK = (BQ * RS + 63) / 64;     // 1 KiB wave loads per tile
     constexpr int TILE = TBLK * 512;              // bf16 elements per tile buffer
     constexpr int TBW = (TBLK + NW - 1) / NW;     // per wave and tensor
-    constexpr int NSTAGE = 3;
+    constexpr int NSTAGE = 4;
     __shared__ __attribute__((aligned(1024))) __bf16 sq[NSTAGE][TILE];
     __shared__ __attribute__((aligned(1024))) __bf16 sdo[NSTAGE][TILE];
     __shared__ __attribute__((aligned(1024))) float sld[NSTAGE][2][256];  // lse, D (32 used)
@@ -347,10 +354,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_
     const int n_steps = G * nq;
 
     // loads of one step: Q and dO tiles (wave w: blocks w, w + NW, ...), lse (wave 0), D (wave 1)
-    const buffer_rsrc qrs = make_rsrc(a.q + bk * G * (size_t)T * H, G * T * H * 2);
-    const buffer_rsrc drs = make_rsrc(a.dout + bk * G * (size_t)T * H, G * T * H * 2);
-    const buffer_rsrc lrs = make_rsrc(a.lse + bk * G * (size_t)T, G * T * 4);
-    const buffer_rsrc ers = make_rsrc(a.delta + bk * G * (size_t)T, G * T * 4);
+    const i32x4 qrs = make_rsrc_words(a.q + bk * G * (size_t)T * H, G * T * H * 2);
+    const i32x4 drs = make_rsrc_words(a.dout + bk * G * (size_t)T * H, G * T * H * 2);
+    const i32x4 lrs = make_rsrc_words(a.lse + bk * G * (size_t)T, G * T * 4);
+    const i32x4 ers = make_rsrc_words(a.delta + bk * G * (size_t)T, G * T * 4);
     // slot p of a tile holds chunk min(p % RS, CPR - 1) of row p / RS (the
     // padding slots repeat the row's last chunk; rows past 31 are not read)
     int t_off[TBW];
@@ -367,17 +374,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_
         int g, t0;
         step_pos(st, g, t0);
         const int row0 = __builtin_amdgcn_readfirstlane(g * T + t0);
+        const unsigned q_dst = lds_addr(sq[0]) + stage * (TILE * 2) + wave * 1024;
+        const unsigned d_dst = lds_addr(sdo[0]) + stage * (TILE * 2) + wave * 1024;
 #pragma unroll
         for (int i = 0; i < TBW; i++) {
             if (wave + i * NW < TBLK) {
-                lds_load16_to(qrs, (char *)sq[stage] + (wave + i * NW) * 1024, t_off[i], row0 * H * 2);
-                lds_load16_to(drs, (char *)sdo[stage] + (wave + i * NW) * 1024, t_off[i], row0 * H * 2);
+                lds_dma16(qrs, __builtin_amdgcn_readfirstlane(q_dst + i * NW * 1024), t_off[i], row0 * H * 2);
+                lds_dma16(drs, __builtin_amdgcn_readfirstlane(d_dst + i * NW * 1024), t_off[i], row0 * H * 2);
             }
         }
         // 32 floats of lse / D: lanes 0-7 fetch them, the other lanes repeat
         // in-range addresses into slots that are not read
-        if (wave == 0) lds_load16_to(lrs, (char *)sld[stage][0], (lane & 7) * 16, row0 * 4);
-        if (wave == 1) lds_load16_to(ers, (char *)sld[stage][1], (lane & 7) * 16, row0 * 4);
+        if (wave < 2)
+            lds_dma16(wave == 0 ? lrs : ers, __builtin_amdgcn_readfirstlane(lds_addr(sld[stage][wave])), (lane & 7) * 16,
+                      row0 * 4);
     };
 
     f32x16 dv_acc[HB], dk_acc[HB];
@@ -403,13 +413,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_
     // causal masking a pair is visible iff 0 <= t - s < T - s, otherwise iff
     // t < T; one unsigned compare per element (a key past S gets bound 0).
     const unsigned vis_bound = k_valid ? (unsigned)(CAUSAL ? T - s : T) : 0u;
-    auto weights = [&](int stage, int t0, const f32x16 &sacc, const f32x16 &pacc, bf16x8 (&pf)[2], bf16x8 (&sf)[2]) {
+    // lse and D of the lane's 16 query rows of a step
+    auto read_ld = [&](int stage, f32x4 (&l4s)[4], f32x4 (&d4s)[4]) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+            l4s[q4] = *(const f32x4 *)(&sld[stage][0][8 * q4 + 4 * c]);
+            d4s[q4] = *(const f32x4 *)(&sld[stage][1][8 * q4 + 4 * c]);
+        }
+    };
+    auto weights = [&](int t0, const f32x4 (&l4s)[4], const f32x4 (&d4s)[4], const f32x16 &sacc, const f32x16 &pacc,
+                       bf16x8 (&pf)[2], bf16x8 (&sf)[2]) {
         const int tb = t0 + 4 * c - (CAUSAL ? s : 0);
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
-            const int r0 = 8 * q4 + 4 * c;
-            const f32x4 l4 = *(const f32x4 *)(&sld[stage][0][r0]);
-            const f32x4 d4 = *(const f32x4 *)(&sld[stage][1][r0]);
+            const f32x4 l4 = l4s[q4];
+            const f32x4 d4 = d4s[q4];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int r = 4 * q4 + e;
@@ -420,62 +438,113 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv2_kernel(BwdArgs a, int n_
             }
         }
     };
-    // dV^T += dO^T P and dK^T += Q^T dS for a step (k = the step's 32 queries)
+    // dV^T += dO^T P and dK^T += Q^T dS for a step (k = the step's 32 queries):
+    // A operands by transpose reads. Lane (gi, hh) of 16-lane group c addresses
+    // query row 16 kk + 4 c + gi / 4 (+ 8 for the upper half) at
+    // h = 32 hb + 16 hh + 4 (gi % 4)
     const int gi = lane & 15, hh = (lane >> 4) & 1;
-    // transpose reads: lane (gi, hh) of 16-lane group c addresses query row
-    // 16 kk + 4 c + gi / 4 (+ 8 for the upper half) at h = 32 hb + 16 hh + 4 (gi % 4)
     const int tr_lane = (4 * c + (gi >> 2)) * RS * 8 + 16 * hh + 4 * (gi & 3);
-    auto dvdk = [&](int stage, const bf16x8 (&pf)[2], const bf16x8 (&sf)[2]) {
-        const __bf16 *qt_base = sq[stage] + tr_lane;
-        const __bf16 *dt_base = sdo[stage] + tr_lane;
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-#pragma unroll
-            for (int hb = 0; hb < HB; hb++) {
-                const int o0 = 16 * kk * RS * 8 + 32 * hb;
-                const int o1 = o0 + 8 * RS * 8;
-                const bf16x8 dot = join_bf16x8(lds_read_tr16(dt_base + o0), lds_read_tr16(dt_base + o1));
-                dv_acc[hb] = mfma32x32x16(dot, pf[kk], dv_acc[hb]);
-                const bf16x8 qt = join_bf16x8(lds_read_tr16(qt_base + o0), lds_read_tr16(qt_base + o1));
-                dk_acc[hb] = mfma32x32x16(qt, sf[kk], dk_acc[hb]);
-            }
-        }
-    };
     if (n_steps > 0) {
+        // prologue: steps 0, 1, 2 into stages 0, 1, 2; P and dS of step 0,
+        // S and dP of step 1
         issue_step(0, 0);
-        if (n_steps > 1) issue_step(1, 1);
+        issue_step(1, 1);
+        issue_step(2, 2);
         wait_lds_loads();
         __syncthreads();
-        f32x16 sa, pa;
-        bf16x8 pfa[2], sfa[2];
-        sdp(0, sa, pa);
+        f32x16 sa, pa;          // S, dP of step i+1 at the top of iteration i
+        bf16x8 pfa[2], sfa[2];  // P, dS of step i
         {
+            f32x16 s0, p0;
+            sdp(0, s0, p0);
             int g0, t00;
             step_pos(0, g0, t00);
-            weights(0, t00, sa, pa, pfa, sfa);
+            f32x4 l4s[4], d4s[4];
+            read_ld(0, l4s, d4s);
+            weights(t00, l4s, d4s, s0, p0, pfa, sfa);
+            sdp(1, sa, pa);
         }
-        // iteration i: stage i % 3 holds step i (dV / dK now), stage (i+1) % 3
-        // step i+1 (S / dP now); step i+2 is loaded into stage (i+2) % 3, which
-        // held step i-1 (read in the previous iteration). Past the last step the
-        // load is a bounds-checked zero read into a stage that is not read again.
-        int stage = 0;
-        for (int i = 0; i + 1 < n_steps; i++) {
-            const int st1 = stage == NSTAGE - 1 ? 0 : stage + 1;
-            const int st2 = st1 == NSTAGE - 1 ? 0 : st1 + 1;
+        // Iteration i: dV / dK of step i (stage i % 4), the weights of step i+1
+        // (S and dP from the previous iteration, lse and D from stage
+        // (i+1) % 4) and S / dP of step i+2 (stage (i+2) % 4). Step i+3 is loaded
+        // into stage (i+3) % 4, which held step i-1. Near the end the steps past
+        // the last are bounds-checked zero reads whose products are not used.
+        //
+        // Explicit schedule in NSLOT fenced slots: slot m issues MFMA m and the
+        // operand reads of MFMA m + PREF; slots 0 .. NQ - 1 are the S / dP
+        // MFMAs, the rest the dV / dK MFMAs; every other slot also computes one
+        // weight (P and dS) of step i+1, so the VALU work runs beside the MFMAs.
+        constexpr int NQ = 2 * KSTEPS, NSLOT = NQ + 4 * HB, PREF = GQA_BWD_DKV_PREF;
+        constexpr int WSTRIDE = NSLOT / 16;  // slots per weight
+        static_assert(WSTRIDE * 16 == NSLOT, "16 weights per lane and step");
+        for (int i = 0; i < n_steps; i++) {
+            const int st0 = i & 3, st1 = (i + 1) & 3, st2 = (i + 2) & 3;
             barrier_no_drain();
-            issue_step(i + 2, st2);
-            f32x16 sb, pb;
-            sdp(st1, sb, pb);
-            dvdk(stage, pfa, sfa);
+            issue_step(i + 3, (i + 3) & 3);
+            f32x4 l4s[4], d4s[4];
+            read_ld(st1, l4s, d4s);
             int g1, t01;
             step_pos(i + 1, g1, t01);
-            weights(st1, t01, sb, pb, pfa, sfa);
-            // the loads of step i+2 land before the next barrier
+            const int tb = t01 + 4 * c - (CAUSAL ? s : 0);
+            auto read_op = [&](int m) -> bf16x8 {
+                if (m < NQ) {
+                    const __bf16 *base = (m & 1) ? sdo[st2] : sq[st2];
+                    return *(const bf16x8 *)(base + row_lane + 16 * (m >> 1));
+                }
+                const int j = m - NQ, kk = j / (2 * HB), hb = (j >> 1) % HB;
+                const __bf16 *base = ((j & 1) ? sq[st0] : sdo[st0]) + tr_lane + 16 * kk * RS * 8 + 32 * hb;
+                return join_bf16x8(lds_read_tr16(base), lds_read_tr16(base + 8 * RS * 8));
+            };
+            bf16x8 op[NSLOT];
+#pragma unroll
+            for (int m = 0; m < PREF; m++) op[m] = read_op(m);
+            sched_fence();
+            f32x16 sb, pb;
+            bf16x8 pfb[2], sfb[2];
+            float p_even = 0.f, ds_even = 0.f;
+#pragma unroll
+            for (int m = 0; m < NSLOT; m++) {
+                if (m + PREF < NSLOT) op[m + PREF] = read_op(m + PREF);
+                if (m < NQ) {
+                    const int ks = m >> 1;
+                    if (m & 1)
+                        pb = mfma32x32x16(op[m], vf[ks], ks == 0 ? f32x16{} : pb);
+                    else
+                        sb = mfma32x32x16(op[m], kf[ks], ks == 0 ? f32x16{} : sb);
+                } else {
+                    const int j = m - NQ, kk = j / (2 * HB), hb = (j >> 1) % HB;
+                    if (j & 1)
+                        dk_acc[hb] = mfma32x32x16(op[m], sfa[kk], dk_acc[hb]);
+                    else
+                        dv_acc[hb] = mfma32x32x16(op[m], pfa[kk], dv_acc[hb]);
+                }
+                if (m % WSTRIDE == WSTRIDE - 1) {
+                    // weight r of step i+1: row 8 (r / 4) + 4 c + r % 4 of its tile
+                    const int r = m / WSTRIDE, q4 = r >> 2, e = r & 3;
+                    float p = exp2_fast(__builtin_fmaf(sa[r], kLog2e, -l4s[q4][e] * kLog2e));
+                    p = (unsigned)(tb + 8 * q4 + e) < vis_bound ? p : 0.f;
+                    const float ds = p * (pa[r] - d4s[q4][e]);
+                    if (r & 1) {
+                        pfb[r >> 3][(r & 7) - 1] = (__bf16)p_even;
+                        pfb[r >> 3][r & 7] = (__bf16)p;
+                        sfb[r >> 3][(r & 7) - 1] = (__bf16)ds_even;
+                        sfb[r >> 3][r & 7] = (__bf16)ds;
+                    } else {
+                        p_even = p;
+                        ds_even = ds;
+                    }
+                }
+                sched_fence();
+            }
+            pfa[0] = pfb[0];
+            pfa[1] = pfb[1];
+            sfa[0] = sfb[0];
+            sfa[1] = sfb[1];
+            sa = sb;
+            pa = pb;
+            // the loads of step i+3 land before the next barrier
             wait_lds_loads();
-            stage = st1;
         }
-        barrier_no_drain();
-        dvdk(stage, pfa, sfa);
     }
 
     // dK, dV rows (fp32): lane (n, c) holds h = 32hb + acc_row(r, c) of key s

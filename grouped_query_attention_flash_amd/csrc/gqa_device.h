@@ -115,6 +115,34 @@ __device__ __forceinline__ void lds_load16_to(const buffer_rsrc &rs, void *dst, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voffset, soffset, 0, 0);
 }
 
+// Buffer descriptor as four wave-uniform words (for inline assembly): base,
+// stride 0, num_records = bytes, raw 32-bit data format. Loads past the end
+// return zeros.
+__device__ __forceinline__ i32x4 make_rsrc_words(const void *base, int bytes) {
+    const uint64_t p = (uint64_t)(size_t)base;
+    return i32x4{(int)__builtin_amdgcn_readfirstlane((uint32_t)p), (int)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)),
+                 __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+// 16 bytes per lane from a buffer into LDS (lane l writes LDS byte address
+// dst + 16 l; dst wave-uniform), issued from inline assembly. The compiler
+// does not track this load: it inserts no wait for it anywhere, so an LDS
+// read of another stage of the same array is not held back until the load
+// lands. The caller waits itself (wait_lds_loads / wait_lds_loads_but) and
+// passes a barrier before any wave reads the destination. M0 carries the
+// destination (one wait state before the load reads it) and is restored.
+__device__ __forceinline__ void lds_dma16(const i32x4 &rs, unsigned dst, int voffset, int soffset) {
+    int saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(dst), "v"(voffset), "s"(rs), "s"(soffset));
+}
+
 // Wait until this wave's LDS-direct loads have landed (vmcnt = 0 only).
 __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Wait until at most N of this wave's vector-memory loads are outstanding (they
@@ -128,10 +156,11 @@ __device__ __forceinline__ void wait_lds_loads_but() {
 // Workgroup barrier without the release/acquire fence of __syncthreads(),
 // which would make every wave drain all of its outstanding global-to-LDS
 // loads first. Callers wait themselves (wait_lds_loads_but / wait_lds_loads)
-// for the loads that other waves read after the barrier; LDS operand reads are
-// consumed (waited for) before the barrier. The memory clobber keeps the
+// for the loads that other waves read after the barrier. The wave's own LDS
+// reads complete first (lgkmcnt 0), so no wave overwrites a buffer after the
+// barrier that another wave is still reading. The memory clobber keeps the
 // compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_no_drain() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void barrier_no_drain() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Keep the compiler's scheduler from moving instructions across this point
 // (bounds how far ahead it hoists LDS operand reads, and so register pressure).
