@@ -17,9 +17,10 @@ int check_common(const void *q, const void *k, const void *v, const void *o,
                  int B, int K, int G, int T, int S, int H) {
     if (!q || !k || !v || !o) return GQA_ATTN_ERR_NULL;
     if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return GQA_ATTN_ERR_SHAPE;
-    // 32-bit grid and per-(b, kv head) element offsets must not overflow
+    // 32-bit grid and per-(b, kv head) offsets must not overflow: each slice
+    // is addressed in bytes by a signed 32-bit offset (buffer descriptors)
     const long long q_slice = (long long)G * T * H, kv_slice = (long long)S * H;
-    if (q_slice >= INT_MAX || kv_slice >= INT_MAX) return GQA_ATTN_ERR_SHAPE;
+    if (2 * q_slice >= INT_MAX || 2 * kv_slice >= INT_MAX) return GQA_ATTN_ERR_SHAPE;
     if ((long long)B * K * G * ((long long)T + 31) >= INT_MAX) return GQA_ATTN_ERR_SHAPE;
     if (H != 64 && H != 128 && H != 256) return GQA_ATTN_ERR_HEADDIM;
     if ((q_seg == nullptr) != (kv_seg == nullptr)) return GQA_ATTN_ERR_SEGMENTS;
@@ -129,7 +130,7 @@ const char *attn_strerror(int code) {
     switch (code) {
         case GQA_ATTN_OK: return "success";
         case GQA_ATTN_ERR_NULL: return "a required pointer is NULL";
-        case GQA_ATTN_ERR_SHAPE: return "invalid sizes: B, K, G, T, S must be >= 1 and each tensor slice < 2^31 elements";
+        case GQA_ATTN_ERR_SHAPE: return "invalid sizes: B, K, G, T, S must be >= 1 and each (b, kv head) slice of q or k < 2^30 elements";
         case GQA_ATTN_ERR_HEADDIM: return "unsupported head dimension H (supported: 64, 128, 256)";
         case GQA_ATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte alignment, segment ids 4-byte)";
         case GQA_ATTN_ERR_SEGMENTS: return "q_seg and kv_seg must both be given or both be NULL";

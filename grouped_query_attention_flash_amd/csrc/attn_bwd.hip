@@ -36,6 +36,14 @@
 #ifndef GQA_BWD_DKV_PREF
 #define GQA_BWD_DKV_PREF 6
 #endif
+// its bf16 weight conversions pinned into their slots
+#ifndef GQA_BWD_CVTPIN
+#define GQA_BWD_CVTPIN 0
+#endif
+// its lse / D reads at the end of the iteration before (1) or at the top (0)
+#ifndef GQA_BWD_LDPRE
+#define GQA_BWD_LDPRE 1
+#endif
 
 namespace gqa {
 
@@ -316,10 +324,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     constexpr int TBLK = (BQ * RS + 63) / 64;     // 1 KiB wave loads per tile
     constexpr int TILE = TBLK * 512;              // bf16 elements per tile buffer
     constexpr int TBW = (TBLK + NW - 1) / NW;     // per wave and tensor
-    constexpr int NSTAGE = 4;
+    constexpr int NLD = 2 * TBW + 1;              // loads per wave and step (Q, dO blocks; lse or D)
+    constexpr int NSTAGE = 5;
     __shared__ __attribute__((aligned(1024))) __bf16 sq[NSTAGE][TILE];
     __shared__ __attribute__((aligned(1024))) __bf16 sdo[NSTAGE][TILE];
     __shared__ __attribute__((aligned(1024))) float sld[NSTAGE][2][256];  // lse, D (32 used)
+    // destination of the loads a wave issues only to keep its count per step
+    // the same as the other waves' (out of range: they read nothing)
+    __shared__ __attribute__((aligned(1024))) char sdummy[1024];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -353,11 +365,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int nq = n_qt - qt_begin;
     const int n_steps = G * nq;
 
-    // loads of one step: Q and dO tiles (wave w: blocks w, w + NW, ...), lse (wave 0), D (wave 1)
+    // loads of one step: Q and dO tiles (wave w: blocks w, w + NW, ...), lse
+    // (wave 0), D (wave 1). Every wave issues NLD loads per step, without
+    // branches: a block past the tile, the lse / D load of waves 2 and 3, and
+    // every load of a step past the last one get an out-of-range offset and
+    // the dummy destination.
     const i32x4 qrs = make_rsrc_words(a.q + bk * G * (size_t)T * H, G * T * H * 2);
     const i32x4 drs = make_rsrc_words(a.dout + bk * G * (size_t)T * H, G * T * H * 2);
-    const i32x4 lrs = make_rsrc_words(a.lse + bk * G * (size_t)T, G * T * 4);
-    const i32x4 ers = make_rsrc_words(a.delta + bk * G * (size_t)T, G * T * 4);
+    const i32x4 ldrs = wave == 0 ? make_rsrc_words(a.lse + bk * G * (size_t)T, G * T * 4)
+                                 : make_rsrc_words(a.delta + bk * G * (size_t)T, G * T * 4);
+    constexpr unsigned kOutOfRange = 0x80000000u;
     // slot p of a tile holds chunk min(p % RS, CPR - 1) of row p / RS (the
     // padding slots repeat the row's last chunk; rows past 31 are not read)
     int t_off[TBW];
@@ -366,28 +383,41 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int p = (wave + i * NW) * 64 + lane;
         t_off[i] = ((p / RS) * H + min(p % RS, CPR - 1) * 8) * 2;
     }
-    auto step_pos = [&](int st, int &g, int &t0) {
-        g = st / nq;
-        t0 = (qt_begin + st - g * nq) * BQ;
-    };
-    auto issue_step = [&](int st, int stage) {
-        int g, t0;
-        step_pos(st, g, t0);
-        const int row0 = __builtin_amdgcn_readfirstlane(g * T + t0);
-        const unsigned q_dst = lds_addr(sq[0]) + stage * (TILE * 2) + wave * 1024;
-        const unsigned d_dst = lds_addr(sdo[0]) + stage * (TILE * 2) + wave * 1024;
-#pragma unroll
-        for (int i = 0; i < TBW; i++) {
-            if (wave + i * NW < TBLK) {
-                lds_dma16(qrs, __builtin_amdgcn_readfirstlane(q_dst + i * NW * 1024), t_off[i], row0 * H * 2);
-                lds_dma16(drs, __builtin_amdgcn_readfirstlane(d_dst + i * NW * 1024), t_off[i], row0 * H * 2);
-            }
+    const unsigned q_dst0 = lds_addr(sq[0]) + wave * 1024, d_dst0 = lds_addr(sdo[0]) + wave * 1024;
+    const unsigned ld_dst0 = lds_addr(sld[0][wave & 1]), dummy = lds_addr(sdummy);
+    // load j (< NLD) of a step whose query rows start at row0 (g T + t0), or
+    // of no step (row0 < 0), into a stage
+    auto issue_load = [&](int j, int row0, int stage) {
+        if (j < 2 * TBW) {
+            const int i = j >> 1;
+            const bool ok = row0 >= 0 && wave + i * NW < TBLK;
+            const unsigned voff = ok ? (unsigned)(row0 * H * 2 + t_off[i]) : kOutOfRange;
+            const unsigned dst = ok ? ((j & 1) ? d_dst0 : q_dst0) + stage * (TILE * 2) + i * NW * 1024 : dummy;
+            lds_dma16((j & 1) ? drs : qrs, __builtin_amdgcn_readfirstlane(dst), voff);
+        } else {
+            // 32 floats of lse / D: lanes 0-7 fetch them, the other lanes repeat
+            // in-range addresses into slots that are not read
+            const bool ok = row0 >= 0 && wave < 2;
+            const unsigned voff = ok ? (unsigned)(row0 * 4 + (lane & 7) * 16) : kOutOfRange;
+            const unsigned dst = ok ? ld_dst0 + stage * (2 * 256 * 4) : dummy;
+            lds_dma16(ldrs, __builtin_amdgcn_readfirstlane(dst), voff);
         }
-        // 32 floats of lse / D: lanes 0-7 fetch them, the other lanes repeat
-        // in-range addresses into slots that are not read
-        if (wave < 2)
-            lds_dma16(wave == 0 ? lrs : ers, __builtin_amdgcn_readfirstlane(lds_addr(sld[stage][wave])), (lane & 7) * 16,
-                      row0 * 4);
+    };
+    // steps walk (g, query tile) with g outer; a cursor gives a step's first
+    // query row (g T + t0), or -1 past the last step
+    struct Cursor {
+        int g, qt;
+    };
+    auto advance = [&](Cursor &cu) {
+        if (++cu.qt == n_qt) {
+            cu.qt = qt_begin;
+            ++cu.g;
+        }
+    };
+    auto row_of = [&](const Cursor &cu) { return cu.g < G ? cu.g * T + cu.qt * BQ : -1; };
+    auto issue_step = [&](int row0, int stage) {
+#pragma unroll
+        for (int j = 0; j < NLD; j++) issue_load(j, row0, stage);
     };
 
     f32x16 dv_acc[HB], dk_acc[HB];
@@ -445,11 +475,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int gi = lane & 15, hh = (lane >> 4) & 1;
     const int tr_lane = (4 * c + (gi >> 2)) * RS * 8 + 16 * hh + 4 * (gi & 3);
     if (n_steps > 0) {
-        // prologue: steps 0, 1, 2 into stages 0, 1, 2; P and dS of step 0,
-        // S and dP of step 1
-        issue_step(0, 0);
-        issue_step(1, 1);
-        issue_step(2, 2);
+        // prologue: steps 0 .. 3 into stages 0 .. 3; P and dS of step 0, S and
+        // dP of step 1
+        Cursor c_ld{0, qt_begin};  // the next step to load
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            issue_step(row_of(c_ld), st);
+            advance(c_ld);
+        }
         wait_lds_loads();
         __syncthreads();
         f32x16 sa, pa;          // S, dP of step i+1 at the top of iteration i
@@ -457,35 +490,46 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         {
             f32x16 s0, p0;
             sdp(0, s0, p0);
-            int g0, t00;
-            step_pos(0, g0, t00);
             f32x4 l4s[4], d4s[4];
             read_ld(0, l4s, d4s);
-            weights(t00, l4s, d4s, s0, p0, pfa, sfa);
+            weights(qt_begin * BQ, l4s, d4s, s0, p0, pfa, sfa);
             sdp(1, sa, pa);
         }
-        // Iteration i: dV / dK of step i (stage i % 4), the weights of step i+1
+        Cursor c_w{0, qt_begin};  // step i+1 in iteration i (its weights)
+        advance(c_w);
+        // Iteration i: dV / dK of step i (stage i % 5), the weights of step i+1
         // (S and dP from the previous iteration, lse and D from stage
-        // (i+1) % 4) and S / dP of step i+2 (stage (i+2) % 4). Step i+3 is loaded
-        // into stage (i+3) % 4, which held step i-1. Near the end the steps past
-        // the last are bounds-checked zero reads whose products are not used.
+        // (i+1) % 5) and S / dP of step i+2 (stage (i+2) % 5). Step i+4 is
+        // loaded into stage (i+4) % 5, which held step i-1, and must land by the
+        // end of iteration i+1; steps past the last load nothing. The products
+        // of steps past the last are never used.
         //
         // Explicit schedule in NSLOT fenced slots: slot m issues MFMA m and the
         // operand reads of MFMA m + PREF; slots 0 .. NQ - 1 are the S / dP
-        // MFMAs, the rest the dV / dK MFMAs; every other slot also computes one
-        // weight (P and dS) of step i+1, so the VALU work runs beside the MFMAs.
+        // MFMAs, the rest the dV / dK MFMAs; every WSTRIDE-th slot also computes
+        // one weight (P and dS) of step i+1, so the VALU work runs beside the
+        // MFMAs, and every LSTRIDE-th slot issues one of the NLD loads of step
+        // i+4. The lse and D of an iteration are read at the end of the one
+        // before (their stage is complete by then).
         constexpr int NQ = 2 * KSTEPS, NSLOT = NQ + 4 * HB, PREF = GQA_BWD_DKV_PREF;
         constexpr int WSTRIDE = NSLOT / 16;  // slots per weight
         static_assert(WSTRIDE * 16 == NSLOT, "16 weights per lane and step");
+        constexpr int LSTRIDE = NSLOT / NLD;
+        static_assert(LSTRIDE >= 1, "a slot per load");
+        int st0 = 0, st1 = 1, st2 = 2, st4 = 4;  // stages of steps i, i+1, i+2, i+4
+        f32x4 l4s[4], d4s[4];
+#if GQA_BWD_LDPRE
+        read_ld(st1, l4s, d4s);
+#endif
         for (int i = 0; i < n_steps; i++) {
-            const int st0 = i & 3, st1 = (i + 1) & 3, st2 = (i + 2) & 3;
             barrier_no_drain();
-            issue_step(i + 3, (i + 3) & 3);
-            f32x4 l4s[4], d4s[4];
+#if !GQA_BWD_LDPRE
             read_ld(st1, l4s, d4s);
-            int g1, t01;
-            step_pos(i + 1, g1, t01);
-            const int tb = t01 + 4 * c - (CAUSAL ? s : 0);
+#endif
+            const int row_ld = row_of(c_ld);
+            advance(c_ld);
+            const int tb = c_w.qt * BQ + 4 * c - (CAUSAL ? s : 0);
+            advance(c_w);
             auto read_op = [&](int m) -> bf16x8 {
                 if (m < NQ) {
                     const __bf16 *base = (m & 1) ? sdo[st2] : sq[st2];
@@ -529,11 +573,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                         pfb[r >> 3][r & 7] = (__bf16)p;
                         sfb[r >> 3][(r & 7) - 1] = (__bf16)ds_even;
                         sfb[r >> 3][r & 7] = (__bf16)ds;
+#if GQA_BWD_CVTPIN
+                        // convert in this slot (the compiler would leave all
+                        // conversions to the end of the iteration)
+                        if ((r & 7) == 7 || GQA_BWD_CVTPIN > 1) {
+                            pin_value(pfb[r >> 3]);
+                            pin_value(sfb[r >> 3]);
+                        }
+#endif
                     } else {
                         p_even = p;
                         ds_even = ds;
                     }
                 }
+                if (m % LSTRIDE == LSTRIDE / 2 && m / LSTRIDE < NLD) issue_load(m / LSTRIDE, row_ld, st4);
                 sched_fence();
             }
             pfa[0] = pfb[0];
@@ -542,9 +595,22 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             sfa[1] = sfb[1];
             sa = sb;
             pa = pb;
-            // the loads of step i+3 land before the next barrier
-            wait_lds_loads();
+            // the loads of step i+3 (issued in the previous iteration) land
+            // before the next barrier; this iteration's NLD stay in flight
+            wait_lds_loads_but<NLD>();
+            st0 = st1;
+            st1 = st2;
+            st2 = st2 == NSTAGE - 1 ? 0 : st2 + 1;
+            st4 = st4 == NSTAGE - 1 ? 0 : st4 + 1;
+#if GQA_BWD_LDPRE
+            // the next iteration's lse / D (step i+2: landed before this
+            // iteration's barrier)
+            read_ld(st1, l4s, d4s);
+#endif
         }
+        // the last iteration's loads (of no step: out of range) complete
+        // before the workgroup's LDS is released
+        wait_lds_loads();
     }
 
     // dK, dV rows (fp32): lane (n, c) holds h = 32hb + acc_row(r, c) of key s

@@ -237,8 +237,8 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     // 16-byte slots blk*64 .. blk*64+63; slot p holds chunk p % RS of key row
     // p / RS, and the padding slots (chunk >= CPR) repeat the row's last chunk.
     // This wave issues loads blk = wave, wave + NW, ...; their per-lane byte
-    // offsets within a tile are fixed, and the tile's own offset goes in the
-    // instruction's scalar offset.
+    // offsets within a tile are fixed, and the tile's own offset is added to
+    // them (the range check zero-fills the rows of a last, partial tile past S).
     constexpr int K_PER_WAVE = (L::K_BLOCKS + NW - 1) / NW;
     constexpr int V_PER_WAVE = (L::V_BLOCKS + NW - 1) / NW;
     int k_off[K_PER_WAVE], v_off[V_PER_WAVE];
@@ -263,9 +263,9 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
 #pragma unroll
         for (int i = 0; i < K_PER_WAVE; i++) {
             if constexpr (decltype(full)::value) {
-                if (i < K_FULL) lds_load16_to(krs, base + i * NW * 1024, k_off[i], tile);
+                if (i < K_FULL) lds_load16_to(krs, base + i * NW * 1024, k_off[i] + tile);
             } else {
-                if (i >= K_FULL && wave + i * NW < L::K_BLOCKS) lds_load16_to(krs, base + i * NW * 1024, k_off[i], tile);
+                if (i >= K_FULL && wave + i * NW < L::K_BLOCKS) lds_load16_to(krs, base + i * NW * 1024, k_off[i] + tile);
             }
         }
     };
@@ -275,9 +275,9 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
 #pragma unroll
         for (int i = 0; i < V_PER_WAVE; i++) {
             if constexpr (decltype(full)::value) {
-                if (i < V_FULL) lds_load16_to(vrs, base + i * NW * 1024, v_off[i], tile);
+                if (i < V_FULL) lds_load16_to(vrs, base + i * NW * 1024, v_off[i] + tile);
             } else {
-                if (i >= V_FULL && wave + i * NW < L::V_BLOCKS) lds_load16_to(vrs, base + i * NW * 1024, v_off[i], tile);
+                if (i >= V_FULL && wave + i * NW < L::V_BLOCKS) lds_load16_to(vrs, base + i * NW * 1024, v_off[i] + tile);
             }
         }
     };
@@ -710,6 +710,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
         const int pslot = (gwv + i * NG) * 64 + lane;
         ld_off[i] = ((pslot / rs) * H + min(pslot % rs, CPR - 1) * 8) * 2;
     }
+    // Tiles j < n_t lie wholly inside K and V (S % BKV == 0, rows < BKV), so
+    // the tile offset may go in the scalar offset, which the range check does
+    // not cover.
     auto issue_tile = [&](int j, int slot) {
         const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
         if (grp == 0) {

@@ -98,18 +98,17 @@ __device__ __forceinline__ unsigned lds_addr(const void *p) {
 }
 
 // 16 bytes per lane from a buffer straight into LDS (no registers). The wave's
-// 64 lanes write 1 KiB at LDS byte address dst (wave-uniform, kept in M0):
-// lane l at dst + 16 l. The byte offset in the buffer is voffset (per lane) +
-// soffset (wave-uniform).
-__device__ __forceinline__ void lds_load16(const buffer_rsrc &rs, unsigned dst, int voffset, int soffset) {
+// 64 lanes write 1 KiB at the LDS destination (a pointer into a __shared__
+// array plus a wave-uniform offset, so that the compiler knows which array the
+// load writes): lane l at dst + 16 l. voffset is the lane's whole byte offset
+// in the buffer: the hardware's range check (a lane at or past the end reads
+// zeros) covers the per-lane offset only, not a scalar offset, so none is used.
+__device__ __forceinline__ void lds_load16_to(const buffer_rsrc &rs, void *dst, int voffset) {
     typedef __attribute__((address_space(3))) void lds_void;
-    lds_void *p = (lds_void *)(size_t)__builtin_amdgcn_readfirstlane(dst);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, p, 16, voffset, soffset, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voffset, 0, 0, 0);
 }
-
-// The same load with the LDS destination given as a pointer into a __shared__
-// array (plus a wave-uniform offset): the compiler then knows which array the
-// load writes and may move LDS reads of other arrays across it.
+// The same with a wave-uniform scalar offset added to the address: only for
+// loads known to stay inside the buffer (the range check ignores soffset).
 __device__ __forceinline__ void lds_load16_to(const buffer_rsrc &rs, void *dst, int voffset, int soffset) {
     typedef __attribute__((address_space(3))) void lds_void;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voffset, soffset, 0, 0);
@@ -125,22 +124,24 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void *base, int bytes) {
 }
 
 // 16 bytes per lane from a buffer into LDS (lane l writes LDS byte address
-// dst + 16 l; dst wave-uniform), issued from inline assembly. The compiler
-// does not track this load: it inserts no wait for it anywhere, so an LDS
-// read of another stage of the same array is not held back until the load
-// lands. The caller waits itself (wait_lds_loads / wait_lds_loads_but) and
-// passes a barrier before any wave reads the destination. M0 carries the
-// destination (one wait state before the load reads it) and is restored.
-__device__ __forceinline__ void lds_dma16(const i32x4 &rs, unsigned dst, int voffset, int soffset) {
+// dst + 16 l; dst wave-uniform), issued from inline assembly. voffset is the
+// lane's whole byte offset (range-checked as above; 0x80000000 or more reads
+// zeros without touching memory). The compiler does not track this load: it
+// inserts no wait for it anywhere, so an LDS read of another stage of the same
+// array is not held back until the load lands. The caller waits itself
+// (wait_lds_loads / wait_lds_loads_but) and passes a barrier before any wave
+// reads the destination. M0 carries the destination (one wait state before
+// the load reads it) and is restored.
+__device__ __forceinline__ void lds_dma16(const i32x4 &rs, unsigned dst, unsigned voffset) {
     int saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "s"(dst), "v"(voffset), "s"(rs), "s"(soffset));
+        : "s"(dst), "v"(voffset), "s"(rs));
 }
 
 // Wait until this wave's LDS-direct loads have landed (vmcnt = 0 only).
@@ -161,6 +162,14 @@ __device__ __forceinline__ void wait_lds_loads_but() {
 // barrier that another wave is still reading. The memory clobber keeps the
 // compiler from moving memory accesses across it.
 __device__ __forceinline__ void barrier_no_drain() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Make a value exist in registers at this point of the program: the compiler
+// may not sink its computation past here (an empty volatile asm that reads
+// and rewrites it).
+template <typename V>
+__device__ __forceinline__ void pin_value(V &x) {
+    asm volatile("" : "+v"(x));
+}
 
 // Keep the compiler's scheduler from moving instructions across this point
 // (bounds how far ahead it hoists LDS operand reads, and so register pressure).

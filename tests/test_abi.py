@@ -55,6 +55,10 @@ def test_check_fwd_codes():
     for bad in (dict(B=0), dict(K=0), dict(G=0), dict(T=0), dict(S=-1)):
         assert check_fwd(**bad) == gqa.GQA_ATTN_ERR_SHAPE, bad
     assert check_fwd(G=1 << 12, T=1 << 20) == gqa.GQA_ATTN_ERR_SHAPE  # slice >= 2^31 elements
+    # each (b, kv head) slice is addressed in bytes by a signed 32-bit offset
+    assert check_fwd(G=1, T=(1 << 23) - 1, S=64) == gqa.GQA_ATTN_OK      # q slice just under 2^30 elements
+    assert check_fwd(G=1, T=1 << 23, S=64) == gqa.GQA_ATTN_ERR_SHAPE     # q slice 2^30 elements
+    assert check_fwd(G=1, T=64, S=1 << 23) == gqa.GQA_ATTN_ERR_SHAPE     # k slice 2^30 elements
     for h in (0, 32, 96, 129, 512):
         assert check_fwd(H=h) == gqa.GQA_ATTN_ERR_HEADDIM, h
     for h in (64, 128, 256):
