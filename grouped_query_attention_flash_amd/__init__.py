@@ -31,7 +31,8 @@ GQA_ATTN_ERR_WORKSPACE = 6
 GQA_ATTN_ERR_HIP = 7
 
 EXPORTED_SYMBOLS = (
-    "attn_fwd", "attn_check_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_check_bwd",
+    "attn_fwd", "attn_check_fwd", "attn_fwd_ws", "attn_check_fwd_ws", "attn_fwd_workspace_bytes",
+    "attn_fwd_split_count", "attn_bwd_workspace_bytes", "attn_bwd", "attn_check_bwd",
     "attn_strerror", "attn_last_hip_error",
 )
 
@@ -63,6 +64,14 @@ def load_library():
     lib.attn_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.attn_check_fwd.restype = I
     lib.attn_check_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I]
+    lib.attn_fwd_ws.restype = I
+    lib.attn_fwd_ws.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, SZ, P]
+    lib.attn_check_fwd_ws.restype = I
+    lib.attn_check_fwd_ws.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, SZ]
+    lib.attn_fwd_workspace_bytes.restype = SZ
+    lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_fwd_split_count.restype = I
+    lib.attn_fwd_split_count.argtypes = [I, I, I, I, I, I]
     lib.attn_bwd_workspace_bytes.restype = SZ
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_bwd.restype = I
@@ -87,6 +96,14 @@ def attn_last_hip_error() -> int:
 
 def attn_bwd_workspace_bytes(B: int, K: int, G: int, T: int, S: int, H: int) -> int:
     return int(load_library().attn_bwd_workspace_bytes(B, K, G, T, S, H))
+
+
+def attn_fwd_workspace_bytes(B: int, K: int, G: int, T: int, S: int, H: int) -> int:
+    return int(load_library().attn_fwd_workspace_bytes(B, K, G, T, S, H))
+
+
+def attn_fwd_split_count(B: int, K: int, G: int, T: int, S: int, H: int) -> int:
+    return int(load_library().attn_fwd_split_count(B, K, G, T, S, H))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -120,8 +137,14 @@ def _check_tensor(name, t, dtype, shape=None):
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
              q_seg: Optional[torch.Tensor] = None, kv_seg: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-             want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Forward pass on the current stream. Returns (o, lse)."""
+             want_lse: bool = True, split_kv: bool = False,
+             workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward pass on the current stream. Returns (o, lse).
+
+    split_kv=True calls attn_fwd_ws, which splits the key range across
+    workgroups for shapes that would leave the GPU idle (decoding); the
+    workspace (uint8, at least attn_fwd_workspace_bytes) is allocated when not
+    given."""
     B, K, G, T, S, H = _dims(q, k)
     _check_tensor("q", q, torch.bfloat16)
     _check_tensor("k", k, torch.bfloat16)
@@ -138,6 +161,18 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
         lse = torch.empty(B, K, G, T, dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_tensor("lse", lse, torch.float32, (B, K, G, T))
+    if split_kv:
+        wsb = attn_fwd_workspace_bytes(B, K, G, T, S, H)
+        if workspace is None and wsb > 0:
+            workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            _check_tensor("workspace", workspace, torch.uint8)
+        rc = load_library().attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg), _ptr(kv_seg),
+                                        B, K, G, T, S, H, int(bool(causal)), _ptr(workspace),
+                                        0 if workspace is None else workspace.numel(), _stream_handle(q.device))
+        if rc != GQA_ATTN_OK:
+            raise GqaAttnError(rc, "attn_fwd_ws")
+        return out, lse
     rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg), _ptr(kv_seg),
                                  B, K, G, T, S, H, int(bool(causal)), _stream_handle(q.device))
     if rc != GQA_ATTN_OK:

@@ -50,11 +50,12 @@ int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, c
     return GQA_ATTN_OK;
 }
 
-int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
-             const int32_t *q_seg, const int32_t *kv_seg,
-             int B, int K, int G, int T, int S, int H, int causal, void *stream) {
-    int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal);
-    if (rc) return rc;
+// Forward with an optional split-KV plan (plan.n_splits > 1 needs the
+// workspace: partial outputs first, then partial lse).
+static int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal,
+                   gqa::SplitPlan plan, void *workspace, void *stream) {
     const gqa::FwdConfig cfg = gqa::fwd_config(G, T, H);
     gqa::FwdArgs a;
     a.q = (const __bf16 *)q;
@@ -70,9 +71,65 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
     a.bq = cfg.bq;
     a.n_gsplit = G / cfg.gw;
     a.n_qblocks = (T + cfg.bq - 1) / cfg.bq;
+    a.n_splits = plan.n_splits;
+    a.split_tiles = plan.split_tiles;
+    a.o_part = nullptr;
+    a.lse_part = nullptr;
+    if (plan.n_splits > 1) {
+        const size_t rows = (size_t)B * K * G * T;
+        a.o_part = (float *)workspace;
+        a.lse_part = a.o_part + (size_t)plan.n_splits * rows * H;
+    }
     hipError_t e = gqa::launch_fwd(a, H, (hipStream_t)stream);
+    if (e == hipSuccess && plan.n_splits > 1) e = gqa::launch_fwd_merge(a, H, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return GQA_ATTN_OK;
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             const int32_t *q_seg, const int32_t *kv_seg,
+             int B, int K, int G, int T, int S, int H, int causal, void *stream) {
+    int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal);
+    if (rc) return rc;
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, gqa::SplitPlan{1, 0}, nullptr, stream);
+}
+
+size_t attn_fwd_workspace_bytes(int B, int K, int G, int T, int S, int H) {
+    if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return 0;
+    if (H != 64 && H != 128 && H != 256) return 0;
+    const gqa::SplitPlan plan = gqa::fwd_split_plan(B, K, G, T, S, H);
+    if (plan.n_splits <= 1) return 0;
+    const size_t rows = (size_t)B * K * G * T;
+    return round256(sizeof(float) * (size_t)plan.n_splits * rows * (H + 1));
+}
+
+int attn_check_fwd_ws(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                      const int32_t *q_seg, const int32_t *kv_seg,
+                      int B, int K, int G, int T, int S, int H, int causal,
+                      const void *workspace, size_t workspace_bytes) {
+    int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal);
+    if (rc) return rc;
+    const size_t need = attn_fwd_workspace_bytes(B, K, G, T, S, H);
+    if (need == 0) return GQA_ATTN_OK;
+    if (!workspace || workspace_bytes < need) return GQA_ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return GQA_ATTN_ERR_ALIGN;
+    return GQA_ATTN_OK;
+}
+
+int attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                const int32_t *q_seg, const int32_t *kv_seg,
+                int B, int K, int G, int T, int S, int H, int causal,
+                void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = attn_check_fwd_ws(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace, workspace_bytes);
+    if (rc) return rc;
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, gqa::fwd_split_plan(B, K, G, T, S, H),
+                   workspace, stream);
+}
+
+int attn_fwd_split_count(int B, int K, int G, int T, int S, int H) {
+    if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return 0;
+    if (H != 64 && H != 128 && H != 256) return 0;
+    return gqa::fwd_split_plan(B, K, G, T, S, H).n_splits;
 }
 
 size_t attn_bwd_workspace_bytes(int B, int K, int G, int T, int S, int H) {

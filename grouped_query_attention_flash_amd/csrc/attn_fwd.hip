@@ -134,11 +134,15 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, c = lane >> 5;
 
-    // ---- work unit; causal blocks are issued heaviest (last query block) first
+    // ---- work unit; causal blocks are issued heaviest (last query block) first;
+    // with split-KV the grid holds one copy per split
     const int units = a.B * a.K * a.n_gsplit;
-    int qb = blockIdx.x / units;
+    const int per_split = units * a.n_qblocks;
+    const int split = a.o_part ? (int)blockIdx.x / per_split : 0;
+    const int bid = a.o_part ? (int)blockIdx.x % per_split : (int)blockIdx.x;
+    int qb = bid / units;
     if (CAUSAL) qb = a.n_qblocks - 1 - qb;
-    const int u = blockIdx.x % units;
+    const int u = bid % units;
     const int gs = u % a.n_gsplit;
     const int kh = (u / a.n_gsplit) % a.K;
     const int b = u / (a.n_gsplit * a.K);
@@ -194,10 +198,16 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
     }
 
-    // ---- key-tile range: causal stops at the block's last query
+    // ---- key-tile range: causal stops at the block's last query; a split
+    // covers its own range of tiles
     const int n_tiles = (S + BKV - 1) / BKV;
     int j_end = n_tiles;
     if (CAUSAL) j_end = min(j_end, (min(t0 + a.bq, T) - 1) / BKV + 1);
+    int j_begin = 0;
+    if (!DENSE && a.o_part) {
+        j_begin = split * a.split_tiles;
+        j_end = min(j_end, j_begin + a.split_tiles);
+    }
 
     // kv-id range of tile j (wave-uniform; every wave computes the same value)
     auto tile_ids = [&](int j, int &kmin, int &kmax) {
@@ -522,7 +532,7 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         // n_{i-1}, issues the QK^T MFMAs of n_{i+1} and, while they run, does the
         // softmax and PV of n_i. Even iterations use (sk0 | sk1, sv0 | sv1), odd ones
         // the swapped pairs, so S^T buffers alternate without register copies.
-        int j_cur = next_tile(0);
+        int j_cur = j_begin < j_end ? next_tile(j_begin) : j_end;
         int j_nxt = j_cur < j_end ? next_tile(j_cur + 1) : j_end;
         if (j_cur < j_end) {
             issue_k(j_cur, sk0);
@@ -595,8 +605,26 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         }
     }
 
-    // ---- finalize: O = acc / l in bf16, lse = ln(sum exp(logits))
+    // ---- finalize: O = acc / l in bf16, lse = ln(sum exp(logits)); a split
+    // writes both in fp32 to its part of the workspace
     l_run += __shfl_xor(l_run, 32);  // the two halves of each row
+    if (!DENSE && a.o_part) {
+        if (q_valid) {
+            const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+            const size_t row = (bk * a.G + g) * (size_t)T + t;
+            const size_t rows = (size_t)a.B * a.K * a.G * T;
+            float *orow = a.o_part + ((size_t)split * rows + row) * H;
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++)
+                    *(f32x4 *)(orow + 32 * hb + 8 * q4 + 4 * c) =
+                        f32x4{oacc[hb][4 * q4] * inv, oacc[hb][4 * q4 + 1] * inv, oacc[hb][4 * q4 + 2] * inv,
+                              oacc[hb][4 * q4 + 3] * inv};
+            if (c == 0) a.lse_part[(size_t)split * rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+        }
+        return;
+    }
     if (q_valid) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
         __bf16 *orow = a.o + qrow_off;
@@ -927,9 +955,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
 
 template <int H, int BKV, int NW, int WPS>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-    const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks);
+    const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks * (a.o_part ? a.n_splits : 1));
     const bool all_waves = a.gw * a.bq == 32 * NW;
-    const bool dense = a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
+    const bool dense = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
                        (!a.causal || (a.T == a.S && a.bq == BKV));
     if constexpr (GQA_FWD_PINGPONG && H <= 128 && NW == 8) {
         if (dense) {
@@ -966,6 +994,73 @@ FwdConfig fwd_config(int G, int T, int H) {
     cfg.bq = 32 * (cfg.nw / gw);
     (void)T;
     return cfg;
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV merge. The splits of a row hold normalised partial outputs O_j and
+// log-sum-exps lse_j over disjoint key ranges; the whole row's result is
+//   lse = ln sum_j exp(lse_j),   O = sum_j exp(lse_j - lse) O_j,
+// which is the online-softmax combination applied across the splits. A split
+// that sees no key has lse_j = -inf and weight 0; a row that sees none gets
+// O = 0 and lse = -inf. One wave per row, each lane H / 64 elements.
+template <int H>
+__global__ __launch_bounds__(256) void attn_fwd_merge_kernel(FwdArgs a, int rows) {
+    constexpr int EPL = H / 64;  // elements per lane
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    float m = -INFINITY;
+    for (int j = 0; j < a.n_splits; j++) m = max_nan(m, a.lse_part[(size_t)j * rows + row]);
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; e++) acc[e] = 0.f;
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+        for (int j = 0; j < a.n_splits; j++) {
+            const float w = exp2_fast((a.lse_part[(size_t)j * rows + row] - m) * kLog2e);
+            wsum += w;
+            const float *op = a.o_part + ((size_t)j * rows + row) * H + lane * EPL;
+#pragma unroll
+            for (int e = 0; e < EPL; e++) acc[e] += w * op[e];
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    __bf16 *orow = a.o + (size_t)row * H + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; e++) orow[e] = (__bf16)(acc[e] * inv);
+    if (lane == 0 && a.lse) a.lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+}
+
+hipError_t launch_fwd_merge(const FwdArgs &a, int H, hipStream_t stream) {
+    const int rows = a.B * a.K * a.G * a.T;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    switch (H) {
+        case 64: hipLaunchKernelGGL((attn_fwd_merge_kernel<64>), grid, dim3(256), 0, stream, a, rows); break;
+        case 128: hipLaunchKernelGGL((attn_fwd_merge_kernel<128>), grid, dim3(256), 0, stream, a, rows); break;
+        case 256: hipLaunchKernelGGL((attn_fwd_merge_kernel<256>), grid, dim3(256), 0, stream, a, rows); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Split-KV pays when the usual grid leaves the GPU idle (few (b, kv head)
+// units and query blocks, as in decoding with T << S): the key range is then
+// cut into splits of whole tiles until the grid has about kTargetBlocks
+// workgroups, keeping at least kMinSplitTiles tiles per split.
+SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H) {
+    constexpr long long kTargetBlocks = 1024;
+    constexpr int kMinSplitTiles = 4;
+    const FwdConfig cfg = fwd_config(G, T, H);
+    const long long base = (long long)B * K * (G / cfg.gw) * ((T + cfg.bq - 1) / cfg.bq);
+    const int n_tiles = (S + cfg.bkv - 1) / cfg.bkv;
+    SplitPlan p{1, n_tiles};
+    if (base >= kTargetBlocks / 2 || n_tiles < 2 * kMinSplitTiles) return p;
+    int want = (int)((kTargetBlocks + base - 1) / base);
+    want = min(want, n_tiles / kMinSplitTiles);
+    if (want < 2) return p;
+    p.split_tiles = (n_tiles + want - 1) / want;
+    p.n_splits = (n_tiles + p.split_tiles - 1) / p.split_tiles;
+    return p;
 }
 
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {

@@ -17,7 +17,23 @@ struct FwdArgs {
     int bq;         // queries per workgroup; gw * bq is a multiple of 32
     int n_gsplit;   // G / gw
     int n_qblocks;  // ceil(T / bq)
+    // Split-KV (o_part non-null): the grid is n_splits copies of the usual
+    // one; copy j covers key tiles [j split_tiles, (j+1) split_tiles) and
+    // writes its normalised fp32 O and its lse for every row to
+    // o_part[j][row][H] and lse_part[j][row] (row = (b K + k) G T + g T + t).
+    // A merge kernel then combines the copies into o and lse.
+    int n_splits;
+    int split_tiles;
+    float *o_part;
+    float *lse_part;
 };
+
+// Split-KV plan of a shape (pure host function): n_splits == 1 means none.
+struct SplitPlan {
+    int n_splits, split_tiles;
+};
+SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H);
+hipError_t launch_fwd_merge(const FwdArgs &a, int H, hipStream_t stream);
 
 struct FwdConfig {
     int nw, gw, bq, bkv;

@@ -79,6 +79,43 @@ int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, c
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal);
 
+/* Forward pass for shapes with few query rows per kv head, such as decoding
+ * (T = 1, S the context length), where the pages note that the intensity
+ * falls to about G FLOP per byte (danielwatson6.github.io/fa, "Quick
+ * digression: what about inference?"). Same arguments and result as
+ * attn_fwd, plus a caller-owned device workspace. When the usual grid would
+ * leave the GPU idle, the key range is split across workgroups: each split
+ * writes a normalised fp32 partial output and its logsumexp to the
+ * workspace, and a merge kernel combines them with the online softmax's
+ * rescaling (O = sum_j exp(lse_j - lse) O_j, lse = ln sum_j exp(lse_j)).
+ * Otherwise it runs exactly as attn_fwd and the workspace is not touched.
+ *   workspace        device buffer of at least attn_fwd_workspace_bytes()
+ *                    (which may be 0: then NULL is fine), 16-byte aligned,
+ *                    owned by the caller, contents ignored
+ * Errors as attn_fwd, plus ERR_WORKSPACE (NULL or too small when needed) and
+ * ERR_ALIGN for a misaligned workspace. Enqueues one kernel, or the split
+ * kernel and the merge kernel, on `stream`. */
+int attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                const int32_t *q_seg, const int32_t *kv_seg,
+                int B, int K, int G, int T, int S, int H, int causal,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace attn_fwd_ws needs for these sizes: 0 when it
+ * does not split, else n_splits * B*K*G*T * (H + 1) fp32 rounded up to 256
+ * bytes (partial outputs [n_splits,B,K,G,T,H], then partial lse
+ * [n_splits,B,K,G,T]). Returns 0 for invalid sizes. */
+size_t attn_fwd_workspace_bytes(int B, int K, int G, int T, int S, int H);
+
+/* Number of key splits attn_fwd_ws uses for these sizes (1: no split; 0 for
+ * invalid sizes). Host-only. */
+int attn_fwd_split_count(int B, int K, int G, int T, int S, int H);
+
+/* Host-only validation of attn_fwd_ws's arguments. Same return codes. */
+int attn_check_fwd_ws(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                      const int32_t *q_seg, const int32_t *kv_seg,
+                      int B, int K, int G, int T, int S, int H, int causal,
+                      const void *workspace, size_t workspace_bytes);
+
 /* Bytes of device workspace attn_bwd needs for these sizes (the per-row
  * D = sum_s P[t,s] dP[t,s] vector, fp32 [B,K,G,T], rounded up to 256 bytes).
  * Returns 0 for invalid sizes. */

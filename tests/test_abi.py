@@ -89,6 +89,46 @@ def test_check_bwd_codes_and_workspace():
     assert check_bwd(qs=A16) == gqa.GQA_ATTN_ERR_SEGMENTS
 
 
+def check_fwd_ws(ws=A16, wsb=None, B=1, K=2, G=4, T=1, S=4096, H=128, causal=0):
+    P = ctypes.c_void_p
+    if wsb is None:
+        wsb = gqa.attn_fwd_workspace_bytes(B, K, G, T, S, H)
+    return gqa.load_library().attn_check_fwd_ws(P(A16), P(A16), P(A16), P(A16), P(A16), None, None,
+                                                B, K, G, T, S, H, causal, P(ws), wsb)
+
+
+def test_split_plan_and_workspace_size():
+    # the headline training shape fills the GPU: no split, no workspace
+    assert gqa.attn_fwd_split_count(1, 8, 4, 8192, 8192, 128) == 1
+    assert gqa.attn_fwd_workspace_bytes(1, 8, 4, 8192, 8192, 128) == 0
+    # decoding shapes split the key range; the workspace holds every split's
+    # fp32 output rows and lse, rounded up to 256 bytes
+    for (B, K, G, T, S, H) in [(1, 2, 4, 1, 4096, 128), (16, 8, 4, 1, 32768, 128), (1, 1, 8, 1, 1030, 64),
+                               (1, 1, 4, 5, 2500, 256)]:
+        n = gqa.attn_fwd_split_count(B, K, G, T, S, H)
+        assert n > 1, (B, K, G, T, S, H)
+        rows = B * K * G * T
+        want = 4 * n * rows * (H + 1)
+        assert gqa.attn_fwd_workspace_bytes(B, K, G, T, S, H) == (want + 255) // 256 * 256
+    # too few key tiles to split, and invalid sizes
+    assert gqa.attn_fwd_split_count(1, 1, 4, 1, 100, 128) == 1
+    assert gqa.attn_fwd_split_count(0, 1, 4, 1, 100, 128) == 0
+    assert gqa.attn_fwd_workspace_bytes(1, 1, 4, 1, 100, 96) == 0
+
+
+def test_check_fwd_ws_codes():
+    assert check_fwd_ws() == gqa.GQA_ATTN_OK
+    assert check_fwd_ws(ws=None) == gqa.GQA_ATTN_ERR_WORKSPACE
+    need = gqa.attn_fwd_workspace_bytes(1, 2, 4, 1, 4096, 128)
+    assert check_fwd_ws(wsb=need - 1) == gqa.GQA_ATTN_ERR_WORKSPACE
+    assert check_fwd_ws(ws=A16 + 8) == gqa.GQA_ATTN_ERR_ALIGN
+    # a shape that does not split needs no workspace
+    assert check_fwd_ws(ws=None, wsb=0, T=8192, S=8192, K=8) == gqa.GQA_ATTN_OK
+    # the forward's own checks come first
+    assert check_fwd_ws(H=96) == gqa.GQA_ATTN_ERR_HEADDIM
+    assert check_fwd_ws(B=0) == gqa.GQA_ATTN_ERR_SHAPE
+
+
 def test_strerror_and_hip_error():
     for code in range(0, 8):
         s = gqa.attn_strerror(code)
