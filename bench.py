@@ -15,6 +15,12 @@ MI355X dense bf16 MFMA peak; `cpu_baseline` times the CPU oracle on a
 bounded random sample of the same workload's query rows on the host cores.
 A second leg times the backward (dQ, dK, dV from the saved lse) on the same
 tensors and reports it under "backward".
+
+--workload decode instead times the decoding shape B=16, K=8, G=4, T=1,
+S=32768, H=128 (non-causal: the query sees the whole context) through the
+split-KV forward (attn_fwd_ws), and prints one JSON line whose value is the
+HBM bandwidth achieved on the algorithmic bytes (q, k, v, o, lse once each),
+with the single-pass forward's time beside it.
 """
 from __future__ import annotations
 
@@ -95,7 +101,7 @@ def cpu_baseline(inp, w, o_gpu, target_s=12.0):
     rng = np.random.default_rng(12345)
     total_rows = w.B * w.K * w.G * w.T
     # calibrate on a small sample, then size the timed sample to ~target_s
-    n = 2048
+    n = min(2048, total_rows)
     rows = np.sort(rng.choice(total_rows, size=n, replace=False))
     t0 = time.perf_counter()
     oracle.fwd(inp["q"], inp["k"], inp["v"], causal=w.causal, rows=rows)
@@ -121,7 +127,80 @@ def cpu_baseline(inp, w, o_gpu, target_s=12.0):
             n, flops / full, elapsed),
         "sample_max_abs_vs_gpu": err,
         "sample_rel_l2_vs_gpu": rel,
+        "rows": int(n),
+        "elapsed_s": elapsed,
     }
+
+
+def decode_bench(args):
+    """The decoding workload through the split-KV forward: HBM-bound."""
+    import torch
+    import grouped_query_attention_flash_amd as gqa
+    from workloads import DECODE, attention_flops, make_qkv
+
+    w = DECODE
+    q, k, v = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed)
+    inp_cpu = {"q": q, "k": k, "v": v}
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(w.B, w.K, w.G, w.T, dtype=torch.float32, device=dev)
+    n_splits = gqa.attn_fwd_split_count(w.B, w.K, w.G, w.T, w.S, w.H)
+    ws = torch.empty(max(1, gqa.attn_fwd_workspace_bytes(w.B, w.K, w.G, w.T, w.S, w.H)), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        gqa.attn_fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse, split_kv=True, workspace=ws)
+
+    def step_single():
+        gqa.attn_fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse)
+
+    ms_single = time_launches(step_single, max(5, args.steps // 2), max(2, args.warmup // 2), args.settle_seconds)
+    ms = time_launches(step, args.steps, args.warmup, args.settle_seconds)
+    hbm_bytes = 2 * (qd.numel() + kd.numel() + vd.numel() + o.numel()) + 4 * lse.numel()
+    gbps = hbm_bytes / (ms * 1e-3) / 1e9
+    flops = attention_flops(w.B, w.K, w.G, w.T, w.S, w.H, w.causal)
+    result = {
+        "metric": "decode attention HBM GB/s (fwd, T=1, split-KV) at 1 GPU; % of HBM peak",
+        "value": gbps,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, q pre-scaled by H^-1/2)",
+        "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
+                   "causal": w.causal, "n_splits": n_splits},
+        "roofline": {
+            "kernel": "attn_fwd_kernel split-KV + attn_fwd_merge_kernel (whole call)",
+            "bound": "hbm",
+            "achieved": gbps,
+            "peak": MI355X_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": gbps / MI355X_HBM_GBPS,
+            "traffic": None,
+            "algorithmic_hbm_bytes_per_launch": hbm_bytes,
+            "algorithmic_flops_per_launch": flops,
+        },
+        "single_pass": {"ms": ms_single, "gbps": hbm_bytes / (ms_single * 1e-3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        step()
+        torch.cuda.synchronize()
+        cb = cpu_baseline(inp_cpu, w, o, target_s=12.0)
+        # the oracle's rate in the metric's unit: each sampled row stands for
+        # its share of the launch's algorithmic bytes
+        total_rows = w.B * w.K * w.G * w.T
+        cb["value_tflops"] = cb["value"]
+        cb["value"] = cb["rows"] / total_rows * hbm_bytes / cb["elapsed_s"] / 1e9
+        cb["unit"] = "GB/s"
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -133,6 +212,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed launches before the warm-up steps, for the clock to settle")
+    ap.add_argument("--workload", choices=["headline", "decode"], default="headline",
+                    help="headline: the causal T=S=8192 forward (default); decode: T=1 against S=32768")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a known-size "
                          "reference dispatch for the HBM byte counters)")
@@ -149,6 +230,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "decode":
+        decode_bench(args)
+        return
     w = HEADLINE
     q, k, v, do = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=True)
     inp_cpu = {"q": q, "k": k, "v": v}

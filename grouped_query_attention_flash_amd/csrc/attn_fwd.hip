@@ -60,6 +60,10 @@
 #define GQA_PP_MSCHED 1
 #endif
 // ping-pong: O leaves through LDS in coalesced 1 KiB stores
+// split-KV: workgroups the split plan aims for
+#ifndef GQA_SPLIT_TARGET
+#define GQA_SPLIT_TARGET 1024
+#endif
 #ifndef GQA_PP_OSTAGE
 #define GQA_PP_OSTAGE 1
 #endif
@@ -979,6 +983,33 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Split-KV copies of the general kernel run 4 waves per workgroup at every
+// head size, so that at H <= 128 two workgroups share a CU (a decoding
+// workgroup has few query rows, and two of them keep twice the K/V bytes in
+// flight). H = 256 keeps one wave per SIMD (its O^T carry needs the registers).
+template <int H, int BKV, int WPS>
+static hipError_t launch_fwd_split_t(const FwdArgs &a, hipStream_t stream) {
+    const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks * a.n_splits);
+    if (a.causal)
+        hipLaunchKernelGGL((attn_fwd_kernel<H, BKV, 4, WPS, true, false>), dim3(grid), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<H, BKV, 4, WPS, false, false>), dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+FwdConfig fwd_config_split(int G, int T, int H) {
+    FwdConfig cfg;
+    cfg.nw = 4;
+    cfg.bkv = (H == 256) ? 32 : 64;
+    int gw = 1;
+    for (int d = 1; d <= cfg.nw && d <= G; d++)
+        if (G % d == 0) gw = d;
+    cfg.gw = gw;
+    cfg.bq = 32 * (cfg.nw / gw);
+    (void)T;
+    return cfg;
+}
+
 FwdConfig fwd_config(int G, int T, int H) {
     // 32 query rows per wave. H <= 128: 8 waves (2 per SIMD, <= 256 registers
     // each). H = 256: the O^T carry alone is 128 registers per lane, so 4 waves
@@ -1048,13 +1079,15 @@ hipError_t launch_fwd_merge(const FwdArgs &a, int H, hipStream_t stream) {
 // cut into splits of whole tiles until the grid has about kTargetBlocks
 // workgroups, keeping at least kMinSplitTiles tiles per split.
 SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H) {
-    constexpr long long kTargetBlocks = 1024;
+    constexpr long long kTargetBlocks = GQA_SPLIT_TARGET;
     constexpr int kMinSplitTiles = 4;
-    const FwdConfig cfg = fwd_config(G, T, H);
+    const FwdConfig full = fwd_config(G, T, H);
+    const long long base_full = (long long)B * K * (G / full.gw) * ((T + full.bq - 1) / full.bq);
+    const FwdConfig cfg = fwd_config_split(G, T, H);
     const long long base = (long long)B * K * (G / cfg.gw) * ((T + cfg.bq - 1) / cfg.bq);
     const int n_tiles = (S + cfg.bkv - 1) / cfg.bkv;
     SplitPlan p{1, n_tiles};
-    if (base >= kTargetBlocks / 2 || n_tiles < 2 * kMinSplitTiles) return p;
+    if (base_full >= kTargetBlocks / 2 || n_tiles < 2 * kMinSplitTiles) return p;
     int want = (int)((kTargetBlocks + base - 1) / base);
     want = min(want, n_tiles / kMinSplitTiles);
     if (want < 2) return p;
@@ -1064,6 +1097,14 @@ SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H) {
 }
 
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
+    if (a.o_part) {
+        switch (H) {
+            case 64: return launch_fwd_split_t<64, 64, 2>(a, stream);
+            case 128: return launch_fwd_split_t<128, 64, 2>(a, stream);
+            case 256: return launch_fwd_split_t<256, 32, 1>(a, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (H) {
         case 64: return launch_fwd_t<64, 64, 8, 2>(a, stream);
         case 128: return launch_fwd_t<128, GQA_FWD_BKV128, GQA_FWD_NW128, 2>(a, stream);

@@ -39,8 +39,10 @@ struct FwdConfig {
     int nw, gw, bq, bkv;
 };
 
-// Tile configuration for a shape (pure host function).
+// Tile configuration for a shape (pure host function), and the one the
+// split-KV path uses (4 waves per workgroup).
 FwdConfig fwd_config(int G, int T, int H);
+FwdConfig fwd_config_split(int G, int T, int H);
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream);
 
 struct BwdArgs {

@@ -63,6 +63,13 @@ HEADLINE = dataclasses.replace(
     name="causal_b1_k8_g4_t8192_h128", backward=False)
 
 
+# Decoding: one query row per head (T = 1) against a 32768-token context, the
+# regime where the intensity is about G FLOP per byte and the forward is bound
+# by reading K and V. Not one of the five workloads; bench.py times it with
+# --workload decode.
+DECODE = Workload("decode_b16_k8_g4_t1_s32768_h128", 16, 8, 4, 1, 32768, 128, False, False, False, 6)
+
+
 def make_qkv(B: int, K: int, G: int, T: int, S: int, H: int, seed: int,
              with_do: bool = False, q_scale: Optional[float] = None):
     """Draw q, k, v (and dO) as bf16 CPU tensors, contiguous, H innermost."""
