@@ -32,7 +32,8 @@ GQA_ATTN_ERR_HIP = 7
 
 EXPORTED_SYMBOLS = (
     "attn_fwd", "attn_check_fwd", "attn_fwd_ws", "attn_check_fwd_ws", "attn_fwd_workspace_bytes",
-    "attn_fwd_split_count", "attn_bwd_workspace_bytes", "attn_bwd", "attn_check_bwd",
+    "attn_fwd_split_count", "attn_fwd_local", "attn_check_fwd_local", "attn_bwd_workspace_bytes", "attn_bwd",
+    "attn_check_bwd", "attn_bwd_local", "attn_check_bwd_local",
     "attn_strerror", "attn_last_hip_error",
 )
 
@@ -68,6 +69,14 @@ def load_library():
     lib.attn_fwd_ws.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, SZ, P]
     lib.attn_check_fwd_ws.restype = I
     lib.attn_check_fwd_ws.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, SZ]
+    lib.attn_fwd_local.restype = I
+    lib.attn_fwd_local.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, SZ, P]
+    lib.attn_check_fwd_local.restype = I
+    lib.attn_check_fwd_local.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, SZ]
+    lib.attn_bwd_local.restype = I
+    lib.attn_bwd_local.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, SZ, P]
+    lib.attn_check_bwd_local.restype = I
+    lib.attn_check_bwd_local.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, SZ]
     lib.attn_fwd_workspace_bytes.restype = SZ
     lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_fwd_split_count.restype = I
@@ -138,13 +147,16 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
              q_seg: Optional[torch.Tensor] = None, kv_seg: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
              want_lse: bool = True, split_kv: bool = False,
-             workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+             workspace: Optional[torch.Tensor] = None,
+             window: Optional[Tuple[int, int]] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Forward pass on the current stream. Returns (o, lse).
 
     split_kv=True calls attn_fwd_ws, which splits the key range across
     workgroups for shapes that would leave the GPU idle (decoding); the
     workspace (uint8, at least attn_fwd_workspace_bytes) is allocated when not
-    given."""
+    given. window=(left, right) calls attn_fwd_local: key s is visible to
+    query t only when t - left <= s <= t + right (-1: unbounded side); it
+    splits like split_kv."""
     B, K, G, T, S, H = _dims(q, k)
     _check_tensor("q", q, torch.bfloat16)
     _check_tensor("k", k, torch.bfloat16)
@@ -161,6 +173,19 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
         lse = torch.empty(B, K, G, T, dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_tensor("lse", lse, torch.float32, (B, K, G, T))
+    if window is not None:
+        wsb = attn_fwd_workspace_bytes(B, K, G, T, S, H)
+        if workspace is None and wsb > 0:
+            workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            _check_tensor("workspace", workspace, torch.uint8)
+        rc = load_library().attn_fwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg),
+                                           _ptr(kv_seg), B, K, G, T, S, H, int(bool(causal)), int(window[0]),
+                                           int(window[1]), _ptr(workspace),
+                                           0 if workspace is None else workspace.numel(), _stream_handle(q.device))
+        if rc != GQA_ATTN_OK:
+            raise GqaAttnError(rc, "attn_fwd_local")
+        return out, lse
     if split_kv:
         wsb = attn_fwd_workspace_bytes(B, K, G, T, S, H)
         if workspace is None and wsb > 0:
@@ -184,10 +209,11 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              do: torch.Tensor, *, causal: bool = False, q_seg: Optional[torch.Tensor] = None,
              kv_seg: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
              dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None):
+             workspace: Optional[torch.Tensor] = None, window: Optional[Tuple[int, int]] = None):
     """Backward pass on the current stream. Returns (dq, dk, dv) in fp32.
 
-    `o` (the forward output) may be None: the library does not read it."""
+    `o` (the forward output) may be None: the library does not read it.
+    window=(left, right) calls attn_bwd_local with that local window."""
     B, K, G, T, S, H = _dims(q, k)
     for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
         _check_tensor(name, t, torch.bfloat16)
@@ -206,6 +232,14 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     wsb = attn_bwd_workspace_bytes(B, K, G, T, S, H)
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    if window is not None:
+        rc = load_library().attn_bwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                           _ptr(dk), _ptr(dv), _ptr(q_seg), _ptr(kv_seg), B, K, G, T, S, H,
+                                           int(bool(causal)), int(window[0]), int(window[1]), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream_handle(dev))
+        if rc != GQA_ATTN_OK:
+            raise GqaAttnError(rc, "attn_bwd_local")
+        return dq, dk, dv
     rc = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _ptr(q_seg), _ptr(kv_seg), B, K, G, T, S, H, int(bool(causal)),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -54,7 +54,7 @@ int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, c
 // workspace: partial outputs first, then partial lse).
 static int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                    const int32_t *q_seg, const int32_t *kv_seg,
-                   int B, int K, int G, int T, int S, int H, int causal,
+                   int B, int K, int G, int T, int S, int H, int causal, int wl, int wr,
                    gqa::SplitPlan plan, void *workspace, void *stream) {
     const gqa::FwdConfig cfg = plan.n_splits > 1 ? gqa::fwd_config_split(G, T, H) : gqa::fwd_config(G, T, H);
     gqa::FwdArgs a;
@@ -67,6 +67,8 @@ static int run_fwd(const void *q, const void *k, const void *v, void *o, float *
     a.kv_seg = kv_seg;
     a.B = B, a.K = K, a.G = G, a.T = T, a.S = S;
     a.causal = causal ? 1 : 0;
+    a.wl = wl;
+    a.wr = wr;
     a.gw = cfg.gw;
     a.bq = cfg.bq;
     a.n_gsplit = G / cfg.gw;
@@ -91,7 +93,8 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int K, int G, int T, int S, int H, int causal, void *stream) {
     int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal);
     if (rc) return rc;
-    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, gqa::SplitPlan{1, 0}, nullptr, stream);
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, -1, -1, gqa::SplitPlan{1, 0}, nullptr,
+                   stream);
 }
 
 size_t attn_fwd_workspace_bytes(int B, int K, int G, int T, int S, int H) {
@@ -122,8 +125,27 @@ int attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse
                 void *workspace, size_t workspace_bytes, void *stream) {
     int rc = attn_check_fwd_ws(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace, workspace_bytes);
     if (rc) return rc;
-    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, gqa::fwd_split_plan(B, K, G, T, S, H),
-                   workspace, stream);
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, -1, -1,
+                   gqa::fwd_split_plan(B, K, G, T, S, H), workspace, stream);
+}
+
+int attn_check_fwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                         const int32_t *q_seg, const int32_t *kv_seg,
+                         int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                         const void *workspace, size_t workspace_bytes) {
+    if (window_left < -1 || window_right < -1) return GQA_ATTN_ERR_SHAPE;
+    return attn_check_fwd_ws(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace, workspace_bytes);
+}
+
+int attn_fwd_local(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = attn_check_fwd_local(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left, window_right,
+                                  workspace, workspace_bytes);
+    if (rc) return rc;
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left, window_right,
+                   gqa::fwd_split_plan(B, K, G, T, S, H), workspace, stream);
 }
 
 int attn_fwd_split_count(int B, int K, int G, int T, int S, int H) {
@@ -155,14 +177,11 @@ int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, c
     return GQA_ATTN_OK;
 }
 
-int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
-             const void *dO, float *dq, float *dk, float *dv,
-             const int32_t *q_seg, const int32_t *kv_seg,
-             int B, int K, int G, int T, int S, int H, int causal,
-             void *workspace, size_t workspace_bytes, void *stream) {
-    int rc = attn_check_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal,
-                            workspace, workspace_bytes);
-    if (rc) return rc;
+static int run_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dO, float *dq, float *dk, float *dv,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal, int wl, int wr,
+                   void *workspace, void *stream) {
     gqa::BwdArgs a;
     a.q = (const __bf16 *)q;
     a.k = (const __bf16 *)k;
@@ -178,9 +197,45 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
     a.kv_seg = kv_seg;
     a.B = B, a.K = K, a.G = G, a.T = T, a.S = S;
     a.causal = causal ? 1 : 0;
+    a.wl = wl;
+    a.wr = wr;
     hipError_t e = gqa::launch_bwd(a, H, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return GQA_ATTN_OK;
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dO, float *dq, float *dk, float *dv,
+             const int32_t *q_seg, const int32_t *kv_seg,
+             int B, int K, int G, int T, int S, int H, int causal,
+             void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = attn_check_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal,
+                            workspace, workspace_bytes);
+    if (rc) return rc;
+    return run_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, -1, -1, workspace,
+                   stream);
+}
+
+int attn_check_bwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                         const void *dO, const float *dq, const float *dk, const float *dv,
+                         const int32_t *q_seg, const int32_t *kv_seg,
+                         int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                         const void *workspace, size_t workspace_bytes) {
+    if (window_left < -1 || window_right < -1) return GQA_ATTN_ERR_SHAPE;
+    return attn_check_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace,
+                          workspace_bytes);
+}
+
+int attn_bwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dO, float *dq, float *dk, float *dv,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = attn_check_bwd_local(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal,
+                                  window_left, window_right, workspace, workspace_bytes);
+    if (rc) return rc;
+    return run_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left,
+                   window_right, workspace, stream);
 }
 
 const char *attn_strerror(int code) {

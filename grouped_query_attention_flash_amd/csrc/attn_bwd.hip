@@ -122,9 +122,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
         w_kmax = wave_max_i(k_valid ? my_kid : INT_MIN);
     }
 
-    // query tiles: causal -> only tiles holding some t >= s0_wg
-    const int n_qt = (T + BQ - 1) / BQ;
-    const int qt_begin = a.causal ? min(n_qt, s0_wg / BQ) : 0;
+    // query tiles that can see the block's keys: t in [s - R, s + L] for the
+    // window sides L, R (causal: R = 0)
+    const int WL = win_left(a.wl), WR = win_right(a.wr, a.causal);
+    const int n_qt_all = (T + BQ - 1) / BQ;
+    const int qt_begin = min(n_qt_all, max(0, s0_wg - WR) / BQ);
+    const int n_qt = max(qt_begin, min(n_qt_all, (s0_wg + 32 * NW - 1 + WL) / BQ + 1));  // end of the tile range
     const int n_steps = G * (n_qt - qt_begin);  // (g, query tile) pairs, g outer
 
     auto q_ids = [&](int qt, int &qmin, int &qmax) {
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
         if (st_next < n_steps) load_step(st_next);
 
         const int t0 = (qt_begin + st % (n_qt - qt_begin)) * BQ;
-        bool run = wave_active && !(a.causal && t0 + BQ - 1 < s_w);
+        bool run = wave_active && t0 + BQ - 1 >= s_w - WR && t0 <= s_w + 31 + WL;
         bool seg_mask = false;
         if (run && segs) {
             int qmin, qmax;
@@ -230,7 +233,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
                     pacc = mfma32x32x16(*(const bf16x8 *)(drow + off), vf[ks], pacc);
                 }
             }
-            const bool need_mask = (a.causal && s_w + 31 > t0) || (s_w + 32 > S) || (t0 + BQ > T) || seg_mask;
+            const bool need_mask = (s_w + 31 > t0 + WR) || (s_w < t0 + BQ - 1 - WL) || (s_w + 32 > S) ||
+                                   (t0 + BQ > T) || seg_mask;
             // P = exp2(S log2e - lse log2e); dS = P (dP - D)
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++) {
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
                     float x = sacc[r];
                     if (need_mask) {
                         const int t = t0 + r0 + e;
-                        bool vis = k_valid && t < T && !(a.causal && s > t);
+                        bool vis = k_valid && t < T && s <= t + WR && s >= t - WL;
                         if (segs && vis) vis = qsb[t] == my_kid;
                         if (!vis) x = -INFINITY;
                     }
@@ -360,9 +364,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
 
     // steps: (g, query tile) pairs, g outer; causal: tiles holding some t >= s0_wg
+    // query tiles that can see the block's keys: t in [s - R, s + L] for the
+    // window sides L, R (causal: R = 0); qt_end is exclusive
+    const int WL = win_left(a.wl), WR = win_right(a.wr, CAUSAL);
     const int n_qt = (T + BQ - 1) / BQ;
-    const int qt_begin = CAUSAL ? min(n_qt, s0_wg / BQ) : 0;
-    const int nq = n_qt - qt_begin;
+    const int qt_begin = min(n_qt, max(0, s0_wg - WR) / BQ);
+    const int qt_end = max(qt_begin, min(n_qt, (s0_wg + 32 * NW - 1 + WL) / BQ + 1));
+    const int nq = qt_end - qt_begin;
     const int n_steps = G * nq;
 
     // loads of one step: Q and dO tiles (wave w: blocks w, w + NW, ...), lse
@@ -409,7 +417,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         int g, qt;
     };
     auto advance = [&](Cursor &cu) {
-        if (++cu.qt == n_qt) {
+        if (++cu.qt == qt_end) {
             cu.qt = qt_begin;
             ++cu.g;
         }
@@ -439,10 +447,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         }
     };
     // P = exp2(S log2e - lse log2e) and dS = P (dP - D), as bf16 MFMA operands
-    // (2 x 8 queries each). Invisible (query, key) pairs get P = 0: with
-    // causal masking a pair is visible iff 0 <= t - s < T - s, otherwise iff
-    // t < T; one unsigned compare per element (a key past S gets bound 0).
-    const unsigned vis_bound = k_valid ? (unsigned)(CAUSAL ? T - s : T) : 0u;
+    // (2 x 8 queries each). Invisible (query, key) pairs get P = 0. A pair is
+    // visible iff u = t - s + R lies in [0, min(L + R + 1, T - s + R)), which
+    // covers the window, causal masking (R = 0) and t < T with one unsigned
+    // compare per element. The bound is clamped at 0: a key that no query can
+    // see (past S, or past T - 1 + R) gets bound 0.
+    const unsigned vis_bound = k_valid ? (unsigned)max(0, min(WL + WR + 1, T - s + WR)) : 0u;
     // lse and D of the lane's 16 query rows of a step
     auto read_ld = [&](int stage, f32x4 (&l4s)[4], f32x4 (&d4s)[4]) {
 #pragma unroll
@@ -453,7 +463,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     };
     auto weights = [&](int t0, const f32x4 (&l4s)[4], const f32x4 (&d4s)[4], const f32x16 &sacc, const f32x16 &pacc,
                        bf16x8 (&pf)[2], bf16x8 (&sf)[2]) {
-        const int tb = t0 + 4 * c - (CAUSAL ? s : 0);
+        const int tb = t0 + 4 * c - s + WR;
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
             const f32x4 l4 = l4s[q4];
@@ -528,7 +538,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #endif
             const int row_ld = row_of(c_ld);
             advance(c_ld);
-            const int tb = c_w.qt * BQ + 4 * c - (CAUSAL ? s : 0);
+            const int tb = c_w.qt * BQ + 4 * c - s + WR;
             advance(c_w);
             auto read_op = [&](int m) -> bf16x8 {
                 if (m < NQ) {
@@ -721,9 +731,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
         w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
     }
 
+    // key tiles: the window (causal: R = 0) bounds them by the block's first
+    // and last query
+    const int WL = win_left(a.wl), WR = win_right(a.wr, a.causal);
     const int n_tiles = (S + BKV - 1) / BKV;
-    int j_end = n_tiles;
-    if (a.causal) j_end = min(j_end, (min(t0 + bq, T) - 1) / BKV + 1);
+    const int j_end = min(n_tiles, (min(min(t0 + bq, T) - 1 + WR, S - 1)) / BKV + 1);
+    const int j_begin = t0 - WL > 0 ? (t0 - WL) / BKV : 0;
 
     auto tile_ids = [&](int j, int &kmin, int &kmax) {
         const int ss = j * BKV + lane;
@@ -770,7 +783,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
 #pragma unroll
     for (int hb = 0; hb < HB; hb++) dq_acc[hb] = f32x16{};
 
-    int j = next_tile(0);
+    int j = j_begin < j_end ? next_tile(j_begin) : j_end;
     if (j < j_end) load_tile(j);
     while (j < j_end) {
         __syncthreads();
@@ -780,7 +793,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
         if (jn < j_end) load_tile(jn);
 
         const int s0 = j * BKV;
-        bool run = wave_active && !(a.causal && s0 > tmax_w);
+        bool run = wave_active && s0 <= tmax_w + WR && s0 + BKV - 1 >= tmin_w - WL;
         bool seg_mask = false;
         if (run && segs) {
             int kmin, kmax;
@@ -803,7 +816,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
                     pacc[mb] = mfma32x32x16(*(const bf16x8 *)(sv + off), df[ks], pacc[mb]);
                 }
             }
-            const bool need_mask = (a.causal && s0 + BKV - 1 > tmin_w) || (s0 + BKV > S) || seg_mask;
+            const bool need_mask =
+                (s0 + BKV - 1 > tmin_w + WR) || (s0 < tmax_w - WL) || (s0 + BKV > S) || seg_mask;
 #pragma unroll
             for (int mb = 0; mb < MB; mb++)
 #pragma unroll
@@ -811,7 +825,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
                     float x = sacc[mb][r];
                     if (need_mask) {
                         const int ss = s0 + 32 * mb + acc_row(r, c);
-                        bool vis = ss < S && !(a.causal && ss > t);
+                        bool vis = ss < S && ss <= t + WR && ss >= t - WL;
                         if (segs && vis) vis = kvs[ss] == my_qid;
                         if (!vis) x = -INFINITY;
                     }

@@ -202,15 +202,15 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
     }
 
-    // ---- key-tile range: causal stops at the block's last query; a split
-    // covers its own range of tiles
+    // ---- key-tile range: the window (causal: R = 0) bounds it on both sides
+    // by the block's first and last query; a split covers its own range
+    const int WL = win_left(a.wl), WR = win_right(a.wr, CAUSAL);
     const int n_tiles = (S + BKV - 1) / BKV;
-    int j_end = n_tiles;
-    if (CAUSAL) j_end = min(j_end, (min(t0 + a.bq, T) - 1) / BKV + 1);
-    int j_begin = 0;
+    int j_end = min(n_tiles, (min(min(t0 + a.bq, T) - 1 + WR, S - 1)) / BKV + 1);
+    int j_begin = t0 - WL > 0 ? (t0 - WL) / BKV : 0;
     if (!DENSE && a.o_part) {
-        j_begin = split * a.split_tiles;
-        j_end = min(j_end, j_begin + a.split_tiles);
+        j_begin = max(j_begin, split * a.split_tiles);
+        j_end = min(j_end, split * a.split_tiles + a.split_tiles);
     }
 
     // kv-id range of tile j (wave-uniform; every wave computes the same value)
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     // does this wave compute tile j, and does it need an element mask there
     auto tile_flags = [&](int j, bool &run, bool &mask) {
         const int s0 = j * BKV;
-        run = j < j_end && wave_active && !(CAUSAL && s0 > tmax_w);
+        run = j < j_end && wave_active && s0 <= tmax_w + WR && s0 + BKV - 1 >= tmin_w - WL;
         bool seg_mask = false;
         if (run && segs) {
             int kmin, kmax;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
             if (kmax < w_qmin || kmin > w_qmax) run = false;
             seg_mask = !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
         }
-        mask = (CAUSAL && s0 + BKV - 1 > tmin_w) || (s0 + BKV > S) || seg_mask;
+        mask = (s0 + BKV - 1 > tmin_w + WR) || (s0 < tmax_w - WL) || (s0 + BKV > S) || seg_mask;
     };
 
     // One tile of K (row stride L::KRS chunks) or V (L::VRS) into LDS, straight
@@ -331,13 +331,14 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     // Register r of block mb holds key s0 + 32mb + acc_row(r, c); with the lane's
     // half c folded into one limit, every comparison is against a constant.
     auto mask_tile = [&](f32x16 (&sacc)[MB], int s0) {
-        const int lim = min(CAUSAL ? t : INT_MAX, S - 1) - s0 - 4 * c;  // last visible key offset
+        const int lim = min(t + WR, S - 1) - s0 - 4 * c;  // last visible key offset
+        const int first = t - WL - s0 - 4 * c;           // first visible key offset
 #pragma unroll
         for (int mb = 0; mb < MB; mb++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int off = 32 * mb + 8 * (r >> 2) + (r & 3);
-                bool vis = off <= lim;
+                bool vis = off <= lim && off >= first;
                 if (segs && vis) vis = kvs[s0 + off + 4 * c] == my_qid;
                 if (!vis) sacc[mb][r] = -INFINITY;
             }
@@ -962,7 +963,7 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks * (a.o_part ? a.n_splits : 1));
     const bool all_waves = a.gw * a.bq == 32 * NW;
     const bool dense = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
-                       (!a.causal || (a.T == a.S && a.bq == BKV));
+                       !windowed(a.wl, a.wr, a.causal) && (!a.causal || (a.T == a.S && a.bq == BKV));
     if constexpr (GQA_FWD_PINGPONG && H <= 128 && NW == 8) {
         if (dense) {
             if (a.causal)

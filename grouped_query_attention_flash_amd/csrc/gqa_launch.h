@@ -13,6 +13,7 @@ struct FwdArgs {
     const int32_t *q_seg, *kv_seg;   // both null or both set
     int B, K, G, T, S;
     int causal;
+    int wl, wr;     // local window: keys s with t - wl <= s <= t + wr (< 0: unbounded)
     int gw;         // query heads per workgroup (divides G)
     int bq;         // queries per workgroup; gw * bq is a multiple of 32
     int n_gsplit;   // G / gw
@@ -53,6 +54,7 @@ struct BwdArgs {
     const int32_t *q_seg, *kv_seg;
     int B, K, G, T, S;
     int causal;
+    int wl, wr;                      // local window, as in FwdArgs
 };
 
 hipError_t launch_bwd(const BwdArgs &a, int H, hipStream_t stream);

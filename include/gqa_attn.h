@@ -110,6 +110,28 @@ size_t attn_fwd_workspace_bytes(int B, int K, int G, int T, int S, int H);
  * invalid sizes). Host-only. */
 int attn_fwd_split_count(int B, int K, int G, int T, int S, int H);
 
+/* Forward pass with a local (sliding) window: key s is visible to query t
+ * only when t - window_left <= s <= t + window_right, in addition to the
+ * causal rule and segment ids; -1 leaves a side unbounded, and causal = 1
+ * already bounds the right side at 0. The pages run splash attention with a
+ * FullMask through its block mask processing (danielwatson6.github.io/fa,
+ * "Our first kernel": make_splash_fn_nojit); a band of diagonals is the
+ * simplest mask whose block classification is not all-full, and here it is
+ * applied lazily as the causal mask is: key tiles outside the band are not
+ * visited, and only tiles crossing an edge get an element mask. Otherwise as
+ * attn_fwd_ws (workspace as there; window_left / window_right below -1 ->
+ * ERR_SHAPE). With both sides unbounded it computes what attn_fwd_ws does. */
+int attn_fwd_local(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only validation of attn_fwd_local's arguments. Same return codes. */
+int attn_check_fwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                         const int32_t *q_seg, const int32_t *kv_seg,
+                         int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                         const void *workspace, size_t workspace_bytes);
+
 /* Host-only validation of attn_fwd_ws's arguments. Same return codes. */
 int attn_check_fwd_ws(const void *q, const void *k, const void *v, const void *o, const float *lse,
                       const int32_t *q_seg, const int32_t *kv_seg,
@@ -146,6 +168,23 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
              const int32_t *q_seg, const int32_t *kv_seg,
              int B, int K, int G, int T, int S, int H, int causal,
              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward pass of attn_fwd_local: the same window (window_left, window_right,
+ * -1 unbounded) restricts every recomputed weight, and the kernels visit only
+ * the tiles inside the band. Otherwise as attn_bwd; window sides below -1 ->
+ * ERR_SHAPE. */
+int attn_bwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dO, float *dq, float *dk, float *dv,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only validation of attn_bwd_local's arguments. Same return codes. */
+int attn_check_bwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                         const void *dO, const float *dq, const float *dk, const float *dv,
+                         const int32_t *q_seg, const int32_t *kv_seg,
+                         int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                         const void *workspace, size_t workspace_bytes);
 
 /* Host-only validation of attn_bwd's arguments. Same return codes. */
 int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,

@@ -47,10 +47,10 @@ def _load():
         I64 = ctypes.c_int64
         lib.oracle_fwd_rows.restype = ctypes.c_int
         lib.oracle_fwd_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_int,
-                                        I64, P, P, P]
+                                        I64, I64, I64, P, P, P]
         lib.oracle_bwd_rows.restype = ctypes.c_int
         lib.oracle_bwd_rows.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_int,
-                                        I64, P, P, P, I64, P, P, P]
+                                        I64, I64, I64, P, P, P, I64, P, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -101,11 +101,21 @@ def _rows(rows):
     return np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
 
 
-def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None):
+def _window(window):
+    if window is None:
+        return -1, -1
+    wl, wr = int(window[0]), int(window[1])
+    assert wl >= -1 and wr >= -1
+    return wl, wr
+
+
+def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None, window=None):
     """Plain fp64 attention. Returns (O, lse) as float64 numpy arrays.
 
     rows=None: O has q's shape and lse q's shape minus H.
     rows given (flat indices into [B,K,G,T]): O is [len(rows), H], lse [len(rows)].
+    window=(wl, wr): key s visible to query t only if t - wl <= s <= t + wr
+    (a side of -1 is unbounded).
     """
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
     B, K, G, T, H = qb.shape
@@ -119,7 +129,8 @@ def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None)
     o = np.empty((n, H), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
     rc = _load().oracle_fwd_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(qs), _ptr(ks), _ptr(mk),
-                                 B, K, G, T, S, H, int(bool(causal)), n, _ptr(r), _ptr(o), _ptr(lse))
+                                 B, K, G, T, S, H, int(bool(causal)), *_window(window), n, _ptr(r), _ptr(o),
+                                 _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_fwd_rows failed with code %d" % rc)
     if r is None:
@@ -128,7 +139,7 @@ def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None)
 
 
 def bwd(q, k, v, do, *, causal=False, q_seg=None, kv_seg=None, mask=None, qrows=None, kvrows=None,
-        want_dq=True, want_dkv=True):
+        want_dq=True, want_dkv=True, window=None):
     """Plain fp64 gradients of sum(O * dO). Returns dict with dq, dk, dv, D.
 
     Full tensors when the row lists are None, else [n, H] arrays for the
@@ -150,7 +161,7 @@ def bwd(q, k, v, do, *, causal=False, q_seg=None, kv_seg=None, mask=None, qrows=
     dk = np.empty((max(nkv, 1), H), dtype=np.float64)
     dv = np.empty((max(nkv, 1), H), dtype=np.float64)
     rc = _load().oracle_bwd_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(db), _ptr(qs), _ptr(ks), _ptr(mk),
-                                 B, K, G, T, S, H, int(bool(causal)),
+                                 B, K, G, T, S, H, int(bool(causal)), *_window(window),
                                  nq, _ptr(qr), _ptr(dq) if nq else None, _ptr(dd) if nq else None,
                                  nkv, _ptr(kr), _ptr(dk) if nkv else None, _ptr(dv) if nkv else None)
     if rc != 0:

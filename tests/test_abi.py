@@ -129,6 +129,20 @@ def test_check_fwd_ws_codes():
     assert check_fwd_ws(B=0) == gqa.GQA_ATTN_ERR_SHAPE
 
 
+def test_check_local_window_codes():
+    P = ctypes.c_void_p
+    lib = gqa.load_library()
+    args = (P(A16), P(A16), P(A16), P(A16), P(A16), None, None, 1, 1, 4, 64, 64, 128, 1)
+    for wl, wr, want in [(-1, -1, gqa.GQA_ATTN_OK), (0, 0, gqa.GQA_ATTN_OK), (31, -1, gqa.GQA_ATTN_OK),
+                         (-2, 0, gqa.GQA_ATTN_ERR_SHAPE), (0, -5, gqa.GQA_ATTN_ERR_SHAPE)]:
+        assert lib.attn_check_fwd_local(*args, wl, wr, None, 0) == want, (wl, wr)
+    wsb = gqa.attn_bwd_workspace_bytes(1, 1, 4, 64, 64, 128)
+    bargs = (P(A16),) * 9 + (None, None, 1, 1, 4, 64, 64, 128, 1)
+    assert lib.attn_check_bwd_local(*bargs, 5, -1, P(A16), wsb) == gqa.GQA_ATTN_OK
+    assert lib.attn_check_bwd_local(*bargs, -3, -1, P(A16), wsb) == gqa.GQA_ATTN_ERR_SHAPE
+    assert lib.attn_check_bwd_local(*bargs, 5, -1, None, wsb) == gqa.GQA_ATTN_ERR_WORKSPACE
+
+
 def test_strerror_and_hip_error():
     for code in range(0, 8):
         s = gqa.attn_strerror(code)

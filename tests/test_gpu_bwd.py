@@ -28,6 +28,8 @@ SMALL = [
     (1, 2, 4, 320, 320, 128, True, None),
     (2, 1, 4, 200, 200, 128, True, None),
     (1, 1, 4, 100, 300, 128, False, None),
+    (1, 1, 4, 100, 300, 128, True, None),  # causal with S > T: keys past T - 1 see no query
+    (1, 2, 4, 130, 200, 64, True, None),
     (1, 2, 4, 160, 160, 128, True, (5, 40)),
     (2, 1, 4, 384, 384, 128, True, (16, 200)),
     (1, 1, 3, 130, 130, 128, True, None),

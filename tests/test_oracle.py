@@ -328,3 +328,84 @@ def test_bwd_directional_derivative_in_v_is_exact():
             continue
         f1 = (oracle.fwd(q, k, v2, causal=True)[0] * f64(do).numpy()).sum()
         assert abs((f1 - f0) / 2.0 ** -3 - g["dv"][0, 0, s, h]) < 1e-10
+
+
+# ---- local window (a band of diagonals: t - wl <= s <= t + wr, -1 unbounded)
+
+def band_mask(B, T, S, wl, wr, causal):
+    """The band through torch's own tril / triu (diagonal offsets), and causal."""
+    m = torch.ones(T, S, dtype=torch.bool)
+    if wr >= 0:
+        m = m.tril(diagonal=wr)
+    if wl >= 0:
+        m = m.triu(diagonal=-wl)
+    if causal:
+        m = m.tril(diagonal=0)
+    return m[None].expand(B, T, S).contiguous()
+
+
+@pytest.mark.parametrize("case", [
+    # B, K, G, T, S, H, causal, wl, wr
+    (1, 1, 2, 24, 24, 8, True, 3, -1),
+    (2, 2, 2, 20, 31, 16, False, 5, 2),
+    (1, 2, 3, 17, 17, 8, False, -1, 4),
+    (1, 1, 4, 30, 22, 16, False, 2, -1),
+    (2, 1, 2, 16, 16, 32, True, 0, 0),
+])
+def test_window_matches_torch_sdpa_band(case):
+    B, K, G, T, S, H, causal, wl, wr = case
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=71 + T + S)
+    o, lse = oracle.fwd(q, k, v, causal=causal, window=(wl, wr))
+    mask = band_mask(B, T, S, wl, wr, causal)
+    # rows with no visible key follow the library-free convention (O = 0,
+    # lse = -inf); SDPA gives NaN there, so compare the others
+    vis = mask.any(dim=-1).numpy()  # [B, T]
+    ro, rl = sdpa_reference(q, k, v, mask)
+    sel = np.broadcast_to(vis[:, None, None, :], lse.shape)
+    np.testing.assert_allclose(o[sel], ro[sel], atol=1e-12)
+    np.testing.assert_allclose(lse[sel], rl[sel], atol=1e-12)
+    assert np.all(o[~sel] == 0) and np.all(np.isneginf(lse[~sel]))
+
+
+def test_window_zero_width_is_the_diagonal():
+    """wl = wr = 0: each query sees only key s = t, so O[t] = v[t] exactly and
+    lse[t] = q[t].k[t] (a closed form, with no softmax left)."""
+    B, K, G, T, H = 1, 2, 3, 12, 16
+    q, k, v = make_qkv(B, K, G, T, T, H, seed=73)
+    o, lse = oracle.fwd(q, k, v, causal=False, window=(0, 0))
+    qf, kf, vf = f64(q).numpy(), f64(k).numpy(), f64(v).numpy()
+    assert np.array_equal(o, np.broadcast_to(vf[:, :, None], o.shape))
+    np.testing.assert_allclose(lse, np.einsum("bkgth,bkth->bkgt", qf, kf), rtol=0, atol=1e-12)
+
+
+def test_window_loose_equals_no_window():
+    B, K, G, T, S, H = 1, 2, 2, 15, 19, 8
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=79)
+    for causal in (False, True):
+        o0, l0 = oracle.fwd(q, k, v, causal=causal)
+        o1, l1 = oracle.fwd(q, k, v, causal=causal, window=(T + S, T + S))
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+@pytest.mark.parametrize("case", [
+    (1, 1, 2, 16, 16, 8, True, 4, -1),
+    (2, 2, 2, 14, 21, 16, False, 3, 2),
+])
+def test_bwd_window_matches_torch_autograd(case):
+    B, K, G, T, S, H, causal, wl, wr = case
+    q, k, v, do = make_qkv(B, K, G, T, S, H, seed=83 + T, with_do=True)
+    g = oracle.bwd(q, k, v, do, causal=causal, window=(wl, wr))
+    dq, dk, dv = autograd_reference(q, k, v, do, band_mask(B, T, S, wl, wr, causal))
+    np.testing.assert_allclose(g["dq"], dq, atol=1e-11)
+    np.testing.assert_allclose(g["dk"], dk, atol=1e-11)
+    np.testing.assert_allclose(g["dv"], dv, atol=1e-11)
+
+
+def test_bwd_window_zero_width_closed_form():
+    """wl = wr = 0: P is the identity on the diagonal, so dS = P (dP - D) = 0,
+    dQ = dK = 0, and dV[s] is the sum over heads g of dO[g, t = s]."""
+    B, K, G, T, H = 1, 2, 3, 10, 8
+    q, k, v, do = make_qkv(B, K, G, T, T, H, seed=89, with_do=True)
+    g = oracle.bwd(q, k, v, do, causal=True, window=(0, 0))
+    assert np.all(g["dq"] == 0) and np.all(g["dk"] == 0)
+    np.testing.assert_allclose(g["dv"], f64(do).numpy().sum(axis=2), rtol=0, atol=1e-12)
