@@ -16,6 +16,9 @@ bounded random sample of the same workload's query rows on the host cores.
 A second leg times the backward (dQ, dK, dV from the saved lse) on the same
 tensors and reports it under "backward".
 
+--workload window times the headline shape with a causal sliding window of
+1024 keys (attn_fwd_local, attn_bwd_local), FLOPs counted on visible pairs.
+
 --workload decode instead times the decoding shape B=16, K=8, G=4, T=1,
 S=32768, H=128 (non-causal: the query sees the whole context) through the
 split-KV forward (attn_fwd_ws), and prints one JSON line whose value is the
@@ -203,6 +206,110 @@ def decode_bench(args):
     print(json.dumps(result), flush=True)
 
 
+def window_bench(args):
+    """The headline shape with a causal sliding window (attn_fwd_local /
+    attn_bwd_local): MFMA-bound, FLOPs counted on the visible pairs."""
+    import torch
+    import grouped_query_attention_flash_amd as gqa
+    from workloads import WINDOW, WINDOW_LEFT, make_qkv, window_pairs
+
+    w = WINDOW
+    win = (WINDOW_LEFT, -1)
+    q, k, v, do = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=True)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o = torch.empty_like(qd)
+    lse = torch.empty(w.B, w.K, w.G, w.T, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        gqa.attn_fwd(qd, kd, vd, causal=True, out=o, lse=lse, window=win)
+
+    ms = time_launches(step, args.steps, args.warmup, args.settle_seconds)
+    pairs = window_pairs(w.T, w.S, WINDOW_LEFT) * w.B * w.K * w.G
+    flops = 4.0 * w.H * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "sliding-window attention TFLOP/s (fwd, causal, window 1024) at 1 GPU; % of bf16 MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, q pre-scaled by H^-1/2)",
+        "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
+                   "causal": True, "window_left": WINDOW_LEFT, "window_right": -1},
+        "roofline": {
+            "kernel": "attn_fwd_kernel<128,64,8,2,true,false> (general, windowed)",
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MI355X_BF16_DENSE_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "visible_pairs": pairs,
+        },
+    }
+    if not args.no_backward:
+        ws = torch.empty(gqa.attn_bwd_workspace_bytes(w.B, w.K, w.G, w.T, w.S, w.H), dtype=torch.uint8, device=dev)
+        dq = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(kd.shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(vd.shape, dtype=torch.float32, device=dev)
+        step()
+
+        def bstep():
+            gqa.attn_bwd(qd, kd, vd, o, lse, dod, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws, window=win)
+
+        bms = time_launches(bstep, max(5, args.steps // 2), max(2, args.warmup // 2), args.settle_seconds)
+        result["backward"] = {"ms": bms, "tflops": 2.5 * flops / (bms * 1e-3) / 1e12,
+                              "flops_convention": "2.5x forward (5 matmuls per visible pair)"}
+    if not args.no_cpu_baseline:
+        step()
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = window_cpu_baseline(q, k, v, w, win, o, pairs)
+    print(json.dumps(result), flush=True)
+
+
+def window_cpu_baseline(q, k, v, w, win, o_gpu, pairs, target_s=12.0):
+    """The fp64 oracle with the same window on random query rows (host cores)."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.max_threads()
+    rng = np.random.default_rng(12345)
+    total_rows = w.B * w.K * w.G * w.T
+    n = min(2048, total_rows)
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, causal=True, rows=rows, window=win)
+    per_row = (time.perf_counter() - t0) / n
+    n = int(min(total_rows, max(n, target_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t0 = time.perf_counter()
+    ref_o, _ = oracle.fwd(q, k, v, causal=True, rows=rows, window=win)
+    elapsed = time.perf_counter() - t0
+    t = rows % w.T
+    visible = np.minimum(t, w.S - 1) - np.maximum(0, t - win[0]) + 1
+    flops = float(4.0 * w.H * visible.sum())
+    got = o_gpu.reshape(-1, w.H)[rows].float().cpu().numpy()
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d random query rows (%.3g of the visible pairs), fp64 oracle, %.1f s" % (
+            n, visible.sum() / pairs, elapsed),
+        "sample_max_abs_vs_gpu": float(np.abs(got - ref_o).max()),
+        "sample_rel_l2_vs_gpu": float(np.linalg.norm(got - ref_o) / np.linalg.norm(ref_o)),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,8 +319,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed launches before the warm-up steps, for the clock to settle")
-    ap.add_argument("--workload", choices=["headline", "decode"], default="headline",
-                    help="headline: the causal T=S=8192 forward (default); decode: T=1 against S=32768")
+    ap.add_argument("--workload", choices=["headline", "decode", "window"], default="headline",
+                    help="headline: the causal T=S=8192 forward (default); decode: T=1 against S=32768; "
+                         "window: the headline shape with a causal 1024-key sliding window")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a known-size "
                          "reference dispatch for the HBM byte counters)")
@@ -232,6 +340,9 @@ def main():
         sys.exit(1)
     if args.workload == "decode":
         decode_bench(args)
+        return
+    if args.workload == "window":
+        window_bench(args)
         return
     w = HEADLINE
     q, k, v, do = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=True)

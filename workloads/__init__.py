@@ -70,6 +70,18 @@ HEADLINE = dataclasses.replace(
 DECODE = Workload("decode_b16_k8_g4_t1_s32768_h128", 16, 8, 4, 1, 32768, 128, False, False, False, 6)
 
 
+# Sliding window: the headline shape with a causal band of 1024 keys (each
+# query sees itself and the 1023 keys before it). bench.py --workload window.
+WINDOW = Workload("window1024_causal_b1_k8_g4_t8192_h128", 1, 8, 4, 8192, 8192, 128, True, False, True, 7)
+WINDOW_LEFT = 1023
+
+
+def window_pairs(T: int, S: int, wl: int, causal: bool = True) -> int:
+    """Visible (t, s) pairs per head of a causal band t - wl <= s <= t."""
+    assert causal
+    return sum(min(t, S - 1) - max(0, t - wl) + 1 for t in range(T) if t - wl <= S - 1)
+
+
 def make_qkv(B: int, K: int, G: int, T: int, S: int, H: int, seed: int,
              with_do: bool = False, q_scale: Optional[float] = None):
     """Draw q, k, v (and dO) as bf16 CPU tensors, contiguous, H innermost."""
