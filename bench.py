@@ -245,7 +245,7 @@ def window_bench(args):
         "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
                    "causal": True, "window_left": WINDOW_LEFT, "window_right": -1},
         "roofline": {
-            "kernel": "attn_fwd_kernel<128,64,8,2,true,false> (general, windowed)",
+            "kernel": "attn_fwd_pp_kernel<128,64,true,true> (ping-pong, windowed)",
             "bound": "mfma",
             "achieved": tflops,
             "peak": MI355X_BF16_DENSE_TFLOPS,
@@ -303,8 +303,8 @@ def window_cpu_baseline(q, k, v, w, win, o_gpu, pairs, target_s=12.0):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "%d random query rows (%.3g of the visible pairs), fp64 oracle, %.1f s" % (
-            n, visible.sum() / pairs, elapsed),
+        "sample": "%d of the %d query rows, drawn at random (%.3g of the visible pairs), fp64 oracle, %.1f s" % (
+            n, total_rows, visible.sum() / pairs, elapsed),
         "sample_max_abs_vs_gpu": float(np.abs(got - ref_o).max()),
         "sample_rel_l2_vs_gpu": float(np.linalg.norm(got - ref_o) / np.linalg.norm(ref_o)),
     }

@@ -685,7 +685,7 @@ __device__ __forceinline__ void m_phase_schedule(std::integer_sequence<int, P...
 // V(i+1) into slot (i+1) % 3, whose previous contents (read by M(i-2)) are
 // dead by then. Every wave waits for its own loads at the end of each of its
 // M phases, one barrier before any wave reads them.
-template <int H, int BKV, bool CAUSAL>
+template <int H, int BKV, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     constexpr int NG = 4;  // waves per group (8 per workgroup)
     constexpr int CPR = H / 8;
@@ -729,7 +729,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
 
     const buffer_rsrc krs = make_rsrc(a.k + bk * (size_t)S * H, S * H * 2);
     const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
-    const int n_t = CAUSAL ? qb + 1 : S / BKV;
+    // key tiles j0 .. j0 + n_t - 1; a left window (causal only, WIN) starts the
+    // block's range at the first tile its first query can see
+    const int WL = win_left(a.wl);
+    const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
+    const int n_t = (CAUSAL ? qb + 1 : S / BKV) - j0;
 
     // ---- global -> LDS loads: group A loads K tiles, group B V tiles; wave gwv
     // of a group issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat
@@ -747,7 +751,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     // the tile offset may go in the scalar offset, which the range check does
     // not cover.
     auto issue_tile = [&](int j, int slot) {
-        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+        const int tile = __builtin_amdgcn_readfirstlane((j0 + j) * BKV * H * 2);
         if (grp == 0) {
 #pragma unroll
             for (int i = 0; i < KL; i++)
@@ -803,12 +807,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
 
     // ---- V phase pieces (as in the kernel above)
     auto mask_tile = [&](int s0) {
-        const int lim = min(CAUSAL ? t : INT_MAX, S - 1) - s0 - 4 * c;
+        const int lim = min(CAUSAL ? t : INT_MAX, S - 1) - s0 - 4 * c;  // last visible key offset
+        const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;          // first visible key offset
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-            for (int r = 0; r < 16; r++)
-                if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) sacc[mb][r] = -INFINITY;
+            for (int r = 0; r < 16; r++) {
+                const int off = 32 * mb + 8 * (r >> 2) + (r & 3);
+                if (off > lim || off < first) sacc[mb][r] = -INFINITY;
+            }
     };
     auto tile_max = [&]() {
         float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -882,22 +889,44 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     if (grp == 1) barrier_no_drain();  // group B runs one phase behind
     m_phase(yes{}, no{}, 2, 0);      // M(-1): S^T of tile 0
     int slot = 0;                    // slot of tile set i: K(i+1), V(i)
-    for (int i = 0; i < n_t - 1; i++) {
+    // one round: V(i) then M(i); MASKED: tile i needs the element mask
+    auto round = [&](int i, auto masked) {
         const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
         barrier_no_drain();
         // V(i)
         if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
-        v_phase_open();
+        if constexpr (decltype(masked)::value)
+            v_phase_masked((j0 + i) * BKV);
+        else
+            v_phase_open();
         barrier_no_drain();
         // M(i)
         m_phase(yes{}, yes{}, slot, slot);
         slot = nslot;
+    };
+    if constexpr (WIN) {
+        // The window's left edge, t - WL over the block's BKV queries, spans at
+        // most two tiles: those before the first tile every query sees whole
+        // take the element mask.
+        int i = 0;
+        for (; i < 2 && i < n_t - 1 && (j0 + i) * BKV < t0 + BKV - 1 - WL; i++) round(i, yes{});
+        for (; i < n_t - 1; i++) round(i, no{});
+    } else {
+        for (int i = 0; i < n_t - 1; i++) {
+            const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
+            barrier_no_drain();
+            if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
+            v_phase_open();
+            barrier_no_drain();
+            m_phase(yes{}, yes{}, slot, slot);
+            slot = nslot;
+        }
     }
     // the last tile (the diagonal one when causal): nothing left to load or to
     // multiply with K
     barrier_no_drain();
     if (CAUSAL)
-        v_phase_masked((n_t - 1) * BKV);
+        v_phase_masked((j0 + n_t - 1) * BKV);
     else
         v_phase_open();
     barrier_no_drain();
@@ -967,9 +996,17 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     if constexpr (GQA_FWD_PINGPONG && H <= 128 && NW == 8) {
         if (dense) {
             if (a.causal)
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
             else
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+            return hipGetLastError();
+        }
+        // a causal left window on an otherwise dense shape: the ping-pong kernel
+        // starting at each block's first visible tile
+        const bool dense_win = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
+                               a.causal && a.wl >= 0 && a.T == a.S && a.bq == BKV;
+        if (dense_win) {
+            hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
             return hipGetLastError();
         }
     }

@@ -26,6 +26,12 @@ CASES = [
     (1, 2, 4, 192, 192, 128, True, 31, -1, True),
     (2, 1, 4, 96, 333, 128, False, -1, 70, False),
     (1, 1, 4, 100, 300, 128, True, 37, -1, False),
+    # causal left windows on whole 64-key tiles, T == S: the ping-pong kernel
+    # from each block's first visible tile (cut first tile, single-tile blocks)
+    (1, 2, 4, 512, 512, 128, True, 127, -1, False),
+    (1, 1, 4, 448, 448, 128, True, 100, -1, False),
+    (1, 1, 4, 256, 256, 128, True, 20, -1, False),
+    (1, 2, 4, 384, 384, 64, True, 191, 5, False),
 ]
 
 
