@@ -378,7 +378,7 @@ def main():
                    "causal": w.causal, "mask": "lazy causal"},
         "pct_of_peak": 100.0 * tflops / MI355X_BF16_DENSE_TFLOPS,
         "roofline": {
-            "kernel": "attn_fwd_pp_kernel<128,64,true> (ping-pong, dense causal)",
+            "kernel": "attn_fwd_pp_kernel<128,64,true,false> (ping-pong, dense causal)",
             "bound": "mfma",
             "achieved": tflops,
             "peak": MI355X_BF16_DENSE_TFLOPS,

@@ -33,6 +33,9 @@
 #define GQA_BWD_DKV2 1
 #endif
 // its operand reads are issued this many MFMAs ahead of their use
+#ifndef GQA_BWD_D_BKV
+#define GQA_BWD_D_BKV 64
+#endif
 #ifndef GQA_BWD_DKV_PREF
 #define GQA_BWD_DKV_PREF 6
 #endif
@@ -895,8 +898,11 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     const int n_gsplit = a.G / gw;
     const int n_qblocks = (a.T + bq - 1) / bq;
     const dim3 qgrid((unsigned)(a.B * a.K * n_gsplit * n_qblocks));
-    // D = rowsum(P * dP), then dQ, then dK / dV (both read D)
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<H, BKV_DQ, NW_DQ, true>), qgrid, dim3(NW_DQ * 64), 0, stream, a, gw, bq,
+    // D = rowsum(P * dP), then dQ, then dK / dV (both read D). The D pass has
+    // no dQ accumulators, so at H <= 128 it takes key tiles of 64 (half the
+    // per-tile barriers and loop overhead of the dQ pass's 32).
+    constexpr int BKV_D = H <= 128 && GQA_BWD_D_BKV > BKV_DQ ? GQA_BWD_D_BKV : BKV_DQ;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<H, BKV_D, NW_DQ, true>), qgrid, dim3(NW_DQ * 64), 0, stream, a, gw, bq,
                        n_gsplit, n_qblocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
