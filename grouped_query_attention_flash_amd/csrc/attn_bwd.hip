@@ -33,6 +33,9 @@
 #define GQA_BWD_DKV2 1
 #endif
 // its operand reads are issued this many MFMAs ahead of their use
+#ifndef GQA_BWD_DELTA_PP
+#define GQA_BWD_DELTA_PP 1
+#endif
 #ifndef GQA_BWD_D_BKV
 #define GQA_BWD_D_BKV 64
 #endif
@@ -889,6 +892,157 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
 }
 
 // ---------------------------------------------------------------------------
+// D pass for dense shapes (no segments, no window, whole tiles; causal needs
+// T = S and query blocks of BKV): the ping-pong scheme of the forward kernel.
+// D[t] = sum_s P[t,s] dP[t,s] with P = exp(S - lse) and dP = dO V^T in fp32.
+//
+// 8 waves, 32 query rows each (the unit's gw heads x BKV queries). Waves 0-3
+// (group A) and 4-7 (group B) alternate, B one phase behind A, with a
+// workgroup barrier between phases:
+//   M(i): S^T = K(i) Q^T and dP^T = V(i) dO^T (MFMA only)
+//   V(i): P and the running sum of P * dP for tile i (VALU only)
+// so each SIMD runs one wave's MFMAs beside the other wave's VALU work.
+// K and V tiles share one row layout (both are A operands read by rows) and
+// move through three LDS slots: tile i sits in slot i % 3. Group A loads the
+// K tiles and group B the V tiles, each two tiles ahead during its V phase,
+// into the slot that M(i-1) of both groups has finished reading; every wave
+// waits for its own loads at the end of its next M phase, a barrier before
+// any wave reads them.
+template <int H, int BKV, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
+                                                                   int n_qblocks) {
+    constexpr int NG = 4;  // waves per group
+    constexpr int KSTEPS = H / 16;
+    constexpr int MB = BKV / 32;
+    constexpr int NX = MB * KSTEPS;
+    constexpr int CPR = H / 8;
+    constexpr int RS = CPR + 1;  // row stride in 16-byte chunks (conflict-free row reads)
+    constexpr int BLOCKS = (BKV * RS + 63) / 64;
+    constexpr int ELEMS = BLOCKS * 512;
+    constexpr int NSLOT = 3;
+    __shared__ __attribute__((aligned(1024))) __bf16 sk[NSLOT][ELEMS];
+    __shared__ __attribute__((aligned(1024))) __bf16 sv[NSLOT][ELEMS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave / NG, gwv = wave % NG;
+    const int n = lane & 31, c = lane >> 5;
+
+    // work unit (causal: heaviest query block first) and this lane's row
+    const int units = a.B * a.K * n_gsplit;
+    int qb = blockIdx.x / units;
+    if (CAUSAL) qb = n_qblocks - 1 - qb;
+    const int u = blockIdx.x % units;
+    const int gs = u % n_gsplit;
+    const int kh = (u / n_gsplit) % a.K;
+    const int b = u / (n_gsplit * a.K);
+    const int t0 = qb * bq;
+    const int T = a.T, S = a.S;
+    const int rho = wave * 32 + n;  // gw * bq == 256: every row belongs to the unit
+    const int g = gs * gw + rho / bq;
+    const int t = t0 + rho % bq;    // t < T: T is a whole number of query blocks
+    const size_t bk = (size_t)b * a.K + kh;
+    const size_t row = (bk * a.G + g) * (size_t)T + t;
+
+    bf16x8 qf[KSTEPS], df[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++) {
+        qf[ks] = *(const bf16x8 *)(a.q + row * H + 16 * ks + 8 * c);
+        df[ks] = *(const bf16x8 *)(a.dout + row * H + 16 * ks + 8 * c);
+    }
+    const float l = a.lse[row];
+    const float lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+
+    const buffer_rsrc krs = make_rsrc(a.k + bk * (size_t)S * H, S * H * 2);
+    const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
+    const int n_t = CAUSAL ? qb + 1 : S / BKV;
+
+    // global -> LDS: group A loads K tiles, group B V tiles; wave gwv of a group
+    // issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat the row's
+    // last chunk)
+    constexpr int NL = (BLOCKS + NG - 1) / NG;
+    int ld_off[NL];
+#pragma unroll
+    for (int i = 0; i < NL; i++) {
+        const int pslot = (gwv + i * NG) * 64 + lane;
+        ld_off[i] = ((pslot / RS) * H + min(pslot % RS, CPR - 1) * 8) * 2;
+    }
+    // tiles j < n_t lie wholly inside K and V (S % BKV == 0), so the tile
+    // offset may go in the scalar offset
+    auto issue_tile = [&](int j, int slot) {
+        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+        __bf16 *dst = grp == 0 ? sk[slot] : sv[slot];
+        const buffer_rsrc &rs = grp == 0 ? krs : vrs;
+#pragma unroll
+        for (int i = 0; i < NL; i++)
+            if (gwv + i * NG < BLOCKS) lds_load16_to(rs, (char *)dst + (gwv + i * NG) * 1024, ld_off[i], tile);
+    };
+
+    f32x16 sacc[MB], pacc[MB];
+    float d_acc = 0.f;
+    const int a_lane = n * RS * 8 + c * 8;
+    auto m_phase = [&](int slot) {
+        const __bf16 *kt = sk[slot];
+        const __bf16 *vt = sv[slot];
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int x = 0; x < NX; x++) {
+            const int mb = x % MB, ks = x / MB;
+            const int off = a_lane + mb * 32 * RS * 8 + ks * 16;
+            const bf16x8 kf = *(const bf16x8 *)(kt + off);
+            const bf16x8 vf = *(const bf16x8 *)(vt + off);
+            sacc[mb] = mfma32x32x16(kf, qf[ks], ks == 0 ? f32x16{} : sacc[mb]);
+            pacc[mb] = mfma32x32x16(vf, df[ks], ks == 0 ? f32x16{} : pacc[mb]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        wait_lds_loads();
+    };
+    // V phase: lane (n, c) holds keys s0 + 32 mb + acc_row(r, c) of query t
+    auto v_phase = [&](int s0, auto masked) {
+        const int lim = t - s0 - 4 * c;  // last visible key offset (causal)
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                float p = exp2_fast(__builtin_fmaf(sacc[mb][r], kLog2e, -lse2));
+                if constexpr (decltype(masked)::value)
+                    if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+                d_acc = __builtin_fmaf(p, pacc[mb][r], d_acc);
+            }
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    // prologue: tiles 0 and 1 -> slots 0 and 1
+    issue_tile(0, 0);
+    if (n_t > 1) issue_tile(1, 1);
+    wait_lds_loads();
+    barrier_no_drain();
+    if (grp == 1) barrier_no_drain();  // group B runs one phase behind
+    m_phase(0);
+    int slot = 0;  // slot of tile i
+    for (int i = 0; i < n_t - 1; i++) {
+        const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
+        const int lslot = nslot == NSLOT - 1 ? 0 : nslot + 1;
+        barrier_no_drain();
+        if (i + 2 < n_t) issue_tile(i + 2, lslot);
+        v_phase(i * BKV, no{});
+        barrier_no_drain();
+        m_phase(nslot);
+        slot = nslot;
+    }
+    barrier_no_drain();
+    if (CAUSAL)
+        v_phase((n_t - 1) * BKV, yes{});
+    else
+        v_phase((n_t - 1) * BKV, no{});
+    if (grp == 0) barrier_no_drain();  // group A's trailing phase
+
+    d_acc += __shfl_xor(d_acc, 32);
+    if (c == 0) a.delta[row] = d_acc;
+}
+
+// ---------------------------------------------------------------------------
 template <int H, int NW_DKV, int BKV_DQ, int NW_DQ>
 static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     int gw = 1;
@@ -902,8 +1056,25 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     // no dQ accumulators, so at H <= 128 it takes key tiles of 64 (half the
     // per-tile barriers and loop overhead of the dQ pass's 32).
     constexpr int BKV_D = H <= 128 && GQA_BWD_D_BKV > BKV_DQ ? GQA_BWD_D_BKV : BKV_DQ;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<H, BKV_D, NW_DQ, true>), qgrid, dim3(NW_DQ * 64), 0, stream, a, gw, bq,
-                       n_gsplit, n_qblocks);
+    bool delta_done = false;
+    if constexpr (GQA_BWD_DELTA_PP && H <= 128 && NW_DQ == 8) {
+        // dense shapes: the ping-pong D pass (query blocks of 64 rows x gw heads)
+        constexpr int BKV_PP = 64;
+        const bool dense = a.q_seg == nullptr && !windowed(a.wl, a.wr, a.causal) && gw * bq == 256 &&
+                           a.T % bq == 0 && a.S % BKV_PP == 0 && (!a.causal || (a.T == a.S && bq == BKV_PP));
+        if (dense) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, true>), qgrid, dim3(512), 0, stream, a, gw,
+                                   bq, n_gsplit, n_qblocks);
+            else
+                hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, false>), qgrid, dim3(512), 0, stream, a, gw,
+                                   bq, n_gsplit, n_qblocks);
+            delta_done = true;
+        }
+    }
+    if (!delta_done)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<H, BKV_D, NW_DQ, true>), qgrid, dim3(NW_DQ * 64), 0, stream, a, gw, bq,
+                           n_gsplit, n_qblocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq_kernel<H, BKV_DQ, NW_DQ, false>), qgrid, dim3(NW_DQ * 64), 0, stream, a, gw, bq,

@@ -50,7 +50,7 @@ struct BwdArgs {
     const __bf16 *q, *k, *v, *o, *dout;
     const float *lse;
     float *dq, *dk, *dv;
-    float *delta;                    // workspace: D = rowsum(dO * O), [B,K,G,T]
+    float *delta;                    // workspace: D = rowsum(P * dP) in fp32, [B,K,G,T]
     const int32_t *q_seg, *kv_seg;
     int B, K, G, T, S;
     int causal;

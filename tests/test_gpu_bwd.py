@@ -39,6 +39,11 @@ SMALL = [
     (1, 2, 4, 192, 192, 64, True, None),
     (1, 1, 4, 128, 128, 256, True, None),
     (1, 1, 4, 90, 130, 256, False, (3, 50)),
+    # dense shapes of the ping-pong D pass: non-causal with T != S, and
+    # eight heads per unit (32-query blocks)
+    (1, 1, 4, 128, 320, 128, False, None),
+    (1, 1, 8, 96, 128, 128, False, None),
+    (1, 1, 4, 64, 192, 64, False, None),
 ]
 
 
