@@ -213,8 +213,39 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         j_end = min(j_end, split * a.split_tiles + a.split_tiles);
     }
 
+    // ---- kv ids of the block's key range staged in LDS (8-wave copies, up to
+    // KV_CAP keys), with each tile's id range: inside the key loop a global
+    // load of ids would be counted behind the tile loads just issued, and
+    // waiting for it would wait for them too.
+    constexpr int KV_CAP = NW == 8 ? 4096 : 1;
+    constexpr int KV_TILES = KV_CAP / BKV > 0 ? KV_CAP / BKV : 1;
+    __shared__ int s_kvid[KV_CAP];
+    __shared__ int s_tmin[KV_TILES], s_tmax[KV_TILES];
+    const int kv_base = j_begin * BKV;
+    const bool kv_lds = segs && NW == 8 && j_end > j_begin && (j_end - j_begin) * BKV <= KV_CAP;
+    if (kv_lds) {
+        for (int jj = j_begin + wave; jj < j_end; jj += NW) {
+            const int s = jj * BKV + lane;
+            const bool ok = lane < BKV && s < S;
+            const int id = ok ? kvs[s] : 0;
+            if (ok) s_kvid[s - kv_base] = id;
+            const int lo = wave_min_i(ok ? id : INT_MAX);
+            const int hi = wave_max_i(ok ? id : INT_MIN);
+            if (lane == 0) {
+                s_tmin[jj - j_begin] = lo;
+                s_tmax[jj - j_begin] = hi;
+            }
+        }
+        __syncthreads();
+    }
+
     // kv-id range of tile j (wave-uniform; every wave computes the same value)
     auto tile_ids = [&](int j, int &kmin, int &kmax) {
+        if (kv_lds) {
+            kmin = __builtin_amdgcn_readfirstlane(s_tmin[j - j_begin]);
+            kmax = __builtin_amdgcn_readfirstlane(s_tmax[j - j_begin]);
+            return;
+        }
         const int s = j * BKV + lane;
         int id = 0;
         const bool ok = lane < BKV && s < S;
@@ -339,7 +370,7 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
             for (int r = 0; r < 16; r++) {
                 const int off = 32 * mb + 8 * (r >> 2) + (r & 3);
                 bool vis = off <= lim && off >= first;
-                if (segs && vis) vis = kvs[s0 + off + 4 * c] == my_qid;
+                if (segs && vis) vis = (kv_lds ? s_kvid[s0 + off + 4 * c - kv_base] : kvs[s0 + off + 4 * c]) == my_qid;
                 if (!vis) sacc[mb][r] = -INFINITY;
             }
         }

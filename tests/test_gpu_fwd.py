@@ -45,6 +45,10 @@ SMALL = [
     (1, 1, 1, 300, 128, 64, False, None),
     (1, 1, 8, 77, 256, 128, False, None),
     (2, 1, 4, 384, 384, 64, True, None),
+    # segment ids over more than 4096 keys per query block (the kernel reads
+    # them from memory instead of its LDS copy) and just under that bound
+    (1, 1, 4, 64, 4200, 128, False, (200, 900)),
+    (1, 1, 4, 4160, 4160, 128, True, (300, 1200)),
 ]
 
 
