@@ -700,8 +700,9 @@ __device__ __forceinline__ void m_phase_schedule(std::integer_sequence<int, P...
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong forward for dense shapes at H <= 128 (the conditions of DENSE
-// above, 8 waves, one workgroup per CU).
+// Ping-pong forward for dense shapes (the conditions of DENSE above, 8 waves,
+// one workgroup per CU): H <= 128 with 64-key tiles, and H = 256 with 32-key
+// tiles when G is a multiple of 8 (8 heads by 32 queries per workgroup).
 //
 // The two waves of each SIMD take turns: waves 0-3 (group A) and waves 4-7
 // (group B) run the same sequence of phases, B one phase behind A, with a
@@ -776,7 +777,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NL; i++) {
         const int pslot = (gwv + i * NG) * 64 + lane;
-        ld_off[i] = ((pslot / rs) * H + min(pslot % rs, CPR - 1) * 8) * 2;
+        // slots past the tile's last padded row (the last K block at H = 256)
+        // re-read row BKV - 1 into the slot's tail
+        ld_off[i] = (min(pslot / rs, BKV - 1) * H + min(pslot % rs, CPR - 1) * 8) * 2;
     }
     // Tiles j < n_t lie wholly inside K and V (S % BKV == 0, rows < BKV), so
     // the tile offset may go in the scalar offset, which the range check does
@@ -969,40 +972,16 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     // fully coalesced 1 KiB stores; lse = ln(sum exp(logits)).
     l_run += __shfl_xor(l_run, 32);
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-#if GQA_PP_OSTAGE
-    // Staging region of this wave: 32 rows of 272 bytes (padded: conflict-free
-    // 8-byte writes), two waves per K slot and the last two in a V slot. Every
-    // K slot and V slot n_t % 3 are dead here: the only phase still running is
-    // group B's last PV, which reads V slot (n_t - 1) % 3, and all loads have
-    // landed (each M phase ends with a wait).
+    // Staging region of this wave: 32 rows of H * 2 + 16 bytes (padded:
+    // conflict-free 8-byte writes), two waves per K slot and the last two in a
+    // V slot. Every K slot and V slot n_t % 3 are dead here: the only phase
+    // still running is group B's last PV, which reads V slot (n_t - 1) % 3,
+    // and all loads have landed (each M phase ends with a wait). At H = 256
+    // the rows do not fit and O leaves straight from registers.
     constexpr int OROW = H * 2 + 16;
-    static_assert(2 * 32 * OROW <= L::K_ELEMS * 2 && 2 * 32 * OROW <= L::V_ELEMS * 2, "staging fits a slot");
-    char *stage = (wave < 6 ? (char *)sk[wave >> 1] : (char *)sv[n_t % NSLOT]) + (wave & 1) * 32 * OROW;
-#pragma unroll
-    for (int hb = 0; hb < HB; hb++)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-            bf16x4 val;
-#pragma unroll
-            for (int e = 0; e < 4; e++) val[e] = (__bf16)(oacc[hb][4 * q4 + e] * inv);
-            *(bf16x4 *)(stage + n * OROW + (32 * hb + 8 * q4 + 4 * c) * 2) = val;
-        }
-    // rows of this wave: queries t_w .. t_w + 31 of head g (all lanes agree)
-    const int t_w = t - n;
-    __bf16 *orows = a.o + ((bk * a.G + g) * (size_t)T + t_w) * H;
-    constexpr int CPR16 = H / 8;  // 16-byte chunks per row
-#pragma unroll
-    for (int j = 0; j < 32 * CPR16 / 64; j++) {
-        const int idx = j * 64 + lane;
-        const int r = idx / CPR16, ch = idx % CPR16;
-        const bf16x8 val = *(const bf16x8 *)(stage + r * OROW + ch * 16);
-        if (t_w + r < T) *(bf16x8 *)(orows + (size_t)r * H + ch * 8) = val;
-    }
-    if (q_valid && c == 0 && a.lse)
-        a.lse[(bk * a.G + g) * (size_t)T + t] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-#else
-    if (q_valid) {
-        __bf16 *orow = a.o + qrow_off;
+    constexpr bool kStage = GQA_PP_OSTAGE && 2 * 32 * OROW <= L::K_ELEMS * 2 && 2 * 32 * OROW <= L::V_ELEMS * 2;
+    if constexpr (kStage) {
+        char *stage = (wave < 6 ? (char *)sk[wave >> 1] : (char *)sv[n_t % NSLOT]) + (wave & 1) * 32 * OROW;
 #pragma unroll
         for (int hb = 0; hb < HB; hb++)
 #pragma unroll
@@ -1010,12 +989,37 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
                 bf16x4 val;
 #pragma unroll
                 for (int e = 0; e < 4; e++) val[e] = (__bf16)(oacc[hb][4 * q4 + e] * inv);
-                *(bf16x4 *)(orow + 32 * hb + 8 * q4 + 4 * c) = val;
+                *(bf16x4 *)(stage + n * OROW + (32 * hb + 8 * q4 + 4 * c) * 2) = val;
             }
-        if (c == 0 && a.lse)
+        // rows of this wave: queries t_w .. t_w + 31 of head g (all lanes agree)
+        const int t_w = t - n;
+        __bf16 *orows = a.o + ((bk * a.G + g) * (size_t)T + t_w) * H;
+        constexpr int CPR16 = H / 8;  // 16-byte chunks per row
+#pragma unroll
+        for (int j = 0; j < 32 * CPR16 / 64; j++) {
+            const int idx = j * 64 + lane;
+            const int r = idx / CPR16, ch = idx % CPR16;
+            const bf16x8 val = *(const bf16x8 *)(stage + r * OROW + ch * 16);
+            if (t_w + r < T) *(bf16x8 *)(orows + (size_t)r * H + ch * 8) = val;
+        }
+        if (q_valid && c == 0 && a.lse)
             a.lse[(bk * a.G + g) * (size_t)T + t] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    } else {
+        if (q_valid) {
+            __bf16 *orow = a.o + qrow_off;
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++) {
+                    bf16x4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) val[e] = (__bf16)(oacc[hb][4 * q4 + e] * inv);
+                    *(bf16x4 *)(orow + 32 * hb + 8 * q4 + 4 * c) = val;
+                }
+            if (c == 0 && a.lse)
+                a.lse[(bk * a.G + g) * (size_t)T + t] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+        }
     }
-#endif
 }
 
 template <int H, int BKV, int NW, int WPS>
@@ -1165,6 +1169,33 @@ SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H) {
     return p;
 }
 
+// H = 256 on the ping-pong kernel: 8 waves of 32 query rows (gw = 8 heads by
+// bq = 32 queries) over 32-key tiles, for dense shapes: no segment ids, no
+// window, whole key tiles, and T == S when causal (the diagonal tile is then
+// each block's last).
+bool fwd_pp256_applies(int G, int T, int S, int causal, bool segments, int wl, int wr) {
+    return GQA_FWD_PINGPONG && G % 8 == 0 && !segments && S % 32 == 0 && !windowed(wl, wr, causal != 0) &&
+           (!causal || T == S);
+}
+
+FwdConfig fwd_config_pp256() {
+    FwdConfig cfg;
+    cfg.nw = 8;
+    cfg.gw = 8;
+    cfg.bq = 32;
+    cfg.bkv = 32;
+    return cfg;
+}
+
+static hipError_t launch_fwd_pp256(const FwdArgs &a, hipStream_t stream) {
+    const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks);
+    if (a.causal)
+        hipLaunchKernelGGL((attn_fwd_pp_kernel<256, 32, true, false>), dim3(grid), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_fwd_pp_kernel<256, 32, false, false>), dim3(grid), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
     if (a.o_part) {
         switch (H) {
@@ -1177,7 +1208,10 @@ hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
     switch (H) {
         case 64: return launch_fwd_t<64, 64, 8, 2>(a, stream);
         case 128: return launch_fwd_t<128, GQA_FWD_BKV128, GQA_FWD_NW128, 2>(a, stream);
-        case 256: return launch_fwd_t<256, 32, 4, 1>(a, stream);
+        case 256:
+            // a configuration from fwd_config_pp256 (all 8 waves hold rows)
+            if (a.gw * a.bq == 256) return launch_fwd_pp256(a, stream);
+            return launch_fwd_t<256, 32, 4, 1>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

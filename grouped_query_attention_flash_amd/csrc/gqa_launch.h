@@ -44,6 +44,9 @@ struct FwdConfig {
 // split-KV path uses (4 waves per workgroup).
 FwdConfig fwd_config(int G, int T, int H);
 FwdConfig fwd_config_split(int G, int T, int H);
+// H = 256 dense shapes that run the ping-pong kernel, and its configuration.
+bool fwd_pp256_applies(int G, int T, int S, int causal, bool segments, int wl, int wr);
+FwdConfig fwd_config_pp256();
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream);
 
 struct BwdArgs {

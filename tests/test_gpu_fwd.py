@@ -45,6 +45,12 @@ SMALL = [
     (1, 1, 1, 300, 128, 64, False, None),
     (1, 1, 8, 77, 256, 128, False, None),
     (2, 1, 4, 384, 384, 64, True, None),
+    # H = 256 with G a multiple of 8 (the ping-pong path at H = 256, 32-key
+    # tiles): one- and three-tile causal blocks, G = 16, ragged T
+    (2, 1, 8, 32, 32, 256, True, None),
+    (1, 1, 8, 96, 96, 256, True, None),
+    (1, 1, 16, 64, 64, 256, False, None),
+    (1, 1, 8, 50, 96, 256, False, None),
     # segment ids over more than 4096 keys per query block (the kernel reads
     # them from memory instead of its LDS copy) and just under that bound
     (1, 1, 4, 64, 4200, 128, False, (200, 900)),
