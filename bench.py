@@ -19,6 +19,14 @@ tensors and reports it under "backward".
 --workload window times the headline shape with a causal sliding window of
 1024 keys (attn_fwd_local, attn_bwd_local), FLOPs counted on visible pairs.
 
+--workload long times the 32k-token shape B=1, K=2, G=8, T=S=32768, H=256
+(causal) in the same format, without the backward leg.
+
+--write-traffic FETCH_CSV WRITE_CSV turns two rocprofv3 --pmc runs (FETCH_SIZE,
+then WRITE_SIZE, each with --copy-calibration-mib) into the HBM bytes per
+launch of the headline forward kernel, scaled by what the same counters read
+for the calibration copy, and stores them with a digest of the kernel source.
+
 --workload decode instead times the decoding shape B=16, K=8, G=4, T=1,
 S=32768, H=128 (non-causal: the query sees the whole context) through the
 split-KV forward (attn_fwd_ws), and prints one JSON line whose value is the
@@ -64,6 +72,42 @@ def measured_traffic():
     if d.get("kernel_digest") != kernel_digest(FWD_SOURCES):
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+HEADLINE_KERNEL = "attn_fwd_pp_kernel<128, 64, true, false>"
+
+
+def write_traffic(fetch_csv, write_csv, calib_mib):
+    """HBM bytes per launch of the headline forward kernel from two rocprofv3
+    --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch). Each counter
+    is scaled by bytes / reading of the largest device copy in the same run
+    (the calibration copy of calib_mib MiB, which reads and writes that much)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    calib = calib_mib * 1024.0  # KiB moved each way by the copy
+    fetch_copy = max(v for k, vs in fetch.items() if "copyBuffer" in k for v in vs)
+    write_copy = max(v for k, vs in write.items() if "copyBuffer" in k for v in vs)
+    fetch_scale, write_scale = calib / fetch_copy, calib / write_copy
+    name = next(k for k in fetch if HEADLINE_KERNEL in k)
+    rd = sum(fetch[name]) / len(fetch[name]) * fetch_scale * 1024.0
+    wr = sum(write[name]) / len(write[name]) * write_scale * 1024.0
+    d = {"kernel": name, "kernel_digest": kernel_digest(FWD_SOURCES), "workload": "causal_b1_k8_g4_t8192_h128",
+         "fetch_scale": fetch_scale, "write_scale": write_scale, "read_bytes_per_launch": rd,
+         "write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    print(json.dumps(d))
 
 
 def settle_clock(fn, seconds=1.0):
@@ -319,13 +363,22 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed launches before the warm-up steps, for the clock to settle")
-    ap.add_argument("--workload", choices=["headline", "decode", "window"], default="headline",
+    ap.add_argument("--workload", choices=["headline", "decode", "window", "long"], default="headline",
                     help="headline: the causal T=S=8192 forward (default); decode: T=1 against S=32768; "
-                         "window: the headline shape with a causal 1024-key sliding window")
+                         "window: the headline shape with a causal 1024-key sliding window; "
+                         "long: the causal T=S=32768 H=256 forward")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the headline kernel's HBM bytes per launch from two rocprofv3 --pmc CSVs "
+                         "(needs --copy-calibration-mib, the size those runs copied) and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a known-size "
                          "reference dispatch for the HBM byte counters)")
     args = ap.parse_args()
+    if args.write_traffic:
+        if not args.copy_calibration_mib:
+            ap.error("--write-traffic needs --copy-calibration-mib")
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.copy_calibration_mib)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (--gpus %d refused)"
               % args.gpus, file=sys.stderr)
@@ -333,7 +386,7 @@ def main():
 
     import torch
     import grouped_query_attention_flash_amd as gqa
-    from workloads import HEADLINE, attention_flops, make_qkv
+    from workloads import HEADLINE, WORKLOADS, attention_flops, make_qkv
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -345,10 +398,17 @@ def main():
         window_bench(args)
         return
     w = HEADLINE
-    q, k, v, do = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=True)
+    kernel = "attn_fwd_pp_kernel<128,64,true,false> (ping-pong, dense causal)"
+    if args.workload == "long":
+        w = WORKLOADS["causal_b1_k2_g8_t32768_h256"]
+        kernel = "attn_fwd_pp_kernel<256,32,true,false> (ping-pong, dense causal)"
+        args.no_backward = True
+    t = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=not args.no_backward)
+    q, k, v = t[:3]
     inp_cpu = {"q": q, "k": k, "v": v}
     dev = torch.device("cuda", 0)
-    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    dod = None if args.no_backward else t[3].to(dev)
     o = torch.empty_like(qd)
     lse = torch.empty(w.B, w.K, w.G, w.T, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -378,13 +438,13 @@ def main():
                    "causal": w.causal, "mask": "lazy causal"},
         "pct_of_peak": 100.0 * tflops / MI355X_BF16_DENSE_TFLOPS,
         "roofline": {
-            "kernel": "attn_fwd_pp_kernel<128,64,true,false> (ping-pong, dense causal)",
+            "kernel": kernel,
             "bound": "mfma",
             "achieved": tflops,
             "peak": MI355X_BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s",
             "frac": tflops / MI355X_BF16_DENSE_TFLOPS,
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic() if w is HEADLINE else None,
             "algorithmic_flops_per_launch": flops,
             "algorithmic_hbm_bytes_per_launch": fwd_bytes,
         },
