@@ -717,7 +717,7 @@ __device__ __forceinline__ void m_phase_schedule(std::integer_sequence<int, P...
 // V(i+1) into slot (i+1) % 3, whose previous contents (read by M(i-2)) are
 // dead by then. Every wave waits for its own loads at the end of each of its
 // M phases, one barrier before any wave reads them.
-template <int H, int BKV, bool CAUSAL, bool WIN>
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG = false>
 __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     constexpr int NG = 4;  // waves per group (8 per workgroup)
     constexpr int CPR = H / 8;
@@ -761,11 +761,72 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
 
     const buffer_rsrc krs = make_rsrc(a.k + bk * (size_t)S * H, S * H * 2);
     const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
-    // key tiles j0 .. j0 + n_t - 1; a left window (causal only, WIN) starts the
-    // block's range at the first tile its first query can see
+
+    // ---- segment ids (SEG, S <= KV_CAP): the kv ids of the block's key tiles
+    // staged in LDS with each tile's id range, and the list of the tiles whose
+    // range meets the block's query-id range (in increasing order; the others
+    // hold no visible pair). The loop walks that list; it is the same for
+    // every wave, so both groups stay in step.
+    constexpr int KV_CAP = SEG ? 8192 : 1;
+    constexpr int NT_CAP = SEG ? KV_CAP / BKV : 1;
+    __shared__ __attribute__((aligned(16))) int s_kvid[KV_CAP];
+    __shared__ int s_tmin[NT_CAP], s_tmax[NT_CAP], s_jlist[NT_CAP];
+    __shared__ int s_nvis;
+    int my_qid = 0, w_qmin = 0, w_qmax = 0, n_vis = 0;
+    if constexpr (SEG) {
+        const int32_t *qs = a.q_seg + (size_t)b * T;
+        const int32_t *kvs = a.kv_seg + (size_t)b * S;
+        my_qid = q_valid ? qs[t] : 0;
+        w_qmin = wave_min_i(q_valid ? my_qid : INT_MAX);
+        w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
+        // the block's queries t0 .. t0 + bq - 1 (bq <= 64: one per lane)
+        const bool qok = lane < a.bq && t0 + lane < T;
+        const int qid = qok ? qs[t0 + lane] : 0;
+        const int wg_qmin = wave_min_i(qok ? qid : INT_MAX), wg_qmax = wave_max_i(qok ? qid : INT_MIN);
+        const int nt_all = CAUSAL ? qb + 1 : S / BKV;
+        for (int jj = wave; jj < nt_all; jj += 8) {
+            const bool ok = lane < BKV;  // whole tiles: jj * BKV + lane < S
+            const int id = ok ? kvs[jj * BKV + lane] : 0;
+            if (ok) s_kvid[jj * BKV + lane] = id;
+            const int lo = wave_min_i(ok ? id : INT_MAX), hi = wave_max_i(ok ? id : INT_MIN);
+            if (lane == 0) {
+                s_tmin[jj] = lo;
+                s_tmax[jj] = hi;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            int cnt = 0;
+            for (int jb = 0; jb < nt_all; jb += 64) {
+                const int j = jb + lane;
+                const bool vis = j < nt_all && !(s_tmax[j] < wg_qmin || s_tmin[j] > wg_qmax);
+                const unsigned long long m = __ballot(vis);
+                if (vis) s_jlist[cnt + __popcll(m & ((1ull << lane) - 1))] = j;
+                cnt += __popcll(m);
+            }
+            if (lane == 0) s_nvis = cnt;
+        }
+        __syncthreads();
+        n_vis = __builtin_amdgcn_readfirstlane(s_nvis);
+        if (n_vis == 0) {
+            // no query of the block shares an id with any key it may see
+            if (q_valid) {
+#pragma unroll
+                for (int k2 = 0; k2 < H / 16; k2++) *(bf16x8 *)(a.o + qrow_off + 8 * (2 * k2 + c)) = bf16x8{};
+                if (c == 0 && a.lse) a.lse[(bk * a.G + g) * (size_t)T + t] = -INFINITY;
+            }
+            return;
+        }
+    }
+
+    // key tiles j0 .. j0 + n_t - 1 (SEG: the n_vis tiles of the list); a left
+    // window (causal only, WIN) starts the block's range at the first tile its
+    // first query can see
     const int WL = win_left(a.wl);
     const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
-    const int n_t = (CAUSAL ? qb + 1 : S / BKV) - j0;
+    const int n_t = SEG ? n_vis : (CAUSAL ? qb + 1 : S / BKV) - j0;
+    // key tile of loop step i
+    auto tile_of = [&](int i) { return SEG ? __builtin_amdgcn_readfirstlane(s_jlist[i]) : j0 + i; };
 
     // ---- global -> LDS loads: group A loads K tiles, group B V tiles; wave gwv
     // of a group issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat
@@ -785,7 +846,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     // the tile offset may go in the scalar offset, which the range check does
     // not cover.
     auto issue_tile = [&](int j, int slot) {
-        const int tile = __builtin_amdgcn_readfirstlane((j0 + j) * BKV * H * 2);
+        const int tile = __builtin_amdgcn_readfirstlane(tile_of(j) * BKV * H * 2);
         if (grp == 0) {
 #pragma unroll
             for (int i = 0; i < KL; i++)
@@ -846,10 +907,24 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int off = 32 * mb + 8 * (r >> 2) + (r & 3);
-                if (off > lim || off < first) sacc[mb][r] = -INFINITY;
+            for (int q4 = 0; q4 < 4; q4++) {
+                // SEG: the ids of keys s0 + 32 mb + 8 q4 + 4 c + 0..3
+                i32x4 ids{};
+                if constexpr (SEG) ids = *(const i32x4 *)&s_kvid[s0 + 32 * mb + 8 * q4 + 4 * c];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = 4 * q4 + e, off = 32 * mb + 8 * q4 + e;
+                    bool hide = off > lim || off < first;
+                    if constexpr (SEG) hide = hide || ids[e] != my_qid;
+                    if (hide) sacc[mb][r] = -INFINITY;
+                }
             }
+    };
+    // SEG: does tile j need the element mask for this wave's rows (not every
+    // id of the tile and of the wave's queries the same)?
+    auto seg_mask = [&](int j) {
+        const int kmin = __builtin_amdgcn_readfirstlane(s_tmin[j]), kmax = __builtin_amdgcn_readfirstlane(s_tmax[j]);
+        return !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
     };
     auto tile_max = [&]() {
         float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -945,6 +1020,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
         int i = 0;
         for (; i < 2 && i < n_t - 1 && (j0 + i) * BKV < t0 + BKV - 1 - WL; i++) round(i, yes{});
         for (; i < n_t - 1; i++) round(i, no{});
+    } else if constexpr (SEG) {
+        for (int i = 0; i < n_t - 1; i++) {
+            const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
+            barrier_no_drain();
+            if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
+            const int j = tile_of(i);
+            if (seg_mask(j))
+                v_phase_masked(j * BKV);
+            else
+                v_phase_open();
+            barrier_no_drain();
+            m_phase(yes{}, yes{}, slot, slot);
+            slot = nslot;
+        }
     } else {
         for (int i = 0; i < n_t - 1; i++) {
             const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
@@ -957,10 +1046,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
         }
     }
     // the last tile (the diagonal one when causal): nothing left to load or to
-    // multiply with K
+    // multiply with K. SEG masks it always (its ids and, when causal, the
+    // diagonal).
     barrier_no_drain();
-    if (CAUSAL)
-        v_phase_masked((j0 + n_t - 1) * BKV);
+    if (CAUSAL || SEG)
+        v_phase_masked(tile_of(n_t - 1) * BKV);
     else
         v_phase_open();
     barrier_no_drain();
@@ -1034,6 +1124,18 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
                 hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
             else
                 hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+            return hipGetLastError();
+        }
+        // segment ids on an otherwise dense shape with at most 8192 keys: the
+        // ping-pong kernel over each block's list of tiles that share an id
+        const bool dense_seg = a.o_part == nullptr && a.q_seg != nullptr && all_waves && a.S % BKV == 0 &&
+                               a.S <= 8192 && !windowed(a.wl, a.wr, a.causal) &&
+                               (!a.causal || (a.T == a.S && a.bq == BKV));
+        if (dense_seg) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+            else
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false, false, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
             return hipGetLastError();
         }
         // a causal left window on an otherwise dense shape: the ping-pong kernel

@@ -45,6 +45,13 @@ SMALL = [
     (1, 1, 1, 300, 128, 64, False, None),
     (1, 1, 8, 77, 256, 128, False, None),
     (2, 1, 4, 384, 384, 64, True, None),
+    # segment ids on whole key tiles with S <= 8192 (the ping-pong path over
+    # each block's list of tiles that share an id): causal packed ids, non-causal
+    # independent q / kv ids with ragged T, H = 64, G = 8 (32-query blocks)
+    (1, 1, 4, 256, 256, 128, True, (16, 100)),
+    (1, 2, 4, 200, 320, 128, False, (20, 90)),
+    (1, 1, 4, 128, 128, 64, True, (8, 40)),
+    (1, 1, 8, 96, 192, 128, False, (10, 60)),
     # H = 256 with G a multiple of 8 (the ping-pong path at H = 256, 32-key
     # tiles): one- and three-tile causal blocks, G = 16, ragged T
     (2, 1, 8, 32, 32, 256, True, None),
@@ -148,6 +155,25 @@ def test_fully_masked_rows_give_zero_and_neg_inf():
     assert torch.all(o[:, :, :, 64:96] == 0)
     assert torch.all(torch.isneginf(lse[:, :, :, 64:96]))
     ref_o, ref_lse = oracle.fwd(q, k, v, causal=False, q_seg=q_seg, kv_seg=kv_seg)
+    assert_close_o(f32(o), ref_o)
+    assert_close_lse(f32(lse), ref_lse)
+
+
+@pytest.mark.parametrize("causal,T", [(False, 192), (True, 256)])
+def test_segment_ids_any_int32_values(causal, T):
+    # ids need not be sorted, contiguous or small: random draws from a pool with
+    # a negative and the largest int32 value, mixed within every tile; batch
+    # row 1's queries share no id with any key (O = 0, lse = -inf)
+    B, K, G, S, H = 2, 1, 4, 256, 128
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=127 + T)
+    gen = torch.Generator().manual_seed(127 + T)
+    pool = torch.tensor([-5, 3, 2 ** 31 - 1, 40], dtype=torch.int32)
+    q_seg = pool[torch.randint(0, 4, (B, T), generator=gen)]
+    kv_seg = pool[torch.randint(0, 4, (B, S), generator=gen)]
+    q_seg[1] = 99
+    o, lse = run_gpu(q, k, v, causal, q_seg, kv_seg)
+    assert torch.all(o[1] == 0) and torch.all(torch.isneginf(lse[1]))
+    ref_o, ref_lse = oracle.fwd(q, k, v, causal=causal, q_seg=q_seg, kv_seg=kv_seg)
     assert_close_o(f32(o), ref_o)
     assert_close_lse(f32(lse), ref_lse)
 
