@@ -22,6 +22,11 @@ tensors and reports it under "backward".
 --workload long times the 32k-token shape B=1, K=2, G=8, T=S=32768, H=256
 (causal) in the same format, without the backward leg.
 
+--workload segments times the packed-sequence shape B=4, K=8, G=4, T=S=2048,
+H=128 (causal and segment ids, segments of 64-1024 tokens) in the same
+format, with value on the causal-half FLOP count and the rate on visible
+pairs beside it; no backward or CPU legs.
+
 --write-traffic FETCH_CSV WRITE_CSV turns two rocprofv3 --pmc runs (FETCH_SIZE,
 then WRITE_SIZE, each with --copy-calibration-mib) into the HBM bytes per
 launch of the headline forward kernel, scaled by what the same counters read
@@ -300,6 +305,11 @@ def window_bench(args):
             "visible_pairs": pairs,
         },
     }
+    if seg is not None:
+        vis = visible_pairs_flops(w.H, w.K, w.G, seg, causal=True)
+        result["visible_pairs"] = {"flops_per_launch": vis, "tflops": vis / (ms * 1e-3) / 1e12,
+                                   "fraction_of_causal_half": vis / flops}
+
     if not args.no_backward:
         ws = torch.empty(gqa.attn_bwd_workspace_bytes(w.B, w.K, w.G, w.T, w.S, w.H), dtype=torch.uint8, device=dev)
         dq = torch.empty(qd.shape, dtype=torch.float32, device=dev)
@@ -363,10 +373,11 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed launches before the warm-up steps, for the clock to settle")
-    ap.add_argument("--workload", choices=["headline", "decode", "window", "long"], default="headline",
+    ap.add_argument("--workload", choices=["headline", "decode", "window", "long", "segments"], default="headline",
                     help="headline: the causal T=S=8192 forward (default); decode: T=1 against S=32768; "
                          "window: the headline shape with a causal 1024-key sliding window; "
-                         "long: the causal T=S=32768 H=256 forward")
+                         "long: the causal T=S=32768 H=256 forward; "
+                         "segments: the packed-sequence T=S=2048 forward with segment ids")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the headline kernel's HBM bytes per launch from two rocprofv3 --pmc CSVs "
                          "(needs --copy-calibration-mib, the size those runs copied) and exit")
@@ -386,7 +397,7 @@ def main():
 
     import torch
     import grouped_query_attention_flash_amd as gqa
-    from workloads import HEADLINE, WORKLOADS, attention_flops, make_qkv
+    from workloads import HEADLINE, WORKLOADS, attention_flops, make_qkv, make_segment_ids, visible_pairs_flops
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -399,10 +410,17 @@ def main():
         return
     w = HEADLINE
     kernel = "attn_fwd_pp_kernel<128,64,true,false> (ping-pong, dense causal)"
+    seg = None
     if args.workload == "long":
         w = WORKLOADS["causal_b1_k2_g8_t32768_h256"]
         kernel = "attn_fwd_pp_kernel<256,32,true,false> (ping-pong, dense causal)"
         args.no_backward = True
+    elif args.workload == "segments":
+        w = WORKLOADS["segments_causal_b4_k8_g4_t2048_h128"]
+        kernel = "attn_fwd_pp_kernel<128,64,true,false,true> (ping-pong, causal with segment ids)"
+        args.no_backward = True
+        args.no_cpu_baseline = True
+        seg = make_segment_ids(w.B, w.T, w.seed)
     t = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=not args.no_backward)
     q, k, v = t[:3]
     inp_cpu = {"q": q, "k": k, "v": v}
@@ -411,10 +429,11 @@ def main():
     dod = None if args.no_backward else t[3].to(dev)
     o = torch.empty_like(qd)
     lse = torch.empty(w.B, w.K, w.G, w.T, dtype=torch.float32, device=dev)
+    segd = None if seg is None else seg.to(dev)
     torch.cuda.synchronize()
 
     def step():
-        gqa.attn_fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse)
+        gqa.attn_fwd(qd, kd, vd, causal=w.causal, q_seg=segd, kv_seg=segd, out=o, lse=lse)
 
     ms = time_launches(step, args.steps, args.warmup, args.settle_seconds)
     flops = attention_flops(w.B, w.K, w.G, w.T, w.S, w.H, w.causal)
@@ -435,7 +454,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, q pre-scaled by H^-1/2)",
         "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
-                   "causal": w.causal, "mask": "lazy causal"},
+                   "causal": w.causal, "mask": "lazy causal" if seg is None else "lazy causal and segment ids"},
         "pct_of_peak": 100.0 * tflops / MI355X_BF16_DENSE_TFLOPS,
         "roofline": {
             "kernel": kernel,
@@ -449,6 +468,11 @@ def main():
             "algorithmic_hbm_bytes_per_launch": fwd_bytes,
         },
     }
+
+    if seg is not None:
+        vis = visible_pairs_flops(w.H, w.K, w.G, seg, causal=True)
+        result["visible_pairs"] = {"flops_per_launch": vis, "tflops": vis / (ms * 1e-3) / 1e12,
+                                   "fraction_of_causal_half": vis / flops}
 
     if not args.no_backward:
         ws = torch.empty(gqa.attn_bwd_workspace_bytes(w.B, w.K, w.G, w.T, w.S, w.H), dtype=torch.uint8, device=dev)
