@@ -79,7 +79,7 @@ def measured_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
-HEADLINE_KERNEL = "attn_fwd_pp_kernel<128, 64, true, false>"
+HEADLINE_KERNEL = "attn_fwd_pp_kernel<128, 64, true, false, false>"
 
 
 def write_traffic(fetch_csv, write_csv, calib_mib):
@@ -294,7 +294,7 @@ def window_bench(args):
         "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
                    "causal": True, "window_left": WINDOW_LEFT, "window_right": -1},
         "roofline": {
-            "kernel": "attn_fwd_pp_kernel<128,64,true,true> (ping-pong, windowed)",
+            "kernel": "attn_fwd_pp_kernel<128,64,true,true,false> (ping-pong, windowed)",
             "bound": "mfma",
             "achieved": tflops,
             "peak": MI355X_BF16_DENSE_TFLOPS,
@@ -409,11 +409,11 @@ def main():
         window_bench(args)
         return
     w = HEADLINE
-    kernel = "attn_fwd_pp_kernel<128,64,true,false> (ping-pong, dense causal)"
+    kernel = "attn_fwd_pp_kernel<128,64,true,false,false> (ping-pong, dense causal)"
     seg = None
     if args.workload == "long":
         w = WORKLOADS["causal_b1_k2_g8_t32768_h256"]
-        kernel = "attn_fwd_pp_kernel<256,32,true,false> (ping-pong, dense causal)"
+        kernel = "attn_fwd_pp_kernel<256,32,true,false,false> (ping-pong, dense causal)"
         args.no_backward = True
     elif args.workload == "segments":
         w = WORKLOADS["segments_causal_b4_k8_g4_t2048_h128"]
