@@ -36,6 +36,15 @@
 #ifndef GQA_BWD_DELTA_PP
 #define GQA_BWD_DELTA_PP 1
 #endif
+// dense shapes at H <= 128 run dQ on the ping-pong kernel
+#ifndef GQA_BWD_DQ_PP
+#define GQA_BWD_DQ_PP 1
+#endif
+// its M phase issues the LDS operand reads of a step this many steps ahead
+// (0: no pinned schedule)
+#ifndef GQA_BWD_DQ_PREF
+#define GQA_BWD_DQ_PREF 2
+#endif
 #ifndef GQA_BWD_D_BKV
 #define GQA_BWD_D_BKV 64
 #endif
@@ -1042,6 +1051,210 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     if (c == 0) a.delta[row] = d_acc;
 }
 
+
+// Interleave pattern of a ping-pong M phase for the machine scheduler: NX
+// steps of NM MFMAs, the R LDS operand reads of step X issued after the
+// MFMAs of step X - D (the first D steps' reads up front).
+template <int X, int NX, int R>
+__device__ __forceinline__ void pp_sched_reads() {
+    if constexpr (X < NX) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+}
+template <int X, int NX, int NM, int R, int D>
+__device__ __forceinline__ void pp_sched_step() {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    pp_sched_reads<X + D, NX, R>();
+}
+template <int NX, int NM, int R, int D, int... P, int... X>
+__device__ __forceinline__ void pp_schedule(std::integer_sequence<int, P...>, std::integer_sequence<int, X...>) {
+    (pp_sched_reads<P, NX, R>(), ...);
+    (pp_sched_step<X, NX, NM, R, D>(), ...);
+}
+
+// ---------------------------------------------------------------------------
+// dQ for dense shapes (no segments, no window, whole 32-key tiles; causal
+// needs T = S) on the forward's ping-pong scheme. 8 waves of 32 query rows
+// (the unit's gw heads x bq queries); waves 0-3 (group A) and 4-7 (group B)
+// run the same phases, B one phase behind A, with a workgroup barrier between
+// phases. A wave alternates
+//   M(i): S^T = K Q^T and dP^T = V dO^T of tile i+1, and dQ^T += K^T dS^T of
+//         tile i (dS as bf16 hi + lo parts, one MFMA each), MFMAs only
+//   V(i): P = exp2(S log2e - lse log2e) and dS = P (dP - D) of tile i
+// An M phase reads K and V of tile i+1 and K of tile i, so tiles rotate
+// through four LDS slots (slot j % 4 holds K(j), V(j)). During V(i) group A
+// loads K(i+2) and group B V(i+2) into slot (i+2) % 4, whose tile (i-2) was
+// last read by M(i-2), over for both groups by then; the M phases running
+// beside V(i) read slots i % 4 and (i +- 1) % 4. Each wave waits for its own
+// loads at the end of its next M phase, one barrier before M(i+1) reads them.
+// K rows are padded to CPR + 3 chunks (its b128 row reads conflict-free and
+// its transpose reads 2-way), V rows to CPR + 1.
+template <int H, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
+                                                                int n_qblocks) {
+    constexpr int BKV = 32;
+    constexpr int NG = 4;            // waves per group
+    constexpr int KSTEPS = H / 16;   // S and dP MFMAs per tile
+    constexpr int HB = H / 32;
+    constexpr int PK = BKV / 16;     // 16-key chunks of a tile
+    static_assert(PK * HB == KSTEPS, "one dQ step per S / dP step");
+    constexpr int CPR = H / 8;
+    constexpr int KRS = CPR + 3, VRS = CPR + 1;
+    constexpr int KBLK = (BKV * KRS + 63) / 64, VBLK = (BKV * VRS + 63) / 64;
+    constexpr int NL = ((KBLK > VBLK ? KBLK : VBLK) + NG - 1) / NG;
+    constexpr int NSLOT = 4;
+    __shared__ __attribute__((aligned(1024))) __bf16 sk[NSLOT][KBLK * 512];
+    __shared__ __attribute__((aligned(1024))) __bf16 sv[NSLOT][VBLK * 512];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave / NG, gwv = wave % NG;
+    const int n = lane & 31, c = lane >> 5;
+
+    // work unit (causal: heaviest query block first) and this lane's row
+    const int units = a.B * a.K * n_gsplit;
+    int qb = blockIdx.x / units;
+    if (CAUSAL) qb = n_qblocks - 1 - qb;
+    const int u = blockIdx.x % units;
+    const int gs = u % n_gsplit;
+    const int kh = (u / n_gsplit) % a.K;
+    const int b = u / (n_gsplit * a.K);
+    const int t0 = qb * bq;
+    const int T = a.T, S = a.S;
+    const int rho = wave * 32 + n;  // gw * bq == 256: every row belongs to the unit
+    const int g = gs * gw + rho / bq;
+    const int t = t0 + rho % bq;    // t < T: T is a whole number of query blocks
+    const int t_w = t - n;          // the wave's first query
+    const size_t bk = (size_t)b * a.K + kh;
+    const size_t row = (bk * a.G + g) * (size_t)T + t;
+
+    bf16x8 qf[KSTEPS], df[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++) {
+        qf[ks] = *(const bf16x8 *)(a.q + row * H + 16 * ks + 8 * c);
+        df[ks] = *(const bf16x8 *)(a.dout + row * H + 16 * ks + 8 * c);
+    }
+    const float l = a.lse[row];
+    const float lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    const float dlt = a.delta[row];
+
+    const buffer_rsrc krs = make_rsrc(a.k + bk * (size_t)S * H, S * H * 2);
+    const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
+    const int n_t = CAUSAL ? (t0 + bq) / BKV : S / BKV;
+
+    // global -> LDS: group A loads K tiles, group B V tiles; wave gwv of a group
+    // issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat the row's
+    // last chunk; slots past the last padded row re-read row BKV - 1)
+    const int rs = grp == 0 ? KRS : VRS;
+    const int nblk = grp == 0 ? KBLK : VBLK;
+    int ld_off[NL];
+#pragma unroll
+    for (int i = 0; i < NL; i++) {
+        const int pslot = (gwv + i * NG) * 64 + lane;
+        ld_off[i] = (min(pslot / rs, BKV - 1) * H + min(pslot % rs, CPR - 1) * 8) * 2;
+    }
+    // tiles j < n_t lie wholly inside K and V (S % BKV == 0), so the tile
+    // offset may go in the scalar offset
+    auto issue_tile = [&](int j, int slot) {
+        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+        char *dst = grp == 0 ? (char *)sk[slot] : (char *)sv[slot];
+        const buffer_rsrc &rsrc = grp == 0 ? krs : vrs;
+#pragma unroll
+        for (int i = 0; i < NL; i++)
+            if (gwv + i * NG < nblk) lds_load16_to(rsrc, dst + (gwv + i * NG) * 1024, ld_off[i], tile);
+    };
+
+    f32x16 sacc, pacc, dq_acc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++) dq_acc[hb] = f32x16{};
+    bf16x8 dsh[PK], dsl[PK];
+    const int k_lane = n * KRS * 8 + c * 8, v_lane = n * VRS * 8 + c * 8;
+    // transpose read of K^T: lane (gi, hh) of 16-lane group c addresses key
+    // 16 kk + 4 c + gi / 4 (+ 8 for the upper half) at h = 32 hb + 16 hh + 4 (gi % 4)
+    const int tr_lane = (4 * c + ((lane & 15) >> 2)) * KRS * 8 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    // M phase: S / dP of the tile in slot `cur` (SD) and dQ of the tile in
+    // slot `prev` (DQ), interleaved S, dQ hi, dP, dQ lo
+    auto m_phase = [&](auto sd, auto dq, int cur, int prev) {
+        const __bf16 *kc = sk[cur];
+        const __bf16 *vc = sv[cur];
+        const __bf16 *kp = sk[prev];
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int x = 0; x < KSTEPS; x++) {
+            const int kk = x / HB, hb = x % HB;
+            bf16x8 kt;
+            if constexpr (decltype(dq)::value) {
+                const __bf16 *p = kp + tr_lane + kk * 16 * KRS * 8 + hb * 32;
+                kt = join_bf16x8(lds_read_tr16(p), lds_read_tr16(p + 8 * KRS * 8));
+            }
+            if constexpr (decltype(sd)::value) {
+                const bf16x8 kf = *(const bf16x8 *)(kc + k_lane + x * 16);
+                sacc = mfma32x32x16(kf, qf[x], x == 0 ? f32x16{} : sacc);
+            }
+            if constexpr (decltype(dq)::value) dq_acc[hb] = mfma32x32x16(kt, dsh[kk], dq_acc[hb]);
+            if constexpr (decltype(sd)::value) {
+                const bf16x8 vf = *(const bf16x8 *)(vc + v_lane + x * 16);
+                pacc = mfma32x32x16(vf, df[x], x == 0 ? f32x16{} : pacc);
+            }
+            if constexpr (decltype(dq)::value) dq_acc[hb] = mfma32x32x16(kt, dsl[kk], dq_acc[hb]);
+        }
+#if GQA_BWD_DQ_PREF > 0
+        constexpr bool SD = decltype(sd)::value, DQ = decltype(dq)::value;
+        constexpr int NM = (SD ? 2 : 0) + (DQ ? 2 : 0);
+        constexpr int D = GQA_BWD_DQ_PREF < KSTEPS ? GQA_BWD_DQ_PREF : KSTEPS;
+        pp_schedule<KSTEPS, NM, NM, D>(std::make_integer_sequence<int, D>(), std::make_integer_sequence<int, KSTEPS>());
+#endif
+        __builtin_amdgcn_s_setprio(0);
+        wait_lds_loads();
+    };
+    // V phase: lane (n, c) holds keys s0 + acc_row(r, c) of query t; dS as
+    // bf16 hi + lo (early causal rows have |dS| of order 10, where one bf16
+    // rounding alone costs ~1e-1 in dQ)
+    auto v_phase = [&](int s0) {
+        const bool masked = CAUSAL && s0 + BKV - 1 > t_w;  // some key after some query of the wave
+        const int lim = t - s0 - 4 * c;                     // last visible key offset (causal)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            float p = exp2_fast(__builtin_fmaf(sacc[r], kLog2e, -lse2));
+            if (masked && 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+            const float ds = p * (pacc[r] - dlt);
+            const __bf16 hi = (__bf16)ds;
+            dsh[r >> 3][r & 7] = hi;
+            dsl[r >> 3][r & 7] = (__bf16)(ds - (float)hi);
+        }
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    // prologue: tiles 0 and 1 -> slots 0 and 1
+    issue_tile(0, 0);
+    if (n_t > 1) issue_tile(1, 1);
+    wait_lds_loads();
+    barrier_no_drain();
+    if (grp == 1) barrier_no_drain();  // group B runs one phase behind
+    m_phase(yes{}, no{}, 0, 0);        // M(-1): S / dP of tile 0
+    for (int i = 0; i < n_t - 1; i++) {
+        barrier_no_drain();
+        if (i + 2 < n_t) issue_tile(i + 2, (i + 2) % NSLOT);
+        v_phase(i * BKV);
+        barrier_no_drain();
+        m_phase(yes{}, yes{}, (i + 1) % NSLOT, i % NSLOT);
+    }
+    barrier_no_drain();
+    v_phase((n_t - 1) * BKV);
+    barrier_no_drain();
+    m_phase(no{}, yes{}, 0, (n_t - 1) % NSLOT);
+    if (grp == 0) barrier_no_drain();  // group A's trailing phase
+
+    // dQ row (fp32): lane (n, c) holds h = 32 hb + acc_row(r, c) of query t
+    float *dqrow = a.dq + row * H;
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++)
+            *(f32x4 *)(dqrow + 32 * hb + 8 * q4 + 4 * c) =
+                f32x4{dq_acc[hb][4 * q4], dq_acc[hb][4 * q4 + 1], dq_acc[hb][4 * q4 + 2], dq_acc[hb][4 * q4 + 3]};
+}
+
 // ---------------------------------------------------------------------------
 template <int H, int NW_DKV, int BKV_DQ, int NW_DQ>
 static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
@@ -1077,8 +1290,24 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
                            n_gsplit, n_qblocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<H, BKV_DQ, NW_DQ, false>), qgrid, dim3(NW_DQ * 64), 0, stream, a, gw, bq,
-                       n_gsplit, n_qblocks);
+    bool dq_done = false;
+    if constexpr (GQA_BWD_DQ_PP && H <= 128 && NW_DQ == 8) {
+        // dense shapes: dQ on the ping-pong kernel (32-key tiles)
+        const bool dense = a.q_seg == nullptr && !windowed(a.wl, a.wr, a.causal) && gw * bq == 256 &&
+                           a.T % bq == 0 && a.S % 32 == 0 && (!a.causal || a.T == a.S);
+        if (dense) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, true>), qgrid, dim3(512), 0, stream, a, gw, bq, n_gsplit,
+                                   n_qblocks);
+            else
+                hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, false>), qgrid, dim3(512), 0, stream, a, gw, bq, n_gsplit,
+                                   n_qblocks);
+            dq_done = true;
+        }
+    }
+    if (!dq_done)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<H, BKV_DQ, NW_DQ, false>), qgrid, dim3(NW_DQ * 64), 0, stream, a, gw, bq,
+                           n_gsplit, n_qblocks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int keys_wg = 32 * NW_DKV;
