@@ -45,6 +45,10 @@
 #ifndef GQA_BWD_DQ_PREF
 #define GQA_BWD_DQ_PREF 2
 #endif
+// the same for the ping-pong D pass
+#ifndef GQA_BWD_D_PREF
+#define GQA_BWD_D_PREF 2
+#endif
 #ifndef GQA_BWD_D_BKV
 #define GQA_BWD_D_BKV 64
 #endif
@@ -61,6 +65,25 @@
 #endif
 
 namespace gqa {
+
+// Interleave pattern of a ping-pong M phase for the machine scheduler: NX
+// steps of NM MFMAs, the R LDS operand reads of step X issued after the
+// MFMAs of step X - D (the first D steps' reads up front).
+template <int X, int NX, int R>
+__device__ __forceinline__ void pp_sched_reads() {
+    if constexpr (X < NX) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+}
+template <int X, int NX, int NM, int R, int D>
+__device__ __forceinline__ void pp_sched_step() {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    pp_sched_reads<X + D, NX, R>();
+}
+template <int NX, int NM, int R, int D, int... P, int... X>
+__device__ __forceinline__ void pp_schedule(std::integer_sequence<int, P...>, std::integer_sequence<int, X...>) {
+    (pp_sched_reads<P, NX, R>(), ...);
+    (pp_sched_step<X, NX, NM, R, D>(), ...);
+}
+
 
 // ---------------------------------------------------------------------------
 // dK, dV. One workgroup per (b, kv head, block of 32*NW keys); wave w owns
@@ -1003,6 +1026,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
             sacc[mb] = mfma32x32x16(kf, qf[ks], ks == 0 ? f32x16{} : sacc[mb]);
             pacc[mb] = mfma32x32x16(vf, df[ks], ks == 0 ? f32x16{} : pacc[mb]);
         }
+#if GQA_BWD_D_PREF > 0
+        constexpr int D = GQA_BWD_D_PREF < NX ? GQA_BWD_D_PREF : NX;
+        pp_schedule<NX, 2, 2, D>(std::make_integer_sequence<int, D>(), std::make_integer_sequence<int, NX>());
+#endif
         __builtin_amdgcn_s_setprio(0);
         wait_lds_loads();
     };
@@ -1051,24 +1078,6 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     if (c == 0) a.delta[row] = d_acc;
 }
 
-
-// Interleave pattern of a ping-pong M phase for the machine scheduler: NX
-// steps of NM MFMAs, the R LDS operand reads of step X issued after the
-// MFMAs of step X - D (the first D steps' reads up front).
-template <int X, int NX, int R>
-__device__ __forceinline__ void pp_sched_reads() {
-    if constexpr (X < NX) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-}
-template <int X, int NX, int NM, int R, int D>
-__device__ __forceinline__ void pp_sched_step() {
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-    pp_sched_reads<X + D, NX, R>();
-}
-template <int NX, int NM, int R, int D, int... P, int... X>
-__device__ __forceinline__ void pp_schedule(std::integer_sequence<int, P...>, std::integer_sequence<int, X...>) {
-    (pp_sched_reads<P, NX, R>(), ...);
-    (pp_sched_step<X, NX, NM, R, D>(), ...);
-}
 
 // ---------------------------------------------------------------------------
 // dQ for dense shapes (no segments, no window, whole 32-key tiles; causal
