@@ -40,6 +40,9 @@ SMALL = [
     (1, 1, 4, 128, 128, 256, True, None),
     (1, 1, 4, 90, 130, 256, False, (3, 50)),
     # dense shapes of the ping-pong D pass: non-causal with T != S, and
+    # one and two heads per unit (256- and 128-query blocks of the dense dQ path)
+    (1, 1, 1, 256, 256, 128, True, None),
+    (1, 2, 2, 256, 384, 128, False, None),
     # eight heads per unit (32-query blocks)
     (1, 1, 4, 128, 320, 128, False, None),
     (1, 1, 8, 96, 128, 128, False, None),
