@@ -51,7 +51,8 @@
 #ifndef GQA_FWD_DMASPREAD
 #define GQA_FWD_DMASPREAD 1
 #endif
-// dense shapes at H <= 128 run the ping-pong kernel
+// dense shapes run the ping-pong kernel (H <= 128, and H = 256 when G is a
+// multiple of 8; at H <= 128 also shapes with segment ids and S <= 8192)
 #ifndef GQA_FWD_PINGPONG
 #define GQA_FWD_PINGPONG 1
 #endif
