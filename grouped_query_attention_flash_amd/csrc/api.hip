@@ -245,7 +245,9 @@ const char *attn_strerror(int code) {
     switch (code) {
         case GQA_ATTN_OK: return "success";
         case GQA_ATTN_ERR_NULL: return "a required pointer is NULL";
-        case GQA_ATTN_ERR_SHAPE: return "invalid sizes: B, K, G, T, S must be >= 1 and each (b, kv head) slice of q or k < 2^30 elements";
+        case GQA_ATTN_ERR_SHAPE:
+            return "invalid sizes: B, K, G, T, S must be >= 1, each (b, kv head) slice of q or k < 2^30 elements and "
+                   "B*K*G*(T+31) < 2^31";
         case GQA_ATTN_ERR_HEADDIM: return "unsupported head dimension H (supported: 64, 128, 256)";
         case GQA_ATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte alignment, segment ids 4-byte)";
         case GQA_ATTN_ERR_SEGMENTS: return "q_seg and kv_seg must both be given or both be NULL";

@@ -49,7 +49,8 @@ extern "C" {
 enum {
     GQA_ATTN_OK = 0,
     GQA_ATTN_ERR_NULL = 1,      /* a required pointer is NULL                    */
-    GQA_ATTN_ERR_SHAPE = 2,     /* B,K,G,T,S < 1, or a (b, kv head) slice of q or k of 2^30 elements or more */
+    GQA_ATTN_ERR_SHAPE = 2,     /* B,K,G,T,S < 1, a (b, kv head) slice of q or k of 2^30 elements or
+                                   more, or B*K*G*(T+31) of 2^31 or more (32-bit grid sizes) */
     GQA_ATTN_ERR_HEADDIM = 3,   /* H not in {64, 128, 256}                       */
     GQA_ATTN_ERR_ALIGN = 4,     /* a pointer is not 16-byte (4 for ids) aligned  */
     GQA_ATTN_ERR_SEGMENTS = 5,  /* exactly one of q_seg / kv_seg given           */

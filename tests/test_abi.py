@@ -59,6 +59,9 @@ def test_check_fwd_codes():
     assert check_fwd(G=1, T=(1 << 23) - 1, S=64) == gqa.GQA_ATTN_OK      # q slice just under 2^30 elements
     assert check_fwd(G=1, T=1 << 23, S=64) == gqa.GQA_ATTN_ERR_SHAPE     # q slice 2^30 elements
     assert check_fwd(G=1, T=64, S=1 << 23) == gqa.GQA_ATTN_ERR_SHAPE     # k slice 2^30 elements
+    # query rows rounded up to whole 32-row waves must stay below 2^31 (grid sizes)
+    assert check_fwd(B=(1 << 26) - 1, G=1, T=1) == gqa.GQA_ATTN_OK        # (2^26 - 1) * 32 rows
+    assert check_fwd(B=1 << 26, G=1, T=1) == gqa.GQA_ATTN_ERR_SHAPE       # 2^31 rows
     for h in (0, 32, 96, 129, 512):
         assert check_fwd(H=h) == gqa.GQA_ATTN_ERR_HEADDIM, h
     for h in (64, 128, 256):
