@@ -305,11 +305,6 @@ def window_bench(args):
             "visible_pairs": pairs,
         },
     }
-    if seg is not None:
-        vis = visible_pairs_flops(w.H, w.K, w.G, seg, causal=True)
-        result["visible_pairs"] = {"flops_per_launch": vis, "tflops": vis / (ms * 1e-3) / 1e12,
-                                   "fraction_of_causal_half": vis / flops}
-
     if not args.no_backward:
         ws = torch.empty(gqa.attn_bwd_workspace_bytes(w.B, w.K, w.G, w.T, w.S, w.H), dtype=torch.uint8, device=dev)
         dq = torch.empty(qd.shape, dtype=torch.float32, device=dev)
