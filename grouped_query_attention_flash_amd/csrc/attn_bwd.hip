@@ -940,7 +940,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
 // into the slot that M(i-1) of both groups has finished reading; every wave
 // waits for its own loads at the end of its next M phase, a barrier before
 // any wave reads them.
-template <int H, int BKV, bool CAUSAL>
+template <int H, int BKV, bool CAUSAL, bool WIN = false>
 __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
                                                                    int n_qblocks) {
     constexpr int NG = 4;  // waves per group
@@ -987,7 +987,11 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
 
     const buffer_rsrc krs = make_rsrc(a.k + bk * (size_t)S * H, S * H * 2);
     const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
-    const int n_t = CAUSAL ? qb + 1 : S / BKV;
+    // key tiles j0 .. j0 + n_t - 1: a left window (causal only, WIN) starts the
+    // block at the tile holding its first query's first visible key
+    const int WL = win_left(a.wl);
+    const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
+    const int n_t = (CAUSAL ? qb + 1 : S / BKV) - j0;
 
     // global -> LDS: group A loads K tiles, group B V tiles; wave gwv of a group
     // issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat the row's
@@ -1002,7 +1006,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     // tiles j < n_t lie wholly inside K and V (S % BKV == 0), so the tile
     // offset may go in the scalar offset
     auto issue_tile = [&](int j, int slot) {
-        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+        const int tile = __builtin_amdgcn_readfirstlane((j0 + j) * BKV * H * 2);
         __bf16 *dst = grp == 0 ? sk[slot] : sv[slot];
         const buffer_rsrc &rs = grp == 0 ? krs : vrs;
 #pragma unroll
@@ -1035,14 +1039,17 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     };
     // V phase: lane (n, c) holds keys s0 + 32 mb + acc_row(r, c) of query t
     auto v_phase = [&](int s0, auto masked) {
-        const int lim = t - s0 - 4 * c;  // last visible key offset (causal)
+        const int lim = t - s0 - 4 * c;                         // last visible key offset (causal)
+        const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;  // first visible key offset (window)
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 float p = exp2_fast(__builtin_fmaf(sacc[mb][r], kLog2e, -lse2));
-                if constexpr (decltype(masked)::value)
-                    if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+                if constexpr (decltype(masked)::value) {
+                    const int off = 32 * mb + 8 * (r >> 2) + (r & 3);
+                    if (off > lim || off < first) p = 0.f;
+                }
                 d_acc = __builtin_fmaf(p, pacc[mb][r], d_acc);
             }
     };
@@ -1062,16 +1069,21 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
         const int lslot = nslot == NSLOT - 1 ? 0 : nslot + 1;
         barrier_no_drain();
         if (i + 2 < n_t) issue_tile(i + 2, lslot);
-        v_phase(i * BKV, no{});
+        // WIN: the window's left edge, t - WL over the block's BKV queries,
+        // cuts at most the block's first two tiles
+        if (WIN && i < 2 && (j0 + i) * BKV < t0 + BKV - 1 - WL)
+            v_phase((j0 + i) * BKV, yes{});
+        else
+            v_phase((j0 + i) * BKV, no{});
         barrier_no_drain();
         m_phase(nslot);
         slot = nslot;
     }
     barrier_no_drain();
     if (CAUSAL)
-        v_phase((n_t - 1) * BKV, yes{});
+        v_phase((j0 + n_t - 1) * BKV, yes{});
     else
-        v_phase((n_t - 1) * BKV, no{});
+        v_phase((j0 + n_t - 1) * BKV, no{});
     if (grp == 0) barrier_no_drain();  // group A's trailing phase
 
     d_acc += __shfl_xor(d_acc, 32);
@@ -1096,7 +1108,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
 // loads at the end of its next M phase, one barrier before M(i+1) reads them.
 // K rows are padded to CPR + 3 chunks (its b128 row reads conflict-free and
 // its transpose reads 2-way), V rows to CPR + 1.
-template <int H, bool CAUSAL>
+template <int H, bool CAUSAL, bool WIN = false>
 __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
                                                                 int n_qblocks) {
     constexpr int BKV = 32;
@@ -1147,7 +1159,11 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
 
     const buffer_rsrc krs = make_rsrc(a.k + bk * (size_t)S * H, S * H * 2);
     const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
-    const int n_t = CAUSAL ? (t0 + bq) / BKV : S / BKV;
+    // key tiles j0 .. j0 + n_t - 1: a left window (causal only, WIN) starts the
+    // block at the tile holding its first query's first visible key
+    const int WL = win_left(a.wl);
+    const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
+    const int n_t = (CAUSAL ? (t0 + bq) / BKV : S / BKV) - j0;
 
     // global -> LDS: group A loads K tiles, group B V tiles; wave gwv of a group
     // issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat the row's
@@ -1163,7 +1179,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     // tiles j < n_t lie wholly inside K and V (S % BKV == 0), so the tile
     // offset may go in the scalar offset
     auto issue_tile = [&](int j, int slot) {
-        const int tile = __builtin_amdgcn_readfirstlane(j * BKV * H * 2);
+        const int tile = __builtin_amdgcn_readfirstlane((j0 + j) * BKV * H * 2);
         char *dst = grp == 0 ? (char *)sk[slot] : (char *)sv[slot];
         const buffer_rsrc &rsrc = grp == 0 ? krs : vrs;
 #pragma unroll
@@ -1219,12 +1235,16 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     // bf16 hi + lo (early causal rows have |dS| of order 10, where one bf16
     // rounding alone costs ~1e-1 in dQ)
     auto v_phase = [&](int s0) {
-        const bool masked = CAUSAL && s0 + BKV - 1 > t_w;  // some key after some query of the wave
-        const int lim = t - s0 - 4 * c;                     // last visible key offset (causal)
+        // some key after some query of the wave, or (WIN) before some query's
+        // first visible key t - WL
+        const bool masked = (CAUSAL && s0 + BKV - 1 > t_w) || (WIN && s0 < t_w + 31 - WL);
+        const int lim = t - s0 - 4 * c;                         // last visible key offset (causal)
+        const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;  // first visible key offset (window)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             float p = exp2_fast(__builtin_fmaf(sacc[r], kLog2e, -lse2));
-            if (masked && 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+            const int off = 8 * (r >> 2) + (r & 3);
+            if (masked && (off > lim || off < first)) p = 0.f;
             const float ds = p * (pacc[r] - dlt);
             const __bf16 hi = (__bf16)ds;
             dsh[r >> 3][r & 7] = hi;
@@ -1244,12 +1264,12 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     for (int i = 0; i < n_t - 1; i++) {
         barrier_no_drain();
         if (i + 2 < n_t) issue_tile(i + 2, (i + 2) % NSLOT);
-        v_phase(i * BKV);
+        v_phase((j0 + i) * BKV);
         barrier_no_drain();
         m_phase(yes{}, yes{}, (i + 1) % NSLOT, i % NSLOT);
     }
     barrier_no_drain();
-    v_phase((n_t - 1) * BKV);
+    v_phase((j0 + n_t - 1) * BKV);
     barrier_no_drain();
     m_phase(no{}, yes{}, 0, (n_t - 1) % NSLOT);
     if (grp == 0) barrier_no_drain();  // group A's trailing phase
@@ -1284,6 +1304,9 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
         constexpr int BKV_PP = 64;
         const bool dense = a.q_seg == nullptr && !windowed(a.wl, a.wr, a.causal) && gw * bq == 256 &&
                            a.T % bq == 0 && a.S % BKV_PP == 0 && (!a.causal || (a.T == a.S && bq == BKV_PP));
+        // a causal left window on an otherwise dense shape
+        const bool dense_win = a.q_seg == nullptr && a.causal && a.wl >= 0 && gw * bq == 256 && a.T % bq == 0 &&
+                               a.S % BKV_PP == 0 && a.T == a.S && bq == BKV_PP;
         if (dense) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, true>), qgrid, dim3(512), 0, stream, a, gw,
@@ -1291,6 +1314,10 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
             else
                 hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, false>), qgrid, dim3(512), 0, stream, a, gw,
                                    bq, n_gsplit, n_qblocks);
+            delta_done = true;
+        } else if (dense_win) {
+            hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, true, true>), qgrid, dim3(512), 0, stream, a, gw,
+                               bq, n_gsplit, n_qblocks);
             delta_done = true;
         }
     }
@@ -1304,6 +1331,9 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
         // dense shapes: dQ on the ping-pong kernel (32-key tiles)
         const bool dense = a.q_seg == nullptr && !windowed(a.wl, a.wr, a.causal) && gw * bq == 256 &&
                            a.T % bq == 0 && a.S % 32 == 0 && (!a.causal || a.T == a.S);
+        // a causal left window on an otherwise dense shape
+        const bool dense_win = a.q_seg == nullptr && a.causal && a.wl >= 0 && gw * bq == 256 && a.T % bq == 0 &&
+                               a.S % 32 == 0 && a.T == a.S;
         if (dense) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, true>), qgrid, dim3(512), 0, stream, a, gw, bq, n_gsplit,
@@ -1311,6 +1341,10 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
             else
                 hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, false>), qgrid, dim3(512), 0, stream, a, gw, bq, n_gsplit,
                                    n_qblocks);
+            dq_done = true;
+        } else if (dense_win) {
+            hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, true, true>), qgrid, dim3(512), 0, stream, a, gw, bq,
+                               n_gsplit, n_qblocks);
             dq_done = true;
         }
     }
