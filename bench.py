@@ -82,7 +82,7 @@ def measured_traffic():
 HEADLINE_KERNEL = "attn_fwd_pp_kernel<128, 64, true, false, false>"
 
 
-def write_traffic(fetch_csv, write_csv, calib_mib):
+def write_traffic(fetch_csv, write_csv, calib_mib, out_path=TRAFFIC_FILE):
     """HBM bytes per launch of the headline forward kernel from two rocprofv3
     --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch). Each counter
     is scaled by bytes / reading of the largest device copy in the same run
@@ -109,10 +109,11 @@ def write_traffic(fetch_csv, write_csv, calib_mib):
     d = {"kernel": name, "kernel_digest": kernel_digest(FWD_SOURCES), "workload": "causal_b1_k8_g4_t8192_h128",
          "fetch_scale": fetch_scale, "write_scale": write_scale, "read_bytes_per_launch": rd,
          "write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(d, f, indent=1)
         f.write("\n")
     print(json.dumps(d))
+    return d
 
 
 def settle_clock(fn, seconds=1.0):
