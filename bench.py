@@ -79,7 +79,7 @@ def measured_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
-HEADLINE_KERNEL = "attn_fwd_pp_kernel<128, 64, true, false, false>"
+HEADLINE_KERNEL = "attn_fwd_pp_kernel<128, 64, true, false, false, 0>"
 
 
 def write_traffic(fetch_csv, write_csv, calib_mib, out_path=TRAFFIC_FILE):
@@ -295,7 +295,7 @@ def window_bench(args):
         "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
                    "causal": True, "window_left": WINDOW_LEFT, "window_right": -1},
         "roofline": {
-            "kernel": "attn_fwd_pp_kernel<128,64,true,true,false> (ping-pong, windowed)",
+            "kernel": "attn_fwd_pp_kernel<128,64,true,true,false,0> (ping-pong, windowed)",
             "bound": "mfma",
             "achieved": tflops,
             "peak": MI355X_BF16_DENSE_TFLOPS,
@@ -405,15 +405,15 @@ def main():
         window_bench(args)
         return
     w = HEADLINE
-    kernel = "attn_fwd_pp_kernel<128,64,true,false,false> (ping-pong, dense causal)"
+    kernel = "attn_fwd_pp_kernel<128,64,true,false,false,0> (ping-pong, dense causal)"
     seg = None
     if args.workload == "long":
         w = WORKLOADS["causal_b1_k2_g8_t32768_h256"]
-        kernel = "attn_fwd_pp_kernel<256,32,true,false,false> (ping-pong, dense causal)"
+        kernel = "attn_fwd_pp_kernel<256,32,true,false,false,0> (ping-pong, dense causal)"
         args.no_backward = True
     elif args.workload == "segments":
         w = WORKLOADS["segments_causal_b4_k8_g4_t2048_h128"]
-        kernel = "attn_fwd_pp_kernel<128,64,true,false,true> (ping-pong, causal with segment ids)"
+        kernel = "attn_fwd_pp_kernel<128,64,true,false,true,2> (ping-pong, causal with segment ids; loads spread over the MFMA phase)"
         args.no_backward = True
         args.no_cpu_baseline = True
         seg = make_segment_ids(w.B, w.T, w.seed)

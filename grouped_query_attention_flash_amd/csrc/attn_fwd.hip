@@ -718,7 +718,19 @@ __device__ __forceinline__ void m_phase_schedule(std::integer_sequence<int, P...
 // V(i+1) into slot (i+1) % 3, whose previous contents (read by M(i-2)) are
 // dead by then. Every wave waits for its own loads at the end of each of its
 // M phases, one barrier before any wave reads them.
-template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG = false>
+//
+// Where a wave issues its tile loads (MLD): 0 in its V phase; 1 all at the
+// start of its M phase; 2 spread among its M phase's MFMAs. 1 and 2 issue them
+// from assembly, so that the compiler adds no wait before the phase's operand
+// reads. M(i) then loads tile i+2: group A its K into slot (i+1) % 3, group B
+// its V into slot (i+2) % 3, and each wave waits for them at the end of its
+// next V phase. K(i+2) is first read by M(i+1), which group A starts right
+// after that wait; V(i+2) by M(i+2), two phases after group B's wait. The
+// slots' previous contents were last read by M(i-2) (K(i-1)) and M(i-1)
+// (V(i-1)), which both groups have finished. The V phase is the longer one
+// when the MFMAs per tile are few (H = 64) or the blocks short (segment ids),
+// and there moving the loads out of it pays.
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG = false, int MLD = 0>
 __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     constexpr int NG = 4;  // waves per group (8 per workgroup)
     constexpr int CPR = H / 8;
@@ -860,6 +872,42 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
                     lds_load16_to(vrs, (char *)sv[slot] + (gwv + i * NG) * 1024, ld_off[i], tile);
         }
     };
+    // the tile load an M phase issues (slot < 0: none)
+    struct MLd {
+        int bytes, slot;
+    };
+    // MLD 1: the loads of issue_tile from assembly, with the tile's byte
+    // offset (wave-uniform) in the scalar offset
+    const i32x4 my_rs = grp == 0 ? make_rsrc_words(a.k + bk * (size_t)S * H, S * H * 2)
+                                 : make_rsrc_words(a.v + bk * (size_t)S * H, S * H * 2);
+    const int my_blocks = grp == 0 ? L::K_BLOCKS : L::V_BLOCKS;
+    // LDS addresses as wave-uniform integers, so that the M phase computes
+    // the destinations on the scalar unit
+    const unsigned my_base0 = __builtin_amdgcn_readfirstlane(grp == 0 ? lds_addr(sk[0]) : lds_addr(sv[0]));
+    const unsigned my_slot_bytes = grp == 0 ? L::K_ELEMS * 2 : L::V_ELEMS * 2;
+    auto issue_tile_asm = [&](MLd ld) {
+        const unsigned base = my_base0 + (unsigned)ld.slot * my_slot_bytes;
+        const int tb = __builtin_amdgcn_readfirstlane(ld.bytes);
+#pragma unroll
+        for (int i = 0; i < NL; i++)
+            if (gwv + i * NG < my_blocks)
+                lds_dma16_so(my_rs, __builtin_amdgcn_readfirstlane(base + (unsigned)(gwv + i * NG) * 1024u), ld_off[i], tb);
+    };
+    // MLD 2: every wave issues NL loads per M phase without branches; a block
+    // past the tile gets an out-of-range offset (no memory is read) and the
+    // dummy destination
+    __shared__ __attribute__((aligned(1024))) char s_ldummy[MLD == 2 ? 1024 : 16];
+    const unsigned dummy_dst = __builtin_amdgcn_readfirstlane(lds_addr(s_ldummy));
+    if constexpr (MLD == 2) {
+#pragma unroll
+        for (int i = 0; i < NL; i++)
+            if (gwv + i * NG >= my_blocks) ld_off[i] = (int)0x80000000u;
+    }
+    auto issue_one = [&](int i, MLd ld) {
+        const unsigned base = my_base0 + (unsigned)ld.slot * my_slot_bytes;
+        const unsigned dst = gwv + i * NG < my_blocks ? base + (unsigned)(gwv + i * NG) * 1024u : dummy_dst;
+        lds_dma16_so(my_rs, __builtin_amdgcn_readfirstlane(dst), ld_off[i], __builtin_amdgcn_readfirstlane(ld.bytes));
+    };
 
     f32x16 sacc[MB];
     bf16x8 pf[PK];
@@ -872,10 +920,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     // ---- M phase: QK^T MFMA x and PV MFMA x alternate (independent chains)
     const int k_lane = n * L::KRS * 8 + c * 8;
     const int v_lane = (4 * c + ((lane & 15) >> 2)) * L::VRS * 8 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    auto m_phase = [&](auto do_qk, auto do_pv, int kslot, int vslot) {
+    auto m_phase = [&](auto do_qk, auto do_pv, int kslot, int vslot, MLd ld, auto loads) {
         const __bf16 *kt = sk[kslot];
         const __bf16 *vt = sv[vslot];
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (MLD == 1) {
+            if (ld.slot >= 0) issue_tile_asm(ld);
+            sched_fence();
+        }
+        constexpr int LSTEP = NQK / NL > 0 ? NQK / NL : 1;
 #pragma unroll
         for (int x = 0; x < NQK; x++) {
             if constexpr (decltype(do_qk)::value) {
@@ -890,6 +943,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
                 const s16x4 hi = lds_read_tr16(vp + 8 * L::VRS * 8);
                 oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf[kk], oacc[hb]);
             }
+            if constexpr (MLD == 2 && decltype(loads)::value)
+                if (x % LSTEP == LSTEP / 2 && x / LSTEP < NL) issue_one(x / LSTEP, ld);
         }
 #if GQA_PP_MSCHED
         constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
@@ -898,7 +953,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
             std::make_integer_sequence<int, D>(), std::make_integer_sequence<int, NQK>());
 #endif
         __builtin_amdgcn_s_setprio(0);
-        wait_lds_loads();
+        if constexpr (MLD == 0) wait_lds_loads();
     };
 
     // ---- V phase pieces (as in the kernel above)
@@ -990,61 +1045,120 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
 
-    // ---- prologue: K(0) -> slot 2, K(1) and V(0) -> slot 0
+    // MLD > 0: the load M(i) issues
+    auto mload = [&](int i, int nslot) {
+        const int nnslot = nslot == NSLOT - 1 ? 0 : nslot + 1;
+        return MLD > 0 && i + 2 < n_t ? MLd{tile_of(i + 2) * BKV * H * 2, grp == 0 ? nslot : nnslot} : MLd{0, -1};
+    };
+
+    // ---- prologue: K(0) -> slot 2, K(1) and V(0) -> slot 0 (MLD > 0: K(1)
+    // and V(1) come from M(-1))
     issue_tile(0, grp == 0 ? 2 : 0);
-    if (grp == 0 && n_t > 1) issue_tile(1, 0);
+    if (MLD == 0 && grp == 0 && n_t > 1) issue_tile(1, 0);
     wait_lds_loads();
     barrier_no_drain();
 
     if (grp == 1) barrier_no_drain();  // group B runs one phase behind
-    m_phase(yes{}, no{}, 2, 0);      // M(-1): S^T of tile 0
-    int slot = 0;                    // slot of tile set i: K(i+1), V(i)
-    // one round: V(i) then M(i); MASKED: tile i needs the element mask
-    auto round = [&](int i, auto masked) {
+    {                                  // M(-1): S^T of tile 0
+        const MLd ld = mload(-1, 0);
+        if (MLD == 2 && ld.slot >= 0)
+            m_phase(yes{}, no{}, 2, 0, ld, yes{});
+        else
+            m_phase(yes{}, no{}, 2, 0, ld, no{});
+    }
+    int slot = 0;                      // slot of tile set i: K(i+1), V(i)
+    // MLD > 0: round i = V(i), the wait for the loads of M(i-1), M(i) with
+    // its loads (rounds 0 .. n_t - 3; MLD 2 keeps the branch out of M by
+    // peeling the last round). VK: how V(i) masks (0: no element mask, 1: the
+    // element mask, 2: segment ids decide per tile).
+    using v_open = std::integral_constant<int, 0>;
+    using v_masked = std::integral_constant<int, 1>;
+    using v_seg = std::integral_constant<int, 2>;
+    auto round_ld = [&](int i, auto vk, auto ld_tag) {
         const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
         barrier_no_drain();
-        // V(i)
-        if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
-        if constexpr (decltype(masked)::value)
-            v_phase_masked((j0 + i) * BKV);
-        else
-            v_phase_open();
-        barrier_no_drain();
-        // M(i)
-        m_phase(yes{}, yes{}, slot, slot);
-        slot = nslot;
-    };
-    if constexpr (WIN) {
-        // The window's left edge, t - WL over the block's BKV queries, spans at
-        // most two tiles: those before the first tile every query sees whole
-        // take the element mask.
-        int i = 0;
-        for (; i < 2 && i < n_t - 1 && (j0 + i) * BKV < t0 + BKV - 1 - WL; i++) round(i, yes{});
-        for (; i < n_t - 1; i++) round(i, no{});
-    } else if constexpr (SEG) {
-        for (int i = 0; i < n_t - 1; i++) {
-            const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
-            barrier_no_drain();
-            if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
+        if constexpr (decltype(vk)::value == 2) {
             const int j = tile_of(i);
             if (seg_mask(j))
                 v_phase_masked(j * BKV);
             else
                 v_phase_open();
-            barrier_no_drain();
-            m_phase(yes{}, yes{}, slot, slot);
-            slot = nslot;
+        } else if constexpr (decltype(vk)::value == 1) {
+            v_phase_masked((j0 + i) * BKV);
+        } else {
+            v_phase_open();
         }
-    } else {
-        for (int i = 0; i < n_t - 1; i++) {
+        const MLd ld = mload(i, nslot);
+        wait_lds_loads();
+        barrier_no_drain();
+        m_phase(yes{}, yes{}, slot, slot, ld, ld_tag);
+        slot = nslot;
+    };
+    auto rounds_from = [&](int i, auto vk) {
+        for (; i < n_t - 2; i++) round_ld(i, vk, yes{});
+        for (; i < n_t - 1; i++) round_ld(i, vk, no{});
+    };
+    if constexpr (MLD == 0) {
+        // one round: V(i) then M(i); MASKED: tile i needs the element mask
+        auto round = [&](int i, auto masked) {
             const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
             barrier_no_drain();
+            // V(i)
             if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
-            v_phase_open();
+            if constexpr (decltype(masked)::value)
+                v_phase_masked((j0 + i) * BKV);
+            else
+                v_phase_open();
             barrier_no_drain();
-            m_phase(yes{}, yes{}, slot, slot);
+            // M(i)
+            m_phase(yes{}, yes{}, slot, slot, MLd{0, -1}, no{});
             slot = nslot;
+        };
+        if constexpr (WIN) {
+            // The window's left edge, t - WL over the block's BKV queries, spans at
+            // most two tiles: those before the first tile every query sees whole
+            // take the element mask.
+            int i = 0;
+            for (; i < 2 && i < n_t - 1 && (j0 + i) * BKV < t0 + BKV - 1 - WL; i++) round(i, yes{});
+            for (; i < n_t - 1; i++) round(i, no{});
+        } else if constexpr (SEG) {
+            for (int i = 0; i < n_t - 1; i++) {
+                const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
+                barrier_no_drain();
+                if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
+                const int j = tile_of(i);
+                if (seg_mask(j))
+                    v_phase_masked(j * BKV);
+                else
+                    v_phase_open();
+                barrier_no_drain();
+                m_phase(yes{}, yes{}, slot, slot, MLd{0, -1}, no{});
+                slot = nslot;
+            }
+        } else {
+            for (int i = 0; i < n_t - 1; i++) {
+                const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
+                barrier_no_drain();
+                if (grp == 0 ? i + 2 < n_t : true) issue_tile(grp == 0 ? i + 2 : i + 1, nslot);
+                v_phase_open();
+                barrier_no_drain();
+                m_phase(yes{}, yes{}, slot, slot, MLd{0, -1}, no{});
+                slot = nslot;
+            }
         }
+    } else if constexpr (WIN) {
+        int i = 0;
+        for (; i < 2 && i < n_t - 1 && (j0 + i) * BKV < t0 + BKV - 1 - WL; i++) {
+            if (i < n_t - 2)
+                round_ld(i, v_masked{}, yes{});
+            else
+                round_ld(i, v_masked{}, no{});
+        }
+        rounds_from(i, v_open{});
+    } else if constexpr (SEG) {
+        rounds_from(0, v_seg{});
+    } else {
+        rounds_from(0, v_open{});
     }
     // the last tile (the diagonal one when causal): nothing left to load or to
     // multiply with K. SEG masks it always (its ids and, when causal, the
@@ -1054,8 +1168,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
         v_phase_masked(tile_of(n_t - 1) * BKV);
     else
         v_phase_open();
+    if (MLD > 0) wait_lds_loads();
     barrier_no_drain();
-    m_phase(no{}, yes{}, slot, slot);
+    m_phase(no{}, yes{}, slot, slot, MLd{0, -1}, no{});
     if (grp == 0) barrier_no_drain();  // group A's trailing phase
 
     // ---- finalize: O = acc / l in bf16 through LDS, so that the wave's 32 rows
@@ -1121,10 +1236,14 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
                        !windowed(a.wl, a.wr, a.causal) && (!a.causal || (a.T == a.S && a.bq == BKV));
     if constexpr (GQA_FWD_PINGPONG && H <= 128 && NW == 8) {
         if (dense) {
+            // H = 64: the loads go into the M phase, which is the shorter one
+            constexpr int MLD = H == 64 ? 1 : 0;
             if (a.causal)
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false, false, MLD>), dim3(grid), dim3(NW * 64), 0,
+                                   stream, a);
             else
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false, false, false, MLD>), dim3(grid), dim3(NW * 64), 0,
+                                   stream, a);
             return hipGetLastError();
         }
         // segment ids on an otherwise dense shape with at most 8192 keys: the
@@ -1134,9 +1253,9 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
                                (!a.causal || (a.T == a.S && a.bq == BKV));
         if (dense_seg) {
             if (a.causal)
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false, true, 2>), dim3(grid), dim3(NW * 64), 0, stream, a);
             else
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false, false, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false, false, true, 2>), dim3(grid), dim3(NW * 64), 0, stream, a);
             return hipGetLastError();
         }
         // a causal left window on an otherwise dense shape: the ping-pong kernel

@@ -154,6 +154,20 @@ __device__ __forceinline__ void lds_dma16(const i32x4 &rs, unsigned dst, unsigne
         : "s"(dst), "v"(voffset), "s"(rs));
 }
 
+// The same with a wave-uniform byte offset in the scalar offset (not covered
+// by the range check: only for loads known to stay inside the buffer).
+__device__ __forceinline__ void lds_dma16_so(const i32x4 &rs, unsigned dst, unsigned voffset, int soffset) {
+    int saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(dst), "v"(voffset), "s"(rs), "s"(soffset));
+}
+
 // Wait until this wave's LDS-direct loads have landed (vmcnt = 0 only).
 __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Wait until at most N of this wave's vector-memory loads are outstanding (they
