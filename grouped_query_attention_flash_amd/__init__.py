@@ -9,6 +9,10 @@ if the library is missing or fails, these functions raise.
 Layouts: q, o, dO [B, K, G, T, H] bf16 (q pre-multiplied by H^-1/2);
 k, v [B, K, S, H] bf16; lse [B, K, G, T] fp32; q_seg [B, T] and
 kv_seg [B, S] int32; gradients fp32 in the layouts of their inputs.
+
+Masks (all lazy): causal=False/0 (none), True/1 or "top_left" (s <= t),
+2 or "end" (s <= t + S - T, end-aligned); window=(left, right) with -1 for
+an unbounded side; prefix=p makes keys s < p visible to every query.
 """
 from __future__ import annotations
 
@@ -29,12 +33,15 @@ GQA_ATTN_ERR_ALIGN = 4
 GQA_ATTN_ERR_SEGMENTS = 5
 GQA_ATTN_ERR_WORKSPACE = 6
 GQA_ATTN_ERR_HIP = 7
+GQA_ATTN_ERR_MASK = 8
+
+CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_END = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
     "attn_fwd", "attn_check_fwd", "attn_fwd_ws", "attn_check_fwd_ws", "attn_fwd_workspace_bytes",
-    "attn_fwd_split_count", "attn_fwd_local", "attn_check_fwd_local", "attn_bwd_workspace_bytes", "attn_bwd",
-    "attn_check_bwd", "attn_bwd_local", "attn_check_bwd_local",
-    "attn_strerror", "attn_last_hip_error",
+    "attn_fwd_split_count", "attn_fwd_local", "attn_check_fwd_local", "attn_fwd_mask", "attn_check_fwd_mask",
+    "attn_bwd_workspace_bytes", "attn_bwd", "attn_check_bwd", "attn_bwd_local", "attn_check_bwd_local",
+    "attn_bwd_mask", "attn_check_bwd_mask", "attn_strerror", "attn_last_hip_error",
 )
 
 _lib = None
@@ -73,10 +80,18 @@ def load_library():
     lib.attn_fwd_local.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, SZ, P]
     lib.attn_check_fwd_local.restype = I
     lib.attn_check_fwd_local.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, SZ]
+    lib.attn_fwd_mask.restype = I
+    lib.attn_fwd_mask.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, SZ, P]
+    lib.attn_check_fwd_mask.restype = I
+    lib.attn_check_fwd_mask.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, SZ]
     lib.attn_bwd_local.restype = I
     lib.attn_bwd_local.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, SZ, P]
     lib.attn_check_bwd_local.restype = I
     lib.attn_check_bwd_local.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, SZ]
+    lib.attn_bwd_mask.restype = I
+    lib.attn_bwd_mask.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, SZ, P]
+    lib.attn_check_bwd_mask.restype = I
+    lib.attn_check_bwd_mask.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, SZ]
     lib.attn_fwd_workspace_bytes.restype = SZ
     lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_fwd_split_count.restype = I
@@ -132,9 +147,11 @@ def _dims(q: torch.Tensor, k: torch.Tensor):
     return B, K, G, T, k.shape[2], H
 
 
-def _check_tensor(name, t, dtype, shape=None):
+def _check_tensor(name, t, dtype, shape=None, device=None):
     if not t.is_cuda:
         raise ValueError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
     if t.dtype != dtype:
         raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
@@ -143,107 +160,138 @@ def _check_tensor(name, t, dtype, shape=None):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
-def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+def causal_mode(causal) -> int:
+    """The C ABI's causal argument: False/0 none, True/1/"top_left" s <= t,
+    2/"end" s <= t + S - T (end-aligned)."""
+    if isinstance(causal, str):
+        modes = {"none": CAUSAL_NONE, "top_left": CAUSAL_TOP_LEFT, "end": CAUSAL_END}
+        if causal not in modes:
+            raise ValueError("causal must be one of %s, got %r" % (sorted(modes), causal))
+        return modes[causal]
+    c = int(causal)
+    if c not in (CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_END):
+        raise GqaAttnError(GQA_ATTN_ERR_MASK, "causal=%r" % (causal,))
+    return c
+
+
+def _check_segments(q_seg, kv_seg, B, T, S, device, where):
+    if (q_seg is None) != (kv_seg is None):
+        raise GqaAttnError(GQA_ATTN_ERR_SEGMENTS, where)
+    if q_seg is not None:
+        _check_tensor("q_seg", q_seg, torch.int32, (B, T), device)
+        _check_tensor("kv_seg", kv_seg, torch.int32, (B, S), device)
+
+
+def _check_workspace(workspace, device):
+    if workspace is not None:
+        _check_tensor("workspace", workspace, torch.uint8, None, device)
+        if workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False,
              q_seg: Optional[torch.Tensor] = None, kv_seg: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
              want_lse: bool = True, split_kv: bool = False,
              workspace: Optional[torch.Tensor] = None,
-             window: Optional[Tuple[int, int]] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+             window: Optional[Tuple[int, int]] = None,
+             prefix: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Forward pass on the current stream. Returns (o, lse).
 
-    split_kv=True calls attn_fwd_ws, which splits the key range across
-    workgroups for shapes that would leave the GPU idle (decoding); the
-    workspace (uint8, at least attn_fwd_workspace_bytes) is allocated when not
-    given. window=(left, right) calls attn_fwd_local: key s is visible to
-    query t only when t - left <= s <= t + right (-1: unbounded side); it
-    splits like split_kv."""
+    causal: see causal_mode(). split_kv=True calls attn_fwd_ws, which splits
+    the key range across workgroups for shapes that would leave the GPU idle
+    (decoding); the workspace (uint8, at least attn_fwd_workspace_bytes) is
+    allocated when not given. window=(left, right) and / or prefix=p call
+    attn_fwd_mask: key s is visible to query t when s < p or t - left <= s <=
+    t + right (-1: unbounded side) and the causal rule holds; it splits like
+    split_kv."""
     B, K, G, T, S, H = _dims(q, k)
+    dev = q.device
     _check_tensor("q", q, torch.bfloat16)
-    _check_tensor("k", k, torch.bfloat16)
-    _check_tensor("v", v, torch.bfloat16, k.shape)
-    if (q_seg is None) != (kv_seg is None):
-        raise GqaAttnError(GQA_ATTN_ERR_SEGMENTS, "attn_fwd")
-    if q_seg is not None:
-        _check_tensor("q_seg", q_seg, torch.int32, (B, T))
-        _check_tensor("kv_seg", kv_seg, torch.int32, (B, S))
+    _check_tensor("k", k, torch.bfloat16, None, dev)
+    _check_tensor("v", v, torch.bfloat16, k.shape, dev)
+    cm = causal_mode(causal)
+    _check_segments(q_seg, kv_seg, B, T, S, dev, "attn_fwd")
     if out is None:
         out = torch.empty_like(q)
-    _check_tensor("out", out, torch.bfloat16, q.shape)
+    _check_tensor("out", out, torch.bfloat16, q.shape, dev)
     if lse is None and want_lse:
-        lse = torch.empty(B, K, G, T, dtype=torch.float32, device=q.device)
+        lse = torch.empty(B, K, G, T, dtype=torch.float32, device=dev)
     if lse is not None:
-        _check_tensor("lse", lse, torch.float32, (B, K, G, T))
-    if window is not None:
+        _check_tensor("lse", lse, torch.float32, (B, K, G, T), dev)
+    masked = window is not None or prefix != 0
+    if masked or split_kv:
         wsb = attn_fwd_workspace_bytes(B, K, G, T, S, H)
         if workspace is None and wsb > 0:
-            workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
-        if workspace is not None:
-            _check_tensor("workspace", workspace, torch.uint8)
-        rc = load_library().attn_fwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg),
-                                           _ptr(kv_seg), B, K, G, T, S, H, int(bool(causal)), int(window[0]),
-                                           int(window[1]), _ptr(workspace),
-                                           0 if workspace is None else workspace.numel(), _stream_handle(q.device))
+            workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        _check_workspace(workspace, dev)
+    wsp, wsn = _ptr(workspace), 0 if workspace is None else workspace.numel()
+    if masked:
+        wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+        rc = load_library().attn_fwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg),
+                                          _ptr(kv_seg), B, K, G, T, S, H, cm, wl, wr, int(prefix), wsp, wsn,
+                                          _stream_handle(dev))
         if rc != GQA_ATTN_OK:
-            raise GqaAttnError(rc, "attn_fwd_local")
+            raise GqaAttnError(rc, "attn_fwd_mask")
         return out, lse
     if split_kv:
-        wsb = attn_fwd_workspace_bytes(B, K, G, T, S, H)
-        if workspace is None and wsb > 0:
-            workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
-        if workspace is not None:
-            _check_tensor("workspace", workspace, torch.uint8)
         rc = load_library().attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg), _ptr(kv_seg),
-                                        B, K, G, T, S, H, int(bool(causal)), _ptr(workspace),
-                                        0 if workspace is None else workspace.numel(), _stream_handle(q.device))
+                                        B, K, G, T, S, H, cm, wsp, wsn, _stream_handle(dev))
         if rc != GQA_ATTN_OK:
             raise GqaAttnError(rc, "attn_fwd_ws")
         return out, lse
     rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg), _ptr(kv_seg),
-                                 B, K, G, T, S, H, int(bool(causal)), _stream_handle(q.device))
+                                 B, K, G, T, S, H, cm, _stream_handle(dev))
     if rc != GQA_ATTN_OK:
         raise GqaAttnError(rc, "attn_fwd")
     return out, lse
 
 
-def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
-             do: torch.Tensor, *, causal: bool = False, q_seg: Optional[torch.Tensor] = None,
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor], lse: torch.Tensor,
+             do: torch.Tensor, *, causal=False, q_seg: Optional[torch.Tensor] = None,
              kv_seg: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
              dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None, window: Optional[Tuple[int, int]] = None):
+             workspace: Optional[torch.Tensor] = None, window: Optional[Tuple[int, int]] = None,
+             prefix: int = 0):
     """Backward pass on the current stream. Returns (dq, dk, dv) in fp32.
 
     `o` (the forward output) may be None: the library does not read it.
-    window=(left, right) calls attn_bwd_local with that local window."""
+    window / prefix call attn_bwd_mask with the forward's mask. Every tensor
+    is checked (device, dtype, shape, contiguity) before anything is
+    launched."""
     B, K, G, T, S, H = _dims(q, k)
-    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
-        _check_tensor(name, t, torch.bfloat16)
-    if o is not None:
-        _check_tensor("o", o, torch.bfloat16, q.shape)
-    _check_tensor("lse", lse, torch.float32, (B, K, G, T))
-    if (q_seg is None) != (kv_seg is None):
-        raise GqaAttnError(GQA_ATTN_ERR_SEGMENTS, "attn_bwd")
     dev = q.device
+    _check_tensor("q", q, torch.bfloat16)
+    _check_tensor("k", k, torch.bfloat16, None, dev)
+    _check_tensor("v", v, torch.bfloat16, k.shape, dev)
+    _check_tensor("do", do, torch.bfloat16, q.shape, dev)
+    if o is not None:
+        _check_tensor("o", o, torch.bfloat16, q.shape, dev)
+    _check_tensor("lse", lse, torch.float32, (B, K, G, T), dev)
+    cm = causal_mode(causal)
+    _check_segments(q_seg, kv_seg, B, T, S, dev, "attn_bwd")
     dq = torch.empty(q.shape, dtype=torch.float32, device=dev) if dq is None else dq
     dk = torch.empty(k.shape, dtype=torch.float32, device=dev) if dk is None else dk
     dv = torch.empty(v.shape, dtype=torch.float32, device=dev) if dv is None else dv
-    _check_tensor("dq", dq, torch.float32, q.shape)
-    _check_tensor("dk", dk, torch.float32, k.shape)
-    _check_tensor("dv", dv, torch.float32, k.shape)
+    _check_tensor("dq", dq, torch.float32, q.shape, dev)
+    _check_tensor("dk", dk, torch.float32, k.shape, dev)
+    _check_tensor("dv", dv, torch.float32, k.shape, dev)
     wsb = attn_bwd_workspace_bytes(B, K, G, T, S, H)
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    if window is not None:
-        rc = load_library().attn_bwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                                           _ptr(dk), _ptr(dv), _ptr(q_seg), _ptr(kv_seg), B, K, G, T, S, H,
-                                           int(bool(causal)), int(window[0]), int(window[1]), _ptr(workspace),
-                                           workspace.numel() * workspace.element_size(), _stream_handle(dev))
+    _check_workspace(workspace, dev)
+    if window is not None or prefix != 0:
+        wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+        rc = load_library().attn_bwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(q_seg), _ptr(kv_seg), B, K, G, T, S, H, cm,
+                                          wl, wr, int(prefix), _ptr(workspace), workspace.numel(),
+                                          _stream_handle(dev))
         if rc != GQA_ATTN_OK:
-            raise GqaAttnError(rc, "attn_bwd_local")
+            raise GqaAttnError(rc, "attn_bwd_mask")
         return dq, dk, dv
     rc = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                                 _ptr(dv), _ptr(q_seg), _ptr(kv_seg), B, K, G, T, S, H, int(bool(causal)),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream_handle(dev))
+                                 _ptr(dv), _ptr(q_seg), _ptr(kv_seg), B, K, G, T, S, H, cm,
+                                 _ptr(workspace), workspace.numel(), _stream_handle(dev))
     if rc != GQA_ATTN_OK:
         raise GqaAttnError(rc, "attn_bwd")
     return dq, dk, dv

@@ -31,6 +31,44 @@ int check_common(const void *q, const void *k, const void *v, const void *o,
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Mask arguments: causal 0 (none), 1 (top-left) or 2 (end-aligned); window
+// sides -1 (unbounded) or >= 0; prefix >= 0.
+int check_mask(int causal, int wl, int wr, int prefix) {
+    if (causal < 0 || causal > 2) return GQA_ATTN_ERR_MASK;
+    if (wl < -1 || wr < -1 || prefix < 0) return GQA_ATTN_ERR_MASK;
+    return GQA_ATTN_OK;
+}
+
+// The lazy mask of a call in the kernels' terms (gqa::MaskSpec): a key is
+// visible when s < prefix or t - wl <= s <= t + wr. A causal diagonal s <= t +
+// coff (coff = 0 top-left, S - T end-aligned) caps the right side. Sides that
+// bound nothing for these sizes (t - wl <= 0 and t + wr >= S - 1 for every
+// query) become kNoWindow, so that huge caller values cannot overflow and a
+// mask that hides nothing takes the unmasked kernels.
+gqa::MaskSpec resolve_mask(int causal, int wl, int wr, int prefix, int T, int S) {
+    gqa::MaskSpec m;
+    m.wl = (wl < 0 || wl >= T - 1) ? gqa::kNoWindow : wl;
+    m.wr = (wr < 0 || wr >= S - 1) ? gqa::kNoWindow : wr;
+    m.causal = causal != 0;
+    m.coff = causal == 2 ? S - T : 0;
+    if (m.causal) {
+        if (m.coff >= S - 1 && m.wr == gqa::kNoWindow) {
+            m.causal = 0;  // every query sees every key (e.g. end-aligned, T = 1)
+            m.coff = 0;
+        } else {
+            m.wr = m.wr < m.coff ? m.wr : m.coff;
+        }
+    }
+    m.prefix = prefix < S ? prefix : S;
+    if (m.prefix == S) {  // every key is a prefix key: nothing is hidden
+        m.causal = 0;
+        m.coff = 0;
+        m.wl = m.wr = gqa::kNoWindow;
+        m.prefix = 0;
+    }
+    return m;
+}
+
 int hip_fail(hipError_t e) {
     g_last_hip_error = (int)e;
     return GQA_ATTN_ERR_HIP;
@@ -43,8 +81,9 @@ extern "C" {
 int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal) {
-    (void)causal;
     int rc = check_common(q, k, v, o, q_seg, kv_seg, B, K, G, T, S, H);
+    if (rc) return rc;
+    rc = check_mask(causal, -1, -1, 0);
     if (rc) return rc;
     if (lse && !aligned(lse, 4)) return GQA_ATTN_ERR_ALIGN;
     return GQA_ATTN_OK;
@@ -54,12 +93,12 @@ int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, c
 // workspace: partial outputs first, then partial lse).
 static int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                    const int32_t *q_seg, const int32_t *kv_seg,
-                   int B, int K, int G, int T, int S, int H, int causal, int wl, int wr,
+                   int B, int K, int G, int T, int S, int H, const gqa::MaskSpec &m,
                    gqa::SplitPlan plan, void *workspace, void *stream) {
     const gqa::FwdConfig cfg =
         plan.n_splits > 1 ? gqa::fwd_config_split(G, T, H)
-        : (H == 256 && gqa::fwd_pp256_applies(G, T, S, causal, q_seg != nullptr, wl, wr)) ? gqa::fwd_config_pp256()
-                                                                                          : gqa::fwd_config(G, T, H);
+        : (H == 256 && gqa::fwd_pp256_applies(G, T, S, m, q_seg != nullptr)) ? gqa::fwd_config_pp256()
+                                                                             : gqa::fwd_config(G, T, H);
     gqa::FwdArgs a;
     a.q = (const __bf16 *)q;
     a.k = (const __bf16 *)k;
@@ -69,9 +108,11 @@ static int run_fwd(const void *q, const void *k, const void *v, void *o, float *
     a.q_seg = q_seg;
     a.kv_seg = kv_seg;
     a.B = B, a.K = K, a.G = G, a.T = T, a.S = S;
-    a.causal = causal ? 1 : 0;
-    a.wl = wl;
-    a.wr = wr;
+    a.causal = m.causal;
+    a.coff = m.coff;
+    a.wl = m.wl;
+    a.wr = m.wr;
+    a.prefix = m.prefix;
     a.gw = cfg.gw;
     a.bq = cfg.bq;
     a.n_gsplit = G / cfg.gw;
@@ -96,8 +137,8 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int K, int G, int T, int S, int H, int causal, void *stream) {
     int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal);
     if (rc) return rc;
-    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, -1, -1, gqa::SplitPlan{1, 0}, nullptr,
-                   stream);
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, resolve_mask(causal, -1, -1, 0, T, S),
+                   gqa::SplitPlan{1, 0}, nullptr, stream);
 }
 
 size_t attn_fwd_workspace_bytes(int B, int K, int G, int T, int S, int H) {
@@ -128,7 +169,28 @@ int attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse
                 void *workspace, size_t workspace_bytes, void *stream) {
     int rc = attn_check_fwd_ws(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace, workspace_bytes);
     if (rc) return rc;
-    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, -1, -1,
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, resolve_mask(causal, -1, -1, 0, T, S),
+                   gqa::fwd_split_plan(B, K, G, T, S, H), workspace, stream);
+}
+
+int attn_check_fwd_mask(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const int32_t *q_seg, const int32_t *kv_seg,
+                        int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                        int prefix, const void *workspace, size_t workspace_bytes) {
+    int rc = attn_check_fwd_ws(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace, workspace_bytes);
+    if (rc) return rc;
+    return check_mask(causal, window_left, window_right, prefix);
+}
+
+int attn_fwd_mask(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int32_t *q_seg, const int32_t *kv_seg,
+                  int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right, int prefix,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = attn_check_fwd_mask(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left,
+                                 window_right, prefix, workspace, workspace_bytes);
+    if (rc) return rc;
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H,
+                   resolve_mask(causal, window_left, window_right, prefix, T, S),
                    gqa::fwd_split_plan(B, K, G, T, S, H), workspace, stream);
 }
 
@@ -136,19 +198,16 @@ int attn_check_fwd_local(const void *q, const void *k, const void *v, const void
                          const int32_t *q_seg, const int32_t *kv_seg,
                          int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                          const void *workspace, size_t workspace_bytes) {
-    if (window_left < -1 || window_right < -1) return GQA_ATTN_ERR_SHAPE;
-    return attn_check_fwd_ws(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace, workspace_bytes);
+    return attn_check_fwd_mask(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left, window_right,
+                               0, workspace, workspace_bytes);
 }
 
 int attn_fwd_local(const void *q, const void *k, const void *v, void *o, float *lse,
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                    void *workspace, size_t workspace_bytes, void *stream) {
-    int rc = attn_check_fwd_local(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left, window_right,
-                                  workspace, workspace_bytes);
-    if (rc) return rc;
-    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left, window_right,
-                   gqa::fwd_split_plan(B, K, G, T, S, H), workspace, stream);
+    return attn_fwd_mask(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left, window_right, 0,
+                         workspace, workspace_bytes, stream);
 }
 
 int attn_fwd_split_count(int B, int K, int G, int T, int S, int H) {
@@ -168,8 +227,9 @@ int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, c
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal,
                    const void *workspace, size_t workspace_bytes) {
-    (void)causal;
     int rc = check_common(q, k, v, dq, q_seg, kv_seg, B, K, G, T, S, H);
+    if (rc) return rc;
+    rc = check_mask(causal, -1, -1, 0);
     if (rc) return rc;
     if (!lse || !dO || !dq || !dk || !dv) return GQA_ATTN_ERR_NULL;
     if (o && !aligned(o, 16)) return GQA_ATTN_ERR_ALIGN;
@@ -183,7 +243,7 @@ int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, c
 static int run_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
                    const void *dO, float *dq, float *dk, float *dv,
                    const int32_t *q_seg, const int32_t *kv_seg,
-                   int B, int K, int G, int T, int S, int H, int causal, int wl, int wr,
+                   int B, int K, int G, int T, int S, int H, const gqa::MaskSpec &m,
                    void *workspace, void *stream) {
     gqa::BwdArgs a;
     a.q = (const __bf16 *)q;
@@ -199,9 +259,11 @@ static int run_bwd(const void *q, const void *k, const void *v, const void *o, c
     a.q_seg = q_seg;
     a.kv_seg = kv_seg;
     a.B = B, a.K = K, a.G = G, a.T = T, a.S = S;
-    a.causal = causal ? 1 : 0;
-    a.wl = wl;
-    a.wr = wr;
+    a.causal = m.causal;
+    a.coff = m.coff;
+    a.wl = m.wl;
+    a.wr = m.wr;
+    a.prefix = m.prefix;
     hipError_t e = gqa::launch_bwd(a, H, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return GQA_ATTN_OK;
@@ -215,8 +277,31 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
     int rc = attn_check_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal,
                             workspace, workspace_bytes);
     if (rc) return rc;
-    return run_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, -1, -1, workspace,
-                   stream);
+    return run_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H,
+                   resolve_mask(causal, -1, -1, 0, T, S), workspace, stream);
+}
+
+int attn_check_bwd_mask(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const void *dO, const float *dq, const float *dk, const float *dv,
+                        const int32_t *q_seg, const int32_t *kv_seg,
+                        int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                        int prefix, const void *workspace, size_t workspace_bytes) {
+    int rc = attn_check_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace,
+                            workspace_bytes);
+    if (rc) return rc;
+    return check_mask(causal, window_left, window_right, prefix);
+}
+
+int attn_bwd_mask(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                  const void *dO, float *dq, float *dk, float *dv,
+                  const int32_t *q_seg, const int32_t *kv_seg,
+                  int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right, int prefix,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = attn_check_bwd_mask(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal,
+                                 window_left, window_right, prefix, workspace, workspace_bytes);
+    if (rc) return rc;
+    return run_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H,
+                   resolve_mask(causal, window_left, window_right, prefix, T, S), workspace, stream);
 }
 
 int attn_check_bwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -224,9 +309,8 @@ int attn_check_bwd_local(const void *q, const void *k, const void *v, const void
                          const int32_t *q_seg, const int32_t *kv_seg,
                          int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                          const void *workspace, size_t workspace_bytes) {
-    if (window_left < -1 || window_right < -1) return GQA_ATTN_ERR_SHAPE;
-    return attn_check_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace,
-                          workspace_bytes);
+    return attn_check_bwd_mask(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal,
+                               window_left, window_right, 0, workspace, workspace_bytes);
 }
 
 int attn_bwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -234,11 +318,8 @@ int attn_bwd_local(const void *q, const void *k, const void *v, const void *o, c
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                    void *workspace, size_t workspace_bytes, void *stream) {
-    int rc = attn_check_bwd_local(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal,
-                                  window_left, window_right, workspace, workspace_bytes);
-    if (rc) return rc;
-    return run_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left,
-                   window_right, workspace, stream);
+    return attn_bwd_mask(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left,
+                         window_right, 0, workspace, workspace_bytes, stream);
 }
 
 const char *attn_strerror(int code) {
@@ -251,8 +332,13 @@ const char *attn_strerror(int code) {
         case GQA_ATTN_ERR_HEADDIM: return "unsupported head dimension H (supported: 64, 128, 256)";
         case GQA_ATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte alignment, segment ids 4-byte)";
         case GQA_ATTN_ERR_SEGMENTS: return "q_seg and kv_seg must both be given or both be NULL";
-        case GQA_ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
+        case GQA_ATTN_ERR_WORKSPACE:
+            return "workspace is NULL or smaller than the call's attn_fwd_workspace_bytes() / "
+                   "attn_bwd_workspace_bytes()";
         case GQA_ATTN_ERR_HIP: return "a HIP launch failed (see attn_last_hip_error)";
+        case GQA_ATTN_ERR_MASK:
+            return "invalid mask: causal must be 0, 1 (top-left) or 2 (end-aligned), window sides -1 or >= 0, "
+                   "prefix >= 0";
         default: return "unknown error code";
     }
 }

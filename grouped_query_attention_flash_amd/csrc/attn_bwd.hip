@@ -161,11 +161,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
     }
 
     // query tiles that can see the block's keys: t in [s - R, s + L] for the
-    // window sides L, R (causal: R = 0)
-    const int WL = win_left(a.wl), WR = win_right(a.wr, a.causal);
+    // band sides L, R, or every query for a block that starts in the prefix
+    const int WL = a.wl, WR = a.wr, PFX = a.prefix;
     const int n_qt_all = (T + BQ - 1) / BQ;
-    const int qt_begin = min(n_qt_all, max(0, s0_wg - WR) / BQ);
-    const int n_qt = max(qt_begin, min(n_qt_all, (s0_wg + 32 * NW - 1 + WL) / BQ + 1));  // end of the tile range
+    const bool blk_pfx = s0_wg < PFX;
+    const int qt_begin = blk_pfx ? 0 : min(n_qt_all, max(0, s0_wg - WR) / BQ);
+    const int n_qt = blk_pfx ? n_qt_all
+                             : max(qt_begin, min(n_qt_all, (s0_wg + 32 * NW - 1 + WL) / BQ + 1));  // end of the tile range
     const int n_steps = G * (n_qt - qt_begin);  // (g, query tile) pairs, g outer
 
     auto q_ids = [&](int qt, int &qmin, int &qmax) {
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
         if (st_next < n_steps) load_step(st_next);
 
         const int t0 = (qt_begin + st % (n_qt - qt_begin)) * BQ;
-        bool run = wave_active && t0 + BQ - 1 >= s_w - WR && t0 <= s_w + 31 + WL;
+        bool run = wave_active && (s_w < PFX || (t0 + BQ - 1 >= s_w - WR && t0 <= s_w + 31 + WL));
         bool seg_mask = false;
         if (run && segs) {
             int qmin, qmax;
@@ -271,8 +273,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
                     pacc = mfma32x32x16(*(const bf16x8 *)(drow + off), vf[ks], pacc);
                 }
             }
-            const bool need_mask = (s_w + 31 > t0 + WR) || (s_w < t0 + BQ - 1 - WL) || (s_w + 32 > S) ||
-                                   (t0 + BQ > T) || seg_mask;
+            // keys wholly inside the prefix need no band mask
+            const bool band_mask = s_w + 31 >= PFX && ((s_w + 31 > t0 + WR) || (s_w < t0 + BQ - 1 - WL));
+            const bool need_mask = band_mask || (s_w + 32 > S) || (t0 + BQ > T) || seg_mask;
             // P = exp2(S log2e - lse log2e); dS = P (dP - D)
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++) {
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
                     float x = sacc[r];
                     if (need_mask) {
                         const int t = t0 + r0 + e;
-                        bool vis = k_valid && t < T && s <= t + WR && s >= t - WL;
+                        bool vis = k_valid && t < T && ((s <= t + WR && s >= t - WL) || s < PFX);
                         if (segs && vis) vis = qsb[t] == my_kid;
                         if (!vis) x = -INFINITY;
                     }
@@ -403,11 +406,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     // steps: (g, query tile) pairs, g outer; causal: tiles holding some t >= s0_wg
     // query tiles that can see the block's keys: t in [s - R, s + L] for the
-    // window sides L, R (causal: R = 0); qt_end is exclusive
-    const int WL = win_left(a.wl), WR = win_right(a.wr, CAUSAL);
+    // band sides L, R, or all of them for a block that starts in the prefix;
+    // qt_end is exclusive
+    const int WL = a.wl, WR = a.wr;
     const int n_qt = (T + BQ - 1) / BQ;
-    const int qt_begin = min(n_qt, max(0, s0_wg - WR) / BQ);
-    const int qt_end = max(qt_begin, min(n_qt, (s0_wg + 32 * NW - 1 + WL) / BQ + 1));
+    const bool blk_pfx = s0_wg < a.prefix;
+    const int qt_begin = blk_pfx ? 0 : min(n_qt, max(0, s0_wg - WR) / BQ);
+    const int qt_end = blk_pfx ? n_qt : max(qt_begin, min(n_qt, (s0_wg + 32 * NW - 1 + WL) / BQ + 1));
     const int nq = qt_end - qt_begin;
     const int n_steps = G * nq;
 
@@ -489,8 +494,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // visible iff u = t - s + R lies in [0, min(L + R + 1, T - s + R)), which
     // covers the window, causal masking (R = 0) and t < T with one unsigned
     // compare per element. The bound is clamped at 0: a key that no query can
-    // see (past S, or past T - 1 + R) gets bound 0.
-    const unsigned vis_bound = k_valid ? (unsigned)max(0, min(WL + WR + 1, T - s + WR)) : 0u;
+    // see (past S, or past T - 1 + R) gets bound 0. A prefix key is visible to
+    // every query: its lane takes unbounded sides (LL = RR = kNoWindow), so
+    // only t < T remains.
+    const bool k_pfx = s < a.prefix;
+    const int LL = k_pfx ? kNoWindow : WL, RR = k_pfx ? kNoWindow : WR;
+    const unsigned vis_bound = k_valid ? (unsigned)max(0, min(LL + RR + 1, T - s + RR)) : 0u;
     // lse and D of the lane's 16 query rows of a step
     auto read_ld = [&](int stage, f32x4 (&l4s)[4], f32x4 (&d4s)[4]) {
 #pragma unroll
@@ -501,7 +510,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     };
     auto weights = [&](int t0, const f32x4 (&l4s)[4], const f32x4 (&d4s)[4], const f32x16 &sacc, const f32x16 &pacc,
                        bf16x8 (&pf)[2], bf16x8 (&sf)[2]) {
-        const int tb = t0 + 4 * c - s + WR;
+        const int tb = t0 + 4 * c - s + RR;
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
             const f32x4 l4 = l4s[q4];
@@ -576,7 +585,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #endif
             const int row_ld = row_of(c_ld);
             advance(c_ld);
-            const int tb = c_w.qt * BQ + 4 * c - s + WR;
+            const int tb = c_w.qt * BQ + 4 * c - s + RR;
             advance(c_w);
             auto read_op = [&](int m) -> bf16x8 {
                 if (m < NQ) {
@@ -769,12 +778,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
         w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
     }
 
-    // key tiles: the window (causal: R = 0) bounds them by the block's first
-    // and last query
-    const int WL = win_left(a.wl), WR = win_right(a.wr, a.causal);
+    // key tiles: the band of the block's first and last query, and the
+    // prefix keys s < PFX
+    const int WL = a.wl, WR = a.wr, PFX = a.prefix;
     const int n_tiles = (S + BKV - 1) / BKV;
-    const int j_end = min(n_tiles, (min(min(t0 + bq, T) - 1 + WR, S - 1)) / BKV + 1);
-    const int j_begin = t0 - WL > 0 ? (t0 - WL) / BKV : 0;
+    const int t_last = min(t0 + bq, T) - 1;
+    const int s_last = max(min(t_last + WR, S - 1), PFX - 1);
+    const int j_end = s_last < 0 ? 0 : min(n_tiles, s_last / BKV + 1);
+    const int j_begin = (PFX > 0 || t0 - WL <= 0) ? 0 : (t0 - WL) / BKV;
 
     auto tile_ids = [&](int j, int &kmin, int &kmax) {
         const int ss = j * BKV + lane;
@@ -783,12 +794,19 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
         kmin = wave_min_i(ok ? id : INT_MAX);
         kmax = wave_max_i(ok ? id : INT_MIN);
     };
+    // next tile at or after j inside the prefix or the block's band, and
+    // (segment ids) sharing an id range with the block
     auto next_tile = [&](int j) {
-        if (!segs) return j;
+        if (!segs && PFX == 0) return j;
         for (; j < j_end; j++) {
-            int kmin, kmax;
-            tile_ids(j, kmin, kmax);
-            if (!(kmax < wg_qmin || kmin > wg_qmax)) break;
+            const int s0 = j * BKV;
+            if (!(s0 < PFX || (s0 + BKV - 1 >= t0 - WL && s0 <= t_last + WR))) continue;
+            if (segs) {
+                int kmin, kmax;
+                tile_ids(j, kmin, kmax);
+                if (kmax < wg_qmin || kmin > wg_qmax) continue;
+            }
+            break;
         }
         return j;
     };
@@ -831,7 +849,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
         if (jn < j_end) load_tile(jn);
 
         const int s0 = j * BKV;
-        bool run = wave_active && s0 <= tmax_w + WR && s0 + BKV - 1 >= tmin_w - WL;
+        bool run = wave_active && (s0 < PFX || (s0 <= tmax_w + WR && s0 + BKV - 1 >= tmin_w - WL));
         bool seg_mask = false;
         if (run && segs) {
             int kmin, kmax;
@@ -854,8 +872,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
                     pacc[mb] = mfma32x32x16(*(const bf16x8 *)(sv + off), df[ks], pacc[mb]);
                 }
             }
-            const bool need_mask =
-                (s0 + BKV - 1 > tmin_w + WR) || (s0 < tmax_w - WL) || (s0 + BKV > S) || seg_mask;
+            // a tile wholly inside the prefix needs no band mask
+            const bool band_mask = s0 + BKV - 1 >= PFX && ((s0 + BKV - 1 > tmin_w + WR) || (s0 < tmax_w - WL));
+            const bool need_mask = band_mask || (s0 + BKV > S) || seg_mask;
 #pragma unroll
             for (int mb = 0; mb < MB; mb++)
 #pragma unroll
@@ -863,7 +882,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
                     float x = sacc[mb][r];
                     if (need_mask) {
                         const int ss = s0 + 32 * mb + acc_row(r, c);
-                        bool vis = ss < S && ss <= t + WR && ss >= t - WL;
+                        bool vis = ss < S && ((ss <= t + WR && ss >= t - WL) || ss < PFX);
                         if (segs && vis) vis = kvs[ss] == my_qid;
                         if (!vis) x = -INFINITY;
                     }
@@ -989,9 +1008,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
     // key tiles j0 .. j0 + n_t - 1: a left window (causal only, WIN) starts the
     // block at the tile holding its first query's first visible key
-    const int WL = win_left(a.wl);
+    const int WL = a.wl;
     const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
-    const int n_t = (CAUSAL ? qb + 1 : S / BKV) - j0;
+    // causal: the block's diagonal tile qb + coff / BKV comes last
+    const int n_t = (CAUSAL ? qb + 1 + a.coff / BKV : S / BKV) - j0;
 
     // global -> LDS: group A loads K tiles, group B V tiles; wave gwv of a group
     // issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat the row's
@@ -1039,7 +1059,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     };
     // V phase: lane (n, c) holds keys s0 + 32 mb + acc_row(r, c) of query t
     auto v_phase = [&](int s0, auto masked) {
-        const int lim = t - s0 - 4 * c;                         // last visible key offset (causal)
+        const int lim = t + a.coff - s0 - 4 * c;                // last visible key offset (causal)
         const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;  // first visible key offset (window)
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
@@ -1161,9 +1181,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
     // key tiles j0 .. j0 + n_t - 1: a left window (causal only, WIN) starts the
     // block at the tile holding its first query's first visible key
-    const int WL = win_left(a.wl);
+    const int WL = a.wl;
     const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
-    const int n_t = (CAUSAL ? (t0 + bq) / BKV : S / BKV) - j0;
+    // causal: up to the tile of the block's last query's diagonal
+    const int n_t = (CAUSAL ? (t0 + bq + a.coff) / BKV : S / BKV) - j0;
 
     // global -> LDS: group A loads K tiles, group B V tiles; wave gwv of a group
     // issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat the row's
@@ -1237,8 +1258,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     auto v_phase = [&](int s0) {
         // some key after some query of the wave, or (WIN) before some query's
         // first visible key t - WL
-        const bool masked = (CAUSAL && s0 + BKV - 1 > t_w) || (WIN && s0 < t_w + 31 - WL);
-        const int lim = t - s0 - 4 * c;                         // last visible key offset (causal)
+        const bool masked = (CAUSAL && s0 + BKV - 1 > t_w + a.coff) || (WIN && s0 < t_w + 31 - WL);
+        const int lim = t + a.coff - s0 - 4 * c;                // last visible key offset (causal)
         const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;  // first visible key offset (window)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
@@ -1299,14 +1320,17 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     // per-tile barriers and loop overhead of the dQ pass's 32).
     constexpr int BKV_D = H <= 128 && GQA_BWD_D_BKV > BKV_DQ ? GQA_BWD_D_BKV : BKV_DQ;
     bool delta_done = false;
+    const MaskSpec m{a.causal, a.coff, a.wl, a.wr, a.prefix};
+    // causal: the diagonal offset a whole number of tiles, T + coff == S
+    auto diag_tiles = [&](int bkv) { return !a.causal || (a.coff >= 0 && a.coff % bkv == 0 && a.T + a.coff == a.S); };
     if constexpr (GQA_BWD_DELTA_PP && H <= 128 && NW_DQ == 8) {
         // dense shapes: the ping-pong D pass (query blocks of 64 rows x gw heads)
         constexpr int BKV_PP = 64;
-        const bool dense = a.q_seg == nullptr && !windowed(a.wl, a.wr, a.causal) && gw * bq == 256 &&
-                           a.T % bq == 0 && a.S % BKV_PP == 0 && (!a.causal || (a.T == a.S && bq == BKV_PP));
+        const bool shape = a.q_seg == nullptr && gw * bq == 256 && a.T % bq == 0 && a.S % BKV_PP == 0 &&
+                           diag_tiles(BKV_PP) && (!a.causal || bq == BKV_PP);
+        const bool dense = shape && !mask_extra(m);
         // a causal left window on an otherwise dense shape
-        const bool dense_win = a.q_seg == nullptr && a.causal && a.wl >= 0 && gw * bq == 256 && a.T % bq == 0 &&
-                               a.S % BKV_PP == 0 && a.T == a.S && bq == BKV_PP;
+        const bool dense_win = shape && mask_left_window_only(m);
         if (dense) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, true>), qgrid, dim3(512), 0, stream, a, gw,
@@ -1329,11 +1353,10 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     bool dq_done = false;
     if constexpr (GQA_BWD_DQ_PP && H <= 128 && NW_DQ == 8) {
         // dense shapes: dQ on the ping-pong kernel (32-key tiles)
-        const bool dense = a.q_seg == nullptr && !windowed(a.wl, a.wr, a.causal) && gw * bq == 256 &&
-                           a.T % bq == 0 && a.S % 32 == 0 && (!a.causal || a.T == a.S);
+        const bool shape = a.q_seg == nullptr && gw * bq == 256 && a.T % bq == 0 && a.S % 32 == 0 && diag_tiles(32);
+        const bool dense = shape && !mask_extra(m);
         // a causal left window on an otherwise dense shape
-        const bool dense_win = a.q_seg == nullptr && a.causal && a.wl >= 0 && gw * bq == 256 && a.T % bq == 0 &&
-                               a.S % 32 == 0 && a.T == a.S;
+        const bool dense_win = shape && mask_left_window_only(m);
         if (dense) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, true>), qgrid, dim3(512), 0, stream, a, gw, bq, n_gsplit,

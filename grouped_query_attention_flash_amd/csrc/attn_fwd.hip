@@ -110,8 +110,9 @@ __device__ __forceinline__ void dense_schedule(std::integer_sequence<int, P...>,
     (sched_slot<M, N_QK, N_MFMA, D, VALU_PER>(), ...);
 }
 
-// DENSE: no segment ids, whole key tiles (S % BKV == 0) and, when causal,
-// T == S with one query block per key tile (bq == BKV): only the last tile of
+// DENSE: no segment ids, window or prefix, whole key tiles (S % BKV == 0)
+// and, when causal, T + coff == S with one query block per key tile (bq ==
+// BKV) and the diagonal offset a whole number of tiles: only the last tile of
 // a block (its diagonal) needs an element mask, and the key loop has scalar
 // control and a branch-free steady state.
 template <int H, int BKV, int NW, int WAVES_PER_SIMD, bool CAUSAL, bool DENSE>
@@ -203,12 +204,14 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
     }
 
-    // ---- key-tile range: the window (causal: R = 0) bounds it on both sides
-    // by the block's first and last query; a split covers its own range
-    const int WL = win_left(a.wl), WR = win_right(a.wr, CAUSAL);
+    // ---- key-tile range: the band [t - WL, t + WR] of the block's first and
+    // last query, and the prefix keys s < PFX; a split covers its own range
+    const int WL = a.wl, WR = a.wr, PFX = a.prefix;
     const int n_tiles = (S + BKV - 1) / BKV;
-    int j_end = min(n_tiles, (min(min(t0 + a.bq, T) - 1 + WR, S - 1)) / BKV + 1);
-    int j_begin = t0 - WL > 0 ? (t0 - WL) / BKV : 0;
+    const int t_last = min(t0 + a.bq, T) - 1;  // the block's last query
+    const int s_last = max(min(t_last + WR, S - 1), PFX - 1);
+    int j_end = s_last < 0 ? 0 : min(n_tiles, s_last / BKV + 1);
+    int j_begin = (PFX > 0 || t0 - WL <= 0) ? 0 : (t0 - WL) / BKV;
     if (!DENSE && a.o_part) {
         j_begin = max(j_begin, split * a.split_tiles);
         j_end = min(j_end, split * a.split_tiles + a.split_tiles);
@@ -254,20 +257,26 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         kmin = wave_min_i(ok ? id : INT_MAX);
         kmax = wave_max_i(ok ? id : INT_MIN);
     };
-    // next tile at or after j that some query of the workgroup can see
+    // next tile at or after j that some query of the workgroup can see: inside
+    // the prefix or the block's band, and (segment ids) sharing an id range
     auto next_tile = [&](int j) {
-        if (!segs) return j;
+        if (!segs && PFX == 0) return j;
         for (; j < j_end; j++) {
-            int kmin, kmax;
-            tile_ids(j, kmin, kmax);
-            if (!(kmax < wg_qmin || kmin > wg_qmax)) break;
+            const int s0 = j * BKV;
+            if (!(s0 < PFX || (s0 + BKV - 1 >= t0 - WL && s0 <= t_last + WR))) continue;
+            if (segs) {
+                int kmin, kmax;
+                tile_ids(j, kmin, kmax);
+                if (kmax < wg_qmin || kmin > wg_qmax) continue;
+            }
+            break;
         }
         return j;
     };
     // does this wave compute tile j, and does it need an element mask there
     auto tile_flags = [&](int j, bool &run, bool &mask) {
         const int s0 = j * BKV;
-        run = j < j_end && wave_active && s0 <= tmax_w + WR && s0 + BKV - 1 >= tmin_w - WL;
+        run = j < j_end && wave_active && (s0 < PFX || (s0 <= tmax_w + WR && s0 + BKV - 1 >= tmin_w - WL));
         bool seg_mask = false;
         if (run && segs) {
             int kmin, kmax;
@@ -275,7 +284,9 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
             if (kmax < w_qmin || kmin > w_qmax) run = false;
             seg_mask = !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
         }
-        mask = (s0 + BKV - 1 > tmin_w + WR) || (s0 < tmax_w - WL) || (s0 + BKV > S) || seg_mask;
+        // a tile wholly inside the prefix needs no band mask
+        const bool band_mask = s0 + BKV - 1 >= PFX && ((s0 + BKV - 1 > tmin_w + WR) || (s0 < tmax_w - WL));
+        mask = band_mask || (s0 + BKV > S) || seg_mask;
     };
 
     // One tile of K (row stride L::KRS chunks) or V (L::VRS) into LDS, straight
@@ -365,12 +376,13 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     auto mask_tile = [&](f32x16 (&sacc)[MB], int s0) {
         const int lim = min(t + WR, S - 1) - s0 - 4 * c;  // last visible key offset
         const int first = t - WL - s0 - 4 * c;           // first visible key offset
+        const int plim = PFX - s0 - 4 * c;               // offsets below it are prefix keys (PFX <= S)
 #pragma unroll
         for (int mb = 0; mb < MB; mb++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int off = 32 * mb + 8 * (r >> 2) + (r & 3);
-                bool vis = off <= lim && off >= first;
+                bool vis = (off <= lim && off >= first) || off < plim;
                 if (segs && vis) vis = (kv_lds ? s_kvid[s0 + off + 4 * c - kv_base] : kvs[s0 + off + 4 * c]) == my_qid;
                 if (!vis) sacc[mb][r] = -INFINITY;
             }
@@ -463,7 +475,8 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         // the other halves. The last iteration always runs in the A roles: when
         // n_t - 1 is odd, its S and the previous P are copied over once and the
         // buffer pointers are swapped (uniform values).
-        const int n_t = CAUSAL ? qb + 1 : S / BKV;
+        // causal: the diagonal tile qb + coff / BKV is the block's last
+        const int n_t = CAUSAL ? qb + 1 + a.coff / BKV : S / BKV;
         f32x16 sa[MB], sb[MB];
         bf16x8 pa[PK], pb[PK];
         const __bf16 *kA = sk0, *kB = sk1, *vA = sv0, *vB = sv1;
@@ -792,11 +805,19 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
         my_qid = q_valid ? qs[t] : 0;
         w_qmin = wave_min_i(q_valid ? my_qid : INT_MAX);
         w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
-        // the block's queries t0 .. t0 + bq - 1 (bq <= 64: one per lane)
-        const bool qok = lane < a.bq && t0 + lane < T;
-        const int qid = qok ? qs[t0 + lane] : 0;
-        const int wg_qmin = wave_min_i(qok ? qid : INT_MAX), wg_qmax = wave_max_i(qok ? qid : INT_MIN);
-        const int nt_all = CAUSAL ? qb + 1 : S / BKV;
+        // id range of the block's queries t0 .. t0 + bq - 1 (bq may exceed
+        // the wave's 64 lanes: 128 or 256 queries when a unit holds one or
+        // two heads)
+        int qlo = INT_MAX, qhi = INT_MIN;
+        for (int i = lane; i < a.bq; i += 64) {
+            if (t0 + i < T) {
+                const int id = qs[t0 + i];
+                qlo = min(qlo, id);
+                qhi = max(qhi, id);
+            }
+        }
+        const int wg_qmin = wave_min_i(qlo), wg_qmax = wave_max_i(qhi);
+        const int nt_all = CAUSAL ? qb + 1 + a.coff / BKV : S / BKV;
         for (int jj = wave; jj < nt_all; jj += 8) {
             const bool ok = lane < BKV;  // whole tiles: jj * BKV + lane < S
             const int id = ok ? kvs[jj * BKV + lane] : 0;
@@ -835,9 +856,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     // key tiles j0 .. j0 + n_t - 1 (SEG: the n_vis tiles of the list); a left
     // window (causal only, WIN) starts the block's range at the first tile its
     // first query can see
-    const int WL = win_left(a.wl);
+    const int WL = a.wl;
     const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
-    const int n_t = SEG ? n_vis : (CAUSAL ? qb + 1 : S / BKV) - j0;
+    // causal: the block's diagonal tile qb + coff / BKV comes last
+    const int n_t = SEG ? n_vis : (CAUSAL ? qb + 1 + a.coff / BKV : S / BKV) - j0;
     // key tile of loop step i
     auto tile_of = [&](int i) { return SEG ? __builtin_amdgcn_readfirstlane(s_jlist[i]) : j0 + i; };
 
@@ -958,7 +980,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
 
     // ---- V phase pieces (as in the kernel above)
     auto mask_tile = [&](int s0) {
-        const int lim = min(CAUSAL ? t : INT_MAX, S - 1) - s0 - 4 * c;  // last visible key offset
+        const int lim = min(CAUSAL ? t + a.coff : INT_MAX, S - 1) - s0 - 4 * c;  // last visible key offset
         const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;          // first visible key offset
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
@@ -1232,8 +1254,12 @@ template <int H, int BKV, int NW, int WPS>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks * (a.o_part ? a.n_splits : 1));
     const bool all_waves = a.gw * a.bq == 32 * NW;
-    const bool dense = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
-                       !windowed(a.wl, a.wr, a.causal) && (!a.causal || (a.T == a.S && a.bq == BKV));
+    const MaskSpec m{a.causal, a.coff, a.wl, a.wr, a.prefix};
+    // causal: every block's diagonal lies in its last key tile (one query
+    // block per key tile, the diagonal offset a whole number of tiles)
+    const bool diag_tiles = !a.causal || (a.coff >= 0 && a.coff % BKV == 0 && a.T + a.coff == a.S && a.bq == BKV);
+    const bool dense = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 && !mask_extra(m) &&
+                       diag_tiles;
     if constexpr (GQA_FWD_PINGPONG && H <= 128 && NW == 8) {
         if (dense) {
             // H = 64: the loads go into the M phase, which is the shorter one
@@ -1249,8 +1275,7 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
         // segment ids on an otherwise dense shape with at most 8192 keys: the
         // ping-pong kernel over each block's list of tiles that share an id
         const bool dense_seg = a.o_part == nullptr && a.q_seg != nullptr && all_waves && a.S % BKV == 0 &&
-                               a.S <= 8192 && !windowed(a.wl, a.wr, a.causal) &&
-                               (!a.causal || (a.T == a.S && a.bq == BKV));
+                               a.S <= 8192 && !mask_extra(m) && diag_tiles;
         if (dense_seg) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false, true, 2>), dim3(grid), dim3(NW * 64), 0, stream, a);
@@ -1261,7 +1286,7 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
         // a causal left window on an otherwise dense shape: the ping-pong kernel
         // starting at each block's first visible tile
         const bool dense_win = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
-                               a.causal && a.wl >= 0 && a.T == a.S && a.bq == BKV;
+                               mask_left_window_only(m) && diag_tiles;
         if (dense_win) {
             hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
             return hipGetLastError();
@@ -1393,11 +1418,12 @@ SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H) {
 
 // H = 256 on the ping-pong kernel: 8 waves of 32 query rows (gw = 8 heads by
 // bq = 32 queries) over 32-key tiles, for dense shapes: no segment ids, no
-// window, whole key tiles, and T == S when causal (the diagonal tile is then
+// window or prefix, whole key tiles, and when causal T + coff == S with the
+// diagonal offset coff a whole number of tiles (the diagonal tile is then
 // each block's last).
-bool fwd_pp256_applies(int G, int T, int S, int causal, bool segments, int wl, int wr) {
-    return GQA_FWD_PINGPONG && G % 8 == 0 && !segments && S % 32 == 0 && !windowed(wl, wr, causal != 0) &&
-           (!causal || T == S);
+bool fwd_pp256_applies(int G, int T, int S, const MaskSpec &m, bool segments) {
+    return GQA_FWD_PINGPONG && G % 8 == 0 && !segments && S % 32 == 0 && !mask_extra(m) &&
+           (!m.causal || (m.coff >= 0 && m.coff % 32 == 0 && T + m.coff == S));
 }
 
 FwdConfig fwd_config_pp256() {

@@ -22,15 +22,12 @@ constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kRescaleBound = 256.0f;  // 2^kRescaleLog2
 
-// Local window. A key s is visible to query t when t - L <= s <= t + R,
-// with L = win_left(wl) and R = win_right(wr, causal): a negative window side
-// is unbounded, and causal masking caps R at 0 (s <= t). kNoWindow exceeds
-// any sequence length the API accepts, so t - L and t + R cannot overflow.
+// Lazy mask bounds, resolved on the host (see MaskSpec in gqa_launch.h): key s
+// is visible to query t when s < prefix or t - wl <= s <= t + wr. An
+// unbounded side is kNoWindow, which exceeds any sequence length the API
+// accepts (T, S < 2^23), so t - wl, t + wr and wl + wr + 1 cannot overflow;
+// wr may be negative (a causal diagonal below the first query).
 constexpr int kNoWindow = 1 << 29;
-__host__ __device__ inline int win_left(int wl) { return wl < 0 ? kNoWindow : wl; }
-__host__ __device__ inline int win_right(int wr, bool causal) { return causal ? 0 : (wr < 0 ? kNoWindow : wr); }
-// Does a call need the window at all (beyond plain causal masking)?
-__host__ __device__ inline bool windowed(int wl, int wr, bool causal) { return wl >= 0 || (!causal && wr >= 0); }
 
 // D = A * B + C on a 32x32 fp32 tile, A 32x16 and B 16x32 in bf16.
 // Operand layout (64-wide wave): lane l holds A[l%32][8*(l/32) .. +7] and

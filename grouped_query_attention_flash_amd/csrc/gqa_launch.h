@@ -4,7 +4,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gqa_device.h"
+
 namespace gqa {
+
+// A call's mask after host-side resolution (resolve_mask in api.hip). Key s is
+// visible to query t iff
+//   s < prefix  or  t - wl <= s <= t + wr,
+// and, with segment ids, q_seg[b,t] == kv_seg[b,s]. Sides that bound nothing
+// for these sizes are kNoWindow; wr may be negative (an end-aligned causal
+// diagonal with T > S). causal / coff record where wr came from: a causal
+// diagonal s <= t + coff, top-left (coff = 0) or end-aligned (coff = S - T).
+struct MaskSpec {
+    int causal, coff, wl, wr, prefix;
+};
+// Is there more to the mask than the plain causal diagonal (or nothing)?
+inline bool mask_extra(const MaskSpec &m) {
+    return m.prefix > 0 || m.wl < kNoWindow || m.wr < (m.causal ? m.coff : kNoWindow);
+}
+// Only a causal left window beyond the plain causal diagonal?
+inline bool mask_left_window_only(const MaskSpec &m) {
+    return m.causal && m.prefix == 0 && m.wl < kNoWindow && m.wr == m.coff;
+}
 
 struct FwdArgs {
     const __bf16 *q, *k, *v;
@@ -12,8 +33,15 @@ struct FwdArgs {
     float *lse;                      // may be null
     const int32_t *q_seg, *kv_seg;   // both null or both set
     int B, K, G, T, S;
+    // The lazy mask, as resolved by resolve_mask: key s is visible to query t
+    // when s < prefix or t - wl <= s <= t + wr (and, with segment ids, when
+    // the ids are equal). causal says that wr is a causal diagonal s <= t +
+    // coff (possibly capped by a right window side); it selects the kernels'
+    // causal structure (heaviest blocks first, diagonal tile last).
     int causal;
-    int wl, wr;     // local window: keys s with t - wl <= s <= t + wr (< 0: unbounded)
+    int coff;
+    int wl, wr;
+    int prefix;
     int gw;         // query heads per workgroup (divides G)
     int bq;         // queries per workgroup; gw * bq is a multiple of 32
     int n_gsplit;   // G / gw
@@ -45,7 +73,7 @@ struct FwdConfig {
 FwdConfig fwd_config(int G, int T, int H);
 FwdConfig fwd_config_split(int G, int T, int H);
 // H = 256 dense shapes that run the ping-pong kernel, and its configuration.
-bool fwd_pp256_applies(int G, int T, int S, int causal, bool segments, int wl, int wr);
+bool fwd_pp256_applies(int G, int T, int S, const MaskSpec &m, bool segments);
 FwdConfig fwd_config_pp256();
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream);
 
@@ -56,8 +84,7 @@ struct BwdArgs {
     float *delta;                    // workspace: D = rowsum(P * dP) in fp32, [B,K,G,T]
     const int32_t *q_seg, *kv_seg;
     int B, K, G, T, S;
-    int causal;
-    int wl, wr;                      // local window, as in FwdArgs
+    int causal, coff, wl, wr, prefix;  // the resolved mask, as in FwdArgs
 };
 
 hipError_t launch_bwd(const BwdArgs &a, int H, hipStream_t stream);

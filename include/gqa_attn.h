@@ -18,10 +18,18 @@
  * bf16 inputs, fp32 accumulation, bf16 output (the page's kernel writes its
  * output in the input dtype). The T x S weights are never stored.
  * Masks are generated lazily, never materialised:
- *   causal (apple/axlearn PR 845, lazy causal mask): key s visible to query t
- *     iff s <= t (top-left aligned when T != S);
+ *   causal (apple/axlearn PR 845, lazy causal mask), argument `causal`:
+ *     0  none;
+ *     1  top-left aligned: key s visible to query t iff s <= t;
+ *     2  end-aligned: key s visible to query t iff s <= t + (S - T), so the
+ *        last query sees every key, as a block of T new queries appended to
+ *        an S-token context does (the decoding regime of
+ *        danielwatson6.github.io/fa, "Quick digression: what about
+ *        inference?"). With T == S the two alignments agree; with T > S the
+ *        first T - S queries see no key.
  *   segments (fjformer Pallas flash-attention docs, SegmentIds): key s visible
- *     to query t iff q_seg[b,t] == kv_seg[b,s]; combined with causal by AND.
+ *     to query t iff q_seg[b,t] == kv_seg[b,s]; combined with the rest by AND.
+ *   window and prefix (attn_fwd_mask / attn_bwd_mask below).
  * A query row that sees no key gets O = 0 and lse = -inf.
  *
  * Conventions for every call:
@@ -33,8 +41,15 @@
  *     nonzero return nothing has been launched and no output is written.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL =
  *     the default stream) without any host synchronisation.
- *   - Returns 0 on success or a positive GQA_ATTN_ERR_* code.
+ *   - Returns 0 on success or a positive GQA_ATTN_ERR_* code. The codes carry
+ *     the library's GQA_ATTN_ prefix (rather than a bare ATTN_) so that they
+ *     cannot collide with another attention library's enums in one program.
  *   - Thread-safe: concurrent calls on different streams are independent.
+ * Error checking stands in for the pages' own argument checks: the shape
+ * asserts at the top of the fused kernel's wrapper
+ * (danielwatson6.github.io/fa, "Optimizing the kernel") and the ValueError
+ * that fjformer's BlockSizes dataclass raises on inconsistent block sizes.
+ * Unlike those, every size >= 1 is accepted here (ragged tiles are masked).
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -55,7 +70,9 @@ enum {
     GQA_ATTN_ERR_ALIGN = 4,     /* a pointer is not 16-byte (4 for ids) aligned  */
     GQA_ATTN_ERR_SEGMENTS = 5,  /* exactly one of q_seg / kv_seg given           */
     GQA_ATTN_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required       */
-    GQA_ATTN_ERR_HIP = 7        /* a HIP launch failed: see gqa_attn_last_hip_error */
+    GQA_ATTN_ERR_HIP = 7,       /* a HIP launch failed: see attn_last_hip_error  */
+    GQA_ATTN_ERR_MASK = 8       /* causal not 0/1/2, a window side below -1, or a
+                                   negative prefix                               */
 };
 
 /* Forward pass (danielwatson6.github.io/fa, "Optimizing the kernel": the fused
@@ -67,15 +84,20 @@ enum {
  *   lse      fp32 [B,K,G,T]    (written: natural-log logsumexp of each row's
  *            visible logits, the residual the backward needs), or NULL
  *   q_seg    int32 [B,T] and kv_seg int32 [B,S]: both or neither (NULL)
- *   causal   0 or 1
+ *   causal   0, 1 (top-left) or 2 (end-aligned), as above
  * Errors: NULL q/k/v/o -> ERR_NULL; bad sizes -> ERR_SHAPE; H -> ERR_HEADDIM;
- * alignment -> ERR_ALIGN; one segment array -> ERR_SEGMENTS; launch -> ERR_HIP. */
+ * alignment -> ERR_ALIGN; one segment array -> ERR_SEGMENTS; causal outside
+ * 0..2 -> ERR_MASK; launch -> ERR_HIP. */
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              const int32_t *q_seg, const int32_t *kv_seg,
              int B, int K, int G, int T, int S, int H, int causal, void *stream);
 
 /* Host-only validation of attn_fwd's arguments (pointer values are checked for
- * NULL and alignment but never dereferenced). Same return codes. */
+ * NULL and alignment but never dereferenced). Same return codes. It is the
+ * argument check that the shape asserts of the fused kernel's wrapper
+ * (danielwatson6.github.io/fa, "Optimizing the kernel") and the BlockSizes
+ * ValueError (fjformer page, "BlockSizes dataclass") perform, callable
+ * without a GPU. */
 int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal);
@@ -101,14 +123,18 @@ int attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse
                 int B, int K, int G, int T, int S, int H, int causal,
                 void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of device workspace attn_fwd_ws needs for these sizes: 0 when it
- * does not split, else n_splits * B*K*G*T * (H + 1) fp32 rounded up to 256
- * bytes (partial outputs [n_splits,B,K,G,T,H], then partial lse
- * [n_splits,B,K,G,T]). Returns 0 for invalid sizes. */
+/* Bytes of device workspace attn_fwd_ws (and attn_fwd_local, attn_fwd_mask)
+ * needs for these sizes: 0 when it does not split, else n_splits * B*K*G*T *
+ * (H + 1) fp32 rounded up to 256 bytes (partial outputs
+ * [n_splits,B,K,G,T,H], then partial lse [n_splits,B,K,G,T]). Returns 0 for
+ * invalid sizes. The pages describe no such buffer: it belongs to the
+ * split-KV answer to the low-intensity decoding regime of
+ * danielwatson6.github.io/fa, "Quick digression: what about inference?". */
 size_t attn_fwd_workspace_bytes(int B, int K, int G, int T, int S, int H);
 
 /* Number of key splits attn_fwd_ws uses for these sizes (1: no split; 0 for
- * invalid sizes). Host-only. */
+ * invalid sizes). Host-only. Library convention (no passage of the pages):
+ * it exposes the split plan of the decoding path above for callers and tests. */
 int attn_fwd_split_count(int B, int K, int G, int T, int S, int H);
 
 /* Forward pass with a local (sliding) window: key s is visible to query t
@@ -121,27 +147,67 @@ int attn_fwd_split_count(int B, int K, int G, int T, int S, int H);
  * applied lazily as the causal mask is: key tiles outside the band are not
  * visited, and only tiles crossing an edge get an element mask. Otherwise as
  * attn_fwd_ws (workspace as there; window_left / window_right below -1 ->
- * ERR_SHAPE). With both sides unbounded it computes what attn_fwd_ws does. */
+ * ERR_MASK). A side at least as long as the sequence bounds nothing and is
+ * treated as unbounded. With both sides unbounded it computes what
+ * attn_fwd_ws does. Equal to attn_fwd_mask with prefix 0. */
 int attn_fwd_local(const void *q, const void *k, const void *v, void *o, float *lse,
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                    void *workspace, size_t workspace_bytes, void *stream);
 
-/* Host-only validation of attn_fwd_local's arguments. Same return codes. */
+/* Host-only validation of attn_fwd_local's arguments. Same return codes; the
+ * checks of attn_check_fwd (same passages) plus the window sides. */
 int attn_check_fwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
                          const int32_t *q_seg, const int32_t *kv_seg,
                          int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                          const void *workspace, size_t workspace_bytes);
 
-/* Host-only validation of attn_fwd_ws's arguments. Same return codes. */
+/* Host-only validation of attn_fwd_ws's arguments. Same return codes; the
+ * checks of attn_check_fwd (same passages) plus the workspace. */
 int attn_check_fwd_ws(const void *q, const void *k, const void *v, const void *o, const float *lse,
                       const int32_t *q_seg, const int32_t *kv_seg,
                       int B, int K, int G, int T, int S, int H, int causal,
                       const void *workspace, size_t workspace_bytes);
 
+/* Forward pass with the general lazy mask of this library. Key s is visible
+ * to query t iff
+ *     s < prefix  or  (t - window_left <= s <= t + window_right and the
+ *                      causal rule holds),
+ * and, with segment ids, q_seg[b,t] == kv_seg[b,s]. The pages build their
+ * splash baseline from a block mask (danielwatson6.github.io/fa, "Our first
+ * kernel": MultiHeadMask handed to process_mask) that classifies every
+ * (query block, key block) pair as empty, partial or full, and apple/axlearn
+ * PR 845 generates such masks lazily. The same classification is made here
+ * from the closed form, per key tile: empty tiles are never visited, full
+ * ones take no element mask, only partial ones do.
+ *   causal         0, 1 (top-left) or 2 (end-aligned), as for attn_fwd
+ *   window_left,
+ *   window_right   band sides, -1 = unbounded (as attn_fwd_local)
+ *   prefix         keys s < prefix are visible to every query of the row,
+ *                  whatever the causal rule and the band say (bidirectional
+ *                  over a prefix, causal after it: a prefix-LM; with a band
+ *                  it keeps a few leading keys global). 0 = none.
+ *   workspace      as attn_fwd_ws (decoding shapes split the key range)
+ * Errors as attn_fwd_ws, plus ERR_MASK for an invalid causal mode, window
+ * side or prefix. */
+int attn_fwd_mask(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int32_t *q_seg, const int32_t *kv_seg,
+                  int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right, int prefix,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only validation of attn_fwd_mask's arguments. Same return codes; the
+ * checks of attn_check_fwd (same passages) plus the mask arguments. */
+int attn_check_fwd_mask(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const int32_t *q_seg, const int32_t *kv_seg,
+                        int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                        int prefix, const void *workspace, size_t workspace_bytes);
+
 /* Bytes of device workspace attn_bwd needs for these sizes (the per-row
  * D = sum_s P[t,s] dP[t,s] vector, fp32 [B,K,G,T], rounded up to 256 bytes).
- * Returns 0 for invalid sizes. */
+ * Returns 0 for invalid sizes. The pages give no backward; D is the row
+ * quantity of the softmax derivative, kept beside the lse residual that
+ * splash attention's save_residuals returns (danielwatson6.github.io/fa,
+ * "Our first kernel"). */
 size_t attn_bwd_workspace_bytes(int B, int K, int G, int T, int S, int H);
 
 /* Backward pass: gradients of sum(O * dO) with respect to the pre-scaled q,
@@ -173,32 +239,57 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
 /* Backward pass of attn_fwd_local: the same window (window_left, window_right,
  * -1 unbounded) restricts every recomputed weight, and the kernels visit only
  * the tiles inside the band. Otherwise as attn_bwd; window sides below -1 ->
- * ERR_SHAPE. */
+ * ERR_MASK. Equal to attn_bwd_mask with prefix 0. */
 int attn_bwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
                    const void *dO, float *dq, float *dk, float *dv,
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                    void *workspace, size_t workspace_bytes, void *stream);
 
-/* Host-only validation of attn_bwd_local's arguments. Same return codes. */
+/* Host-only validation of attn_bwd_local's arguments. Same return codes; the
+ * checks of attn_check_bwd plus the window sides. */
 int attn_check_bwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
                          const void *dO, const float *dq, const float *dk, const float *dv,
                          const int32_t *q_seg, const int32_t *kv_seg,
                          int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                          const void *workspace, size_t workspace_bytes);
 
-/* Host-only validation of attn_bwd's arguments. Same return codes. */
+/* Backward pass of attn_fwd_mask: the same mask (causal mode, window sides,
+ * prefix) restricts every recomputed weight, and the kernels visit only the
+ * tiles that hold a visible pair. Otherwise as attn_bwd; an invalid mask
+ * argument -> ERR_MASK. */
+int attn_bwd_mask(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                  const void *dO, float *dq, float *dk, float *dv,
+                  const int32_t *q_seg, const int32_t *kv_seg,
+                  int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right, int prefix,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only validation of attn_bwd_mask's arguments. Same return codes; the
+ * checks of attn_check_bwd plus the mask arguments. */
+int attn_check_bwd_mask(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const void *dO, const float *dq, const float *dk, const float *dv,
+                        const int32_t *q_seg, const int32_t *kv_seg,
+                        int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                        int prefix, const void *workspace, size_t workspace_bytes);
+
+/* Host-only validation of attn_bwd's arguments. Same return codes. Like
+ * attn_check_fwd it stands in for the fused kernel wrapper's shape asserts
+ * (danielwatson6.github.io/fa, "Optimizing the kernel") and for the
+ * ValueError of fjformer's BlockSizes dataclass, whose separate *_dkv and *_dq
+ * block sizes are the two backward kernels validated here. */
 int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
                    const void *dO, const float *dq, const float *dk, const float *dv,
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal,
                    const void *workspace, size_t workspace_bytes);
 
-/* Static, NUL-terminated description of a return code. Never NULL. */
+/* Static, NUL-terminated description of a return code. Never NULL. It plays
+ * the part of the message text of the BlockSizes ValueError (fjformer page,
+ * "BlockSizes dataclass"); the Python binding raises it as a ValueError. */
 const char *attn_strerror(int code);
 
 /* The hipError_t behind the calling thread's most recent GQA_ATTN_ERR_HIP
- * (0 if none). */
+ * (0 if none). Library convention, no passage of the pages. */
 int attn_last_hip_error(void);
 
 #ifdef __cplusplus

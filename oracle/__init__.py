@@ -47,10 +47,10 @@ def _load():
         I64 = ctypes.c_int64
         lib.oracle_fwd_rows.restype = ctypes.c_int
         lib.oracle_fwd_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_int,
-                                        I64, I64, I64, P, P, P]
+                                        I64, I64, I64, I64, P, P, P]
         lib.oracle_bwd_rows.restype = ctypes.c_int
         lib.oracle_bwd_rows.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_int,
-                                        I64, I64, I64, P, P, P, I64, P, P, P]
+                                        I64, I64, I64, I64, P, P, P, I64, P, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -109,13 +109,24 @@ def _window(window):
     return wl, wr
 
 
-def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None, window=None):
+def _causal(causal):
+    """0 none, 1 top-left (s <= t), 2 end-aligned (s <= t + S - T)."""
+    if isinstance(causal, str):
+        return {"none": 0, "top_left": 1, "end": 2}[causal]
+    c = int(causal)
+    assert c in (0, 1, 2), causal
+    return c
+
+
+def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None, window=None, prefix=0):
     """Plain fp64 attention. Returns (O, lse) as float64 numpy arrays.
 
     rows=None: O has q's shape and lse q's shape minus H.
     rows given (flat indices into [B,K,G,T]): O is [len(rows), H], lse [len(rows)].
+    causal: False/0, True/1 (s <= t), 2 or "end" (s <= t + S - T).
     window=(wl, wr): key s visible to query t only if t - wl <= s <= t + wr
-    (a side of -1 is unbounded).
+    (a side of -1 is unbounded). prefix=p: keys s < p are visible to every
+    query whatever the causal rule and window say (segments still apply).
     """
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
     B, K, G, T, H = qb.shape
@@ -129,8 +140,8 @@ def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None,
     o = np.empty((n, H), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
     rc = _load().oracle_fwd_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(qs), _ptr(ks), _ptr(mk),
-                                 B, K, G, T, S, H, int(bool(causal)), *_window(window), n, _ptr(r), _ptr(o),
-                                 _ptr(lse))
+                                 B, K, G, T, S, H, _causal(causal), *_window(window), int(prefix), n, _ptr(r),
+                                 _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_fwd_rows failed with code %d" % rc)
     if r is None:
@@ -139,7 +150,7 @@ def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None,
 
 
 def bwd(q, k, v, do, *, causal=False, q_seg=None, kv_seg=None, mask=None, qrows=None, kvrows=None,
-        want_dq=True, want_dkv=True, window=None):
+        want_dq=True, want_dkv=True, window=None, prefix=0):
     """Plain fp64 gradients of sum(O * dO). Returns dict with dq, dk, dv, D.
 
     Full tensors when the row lists are None, else [n, H] arrays for the
@@ -161,7 +172,7 @@ def bwd(q, k, v, do, *, causal=False, q_seg=None, kv_seg=None, mask=None, qrows=
     dk = np.empty((max(nkv, 1), H), dtype=np.float64)
     dv = np.empty((max(nkv, 1), H), dtype=np.float64)
     rc = _load().oracle_bwd_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(db), _ptr(qs), _ptr(ks), _ptr(mk),
-                                 B, K, G, T, S, H, int(bool(causal)), *_window(window),
+                                 B, K, G, T, S, H, _causal(causal), *_window(window), int(prefix),
                                  nq, _ptr(qr), _ptr(dq) if nq else None, _ptr(dd) if nq else None,
                                  nkv, _ptr(kr), _ptr(dk) if nkv else None, _ptr(dv) if nkv else None)
     if rc != 0:

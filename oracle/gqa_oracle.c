@@ -13,15 +13,23 @@
  *   softmax  over the visible s of row t, with the maximum subtracted first
  *            (same page, "Chunked attention": softmax(l) = softmax(l + c))
  *   output   O[t,:] = sum_s P[t,s] * v[s,:];  lse[t] = m + ln(sum exp(l - m))
- *   visible  (!causal || s <= t) && (no segment ids || q_seg[b,t] == kv_seg[b,s])
- *            -- causal masking as in apple/axlearn PR 845 (lazy causal mask),
- *            segment equality as in the SegmentIds docs of the fjformer Pallas
- *            flash-attention page ("only tokens with the same id attend").
- *            && (wl < 0 || s >= t - wl) && (wr < 0 || s <= t + wr)
- *            -- the last two terms are a local window (a band of
- *            diagonals; wl = wr = -1 leaves it out). The pages run splash
+ *   visible  (no segment ids || q_seg[b,t] == kv_seg[b,s])
+ *            && (s < prefix || (causal rule && window rule))
+ *            -- segment equality per the SegmentIds section of the fjformer
+ *            Pallas flash-attention page; causal masking as in apple/axlearn
+ *            PR 845 (lazy causal mask), in one of two alignments:
+ *              causal = 1 (top-left):   s <= t
+ *              causal = 2 (end-aligned): s <= t + (S - T), the last query
+ *              seeing every key, as new queries appended to a context do
+ *              (danielwatson6.github.io/fa, "Quick digression: what about
+ *              inference?");
+ *            window rule (wl < 0 || s >= t - wl) && (wr < 0 || s <= t + wr):
+ *            a local window (a band of diagonals; wl = wr = -1 leaves it
+ *            out); prefix: keys s < prefix are visible to every query
+ *            (a prefix-LM; prefix = 0 leaves it out). The pages run splash
  *            attention's block-mask processing only with a FullMask; the band
- *            is the reading used for its non-full case (see the tests' pins).
+ *            and the prefix are the readings used for its non-full cases (see
+ *            the tests' pins).
  *            A test-only explicit mask M[b,t,s] may replace that rule.
  *   A row with no visible key gives O = 0 and lse = -inf (a convention: the
  *   pages are silent on it; parity unpinned).
@@ -57,16 +65,19 @@ typedef struct {
     const int32_t *q_seg, *kv_seg;
     const uint8_t *mask; /* [B, T, S] or NULL */
     int64_t B, K, G, T, S, H;
-    int causal;
+    int causal;     /* 0 none, 1 top-left, 2 end-aligned */
     int64_t wl, wr; /* local window sides, -1 = unbounded */
+    int64_t prefix; /* keys s < prefix visible to every query */
 } problem;
 
 static int is_visible(const problem *p, int64_t b, int64_t t, int64_t s) {
     if (p->mask) return p->mask[(b * p->T + t) * p->S + s] != 0;
-    if (p->causal && s > t) return 0;
+    if (p->q_seg && p->q_seg[b * p->T + t] != p->kv_seg[b * p->S + s]) return 0;
+    if (s < p->prefix) return 1;
+    if (p->causal == 1 && s > t) return 0;
+    if (p->causal == 2 && s > t + (p->S - p->T)) return 0;
     if (p->wl >= 0 && s < t - p->wl) return 0;
     if (p->wr >= 0 && s > t + p->wr) return 0;
-    if (p->q_seg && p->q_seg[b * p->T + t] != p->kv_seg[b * p->S + s]) return 0;
     return 1;
 }
 
@@ -111,11 +122,12 @@ static int64_t row_softmax_stats(const problem *p, int64_t b, int64_t k, int64_t
 int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                     const int32_t *q_seg, const int32_t *kv_seg, const uint8_t *mask,
                     int64_t B, int64_t K, int64_t G, int64_t T, int64_t S, int64_t H, int causal,
-                    int64_t wl, int64_t wr,
+                    int64_t wl, int64_t wr, int64_t prefix,
                     int64_t n_rows, const int64_t *rows, double *o_out, double *lse_out) {
     if (!q || !k || !v || !o_out || B < 1 || K < 1 || G < 1 || T < 1 || S < 1 || H < 1) return 1;
     if ((q_seg == NULL) != (kv_seg == NULL)) return 2;
-    problem p = {q, k, v, NULL, q_seg, kv_seg, mask, B, K, G, T, S, H, causal, wl, wr};
+    if (causal < 0 || causal > 2 || prefix < 0) return 5;
+    problem p = {q, k, v, NULL, q_seg, kv_seg, mask, B, K, G, T, S, H, causal, wl, wr, prefix};
     int64_t total = B * K * G * T;
     if (!rows) n_rows = total;
     int err = 0;
@@ -198,12 +210,13 @@ static void unit_row_stats(const problem *p, int64_t b, int64_t k, double *m_arr
 int oracle_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
                     const int32_t *q_seg, const int32_t *kv_seg, const uint8_t *mask,
                     int64_t B, int64_t K, int64_t G, int64_t T, int64_t S, int64_t H, int causal,
-                    int64_t wl, int64_t wr,
+                    int64_t wl, int64_t wr, int64_t prefix,
                     int64_t n_q, const int64_t *qrows, double *dq_out, double *d_out,
                     int64_t n_kv, const int64_t *kvrows, double *dk_out, double *dv_out) {
     if (!q || !k || !v || !dout || B < 1 || K < 1 || G < 1 || T < 1 || S < 1 || H < 1) return 1;
     if ((q_seg == NULL) != (kv_seg == NULL)) return 2;
-    problem p = {q, k, v, dout, q_seg, kv_seg, mask, B, K, G, T, S, H, causal, wl, wr};
+    if (causal < 0 || causal > 2 || prefix < 0) return 5;
+    problem p = {q, k, v, dout, q_seg, kv_seg, mask, B, K, G, T, S, H, causal, wl, wr, prefix};
     int64_t nq_total = B * K * G * T, nkv_total = B * K * S;
     if (!qrows) n_q = nq_total;
     if (!kvrows) n_kv = nkv_total;

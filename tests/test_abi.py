@@ -137,17 +137,54 @@ def test_check_local_window_codes():
     lib = gqa.load_library()
     args = (P(A16), P(A16), P(A16), P(A16), P(A16), None, None, 1, 1, 4, 64, 64, 128, 1)
     for wl, wr, want in [(-1, -1, gqa.GQA_ATTN_OK), (0, 0, gqa.GQA_ATTN_OK), (31, -1, gqa.GQA_ATTN_OK),
-                         (-2, 0, gqa.GQA_ATTN_ERR_SHAPE), (0, -5, gqa.GQA_ATTN_ERR_SHAPE)]:
+                         (2 ** 31 - 1, 2 ** 31 - 1, gqa.GQA_ATTN_OK),
+                         (-2, 0, gqa.GQA_ATTN_ERR_MASK), (0, -5, gqa.GQA_ATTN_ERR_MASK)]:
         assert lib.attn_check_fwd_local(*args, wl, wr, None, 0) == want, (wl, wr)
     wsb = gqa.attn_bwd_workspace_bytes(1, 1, 4, 64, 64, 128)
     bargs = (P(A16),) * 9 + (None, None, 1, 1, 4, 64, 64, 128, 1)
     assert lib.attn_check_bwd_local(*bargs, 5, -1, P(A16), wsb) == gqa.GQA_ATTN_OK
-    assert lib.attn_check_bwd_local(*bargs, -3, -1, P(A16), wsb) == gqa.GQA_ATTN_ERR_SHAPE
+    assert lib.attn_check_bwd_local(*bargs, -3, -1, P(A16), wsb) == gqa.GQA_ATTN_ERR_MASK
     assert lib.attn_check_bwd_local(*bargs, 5, -1, None, wsb) == gqa.GQA_ATTN_ERR_WORKSPACE
 
 
+def test_check_mask_codes():
+    """causal modes 0..2, window sides >= -1 and prefix >= 0 are accepted by
+    every entry point; anything else is ERR_MASK, reported before any launch."""
+    P = ctypes.c_void_p
+    lib = gqa.load_library()
+    fargs = (P(A16), P(A16), P(A16), P(A16), P(A16), None, None, 1, 1, 4, 64, 128, 128)
+    for causal, wl, wr, pfx, want in [
+            (0, -1, -1, 0, gqa.GQA_ATTN_OK), (1, -1, -1, 0, gqa.GQA_ATTN_OK), (2, -1, -1, 0, gqa.GQA_ATTN_OK),
+            (2, 10, 3, 7, gqa.GQA_ATTN_OK), (1, -1, -1, 1 << 30, gqa.GQA_ATTN_OK),
+            (3, -1, -1, 0, gqa.GQA_ATTN_ERR_MASK), (-1, -1, -1, 0, gqa.GQA_ATTN_ERR_MASK),
+            (1, -1, -1, -1, gqa.GQA_ATTN_ERR_MASK), (1, -2, -1, 0, gqa.GQA_ATTN_ERR_MASK),
+            (0, -1, -7, 0, gqa.GQA_ATTN_ERR_MASK)]:
+        assert lib.attn_check_fwd_mask(*fargs, causal, wl, wr, pfx, None, 0) == want, (causal, wl, wr, pfx)
+    # the plain entry points take the causal mode too
+    assert check_fwd(causal=2) == gqa.GQA_ATTN_OK
+    assert check_fwd(causal=3) == gqa.GQA_ATTN_ERR_MASK
+    wsb = gqa.attn_bwd_workspace_bytes(1, 1, 4, 64, 128, 128)
+    bargs = (P(A16),) * 9 + (None, None, 1, 1, 4, 64, 128, 128)
+    assert lib.attn_check_bwd(*bargs, 2, P(A16), wsb) == gqa.GQA_ATTN_OK
+    assert lib.attn_check_bwd(*bargs, 5, P(A16), wsb) == gqa.GQA_ATTN_ERR_MASK
+    assert lib.attn_check_bwd_mask(*bargs, 2, 4, -1, 16, P(A16), wsb) == gqa.GQA_ATTN_OK
+    assert lib.attn_check_bwd_mask(*bargs, 1, -1, -1, -3, P(A16), wsb) == gqa.GQA_ATTN_ERR_MASK
+    # shape errors still come first
+    assert lib.attn_check_bwd_mask(*(bargs[:11] + (0,) + bargs[12:]), 9, -1, -1, 0, P(A16), wsb) == \
+        gqa.GQA_ATTN_ERR_SHAPE
+
+
+def test_causal_mode_mapping():
+    assert gqa.causal_mode(False) == 0 and gqa.causal_mode(True) == 1
+    assert gqa.causal_mode("top_left") == 1 and gqa.causal_mode("end") == 2 and gqa.causal_mode(2) == 2
+    with pytest.raises(ValueError):
+        gqa.causal_mode(3)
+    with pytest.raises(ValueError):
+        gqa.causal_mode("bottom")
+
+
 def test_strerror_and_hip_error():
-    for code in range(0, 8):
+    for code in range(0, 9):
         s = gqa.attn_strerror(code)
         assert s and s != "unknown error code"
     assert gqa.attn_strerror(99) == "unknown error code"

@@ -62,6 +62,20 @@ SMALL = [
     # them from memory instead of its LDS copy) and just under that bound
     (1, 1, 4, 64, 4200, 128, False, (200, 900)),
     (1, 1, 4, 4160, 4160, 128, True, (300, 1200)),
+    # H = 256 with G not a multiple of 8 on whole 32-key tiles: the general
+    # kernel's DENSE specialisation (4 waves, gw = G heads by 128 / G queries)
+    (1, 1, 4, 128, 128, 256, True, None),
+    (1, 2, 4, 96, 160, 256, False, None),
+    (1, 1, 2, 64, 96, 256, False, None),
+    (1, 1, 1, 160, 160, 256, False, None),
+    (2, 1, 4, 256, 256, 256, True, None),
+    # non-causal segment ids with one or two heads per unit (128- and
+    # 256-query blocks on the ping-pong kernel): ids change many times past
+    # the block's first 64 queries
+    (1, 1, 1, 256, 256, 128, False, (10, 60)),
+    (1, 1, 2, 192, 256, 128, False, (10, 60)),
+    (1, 2, 1, 300, 512, 128, False, (20, 50)),
+    (1, 1, 2, 128, 128, 64, False, (5, 30)),
 ]
 
 

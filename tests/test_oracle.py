@@ -409,3 +409,135 @@ def test_bwd_window_zero_width_closed_form():
     g = oracle.bwd(q, k, v, do, causal=True, window=(0, 0))
     assert np.all(g["dq"] == 0) and np.all(g["dk"] == 0)
     np.testing.assert_allclose(g["dv"], f64(do).numpy().sum(axis=2), rtol=0, atol=1e-12)
+
+
+# ---- end-aligned causal (s <= t + S - T) and prefix keys (s < p visible to all)
+
+def end_aligned_mask(B, T, S):
+    """torch's tril with diagonal offset S - T: key s visible to query t iff
+    s <= t + (S - T)."""
+    return torch.ones(T, S, dtype=torch.bool).tril(diagonal=S - T)[None].expand(B, T, S).contiguous()
+
+
+def prefix_mask(base, p):
+    """Keys s < p visible to every query, on top of another mask."""
+    m = base.clone()
+    m[:, :, :p] = True
+    return m
+
+
+def _compare_with_sdpa(q, k, v, mask, o, lse):
+    # rows with no visible key follow the O = 0 / lse = -inf convention; SDPA
+    # gives NaN there, so those rows are checked against the convention
+    vis = mask.any(dim=-1).numpy()
+    ro, rl = sdpa_reference(q, k, v, mask)
+    sel = np.broadcast_to(vis[:, None, None, :], lse.shape)
+    np.testing.assert_allclose(o[sel], ro[sel], atol=1e-12)
+    np.testing.assert_allclose(lse[sel], rl[sel], atol=1e-12)
+    assert np.all(o[~sel] == 0) and np.all(np.isneginf(lse[~sel]))
+
+
+@pytest.mark.parametrize("case", [
+    # B, K, G, T, S, H
+    (1, 1, 2, 5, 17, 8),    # a chunk of new queries at the end of a longer context
+    (2, 2, 2, 12, 12, 16),  # T == S
+    (1, 2, 3, 19, 11, 8),   # T > S: the first T - S queries see nothing
+    (1, 1, 4, 1, 23, 16),   # one decoding query sees every key
+])
+def test_end_aligned_causal_matches_torch_sdpa(case):
+    B, K, G, T, S, H = case
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=97 + T + S)
+    o, lse = oracle.fwd(q, k, v, causal=2)
+    _compare_with_sdpa(q, k, v, end_aligned_mask(B, T, S), o, lse)
+    assert oracle.fwd(q, k, v, causal="end")[0].tobytes() == o.tobytes()
+
+
+def test_end_aligned_is_the_tail_of_a_longer_causal_run():
+    """T new queries at the end of an S-token context see what the last T rows
+    of the full T' = S top-left causal problem see: the same rows, bitwise."""
+    B, K, G, S, H = 2, 2, 2, 29, 16
+    q_full, k, v = make_qkv(B, K, G, S, S, H, seed=101)
+    for T in (1, 7, 29):
+        q = q_full[:, :, :, S - T:].contiguous()
+        o, lse = oracle.fwd(q, k, v, causal=2)
+        o_full, lse_full = oracle.fwd(q_full, k, v, causal=True)
+        assert np.array_equal(o, o_full[:, :, :, S - T:]) and np.array_equal(lse, lse_full[:, :, :, S - T:])
+
+
+def test_end_aligned_equals_top_left_when_t_equals_s():
+    B, K, G, T, H = 1, 2, 2, 21, 8
+    q, k, v = make_qkv(B, K, G, T, T, H, seed=103)
+    o1, l1 = oracle.fwd(q, k, v, causal=1)
+    o2, l2 = oracle.fwd(q, k, v, causal=2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("case", [
+    # B, K, G, T, S, H, causal, prefix, window, segments
+    (1, 1, 2, 20, 20, 8, 1, 6, None, False),
+    (2, 2, 2, 18, 18, 16, 1, 1, None, False),
+    (1, 2, 3, 24, 24, 8, 1, 5, (3, -1), False),   # global prefix keys + a causal band
+    (2, 1, 2, 16, 16, 16, 1, 7, None, True),      # with segment ids (ANDed)
+    (1, 1, 2, 9, 21, 8, 2, 4, None, False),       # with end-aligned causal
+])
+def test_prefix_matches_torch_sdpa(case):
+    B, K, G, T, S, H, causal, p, window, segs = case
+    q, k, v = make_qkv(B, K, G, T, S, H, seed=107 + T + p)
+    q_seg = kv_seg = None
+    if segs:
+        q_seg = make_segment_ids(B, T, seed=5, lo=2, hi=7)
+        kv_seg = q_seg.clone()
+    o, lse = oracle.fwd(q, k, v, causal=causal, window=window, prefix=p, q_seg=q_seg, kv_seg=kv_seg)
+    base = end_aligned_mask(B, T, S) if causal == 2 else band_mask(B, T, S, *(window or (-1, -1)), True)
+    m = prefix_mask(base, p)
+    if segs:
+        m &= q_seg[:, :, None] == kv_seg[:, None, :]
+    _compare_with_sdpa(q, k, v, m, o, lse)
+
+
+def test_prefix_rows_are_noncausal_over_the_prefix():
+    """A query t < p sees exactly the keys s < p: its row equals non-causal
+    attention over the first p keys alone, bitwise."""
+    B, K, G, T, H, p = 2, 2, 2, 26, 16, 11
+    q, k, v = make_qkv(B, K, G, T, T, H, seed=109)
+    o, lse = oracle.fwd(q, k, v, causal=True, prefix=p)
+    o_p, lse_p = oracle.fwd(q[:, :, :, :p].contiguous(), k[:, :, :p].contiguous(), v[:, :, :p].contiguous())
+    assert np.array_equal(o[:, :, :, :p], o_p) and np.array_equal(lse[:, :, :, :p], lse_p)
+
+
+def test_prefix_limits():
+    B, K, G, T, H = 1, 2, 2, 14, 8
+    q, k, v = make_qkv(B, K, G, T, T, H, seed=113)
+    oc, lc = oracle.fwd(q, k, v, causal=True)
+    on, ln = oracle.fwd(q, k, v, causal=False)
+    o0, l0 = oracle.fwd(q, k, v, causal=True, prefix=0)
+    oa, la = oracle.fwd(q, k, v, causal=True, prefix=T)
+    assert np.array_equal(o0, oc) and np.array_equal(l0, lc)
+    assert np.array_equal(oa, on) and np.array_equal(la, ln)
+
+
+@pytest.mark.parametrize("case", [
+    # B, K, G, T, S, H, causal, prefix, window
+    (1, 1, 2, 8, 19, 8, 2, 0, None),
+    (2, 2, 2, 15, 9, 16, 2, 0, None),
+    (1, 2, 2, 16, 16, 8, 1, 5, None),
+    (2, 1, 3, 14, 14, 16, 1, 3, (2, -1)),
+])
+def test_bwd_end_aligned_and_prefix_match_torch_autograd(case):
+    B, K, G, T, S, H, causal, p, window = case
+    q, k, v, do = make_qkv(B, K, G, T, S, H, seed=127 + T + S, with_do=True)
+    g = oracle.bwd(q, k, v, do, causal=causal, prefix=p, window=window)
+    base = end_aligned_mask(B, T, S) if causal == 2 else band_mask(B, T, S, *(window or (-1, -1)), True)
+    m = prefix_mask(base, p)
+    vis = m.any(dim=-1)
+    # rows that see no key have zero gradient by the oracle's convention; give
+    # autograd a harmless mask there and a zero upstream gradient
+    m2 = m.clone()
+    m2[~vis] = True
+    do2 = do.clone()
+    do2[:, :, :, ~vis[0]] = 0
+    assert bool((vis == vis[0:1]).all())
+    dq, dk, dv = autograd_reference(q, k, v, do2, m2)
+    np.testing.assert_allclose(g["dq"], dq, atol=1e-11)
+    np.testing.assert_allclose(g["dk"], dk, atol=1e-11)
+    np.testing.assert_allclose(g["dv"], dv, atol=1e-11)
