@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "attn_fwd", "attn_check_fwd", "attn_fwd_ws", "attn_check_fwd_ws", "attn_fwd_workspace_bytes",
     "attn_fwd_split_count", "attn_fwd_local", "attn_check_fwd_local", "attn_fwd_mask", "attn_check_fwd_mask",
     "attn_bwd_workspace_bytes", "attn_bwd", "attn_check_bwd", "attn_bwd_local", "attn_check_bwd_local",
-    "attn_bwd_mask", "attn_check_bwd_mask", "attn_strerror", "attn_last_hip_error",
+    "attn_bwd_mask", "attn_check_bwd_mask", "attn_fwd_noalloc", "attn_strerror", "attn_last_hip_error",
 )
 
 _lib = None
@@ -92,6 +92,8 @@ def load_library():
     lib.attn_bwd_mask.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, SZ, P]
     lib.attn_check_bwd_mask.restype = I
     lib.attn_check_bwd_mask.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, SZ]
+    lib.attn_fwd_noalloc.restype = I
+    lib.attn_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P]
     lib.attn_fwd_workspace_bytes.restype = SZ
     lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_fwd_split_count.restype = I
@@ -244,6 +246,33 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False,
                                  B, K, G, T, S, H, cm, _stream_handle(dev))
     if rc != GQA_ATTN_OK:
         raise GqaAttnError(rc, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                     lse: Optional[torch.Tensor] = None, *, causal=False,
+                     q_seg: Optional[torch.Tensor] = None, kv_seg: Optional[torch.Tensor] = None,
+                     window: Optional[Tuple[int, int]] = None, prefix: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """attn_fwd_mask without a workspace (attn_fwd_noalloc): the library keeps
+    the split-KV partials in its own static device array (16 MiB per GPU), so
+    neither this call nor the library allocates device memory; the caller
+    passes `out` (and `lse`, or None). Calls that overlap on one GPU share
+    that array and must not run concurrently."""
+    B, K, G, T, S, H = _dims(q, k)
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16)
+    _check_tensor("k", k, torch.bfloat16, None, dev)
+    _check_tensor("v", v, torch.bfloat16, k.shape, dev)
+    _check_tensor("out", out, torch.bfloat16, q.shape, dev)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, (B, K, G, T), dev)
+    cm = causal_mode(causal)
+    _check_segments(q_seg, kv_seg, B, T, S, dev, "attn_fwd_noalloc")
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    rc = load_library().attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg), _ptr(kv_seg),
+                                         B, K, G, T, S, H, cm, wl, wr, int(prefix), _stream_handle(dev))
+    if rc != GQA_ATTN_OK:
+        raise GqaAttnError(rc, "attn_fwd_noalloc")
     return out, lse
 
 

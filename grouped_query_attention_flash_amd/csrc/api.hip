@@ -5,6 +5,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 namespace {
 
@@ -320,6 +321,65 @@ int attn_bwd_local(const void *q, const void *k, const void *v, const void *o, c
                    void *workspace, size_t workspace_bytes, void *stream) {
     return attn_bwd_mask(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left,
                          window_right, 0, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The allocation-free forward (attn_fwd_noalloc). Its split-KV partial results
+// go to this file-scope device array instead of a caller workspace; each GPU
+// the library runs on holds one copy until the process ends. In host code
+// the name `scratch` is a host-side stand-in, not a device address: host code
+// only ever uses the per-device address hipGetSymbolAddress returns.
+}  // extern "C"
+
+static constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device, resolved on its first call
+
+// The device address of this GPU's copy of `scratch` (the current device,
+// which must be the one the caller's stream belongs to).
+int scratch_on_current_device(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GQA_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                     const int32_t *q_seg, const int32_t *kv_seg,
+                     int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                     int prefix, void *stream) {
+    int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, 0);
+    if (rc) return rc;
+    rc = check_mask(causal, window_left, window_right, prefix);
+    if (rc) return rc;
+    const size_t need = attn_fwd_workspace_bytes(B, K, G, T, S, H);
+    if (need > kScratchBytes) return GQA_ATTN_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        rc = scratch_on_current_device(&ws);
+        if (rc) return rc;
+    }
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H,
+                   resolve_mask(causal, window_left, window_right, prefix, T, S),
+                   gqa::fwd_split_plan(B, K, G, T, S, H), ws, stream);
 }
 
 const char *attn_strerror(int code) {

@@ -283,6 +283,25 @@ int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, c
                    int B, int K, int G, int T, int S, int H, int causal,
                    const void *workspace, size_t workspace_bytes);
 
+/* Forward pass that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc. Same arguments and result as
+ * attn_fwd_mask minus the workspace: when the shape splits the key range
+ * (decoding shapes, as attn_fwd_ws), the partial outputs and lse go to a
+ * static device array of the library, 16 MiB per GPU (2^24 bytes), held from
+ * the first call on a device until the process ends. A shape whose
+ * attn_fwd_workspace_bytes() exceeds 16 MiB returns ERR_WORKSPACE before
+ * anything is launched. The call makes no hipMalloc / hipFree or other
+ * allocating call; its first call on a device looks up that device's copy of
+ * the array (hipGetSymbolAddress). Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (concurrent streams) race and must be
+ * serialised by the caller. Each split writes every row it owns, so no state
+ * carries over from one call to the next. */
+int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                     const int32_t *q_seg, const int32_t *kv_seg,
+                     int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                     int prefix, void *stream);
+
 /* Static, NUL-terminated description of a return code. Never NULL. It plays
  * the part of the message text of the BlockSizes ValueError (fjformer page,
  * "BlockSizes dataclass"); the Python binding raises it as a ValueError. */
