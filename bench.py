@@ -24,13 +24,24 @@ tensors and reports it under "backward".
 
 --workload segments times the packed-sequence shape B=4, K=8, G=4, T=S=2048,
 H=128 (causal and segment ids, segments of 64-1024 tokens) in the same
-format, with value on the causal-half FLOP count and the rate on visible
-pairs beside it; no backward or CPU legs.
+format; value and the roofline fraction count only the visible (t, s) pairs
+(the work the kernel executes), with the causal-half rate beside them.
 
 --write-traffic FETCH_CSV WRITE_CSV turns two rocprofv3 --pmc runs (FETCH_SIZE,
 then WRITE_SIZE, each with --copy-calibration-mib) into the HBM bytes per
 launch of the headline forward kernel, scaled by what the same counters read
 for the calibration copy, and stores them with a digest of the kernel source.
+
+--write-counters SQ_CSV turns a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+GRBM_GUI_ACTIVE run of a workload into each kernel's MFMA-busy fraction and
+running clock (GRBM_GUI_ACTIVE per XCD over the dispatch's own duration), stored
+with a digest of the kernel sources; the bench line reports them, and the
+fraction of the peak at that clock, while the digest matches.
+
+The CPU baseline times the float-accumulation build of the oracle source on a
+sample of the workload's rows (the fp64 build's rate beside it), and checks
+the GPU output against the fp64 oracle on its own sample: a miss of max-abs
+2e-2 or rel-L2 5e-3 marks the line "parity_ok": false and exits with status 3.
 
 --workload decode instead times the decoding shape B=16, K=8, G=4, T=1,
 S=32768, H=128 (non-causal: the query sees the whole context) through the
@@ -47,15 +58,98 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MI355X_BF16_DENSE_TFLOPS = 2500.0   # published dense bf16 MFMA peak
 MI355X_HBM_GBPS = 8000.0            # published HBM3E bandwidth
+MI355X_PEAK_CLOCK_GHZ = 2.4         # the engine clock the published peak assumes
+MI355X_XCDS = 8
+MI355X_SIMDS = 1024                 # 256 CUs x 4
+O_MAX_ABS, O_REL_L2 = 2e-2, 5e-3    # parity bar of the sampled check
 METRIC = "attention TFLOP/s (fwd, causal) at 1 GPU; % of bf16 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_b1_k8_g4_t8192_h128_traffic.json")
 FWD_SOURCES = ["grouped_query_attention_flash_amd/csrc/attn_fwd.hip",
                "grouped_query_attention_flash_amd/csrc/gqa_device.h"]
+ALL_SOURCES = FWD_SOURCES + ["grouped_query_attention_flash_amd/csrc/attn_bwd.hip",
+                             "grouped_query_attention_flash_amd/csrc/gqa_launch.h",
+                             "grouped_query_attention_flash_amd/csrc/api.hip"]
+
+
+def counters_file(workload):
+    return os.path.join(ROOT, "profiles", "%s_counters.json" % workload)
+
+
+def write_counters(sq_csv, workload, out_path=None):
+    """Per-kernel MFMA-busy fraction and running clock from one rocprofv3 --pmc
+    SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE run (its counter CSV carries each
+    dispatch's start and end time). SQ_VALU_MFMA_BUSY_CYCLES sums over the
+    chip's SIMDs and GRBM_GUI_ACTIVE over its XCDs, so per dispatch
+      mfma_busy = (busy / 1024 SIMDs) / (GRBM_GUI_ACTIVE / 8 XCDs)
+      clock     = (GRBM_GUI_ACTIVE / 8 XCDs) / duration."""
+    import csv
+    disp = {}
+    with open(sq_csv) as f:
+        for r in csv.DictReader(f):
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            d = disp.setdefault(key, {"dur_ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    kernels = {}
+    for (_, name), d in disp.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in d or "GRBM_GUI_ACTIVE" not in d or d["dur_ns"] <= 0:
+            continue
+        if "gqa::" not in name:
+            continue
+        k = kernels.setdefault(name, {"dispatches": 0, "busy": 0.0, "grbm": 0.0, "dur_ns": 0.0})
+        k["dispatches"] += 1
+        k["busy"] += d["SQ_VALU_MFMA_BUSY_CYCLES"]
+        k["grbm"] += d["GRBM_GUI_ACTIVE"]
+        k["dur_ns"] += d["dur_ns"]
+    out = {}
+    for name, k in kernels.items():
+        n = k["dispatches"]
+        cyc = k["grbm"] / n / MI355X_XCDS
+        out[name] = {"dispatches": n, "duration_us": k["dur_ns"] / n / 1e3,
+                     "mfma_busy": (k["busy"] / n / MI355X_SIMDS) / cyc,
+                     "clock_ghz": cyc / (k["dur_ns"] / n)}
+    d = {"workload": workload, "source_digest": kernel_digest(ALL_SOURCES),
+         "counters": "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE", "kernels": out}
+    path = out_path or counters_file(workload)
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(d))
+    return d
+
+
+def measured_counters(workload, kernel_substr):
+    """(mfma_busy, clock_ghz) of the kernel whose name contains kernel_substr,
+    from the committed counter file of the workload, or None if missing or
+    taken on other kernel sources."""
+    try:
+        with open(counters_file(workload)) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != kernel_digest(ALL_SOURCES):
+        return None
+    for name, k in d.get("kernels", {}).items():
+        if kernel_substr in name:
+            return k
+    return None
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def kernel_digest(paths):
@@ -144,45 +238,67 @@ def time_launches(fn, steps, warmup, settle_s=1.0):
     return start.elapsed_time(stop) / steps  # ms per launch
 
 
-def cpu_baseline(inp, w, o_gpu, target_s=12.0):
-    """Time the fp64 oracle on random query rows of the workload (host cores)."""
-    import numpy as np
+def _sample_rows(total_rows, per_row_s, target_s, rng, n0):
+    n = int(min(total_rows, max(n0, target_s / max(per_row_s, 1e-9))))
+    return np.sort(rng.choice(total_rows, size=n, replace=False)) if n < total_rows else np.arange(total_rows)
+
+
+def cpu_baseline(inp, w, o_gpu, target_s=8.0, row_flops=None, oracle_kw=None, total_flops=None):
+    """The oracle on the host cores, on bounded samples of the workload's query
+    rows: the float-accumulation build of the oracle source is timed (value),
+    the fp64 build both timed (fp64_value) and compared with the GPU output on
+    its rows (parity_ok: max-abs <= 2e-2 and rel-L2 <= 5e-3)."""
     import oracle
     from workloads import attention_flops
 
+    oracle_kw = dict(oracle_kw or {"causal": w.causal})
     threads = oracle.max_threads()
     rng = np.random.default_rng(12345)
     total_rows = w.B * w.K * w.G * w.T
-    # calibrate on a small sample, then size the timed sample to ~target_s
-    n = min(2048, total_rows)
-    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
-    t0 = time.perf_counter()
-    oracle.fwd(inp["q"], inp["k"], inp["v"], causal=w.causal, rows=rows)
-    per_row = (time.perf_counter() - t0) / n
-    n = int(min(total_rows, max(n, target_s / max(per_row, 1e-9))))
-    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
-    t0 = time.perf_counter()
-    ref_o, _ = oracle.fwd(inp["q"], inp["k"], inp["v"], causal=w.causal, rows=rows)
-    elapsed = time.perf_counter() - t0
-    t = rows % w.T
-    visible = (t + 1) if w.causal else np.full_like(t, w.S)
-    flops = float(4.0 * w.H * visible.sum())
-    got = o_gpu.reshape(-1, w.H)[rows].float().cpu().numpy()
+    if row_flops is None:
+        def row_flops(rows):
+            t = rows % w.T
+            visible = (t + 1) if w.causal else np.full_like(t, w.S)
+            return float(4.0 * w.H * visible.sum())
+    full = total_flops or attention_flops(w.B, w.K, w.G, w.T, w.S, w.H, w.causal)
+    legs = {}
+    for prec in ("f64", "f32"):
+        n0 = min(2048, total_rows)
+        rows = np.sort(rng.choice(total_rows, size=n0, replace=False))
+        t0 = time.perf_counter()
+        oracle.fwd(inp["q"], inp["k"], inp["v"], rows=rows, precision=prec, **oracle_kw)
+        per_row = (time.perf_counter() - t0) / n0
+        rows = _sample_rows(total_rows, per_row, target_s, rng, n0)
+        t0 = time.perf_counter()
+        ref_o, _ = oracle.fwd(inp["q"], inp["k"], inp["v"], rows=rows, precision=prec, **oracle_kw)
+        elapsed = time.perf_counter() - t0
+        legs[prec] = (rows, ref_o, elapsed, row_flops(rows))
+    rows, ref_o, elapsed64, flops64 = legs["f64"]
+    got = o_gpu.reshape(-1, w.H)[torch_index(rows, o_gpu.device)].float().cpu().numpy()
     err = float(np.abs(got - ref_o).max())
     rel = float(np.linalg.norm(got - ref_o) / np.linalg.norm(ref_o))
-    full = attention_flops(w.B, w.K, w.G, w.T, w.S, w.H, w.causal)
+    rows32, _, elapsed32, flops32 = legs["f32"]
     return {
-        "value": flops / elapsed / 1e12,
+        "value": flops32 / elapsed32 / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "%d random query rows of the workload (%.3g of its FLOPs), fp64 oracle, %.1f s" % (
-            n, flops / full, elapsed),
+        "cpu_model": host_cpu_model(),
+        "sample": "%d random query rows (%.3g of the workload's FLOPs) through the float-accumulation build of "
+                  "the oracle source, %.1f s; the fp64 build on %d rows (%.3g), %.1f s" % (
+                      len(rows32), flops32 / full, elapsed32, len(rows), flops64 / full, elapsed64),
+        "fp64_value": flops64 / elapsed64 / 1e12,
         "sample_max_abs_vs_gpu": err,
         "sample_rel_l2_vs_gpu": rel,
-        "rows": int(n),
-        "elapsed_s": elapsed,
+        "parity_ok": bool(err <= O_MAX_ABS and rel <= O_REL_L2),
+        "rows": int(len(rows32)),
+        "elapsed_s": elapsed32,
     }
+
+
+def torch_index(rows, device):
+    import torch
+    return torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(device)
 
 
 def decode_bench(args):
@@ -245,7 +361,7 @@ def decode_bench(args):
     if not args.no_cpu_baseline:
         step()
         torch.cuda.synchronize()
-        cb = cpu_baseline(inp_cpu, w, o, target_s=12.0)
+        cb = cpu_baseline(inp_cpu, w, o)
         # the oracle's rate in the metric's unit: each sampled row stands for
         # its share of the launch's algorithmic bytes
         total_rows = w.B * w.K * w.G * w.T
@@ -253,7 +369,7 @@ def decode_bench(args):
         cb["value"] = cb["rows"] / total_rows * hbm_bytes / cb["elapsed_s"] / 1e9
         cb["unit"] = "GB/s"
         result["cpu_baseline"] = cb
-    print(json.dumps(result), flush=True)
+    finish(result)
 
 
 def window_bench(args):
@@ -322,42 +438,40 @@ def window_bench(args):
     if not args.no_cpu_baseline:
         step()
         torch.cuda.synchronize()
-        result["cpu_baseline"] = window_cpu_baseline(q, k, v, w, win, o, pairs)
+
+        def row_flops(rows):
+            t = rows % w.T
+            return float(4.0 * w.H * (np.minimum(t, w.S - 1) - np.maximum(0, t - win[0]) + 1).sum())
+
+        result["cpu_baseline"] = cpu_baseline({"q": q, "k": k, "v": v}, w, o, row_flops=row_flops,
+                                              oracle_kw={"causal": True, "window": win}, total_flops=flops)
+    finish(result)
+
+
+def finish(result):
+    """Print the one JSON line; a sampled parity miss exits with status 3."""
     print(json.dumps(result), flush=True)
+    cb = result.get("cpu_baseline")
+    if cb is not None and not cb.get("parity_ok", True):
+        print("parity miss: the GPU output differs from the oracle beyond max-abs %.0e / rel-L2 %.0e "
+              "on the sampled rows" % (O_MAX_ABS, O_REL_L2), file=sys.stderr)
+        sys.exit(3)
 
 
-def window_cpu_baseline(q, k, v, w, win, o_gpu, pairs, target_s=12.0):
-    """The fp64 oracle with the same window on random query rows (host cores)."""
-    import numpy as np
-    import oracle
-
-    threads = oracle.max_threads()
-    rng = np.random.default_rng(12345)
-    total_rows = w.B * w.K * w.G * w.T
-    n = min(2048, total_rows)
-    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
-    t0 = time.perf_counter()
-    oracle.fwd(q, k, v, causal=True, rows=rows, window=win)
-    per_row = (time.perf_counter() - t0) / n
-    n = int(min(total_rows, max(n, target_s / max(per_row, 1e-9))))
-    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
-    t0 = time.perf_counter()
-    ref_o, _ = oracle.fwd(q, k, v, causal=True, rows=rows, window=win)
-    elapsed = time.perf_counter() - t0
-    t = rows % w.T
-    visible = np.minimum(t, w.S - 1) - np.maximum(0, t - win[0]) + 1
-    flops = float(4.0 * w.H * visible.sum())
-    got = o_gpu.reshape(-1, w.H)[rows].float().cpu().numpy()
-    return {
-        "value": flops / elapsed / 1e12,
-        "unit": "TFLOP/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": "%d of the %d query rows, drawn at random (%.3g of the visible pairs), fp64 oracle, %.1f s" % (
-            n, total_rows, visible.sum() / pairs, elapsed),
-        "sample_max_abs_vs_gpu": float(np.abs(got - ref_o).max()),
-        "sample_rel_l2_vs_gpu": float(np.linalg.norm(got - ref_o) / np.linalg.norm(ref_o)),
-    }
+def add_counter_figures(roof, workload, kernel_substr, ms):
+    """MFMA-busy fraction, running clock and the fraction of the peak at that
+    clock from the committed counter file (None when it was taken on other
+    kernel sources), and HBM GB/s from the measured traffic."""
+    c = measured_counters(workload, kernel_substr)
+    roof["mfma_busy"] = c["mfma_busy"] if c else None
+    roof["clock_ghz"] = c["clock_ghz"] if c else None
+    roof["frac_at_clock"] = roof["frac"] * MI355X_PEAK_CLOCK_GHZ / c["clock_ghz"] if c else None
+    roof["counters_kernel_us"] = c["duration_us"] if c else None
+    roof["counters_file"] = os.path.relpath(counters_file(workload), ROOT) if c else None
+    alg = roof.get("algorithmic_hbm_bytes_per_launch")
+    roof["algorithmic_hbm_gbps"] = alg / (ms * 1e-3) / 1e9 if alg else None
+    roof["hbm_gbps"] = roof["traffic"] / (ms * 1e-3) / 1e9 if roof.get("traffic") else None
+    roof["hbm_frac"] = roof["hbm_gbps"] / MI355X_HBM_GBPS if roof["hbm_gbps"] else None
 
 
 def main():
@@ -380,11 +494,18 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a known-size "
                          "reference dispatch for the HBM byte counters)")
+    ap.add_argument("--write-counters", metavar="SQ_CSV",
+                    help="write the workload's per-kernel MFMA-busy fraction and clock from a rocprofv3 --pmc "
+                         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE counter CSV and exit")
     args = ap.parse_args()
     if args.write_traffic:
         if not args.copy_calibration_mib:
             ap.error("--write-traffic needs --copy-calibration-mib")
         write_traffic(args.write_traffic[0], args.write_traffic[1], args.copy_calibration_mib)
+        return
+    if args.write_counters:
+        from workloads import workload_by_bench_name
+        write_counters(args.write_counters, workload_by_bench_name(args.workload).name)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (--gpus %d refused)"
@@ -406,16 +527,18 @@ def main():
         return
     w = HEADLINE
     kernel = "attn_fwd_pp_kernel<128,64,true,false,false,0> (ping-pong, dense causal)"
+    kernel_substr = "attn_fwd_pp_kernel<128, 64, true, false, false, 0>"
     seg = None
     if args.workload == "long":
         w = WORKLOADS["causal_b1_k2_g8_t32768_h256"]
         kernel = "attn_fwd_pp_kernel<256,32,true,false,false,0> (ping-pong, dense causal)"
+        kernel_substr = "attn_fwd_pp_kernel<256, 32, true, false, false, 0>"
         args.no_backward = True
     elif args.workload == "segments":
         w = WORKLOADS["segments_causal_b4_k8_g4_t2048_h128"]
         kernel = "attn_fwd_pp_kernel<128,64,true,false,true,2> (ping-pong, causal with segment ids; loads spread over the MFMA phase)"
+        kernel_substr = "attn_fwd_pp_kernel<128, 64, true, false, true, 2>"
         args.no_backward = True
-        args.no_cpu_baseline = True
         seg = make_segment_ids(w.B, w.T, w.seed)
     t = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=not args.no_backward)
     q, k, v = t[:3]
@@ -433,11 +556,18 @@ def main():
 
     ms = time_launches(step, args.steps, args.warmup, args.settle_seconds)
     flops = attention_flops(w.B, w.K, w.G, w.T, w.S, w.H, w.causal)
+    causal_half_flops = flops
+    if seg is not None:
+        # packed segments: the executed work is the visible pairs only
+        flops = visible_pairs_flops(w.H, w.K, w.G, seg, causal=True)
     tflops = flops / (ms * 1e-3) / 1e12
     fwd_bytes = 2 * (qd.numel() + kd.numel() + vd.numel() + o.numel()) + 4 * lse.numel()
+    if seg is not None:
+        fwd_bytes += 4 * 2 * seg.numel()
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if seg is None else
+        "attention TFLOP/s (fwd, causal, packed segments; visible pairs) at 1 GPU; % of bf16 MFMA peak",
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -465,10 +595,11 @@ def main():
         },
     }
 
+    add_counter_figures(result["roofline"], w.name, kernel_substr, ms)
     if seg is not None:
-        vis = visible_pairs_flops(w.H, w.K, w.G, seg, causal=True)
-        result["visible_pairs"] = {"flops_per_launch": vis, "tflops": vis / (ms * 1e-3) / 1e12,
-                                   "fraction_of_causal_half": vis / flops}
+        result["causal_half"] = {"flops_per_launch": causal_half_flops,
+                                 "tflops": causal_half_flops / (ms * 1e-3) / 1e12,
+                                 "visible_fraction": flops / causal_half_flops}
 
     if not args.no_backward:
         ws = torch.empty(gqa.attn_bwd_workspace_bytes(w.B, w.K, w.G, w.T, w.S, w.H), dtype=torch.uint8, device=dev)
@@ -484,8 +615,16 @@ def main():
             bms = time_launches(bstep, max(5, args.steps // 2), max(2, args.warmup // 2), args.settle_seconds)
             bflops = 2.5 * flops
             result["backward"] = {"ms": bms, "tflops": bflops / (bms * 1e-3) / 1e12,
+                                  "frac": bflops / (bms * 1e-3) / 1e12 / MI355X_BF16_DENSE_TFLOPS,
                                   "flops_convention": "2.5x forward (5 matmuls per visible pair)",
                                   "fwd_plus_bwd_tflops": 3.5 * flops / ((ms + bms) * 1e-3) / 1e12}
+            kern = {}
+            for sub in ("attn_bwd_delta", "attn_bwd_dq", "attn_bwd_dkv"):
+                c = measured_counters(w.name, sub)
+                if c:
+                    kern[sub] = {"mfma_busy": c["mfma_busy"], "clock_ghz": c["clock_ghz"],
+                                 "duration_us": c["duration_us"]}
+            result["backward"]["kernels"] = kern or None
         except gqa.GqaAttnError as e:
             result["backward"] = {"error": str(e)}
 
@@ -501,8 +640,23 @@ def main():
     if not args.no_cpu_baseline:
         step()
         torch.cuda.synchronize()
-        result["cpu_baseline"] = cpu_baseline(inp_cpu, w, o, target_s=12.0)
-    print(json.dumps(result), flush=True)
+        row_flops, okw = None, {"causal": w.causal}
+        if seg is not None:
+            # a row sees the keys from its segment's start to itself
+            starts = np.zeros((w.B, w.T), dtype=np.int64)
+            sn = seg.numpy()
+            for b in range(w.B):
+                idx = np.r_[0, np.flatnonzero(sn[b, 1:] != sn[b, :-1]) + 1]
+                starts[b] = idx[np.searchsorted(idx, np.arange(w.T), side="right") - 1]
+
+            def row_flops(rows):
+                t = rows % w.T
+                b = rows // (w.K * w.G * w.T)
+                return float(4.0 * w.H * (t - starts[b, t] + 1).sum())
+
+            okw = {"causal": True, "q_seg": seg, "kv_seg": seg}
+        result["cpu_baseline"] = cpu_baseline(inp_cpu, w, o, row_flops=row_flops, oracle_kw=okw, total_flops=flops)
+    finish(result)
 
 
 if __name__ == "__main__":

@@ -5,6 +5,9 @@ baseline leg import this package; the product path (the HIP library and its
 Python binding) never does, and shares no code with it.
 
 ``fwd`` and ``bwd`` call the plain fp64 C definition in ``gqa_oracle.c``.
+``fwd(..., precision="f32")`` calls the same source built with float
+accumulation (``libgqa_oracle_f32.so``): a timed CPU baseline only, checked
+against the fp64 build, never a parity reference.
 ``online.chunked_fwd`` is a separate numpy model of the chunked
 online-softmax recurrence, used only to cross-check the plain definition.
 
@@ -24,25 +27,32 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gqa_oracle.c")
 _LIB = os.path.join(_HERE, "libgqa_oracle.so")
-_lib = None
+_LIB_F32 = os.path.join(_HERE, "libgqa_oracle_f32.so")
+_libs = {}
+
+
+def _build_one(path, defines, force):
+    if force or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        tmp = path + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", *defines, "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, path)
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP). Returns the library path."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
+    """Compile the oracle with gcc (-O2, OpenMP): the fp64 build and the
+    float-accumulation build of the same source. Returns the fp64 path."""
+    _build_one(_LIB, [], force)
+    _build_one(_LIB_F32, ["-DORACLE_ACC_FLOAT"], force)
     return _LIB
 
 
-def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+def _load(precision="f64"):
+    if precision not in _libs:
+        path = {"f64": _LIB, "f32": _LIB_F32}[precision]
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         lib.oracle_fwd_rows.restype = ctypes.c_int
@@ -53,8 +63,8 @@ def _load():
                                         I64, I64, I64, I64, P, P, P, I64, P, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
-        _lib = lib
-    return _lib
+        _libs[precision] = lib
+    return _libs[precision]
 
 
 def max_threads() -> int:
@@ -118,7 +128,8 @@ def _causal(causal):
     return c
 
 
-def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None, window=None, prefix=0):
+def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None, window=None, prefix=0,
+        precision="f64"):
     """Plain fp64 attention. Returns (O, lse) as float64 numpy arrays.
 
     rows=None: O has q's shape and lse q's shape minus H.
@@ -127,6 +138,7 @@ def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None,
     window=(wl, wr): key s visible to query t only if t - wl <= s <= t + wr
     (a side of -1 is unbounded). prefix=p: keys s < p are visible to every
     query whatever the causal rule and window say (segments still apply).
+    precision="f32" runs the float-accumulation build (timing only).
     """
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
     B, K, G, T, H = qb.shape
@@ -139,7 +151,7 @@ def fwd(q, k, v, *, causal=False, q_seg=None, kv_seg=None, mask=None, rows=None,
     n = B * K * G * T if r is None else len(r)
     o = np.empty((n, H), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
-    rc = _load().oracle_fwd_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(qs), _ptr(ks), _ptr(mk),
+    rc = _load(precision).oracle_fwd_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(qs), _ptr(ks), _ptr(mk),
                                  B, K, G, T, S, H, _causal(causal), *_window(window), int(prefix), n, _ptr(r),
                                  _ptr(o), _ptr(lse))
     if rc != 0:

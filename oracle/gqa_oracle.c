@@ -41,9 +41,14 @@
  *   dK[s,:] = sum_{g,t} dS[g,t,s] q[g,t,:];  dV[s,:] = sum_{g,t} P[g,t,s] dO[g,t,:]
  *   Gradients are with respect to the pre-scaled q as passed.
  *
- * Inputs are bf16 bit patterns (uint16); each is widened exactly to double.
- * All sums run in double, in index order. OpenMP splits independent output
- * rows across threads; it does not change any row's arithmetic.
+ * Inputs are bf16 bit patterns (uint16); each is widened exactly to the
+ * accumulation type acc_t. All sums run in acc_t, in index order. OpenMP
+ * splits independent output rows across threads; it does not change any row's
+ * arithmetic. acc_t is double (the parity reference, libgqa_oracle.so); built
+ * with -DORACLE_ACC_FLOAT it is float (libgqa_oracle_f32.so, the same
+ * definition in single precision, used only as a timed CPU baseline and
+ * checked against the double build). Results are returned as double either
+ * way.
  */
 #include <math.h>
 #include <stdint.h>
@@ -53,11 +58,21 @@
 #include <omp.h>
 #endif
 
-static double bf(uint16_t bits) {
+#ifdef ORACLE_ACC_FLOAT
+typedef float acc_t;
+#define ACC_EXP expf
+#define ACC_LOG logf
+#else
+typedef double acc_t;
+#define ACC_EXP exp
+#define ACC_LOG log
+#endif
+
+static acc_t bf(uint16_t bits) {
     uint32_t u = (uint32_t)bits << 16;
     float f;
     memcpy(&f, &u, sizeof f);
-    return (double)f;
+    return (acc_t)f;
 }
 
 typedef struct {
@@ -89,8 +104,8 @@ static const uint16_t *kv_row(const problem *p, const uint16_t *base, int64_t b,
     return base + ((b * p->K + k) * p->S + s) * p->H;
 }
 
-static double dot_bf(const uint16_t *x, const uint16_t *y, int64_t H) {
-    double acc = 0.0;
+static acc_t dot_bf(const uint16_t *x, const uint16_t *y, int64_t H) {
+    acc_t acc = 0.0;
     for (int64_t h = 0; h < H; h++) acc += bf(x[h]) * bf(y[h]);
     return acc;
 }
@@ -99,19 +114,19 @@ static double dot_bf(const uint16_t *x, const uint16_t *y, int64_t H) {
  * over visible keys; logits written to l[] (S entries, masked ones unused).
  * Returns the number of visible keys. */
 static int64_t row_softmax_stats(const problem *p, int64_t b, int64_t k, int64_t g, int64_t t,
-                                 double *l, double *m_out, double *z_out) {
+                                 acc_t *l, acc_t *m_out, acc_t *z_out) {
     const uint16_t *qr = q_row(p, p->q, b, k, g, t);
     int64_t nvis = 0;
-    double m = -INFINITY;
+    acc_t m = -INFINITY;
     for (int64_t s = 0; s < p->S; s++) {
         if (!is_visible(p, b, t, s)) continue;
         l[s] = dot_bf(qr, kv_row(p, p->k, b, k, s), p->H);
         if (l[s] > m) m = l[s];
         nvis++;
     }
-    double z = 0.0;
+    acc_t z = 0.0;
     for (int64_t s = 0; s < p->S; s++)
-        if (is_visible(p, b, t, s)) z += exp(l[s] - m);
+        if (is_visible(p, b, t, s)) z += ACC_EXP(l[s] - m);
     *m_out = m;
     *z_out = z;
     return nvis;
@@ -133,7 +148,8 @@ int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     int err = 0;
 #pragma omp parallel
     {
-        double *l = (double *)malloc(sizeof(double) * (size_t)S);
+        acc_t *l = (acc_t *)malloc(sizeof(acc_t) * (size_t)(S + H));
+        acc_t *oacc = l ? l + S : NULL; /* the row's output accumulators */
         if (!l) {
 #pragma omp atomic write
             err = 3;
@@ -148,21 +164,23 @@ int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 continue;
             }
             int64_t t = r % T, g = (r / T) % G, kk = (r / (T * G)) % K, b = r / (T * G * K);
-            double m, z;
+            acc_t m, z;
             double *o = o_out + i * H;
             int64_t nvis = row_softmax_stats(&p, b, kk, g, t, l, &m, &z);
-            for (int64_t h = 0; h < H; h++) o[h] = 0.0;
+            for (int64_t h = 0; h < H; h++) oacc[h] = 0.0;
             if (nvis == 0) {
+                for (int64_t h = 0; h < H; h++) o[h] = 0.0;
                 if (lse_out) lse_out[i] = -INFINITY;
                 continue;
             }
             for (int64_t s = 0; s < S; s++) {
                 if (!is_visible(&p, b, t, s)) continue;
-                double w = exp(l[s] - m) / z;
+                acc_t w = ACC_EXP(l[s] - m) / z;
                 const uint16_t *vr = kv_row(&p, v, b, kk, s);
-                for (int64_t h = 0; h < H; h++) o[h] += w * bf(vr[h]);
+                for (int64_t h = 0; h < H; h++) oacc[h] += w * bf(vr[h]);
             }
-            if (lse_out) lse_out[i] = m + log(z);
+            for (int64_t h = 0; h < H; h++) o[h] = (double)oacc[h];
+            if (lse_out) lse_out[i] = (double)(m + ACC_LOG(z));
         }
         free(l);
     }
@@ -171,11 +189,11 @@ int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 
 /* Per-row statistics needed by the backward for every query row of one
  * (b, kv-head) unit: m, Z and D = sum_s P dP.  Arrays of length G*T. */
-static void unit_row_stats(const problem *p, int64_t b, int64_t k, double *m_arr, double *z_arr,
-                           double *d_arr, int *err) {
+static void unit_row_stats(const problem *p, int64_t b, int64_t k, acc_t *m_arr, acc_t *z_arr,
+                           acc_t *d_arr, int *err) {
 #pragma omp parallel
     {
-        double *l = (double *)malloc(sizeof(double) * (size_t)p->S);
+        acc_t *l = (acc_t *)malloc(sizeof(acc_t) * (size_t)p->S);
         if (!l) {
 #pragma omp atomic write
             *err = 3;
@@ -184,16 +202,16 @@ static void unit_row_stats(const problem *p, int64_t b, int64_t k, double *m_arr
         for (int64_t r = 0; r < p->G * p->T; r++) {
             if (!l) continue;
             int64_t g = r / p->T, t = r % p->T;
-            double m, z;
+            acc_t m, z;
             int64_t nvis = row_softmax_stats(p, b, k, g, t, l, &m, &z);
             m_arr[r] = m;
             z_arr[r] = z;
-            double d = 0.0;
+            acc_t d = 0.0;
             if (nvis > 0) {
                 const uint16_t *dor = q_row(p, p->dout, b, k, g, t);
                 for (int64_t s = 0; s < p->S; s++) {
                     if (!is_visible(p, b, t, s)) continue;
-                    double w = exp(l[s] - m) / z;
+                    acc_t w = ACC_EXP(l[s] - m) / z;
                     d += w * dot_bf(dor, kv_row(p, p->v, b, k, s), p->H);
                 }
             }
@@ -235,9 +253,9 @@ int oracle_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
         need[r / S] = 1;
     }
     size_t gt = (size_t)(G * T);
-    double *m_all = (double *)malloc(sizeof(double) * gt * (size_t)(B * K));
-    double *z_all = (double *)malloc(sizeof(double) * gt * (size_t)(B * K));
-    double *d_all = (double *)malloc(sizeof(double) * gt * (size_t)(B * K));
+    acc_t *m_all = (acc_t *)malloc(sizeof(acc_t) * gt * (size_t)(B * K));
+    acc_t *z_all = (acc_t *)malloc(sizeof(acc_t) * gt * (size_t)(B * K));
+    acc_t *d_all = (acc_t *)malloc(sizeof(acc_t) * gt * (size_t)(B * K));
     if (!m_all || !z_all || !d_all) { free(need); free(m_all); free(z_all); free(d_all); return 3; }
     for (int64_t u = 0; u < B * K; u++)
         if (need[u]) unit_row_stats(&p, u / K, u % K, m_all + u * gt, z_all + u * gt, d_all + u * gt, &err);
@@ -249,21 +267,21 @@ int oracle_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
             int64_t r = qrows ? qrows[i] : i;
             int64_t t = r % T, g = (r / T) % G, kk = (r / (T * G)) % K, b = r / (T * G * K);
             int64_t u = b * K + kk;
-            double m = m_all[u * gt + g * T + t], z = z_all[u * gt + g * T + t];
-            double dd = d_all[u * gt + g * T + t];
+            acc_t m = m_all[u * gt + g * T + t], z = z_all[u * gt + g * T + t];
+            acc_t dd = d_all[u * gt + g * T + t];
             double *dq = dq_out + i * H;
             for (int64_t h = 0; h < H; h++) dq[h] = 0.0;
-            if (d_out) d_out[i] = dd;
+            if (d_out) d_out[i] = (double)dd;
             if (z == 0.0) continue;
             const uint16_t *qr = q_row(&p, q, b, kk, g, t);
             const uint16_t *dor = q_row(&p, dout, b, kk, g, t);
             for (int64_t s = 0; s < S; s++) {
                 if (!is_visible(&p, b, t, s)) continue;
                 const uint16_t *kr = kv_row(&p, k, b, kk, s);
-                double w = exp(dot_bf(qr, kr, H) - m) / z;
-                double dp = dot_bf(dor, kv_row(&p, v, b, kk, s), H);
-                double ds = w * (dp - dd);
-                for (int64_t h = 0; h < H; h++) dq[h] += ds * bf(kr[h]);
+                acc_t w = ACC_EXP(dot_bf(qr, kr, H) - m) / z;
+                acc_t dp = dot_bf(dor, kv_row(&p, v, b, kk, s), H);
+                acc_t ds = w * (dp - dd);
+                for (int64_t h = 0; h < H; h++) dq[h] += (double)(ds * bf(kr[h]));
             }
         }
     }
@@ -285,18 +303,18 @@ int oracle_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
             for (int64_t g = 0; g < G; g++) {
                 for (int64_t t = 0; t < T; t++) {
                     if (!is_visible(&p, b, t, s)) continue;
-                    double z = z_all[u * gt + g * T + t];
+                    acc_t z = z_all[u * gt + g * T + t];
                     if (z == 0.0) continue;
-                    double m = m_all[u * gt + g * T + t];
-                    double dd = d_all[u * gt + g * T + t];
+                    acc_t m = m_all[u * gt + g * T + t];
+                    acc_t dd = d_all[u * gt + g * T + t];
                     const uint16_t *qr = q_row(&p, q, b, kk, g, t);
                     const uint16_t *dor = q_row(&p, dout, b, kk, g, t);
-                    double w = exp(dot_bf(qr, kr, H) - m) / z;
-                    double dp = dot_bf(dor, vr, H);
-                    double ds = w * (dp - dd);
+                    acc_t w = ACC_EXP(dot_bf(qr, kr, H) - m) / z;
+                    acc_t dp = dot_bf(dor, vr, H);
+                    acc_t ds = w * (dp - dd);
                     for (int64_t h = 0; h < H; h++) {
-                        if (dk) dk[h] += ds * bf(qr[h]);
-                        if (dv) dv[h] += w * bf(dor[h]);
+                        if (dk) dk[h] += (double)(ds * bf(qr[h]));
+                        if (dv) dv[h] += (double)(w * bf(dor[h]));
                     }
                 }
             }

@@ -46,3 +46,60 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_write_counters_busy_fraction_and_clock(tmp_path):
+    """Per dispatch: mfma_busy = (busy / 1024 SIMDs) / (GRBM_GUI_ACTIVE / 8
+    XCDs), clock = (GRBM_GUI_ACTIVE / 8) / duration; dispatches average and
+    other kernels are kept apart."""
+    path, out = tmp_path / "sq.csv", tmp_path / "counters.json"
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    other = "void gqa::attn_bwd_dkv2_kernel<128, true>(gqa::BwdArgs, int)"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        # dispatch 1: 800000 cycles per XCD over 400 us -> 2.0 GHz; busy 0.5 of them on every SIMD
+        for name, val in (("GRBM_GUI_ACTIVE", 8 * 800000.0), ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 400000.0)):
+            w.writerow({"Dispatch_Id": 1, "Kernel_Name": KERNEL, "Counter_Name": name, "Counter_Value": val,
+                        "Start_Timestamp": 1000, "End_Timestamp": 1000 + 400000})
+        # dispatch 2: 1.5 GHz, busy 0.7
+        for name, val in (("GRBM_GUI_ACTIVE", 8 * 600000.0), ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 420000.0)):
+            w.writerow({"Dispatch_Id": 2, "Kernel_Name": KERNEL, "Counter_Name": name, "Counter_Value": val,
+                        "Start_Timestamp": 5000000, "End_Timestamp": 5000000 + 400000})
+        for name, val in (("GRBM_GUI_ACTIVE", 8 * 100.0), ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 10.0)):
+            w.writerow({"Dispatch_Id": 3, "Kernel_Name": other, "Counter_Name": name, "Counter_Value": val,
+                        "Start_Timestamp": 0, "End_Timestamp": 100})
+        w.writerow({"Dispatch_Id": 4, "Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "GRBM_GUI_ACTIVE",
+                    "Counter_Value": 5.0, "Start_Timestamp": 0, "End_Timestamp": 10})
+    d = bench.write_counters(str(path), "causal_b1_k8_g4_t8192_h128", out_path=str(out))
+    k = d["kernels"][KERNEL]
+    assert k["dispatches"] == 2
+    assert k["clock_ghz"] == pytest.approx(700000.0 / 400000.0)
+    assert k["mfma_busy"] == pytest.approx(410000.0 / 700000.0)
+    assert k["duration_us"] == pytest.approx(400.0)
+    assert d["kernels"][other]["mfma_busy"] == pytest.approx(0.1)
+    assert "__amd_rocclr_copyBuffer" not in d["kernels"]
+    assert d["source_digest"] == bench.kernel_digest(bench.ALL_SOURCES)
+    assert json.loads(out.read_text()) == d
+
+
+def test_counter_figures_need_matching_sources(tmp_path, monkeypatch):
+    roof = {"frac": 0.5, "traffic": 2e8, "algorithmic_hbm_bytes_per_launch": 1.6e8}
+    monkeypatch.setattr(bench, "counters_file", lambda w: str(tmp_path / "c.json"))
+    (tmp_path / "c.json").write_text(json.dumps({"source_digest": "stale", "kernels": {
+        KERNEL: {"mfma_busy": 0.7, "clock_ghz": 2.0, "duration_us": 440.0}}}))
+    bench.add_counter_figures(roof, "w", bench.HEADLINE_KERNEL, 0.4)
+    assert roof["mfma_busy"] is None and roof["clock_ghz"] is None and roof["frac_at_clock"] is None
+    assert roof["hbm_gbps"] == pytest.approx(2e8 / 0.4e-3 / 1e9)
+    (tmp_path / "c.json").write_text(json.dumps({"source_digest": bench.kernel_digest(bench.ALL_SOURCES), "kernels": {
+        KERNEL: {"mfma_busy": 0.7, "clock_ghz": 2.0, "duration_us": 440.0}}}))
+    bench.add_counter_figures(roof, "w", bench.HEADLINE_KERNEL, 0.4)
+    assert roof["mfma_busy"] == 0.7 and roof["frac_at_clock"] == pytest.approx(0.5 * 2.4 / 2.0)
+
+
+def test_finish_exits_3_on_a_parity_miss(capsys):
+    bench.finish({"value": 1.0, "cpu_baseline": {"parity_ok": True}})
+    assert json.loads(capsys.readouterr().out)["value"] == 1.0
+    with pytest.raises(SystemExit) as e:
+        bench.finish({"value": 1.0, "cpu_baseline": {"parity_ok": False}})
+    assert e.value.code == 3

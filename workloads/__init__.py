@@ -76,6 +76,13 @@ WINDOW = Workload("window1024_causal_b1_k8_g4_t8192_h128", 1, 8, 4, 8192, 8192, 
 WINDOW_LEFT = 1023
 
 
+def workload_by_bench_name(name: str) -> Workload:
+    """The workload bench.py's --workload option names."""
+    return {"headline": HEADLINE, "decode": DECODE, "window": WINDOW,
+            "long": WORKLOADS["causal_b1_k2_g8_t32768_h256"],
+            "segments": WORKLOADS["segments_causal_b4_k8_g4_t2048_h128"]}[name]
+
+
 def window_pairs(T: int, S: int, wl: int, causal: bool = True) -> int:
     """Visible (t, s) pairs per head of a causal band t - wl <= s <= t."""
     assert causal
