@@ -220,7 +220,8 @@ int attn_fwd_split_count(int B, int K, int G, int T, int S, int H) {
 size_t attn_bwd_workspace_bytes(int B, int K, int G, int T, int S, int H) {
     (void)H;
     if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return 0;
-    return round256(sizeof(float) * (size_t)B * K * G * T);
+    // D, then lse * log2(e), one fp32 per query row each
+    return 2 * round256(sizeof(float) * (size_t)B * K * G * T);
 }
 
 int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -257,6 +258,7 @@ static int run_bwd(const void *q, const void *k, const void *v, const void *o, c
     a.dk = dk;
     a.dv = dv;
     a.delta = (float *)workspace;
+    a.lse2 = a.delta + round256(sizeof(float) * (size_t)B * K * G * T) / sizeof(float);
     a.q_seg = q_seg;
     a.kv_seg = kv_seg;
     a.B = B, a.K = K, a.G = G, a.T = T, a.S = S;

@@ -13,8 +13,10 @@
 //   dQ = dS K                                                 (bwd_dq)
 // All contractions run on the 32x32x16 bf16 MFMA with fp32 accumulation;
 // P and dS are rounded to bf16 as MFMA operands, except that dS enters the
-// dQ product as a bf16 hi + lo pair. Gradients are written in fp32. The G-sum of dK/dV stays inside one workgroup: no atomics, and the
-// result is deterministic.
+// dQ product as a bf16 hi + lo pair. Gradients are written in fp32. The G-sum
+// of dK/dV stays inside one workgroup: no atomics, and the result is
+// deterministic. The D pass also stores lse * log2(e) per row beside D, the
+// form in which the dK/dV kernel takes it.
 //
 // D equals rowsum(dO * O) in exact arithmetic, but the forward's O carries
 // the rounding of P to bf16 in its PV product; D taken from it moves dQ by
@@ -28,41 +30,9 @@
 #include <type_traits>
 #include <utility>
 
-// pipelined dK/dV kernel for shapes without segment ids at H <= 128
-#ifndef GQA_BWD_DKV2
-#define GQA_BWD_DKV2 1
-#endif
-// its operand reads are issued this many MFMAs ahead of their use
-#ifndef GQA_BWD_DELTA_PP
-#define GQA_BWD_DELTA_PP 1
-#endif
-// dense shapes at H <= 128 run dQ on the ping-pong kernel
-#ifndef GQA_BWD_DQ_PP
-#define GQA_BWD_DQ_PP 1
-#endif
-// its M phase issues the LDS operand reads of a step this many steps ahead
-// (0: no pinned schedule)
-#ifndef GQA_BWD_DQ_PREF
-#define GQA_BWD_DQ_PREF 2
-#endif
-// the same for the ping-pong D pass
-#ifndef GQA_BWD_D_PREF
-#define GQA_BWD_D_PREF 2
-#endif
-#ifndef GQA_BWD_D_BKV
-#define GQA_BWD_D_BKV 64
-#endif
-#ifndef GQA_BWD_DKV_PREF
-#define GQA_BWD_DKV_PREF 6
-#endif
-// its bf16 weight conversions pinned into their slots
-#ifndef GQA_BWD_CVTPIN
-#define GQA_BWD_CVTPIN 0
-#endif
-// its lse / D reads at the end of the iteration before (1) or at the top (0)
-#ifndef GQA_BWD_LDPRE
-#define GQA_BWD_LDPRE 1
-#endif
+// LDS operand reads of the ping-pong M phases (D pass and dQ) are issued this
+// many MFMA steps ahead of their use
+constexpr int kBwdPrefetch = 2;
 
 namespace gqa {
 
@@ -345,41 +315,52 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV for shapes without segment ids at H <= 128: the same products as the
-// kernel above, software-pipelined three steps deep. Q, dO, lse and D of each
-// 32-query step go straight from memory into a four-stage LDS ring (no
-// register staging); iteration i runs the S and dP MFMAs of step i+2 and the
-// dV and dK MFMAs of step i, and computes the weights of step i+1 (whose S and
-// dP came from the previous iteration) between them, so the VALU work never
-// waits on the MFMAs of its own iteration. One wave per SIMD (up to 512
-// registers): the overlap is inside the wave.
+// dK, dV for shapes without segment ids at H <= 128, with the work of each
+// 32-key block split over a pair of waves so that two waves share every SIMD
+// (one wave per SIMD would leave its own VALU work in the way of its MFMAs).
+// One workgroup per (b, kv head, 128 keys), 8 waves: wave p (p < 4, "A") and
+// wave p + 4 ("B") own keys [s0 + 32p, s0 + 32p + 32). Per 32-query step
+// (the same (g, query tile) walk as the kernel above):
+//   A:  S = Q K^T (K^T in registers), P = exp2(S log2e - lse log2e) with the
+//       mask, dV^T += dO^T P; P also goes to LDS in fp32 for B
+//   B:  dP = dO V^T (V^T in registers), dS = P (dP - D) with P from A,
+//       dK^T += Q^T dS
+// Lane (n, c) holds key n and queries acc_row(r, c) of S, P, dP, dS in both
+// waves, so A's P reaches B lane to lane.
 //
-// The loads write 1 KiB per wave instruction lane-linearly into padded-row
-// tiles, each lane fetching the global chunk that belongs in its slot.
+// Iteration i has two phases (workgroup barriers between), so that the two
+// waves of a SIMD alternate between MFMA and VALU work:
+//   phase 1: A  MFMAs S(i+2), dV(i)    B  VALU dS(i) from dP(i) and P(i)
+//   phase 2: A  VALU P(i+1) from S(i+1), written to exchange buffer (i+1) % 2
+//            B  MFMAs dP(i+1), dK(i)
+// B reads P(i) from exchange buffer i % 2, written by A in the iteration
+// before. Q, dO, lse and D of each step go straight from memory into a
+// five-stage LDS ring: A waves load the Q tile and lse, B waves the dO tile
+// and D. Iteration i reads steps i .. i+2 and loads step i+4 into the stage of
+// step i-1, whose last readers finished in iteration i-1; every wave waits for
+// its own loads one iteration later, a barrier before anyone reads them.
 template <int H, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_bwd_dkv2_kernel(BwdArgs a, int n_kblocks) {
-    constexpr int NW = 4, BQ = 32;
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
+    constexpr int NP = 4, BQ = 32;  // wave pairs, queries per step
     constexpr int CPR = H / 8;
     constexpr int KSTEPS = H / 16;
     constexpr int HB = H / 32;
-    // Q / dO tiles in LDS: 32 rows of RS = CPR + 3 16-byte chunks (padded rows:
-    // the b128 row reads are conflict-free and the transpose reads 2-way), so
-    // that every operand address is a per-lane base plus an immediate
-    constexpr int RS = CPR + 3;
-    constexpr int TBLK = (BQ * RS + 63) / 64;     // 1 KiB wave loads per tile
-    constexpr int TILE = TBLK * 512;              // bf16 elements per tile buffer
-    constexpr int TBW = (TBLK + NW - 1) / NW;     // per wave and tensor
-    constexpr int NLD = 2 * TBW + 1;              // loads per wave and step (Q, dO blocks; lse or D)
+    constexpr int RS = CPR + 3;                 // padded Q / dO rows, as in the kernel above
+    constexpr int TBLK = (BQ * RS + 63) / 64;   // 1 KiB wave loads per tile
+    constexpr int TILE = TBLK * 512;
+    constexpr int TBW = (TBLK + NP - 1) / NP;   // tile loads per wave and step
+    constexpr int NLD = TBW + 1;                // + lse (wave 0) or D (wave 4)
     constexpr int NSTAGE = 5;
     __shared__ __attribute__((aligned(1024))) __bf16 sq[NSTAGE][TILE];
     __shared__ __attribute__((aligned(1024))) __bf16 sdo[NSTAGE][TILE];
     __shared__ __attribute__((aligned(1024))) float sld[NSTAGE][2][256];  // lse, D (32 used)
-    // destination of the loads a wave issues only to keep its count per step
-    // the same as the other waves' (out of range: they read nothing)
+    __shared__ __attribute__((aligned(1024))) f32x4 sp[2][NP][4][64];      // P exchange: [buf][pair][q4][lane]
     __shared__ __attribute__((aligned(1024))) char sdummy[1024];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool is_a = wave < NP;
+    const int pair = wave & (NP - 1);
     const int n = lane & 31, c = lane >> 5;
     const int T = a.T, S = a.S, G = a.G;
 
@@ -387,75 +368,61 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int kb_idx = blockIdx.x / units;  // heaviest (causal) key block first
     const int u = blockIdx.x % units;
     const int kh = u % a.K, b = u / a.K;
-    const int s0_wg = kb_idx * 32 * NW;
-    const int s_w = s0_wg + 32 * wave;
+    const int s0_wg = kb_idx * 32 * NP;
+    const int s_w = s0_wg + 32 * pair;
     const int s = s_w + n;
     const bool k_valid = s < S;
     const size_t bk = (size_t)b * a.K + kh;
 
-    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    // A: K^T, B: V^T (the B operands of S and dP): lane (n, c), k-step ks holds
+    // row s, h = 16 ks + 8 c .. + 7
+    bf16x8 kv[KSTEPS];
     {
-        const __bf16 *krow = a.k + (bk * S + s) * H;
-        const __bf16 *vrow = a.v + (bk * S + s) * H;
+        const __bf16 *row = (is_a ? a.k : a.v) + (bk * S + s) * H;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ks++) {
-            kf[ks] = k_valid ? *(const bf16x8 *)(krow + 16 * ks + 8 * c) : bf16x8{};
-            vf[ks] = k_valid ? *(const bf16x8 *)(vrow + 16 * ks + 8 * c) : bf16x8{};
-        }
+        for (int ks = 0; ks < KSTEPS; ks++) kv[ks] = k_valid ? *(const bf16x8 *)(row + 16 * ks + 8 * c) : bf16x8{};
     }
 
-    // steps: (g, query tile) pairs, g outer; causal: tiles holding some t >= s0_wg
-    // query tiles that can see the block's keys: t in [s - R, s + L] for the
-    // band sides L, R, or all of them for a block that starts in the prefix;
-    // qt_end is exclusive
+    // query tiles that can see the block's keys (as in the kernel above)
     const int WL = a.wl, WR = a.wr;
     const int n_qt = (T + BQ - 1) / BQ;
     const bool blk_pfx = s0_wg < a.prefix;
     const int qt_begin = blk_pfx ? 0 : min(n_qt, max(0, s0_wg - WR) / BQ);
-    const int qt_end = blk_pfx ? n_qt : max(qt_begin, min(n_qt, (s0_wg + 32 * NW - 1 + WL) / BQ + 1));
-    const int nq = qt_end - qt_begin;
-    const int n_steps = G * nq;
+    const int qt_end = blk_pfx ? n_qt : max(qt_begin, min(n_qt, (s0_wg + 32 * NP - 1 + WL) / BQ + 1));
+    const int n_steps = G * (qt_end - qt_begin);
 
-    // loads of one step: Q and dO tiles (wave w: blocks w, w + NW, ...), lse
-    // (wave 0), D (wave 1). Every wave issues NLD loads per step, without
-    // branches: a block past the tile, the lse / D load of waves 2 and 3, and
-    // every load of a step past the last one get an out-of-range offset and
-    // the dummy destination.
-    const i32x4 qrs = make_rsrc_words(a.q + bk * G * (size_t)T * H, G * T * H * 2);
-    const i32x4 drs = make_rsrc_words(a.dout + bk * G * (size_t)T * H, G * T * H * 2);
-    const i32x4 ldrs = wave == 0 ? make_rsrc_words(a.lse + bk * G * (size_t)T, G * T * 4)
-                                 : make_rsrc_words(a.delta + bk * G * (size_t)T, G * T * 4);
+    // loads: A waves the Q tile (blocks pair, pair + 4, ...) and, wave 0, lse;
+    // B waves the dO tile and, wave 4, D. Every wave issues NLD loads per step
+    // without branches; a load with nothing to fetch gets an out-of-range
+    // offset (reads nothing) and the dummy destination.
+    const i32x4 trs = is_a ? make_rsrc_words(a.q + bk * G * (size_t)T * H, G * T * H * 2)
+                           : make_rsrc_words(a.dout + bk * G * (size_t)T * H, G * T * H * 2);
+    const i32x4 lrs = is_a ? make_rsrc_words(a.lse2 + bk * G * (size_t)T, G * T * 4)
+                           : make_rsrc_words(a.delta + bk * G * (size_t)T, G * T * 4);
     constexpr unsigned kOutOfRange = 0x80000000u;
-    // slot p of a tile holds chunk min(p % RS, CPR - 1) of row p / RS (the
-    // padding slots repeat the row's last chunk; rows past 31 are not read)
     int t_off[TBW];
 #pragma unroll
     for (int i = 0; i < TBW; i++) {
-        const int p = (wave + i * NW) * 64 + lane;
+        const int p = (pair + i * NP) * 64 + lane;
         t_off[i] = ((p / RS) * H + min(p % RS, CPR - 1) * 8) * 2;
     }
-    const unsigned q_dst0 = lds_addr(sq[0]) + wave * 1024, d_dst0 = lds_addr(sdo[0]) + wave * 1024;
-    const unsigned ld_dst0 = lds_addr(sld[0][wave & 1]), dummy = lds_addr(sdummy);
-    // load j (< NLD) of a step whose query rows start at row0 (g T + t0), or
-    // of no step (row0 < 0), into a stage
+    const unsigned t_dst0 = (is_a ? lds_addr(sq[0]) : lds_addr(sdo[0])) + pair * 1024;
+    const unsigned l_dst0 = lds_addr(sld[0][is_a ? 0 : 1]), dummy = lds_addr(sdummy);
     auto issue_load = [&](int j, int row0, int stage) {
-        if (j < 2 * TBW) {
-            const int i = j >> 1;
-            const bool ok = row0 >= 0 && wave + i * NW < TBLK;
-            const unsigned voff = ok ? (unsigned)(row0 * H * 2 + t_off[i]) : kOutOfRange;
-            const unsigned dst = ok ? ((j & 1) ? d_dst0 : q_dst0) + stage * (TILE * 2) + i * NW * 1024 : dummy;
-            lds_dma16((j & 1) ? drs : qrs, __builtin_amdgcn_readfirstlane(dst), voff);
+        if (j < TBW) {
+            const bool ok = row0 >= 0 && pair + j * NP < TBLK;
+            const unsigned voff = ok ? (unsigned)(row0 * H * 2 + t_off[j]) : kOutOfRange;
+            const unsigned dst = ok ? t_dst0 + stage * (TILE * 2) + j * NP * 1024 : dummy;
+            lds_dma16(trs, __builtin_amdgcn_readfirstlane(dst), voff);
         } else {
-            // 32 floats of lse / D: lanes 0-7 fetch them, the other lanes repeat
-            // in-range addresses into slots that are not read
-            const bool ok = row0 >= 0 && wave < 2;
+            // 32 floats: lanes 0-7 fetch them, the others repeat in-range
+            // addresses into slots that are not read
+            const bool ok = row0 >= 0 && pair == 0;
             const unsigned voff = ok ? (unsigned)(row0 * 4 + (lane & 7) * 16) : kOutOfRange;
-            const unsigned dst = ok ? ld_dst0 + stage * (2 * 256 * 4) : dummy;
-            lds_dma16(ldrs, __builtin_amdgcn_readfirstlane(dst), voff);
+            const unsigned dst = ok ? l_dst0 + stage * (2 * 256 * 4) : dummy;
+            lds_dma16(lrs, __builtin_amdgcn_readfirstlane(dst), voff);
         }
     };
-    // steps walk (g, query tile) with g outer; a cursor gives a step's first
-    // query row (g T + t0), or -1 past the last step
     struct Cursor {
         int g, qt;
     };
@@ -466,226 +433,191 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         }
     };
     auto row_of = [&](const Cursor &cu) { return cu.g < G ? cu.g * T + cu.qt * BQ : -1; };
-    auto issue_step = [&](int row0, int stage) {
-#pragma unroll
-        for (int j = 0; j < NLD; j++) issue_load(j, row0, stage);
-    };
 
-    f32x16 dv_acc[HB], dk_acc[HB];
+    f32x16 acc[HB];  // A: dV^T, B: dK^T
 #pragma unroll
-    for (int hb = 0; hb < HB; hb++) {
-        dv_acc[hb] = f32x16{};
-        dk_acc[hb] = f32x16{};
-    }
+    for (int hb = 0; hb < HB; hb++) acc[hb] = f32x16{};
 
-    // S = Q K^T and dP = dO V^T of a step (32 queries x the wave's 32 keys)
     const int row_lane = n * RS * 8 + c * 8;  // row n, chunk c
-    auto sdp = [&](int stage, f32x16 &sacc, f32x16 &pacc) {
-        const __bf16 *qrow = sq[stage] + row_lane;
-        const __bf16 *drow = sdo[stage] + row_lane;
+    const int gi = lane & 15, hh = (lane >> 4) & 1;
+    const int tr_lane = (4 * c + (gi >> 2)) * RS * 8 + 16 * hh + 4 * (gi & 3);
+    // S (A) or dP (B) of the step in `stage`: 32 queries x the pair's 32 keys
+    auto sdp = [&](int stage, f32x16 &x) {
+        const __bf16 *rowp = (is_a ? sq[stage] : sdo[stage]) + row_lane;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ks++) {
-            sacc = mfma32x32x16(*(const bf16x8 *)(qrow + 16 * ks), kf[ks], ks == 0 ? f32x16{} : sacc);
-            pacc = mfma32x32x16(*(const bf16x8 *)(drow + 16 * ks), vf[ks], ks == 0 ? f32x16{} : pacc);
-        }
+        for (int ks = 0; ks < KSTEPS; ks++) x = mfma32x32x16(*(const bf16x8 *)(rowp + 16 * ks), kv[ks], ks == 0 ? f32x16{} : x);
     };
-    // P = exp2(S log2e - lse log2e) and dS = P (dP - D), as bf16 MFMA operands
-    // (2 x 8 queries each). Invisible (query, key) pairs get P = 0. A pair is
-    // visible iff u = t - s + R lies in [0, min(L + R + 1, T - s + R)), which
-    // covers the window, causal masking (R = 0) and t < T with one unsigned
-    // compare per element. The bound is clamped at 0: a key that no query can
-    // see (past S, or past T - 1 + R) gets bound 0. A prefix key is visible to
-    // every query: its lane takes unbounded sides (LL = RR = kNoWindow), so
-    // only t < T remains.
+    // visibility of (t, s): u = t - s + R in [0, min(L + R + 1, T - s + R)), as
+    // in the kernel above (a prefix key takes unbounded sides)
     const bool k_pfx = s < a.prefix;
     const int LL = k_pfx ? kNoWindow : WL, RR = k_pfx ? kNoWindow : WR;
     const unsigned vis_bound = k_valid ? (unsigned)max(0, min(LL + RR + 1, T - s + RR)) : 0u;
-    // lse and D of the lane's 16 query rows of a step
-    auto read_ld = [&](int stage, f32x4 (&l4s)[4], f32x4 (&d4s)[4]) {
+    // lse * log2(e) (A) or D (B) of the lane's 16 query rows of the step in
+    // `stage`, read into registers a phase before their use
+    auto read_rows = [&](int stage, f32x4 (&r4)[4]) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-            l4s[q4] = *(const f32x4 *)(&sld[stage][0][8 * q4 + 4 * c]);
-            d4s[q4] = *(const f32x4 *)(&sld[stage][1][8 * q4 + 4 * c]);
-        }
+        for (int q4 = 0; q4 < 4; q4++) r4[q4] = *(const f32x4 *)(&sld[stage][is_a ? 0 : 1][8 * q4 + 4 * c]);
     };
-    auto weights = [&](int t0, const f32x4 (&l4s)[4], const f32x4 (&d4s)[4], const f32x16 &sacc, const f32x16 &pacc,
-                       bf16x8 (&pf)[2], bf16x8 (&sf)[2]) {
+    // A: P of a step from its S, its lse * log2(e) and first query t0; returns
+    // the bf16 dV operand, writes fp32 P to exchange buffer `buf` and issues
+    // one of the wave's loads after each group of four weights (ld(j)). The
+    // lane's 16 rows are t0 + 4 c + {0..3, 8..11, 16..19, 24..27}; a step where
+    // every lane sees all of them skips the mask.
+    auto weights_a = [&](const f32x4 (&l4s)[4], int t0, const f32x16 &sx, bf16x8 (&pf)[2], int buf, auto ld) {
         const int tb = t0 + 4 * c - s + RR;
+        auto body = [&](auto masked) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                f32x4 p4;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = 4 * q4 + e;
+                    float p = exp2_fast(__builtin_fmaf(sx[r], kLog2e, -l4s[q4][e]));
+                    if constexpr (decltype(masked)::value) p = (unsigned)(tb + 8 * q4 + e) < vis_bound ? p : 0.f;
+                    p4[e] = p;
+                    pf[r >> 3][r & 7] = (__bf16)p;
+                }
+                sp[buf][pair][q4][lane] = p4;
+                if (q4 < NLD) ld(q4);
+            }
+        };
+        if (__all(tb >= 0 && tb + 27 < (int)vis_bound))
+            body(std::integral_constant<bool, false>{});
+        else
+            body(std::integral_constant<bool, true>{});
+        pin_value(pf[0]);
+        pin_value(pf[1]);
+    };
+    // B: dS = P (dP - D) of a step, P from exchange buffer `buf`, loads
+    // spread as in weights_a
+    auto weights_b = [&](const f32x4 (&d4s)[4], const f32x16 &dpx, bf16x8 (&sf)[2], int buf, auto ld) {
+        f32x4 p4s[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) p4s[q4] = sp[buf][pair][q4][lane];
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
-            const f32x4 l4 = l4s[q4];
-            const f32x4 d4 = d4s[q4];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int r = 4 * q4 + e;
-                float p = exp2_fast(__builtin_fmaf(sacc[r], kLog2e, -l4[e] * kLog2e));
-                p = (unsigned)(tb + 8 * q4 + e) < vis_bound ? p : 0.f;
-                pf[r >> 3][r & 7] = (__bf16)p;
-                sf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - d4[e]));
+                sf[r >> 3][r & 7] = (__bf16)(p4s[q4][e] * (dpx[r] - d4s[q4][e]));
             }
+            if (q4 < NLD) ld(q4);
         }
+        // formed here, in the VALU phase, not sunk into the MFMA phase that reads them
+        pin_value(sf[0]);
+        pin_value(sf[1]);
     };
-    // dV^T += dO^T P and dK^T += Q^T dS for a step (k = the step's 32 queries):
-    // A operands by transpose reads. Lane (gi, hh) of 16-lane group c addresses
-    // query row 16 kk + 4 c + gi / 4 (+ 8 for the upper half) at
-    // h = 32 hb + 16 hh + 4 (gi % 4)
-    const int gi = lane & 15, hh = (lane >> 4) & 1;
-    const int tr_lane = (4 * c + (gi >> 2)) * RS * 8 + 16 * hh + 4 * (gi & 3);
-    if (n_steps > 0) {
-        // prologue: steps 0 .. 3 into stages 0 .. 3; P and dS of step 0, S and
-        // dP of step 1
-        Cursor c_ld{0, qt_begin};  // the next step to load
+    // M phase: the row product of the step in st_row (A: S = Q K^T, B: dP =
+    // dO V^T) into x, and the outer product of the step in st_tr (A: dV^T +=
+    // dO^T P, B: dK^T += Q^T dS) with the weights w, one of each per step x,
+    // their LDS operand reads pinned two steps ahead
+    auto m_phase = [&](int st_row, int st_tr, f32x16 &x, const bf16x8 (&w)[2], int st_rows, f32x4 (&r4)[4]) {
+        const __bf16 *rowp = (is_a ? sq[st_row] : sdo[st_row]) + row_lane;
+        const __bf16 *trp = (is_a ? sdo[st_tr] : sq[st_tr]) + tr_lane;
+        // the next VALU phase's per-row values first (they land during the MFMAs)
+        read_rows(st_rows, r4);
+        sched_fence();
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int xs = 0; xs < KSTEPS; xs++) {
+            x = mfma32x32x16(*(const bf16x8 *)(rowp + 16 * xs), kv[xs], xs == 0 ? f32x16{} : x);
+            const int kk = xs / HB, hb = xs % HB;
+            const __bf16 *base = trp + 16 * kk * RS * 8 + 32 * hb;
+            acc[hb] = mfma32x32x16(join_bf16x8(lds_read_tr16(base), lds_read_tr16(base + 8 * RS * 8)), w[kk], acc[hb]);
+        }
+        pp_schedule<KSTEPS, 2, 3, 2>(std::make_integer_sequence<int, 2>(), std::make_integer_sequence<int, KSTEPS>());
+        // the row product is read only in the next phase: keep the compiler
+        // from sinking its MFMAs past the barrier into the VALU phase
+        pin_value(x);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // The whole walk for one role (ROLE_A: the A waves), so that the two roles'
+    // registers never meet at a branch inside the loop.
+    auto walk = [&](auto role) {
+        constexpr bool ROLE_A = decltype(role)::value;
+        // prologue: steps 0 .. 3 into stages 0 .. 3; A: P(0) (exchange buffer
+        // 0) and S(1); B: dP(0)
+        Cursor c_ld{0, qt_begin};
 #pragma unroll
         for (int st = 0; st < 4; st++) {
-            issue_step(row_of(c_ld), st);
+#pragma unroll
+            for (int j = 0; j < NLD; j++) issue_load(j, row_of(c_ld), st);
             advance(c_ld);
         }
         wait_lds_loads();
         __syncthreads();
-        f32x16 sa, pa;          // S, dP of step i+1 at the top of iteration i
-        bf16x8 pfa[2], sfa[2];  // P, dS of step i
-        {
-            f32x16 s0, p0;
-            sdp(0, s0, p0);
-            f32x4 l4s[4], d4s[4];
-            read_ld(0, l4s, d4s);
-            weights(qt_begin * BQ, l4s, d4s, s0, p0, pfa, sfa);
-            sdp(1, sa, pa);
+        f32x16 sa;     // A: S(i+1), B: dP(i) at the top of iteration i
+        f32x16 sb;     // A: S(i+2), computed in phase 1
+        bf16x8 w[2];   // A: P(i) (dV operand); B: dS(i) (dK operand)
+        f32x4 r4[4];   // A: lse * log2(e) of step i+1; B: D of step i
+        auto no_load = [](int) {};
+        if constexpr (ROLE_A) {
+            sdp(0, sb);
+            read_rows(0, r4);
+            weights_a(r4, qt_begin * BQ, sb, w, 0, no_load);
+            sdp(1, sa);
+        } else {
+            sdp(0, sa);
+            read_rows(0, r4);
         }
-        Cursor c_w{0, qt_begin};  // step i+1 in iteration i (its weights)
+        Cursor c_w{0, qt_begin};  // A: step i+1 in iteration i
         advance(c_w);
-        // Iteration i: dV / dK of step i (stage i % 5), the weights of step i+1
-        // (S and dP from the previous iteration, lse and D from stage
-        // (i+1) % 5) and S / dP of step i+2 (stage (i+2) % 5). Step i+4 is
-        // loaded into stage (i+4) % 5, which held step i-1, and must land by the
-        // end of iteration i+1; steps past the last load nothing. The products
-        // of steps past the last are never used.
-        //
-        // Explicit schedule in NSLOT fenced slots: slot m issues MFMA m and the
-        // operand reads of MFMA m + PREF; slots 0 .. NQ - 1 are the S / dP
-        // MFMAs, the rest the dV / dK MFMAs; every WSTRIDE-th slot also computes
-        // one weight (P and dS) of step i+1, so the VALU work runs beside the
-        // MFMAs, and every LSTRIDE-th slot issues one of the NLD loads of step
-        // i+4. The lse and D of an iteration are read at the end of the one
-        // before (their stage is complete by then).
-        constexpr int NQ = 2 * KSTEPS, NSLOT = NQ + 4 * HB, PREF = GQA_BWD_DKV_PREF;
-        constexpr int WSTRIDE = NSLOT / 16;  // slots per weight
-        static_assert(WSTRIDE * 16 == NSLOT, "16 weights per lane and step");
-        constexpr int LSTRIDE = NSLOT / NLD;
-        static_assert(LSTRIDE >= 1, "a slot per load");
         int st0 = 0, st1 = 1, st2 = 2, st4 = 4;  // stages of steps i, i+1, i+2, i+4
-        f32x4 l4s[4], d4s[4];
-#if GQA_BWD_LDPRE
-        read_ld(st1, l4s, d4s);
-#endif
+        // Two phases per iteration, separated by workgroup barriers, so that
+        // on every SIMD one wave issues MFMAs while the other does its VALU
+        // work:
+        //   phase 1: A  S(i+2), dV(i)        B  dS(i); loads of step i+4
+        //   phase 2: A  P(i+1); loads        B  dP(i+1), dK(i)
+        // Each wave issues its loads of step i+4 in its VALU phase and then
+        // waits for those of step i+3, one barrier before their first reader.
         for (int i = 0; i < n_steps; i++) {
-            barrier_no_drain();
-#if !GQA_BWD_LDPRE
-            read_ld(st1, l4s, d4s);
-#endif
             const int row_ld = row_of(c_ld);
             advance(c_ld);
-            const int tb = c_w.qt * BQ + 4 * c - s + RR;
+            const int t1 = c_w.qt * BQ;
             advance(c_w);
-            auto read_op = [&](int m) -> bf16x8 {
-                if (m < NQ) {
-                    const __bf16 *base = (m & 1) ? sdo[st2] : sq[st2];
-                    return *(const bf16x8 *)(base + row_lane + 16 * (m >> 1));
-                }
-                const int j = m - NQ, kk = j / (2 * HB), hb = (j >> 1) % HB;
-                const __bf16 *base = ((j & 1) ? sq[st0] : sdo[st0]) + tr_lane + 16 * kk * RS * 8 + 32 * hb;
-                return join_bf16x8(lds_read_tr16(base), lds_read_tr16(base + 8 * RS * 8));
-            };
-            bf16x8 op[NSLOT];
-#pragma unroll
-            for (int m = 0; m < PREF; m++) op[m] = read_op(m);
-            sched_fence();
-            f32x16 sb, pb;
-            bf16x8 pfb[2], sfb[2];
-            float p_even = 0.f, ds_even = 0.f;
-#pragma unroll
-            for (int m = 0; m < NSLOT; m++) {
-                if (m + PREF < NSLOT) op[m + PREF] = read_op(m + PREF);
-                if (m < NQ) {
-                    const int ks = m >> 1;
-                    if (m & 1)
-                        pb = mfma32x32x16(op[m], vf[ks], ks == 0 ? f32x16{} : pb);
-                    else
-                        sb = mfma32x32x16(op[m], kf[ks], ks == 0 ? f32x16{} : sb);
-                } else {
-                    const int j = m - NQ, kk = j / (2 * HB), hb = (j >> 1) % HB;
-                    if (j & 1)
-                        dk_acc[hb] = mfma32x32x16(op[m], sfa[kk], dk_acc[hb]);
-                    else
-                        dv_acc[hb] = mfma32x32x16(op[m], pfa[kk], dv_acc[hb]);
-                }
-                if (m % WSTRIDE == WSTRIDE - 1) {
-                    // weight r of step i+1: row 8 (r / 4) + 4 c + r % 4 of its tile
-                    const int r = m / WSTRIDE, q4 = r >> 2, e = r & 3;
-                    float p = exp2_fast(__builtin_fmaf(sa[r], kLog2e, -l4s[q4][e] * kLog2e));
-                    p = (unsigned)(tb + 8 * q4 + e) < vis_bound ? p : 0.f;
-                    const float ds = p * (pa[r] - d4s[q4][e]);
-                    if (r & 1) {
-                        pfb[r >> 3][(r & 7) - 1] = (__bf16)p_even;
-                        pfb[r >> 3][r & 7] = (__bf16)p;
-                        sfb[r >> 3][(r & 7) - 1] = (__bf16)ds_even;
-                        sfb[r >> 3][r & 7] = (__bf16)ds;
-#if GQA_BWD_CVTPIN
-                        // convert in this slot (the compiler would leave all
-                        // conversions to the end of the iteration)
-                        if ((r & 7) == 7 || GQA_BWD_CVTPIN > 1) {
-                            pin_value(pfb[r >> 3]);
-                            pin_value(sfb[r >> 3]);
-                        }
-#endif
-                    } else {
-                        p_even = p;
-                        ds_even = ds;
-                    }
-                }
-                if (m % LSTRIDE == LSTRIDE / 2 && m / LSTRIDE < NLD) issue_load(m / LSTRIDE, row_ld, st4);
-                sched_fence();
+            auto ld = [&](int j) { issue_load(j, row_ld, st4); };
+            barrier_no_drain();
+            if constexpr (ROLE_A) {
+                m_phase(st2, st0, sb, w, st1, r4);  // and lse of step i+1
+            } else {
+                pin_value(sa);  // no weight work hoisted above the barrier
+                weights_b(r4, sa, w, i & 1, ld);
+                wait_lds_loads_but<NLD>();
             }
-            pfa[0] = pfb[0];
-            pfa[1] = pfb[1];
-            sfa[0] = sfb[0];
-            sfa[1] = sfb[1];
-            sa = sb;
-            pa = pb;
-            // the loads of step i+3 (issued in the previous iteration) land
-            // before the next barrier; this iteration's NLD stay in flight
-            wait_lds_loads_but<NLD>();
+            barrier_no_drain();
+            if constexpr (ROLE_A) {
+                pin_value(sa);  // no weight work hoisted above the barrier
+                weights_a(r4, t1, sa, w, (i + 1) & 1, ld);
+                wait_lds_loads_but<NLD>();
+                sa = sb;
+            } else {
+                m_phase(st1, st0, sa, w, st1, r4);  // and D of step i+1
+            }
             st0 = st1;
             st1 = st2;
             st2 = st2 == NSTAGE - 1 ? 0 : st2 + 1;
             st4 = st4 == NSTAGE - 1 ? 0 : st4 + 1;
-#if GQA_BWD_LDPRE
-            // the next iteration's lse / D (step i+2: landed before this
-            // iteration's barrier)
-            read_ld(st1, l4s, d4s);
-#endif
         }
-        // the last iteration's loads (of no step: out of range) complete
-        // before the workgroup's LDS is released
         wait_lds_loads();
+    };
+    if (n_steps > 0) {
+        if (is_a)
+            walk(std::integral_constant<bool, true>{});
+        else
+            walk(std::integral_constant<bool, false>{});
     }
 
-    // dK, dV rows (fp32): lane (n, c) holds h = 32hb + acc_row(r, c) of key s
+    // rows of key s (fp32): A writes dV, B dK; lane (n, c) holds h = 32 hb + acc_row(r, c)
     if (k_valid) {
-        float *dkrow = a.dk + (bk * S + s) * H;
-        float *dvrow = a.dv + (bk * S + s) * H;
+        float *orow = (is_a ? a.dv : a.dk) + (bk * S + s) * H;
 #pragma unroll
         for (int hb = 0; hb < HB; hb++)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; q4++) {
-                const int h = 32 * hb + 8 * q4 + 4 * c;
-                *(f32x4 *)(dkrow + h) = f32x4{dk_acc[hb][4 * q4], dk_acc[hb][4 * q4 + 1], dk_acc[hb][4 * q4 + 2],
-                                              dk_acc[hb][4 * q4 + 3]};
-                *(f32x4 *)(dvrow + h) = f32x4{dv_acc[hb][4 * q4], dv_acc[hb][4 * q4 + 1], dv_acc[hb][4 * q4 + 2],
-                                              dv_acc[hb][4 * q4 + 3]};
-            }
+            for (int q4 = 0; q4 < 4; q4++)
+                *(f32x4 *)(orow + 32 * hb + 8 * q4 + 4 * c) =
+                    f32x4{acc[hb][4 * q4], acc[hb][4 * q4 + 1], acc[hb][4 * q4 + 2], acc[hb][4 * q4 + 3]};
     }
-    (void)n_kblocks;
 }
 
 // ---------------------------------------------------------------------------
@@ -928,7 +860,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
 
     if constexpr (DELTA) {
         d_acc += __shfl_xor(d_acc, 32);
-        if (q_valid && c == 0) a.delta[row] = d_acc;
+        if (q_valid && c == 0) {
+            a.delta[row] = d_acc;
+            a.lse2[row] = lse2;
+        }
         return;
     }
     if (q_valid) {
@@ -1050,10 +985,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
             sacc[mb] = mfma32x32x16(kf, qf[ks], ks == 0 ? f32x16{} : sacc[mb]);
             pacc[mb] = mfma32x32x16(vf, df[ks], ks == 0 ? f32x16{} : pacc[mb]);
         }
-#if GQA_BWD_D_PREF > 0
-        constexpr int D = GQA_BWD_D_PREF < NX ? GQA_BWD_D_PREF : NX;
+        constexpr int D = kBwdPrefetch < NX ? kBwdPrefetch : NX;
         pp_schedule<NX, 2, 2, D>(std::make_integer_sequence<int, D>(), std::make_integer_sequence<int, NX>());
-#endif
         __builtin_amdgcn_s_setprio(0);
         wait_lds_loads();
     };
@@ -1107,7 +1040,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     if (grp == 0) barrier_no_drain();  // group A's trailing phase
 
     d_acc += __shfl_xor(d_acc, 32);
-    if (c == 0) a.delta[row] = d_acc;
+    if (c == 0) {
+        a.delta[row] = d_acc;
+        a.lse2[row] = lse2;
+    }
 }
 
 
@@ -1243,12 +1179,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
             }
             if constexpr (decltype(dq)::value) dq_acc[hb] = mfma32x32x16(kt, dsl[kk], dq_acc[hb]);
         }
-#if GQA_BWD_DQ_PREF > 0
         constexpr bool SD = decltype(sd)::value, DQ = decltype(dq)::value;
         constexpr int NM = (SD ? 2 : 0) + (DQ ? 2 : 0);
-        constexpr int D = GQA_BWD_DQ_PREF < KSTEPS ? GQA_BWD_DQ_PREF : KSTEPS;
+        constexpr int D = kBwdPrefetch < KSTEPS ? kBwdPrefetch : KSTEPS;
         pp_schedule<KSTEPS, NM, NM, D>(std::make_integer_sequence<int, D>(), std::make_integer_sequence<int, KSTEPS>());
-#endif
         __builtin_amdgcn_s_setprio(0);
         wait_lds_loads();
     };
@@ -1318,12 +1252,12 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     // D = rowsum(P * dP), then dQ, then dK / dV (both read D). The D pass has
     // no dQ accumulators, so at H <= 128 it takes key tiles of 64 (half the
     // per-tile barriers and loop overhead of the dQ pass's 32).
-    constexpr int BKV_D = H <= 128 && GQA_BWD_D_BKV > BKV_DQ ? GQA_BWD_D_BKV : BKV_DQ;
+    constexpr int BKV_D = H <= 128 ? 64 : BKV_DQ;
     bool delta_done = false;
     const MaskSpec m{a.causal, a.coff, a.wl, a.wr, a.prefix};
     // causal: the diagonal offset a whole number of tiles, T + coff == S
     auto diag_tiles = [&](int bkv) { return !a.causal || (a.coff >= 0 && a.coff % bkv == 0 && a.T + a.coff == a.S); };
-    if constexpr (GQA_BWD_DELTA_PP && H <= 128 && NW_DQ == 8) {
+    if constexpr (H <= 128 && NW_DQ == 8) {
         // dense shapes: the ping-pong D pass (query blocks of 64 rows x gw heads)
         constexpr int BKV_PP = 64;
         const bool shape = a.q_seg == nullptr && gw * bq == 256 && a.T % bq == 0 && a.S % BKV_PP == 0 &&
@@ -1351,7 +1285,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     bool dq_done = false;
-    if constexpr (GQA_BWD_DQ_PP && H <= 128 && NW_DQ == 8) {
+    if constexpr (H <= 128 && NW_DQ == 8) {
         // dense shapes: dQ on the ping-pong kernel (32-key tiles)
         const bool shape = a.q_seg == nullptr && gw * bq == 256 && a.T % bq == 0 && a.S % 32 == 0 && diag_tiles(32);
         const bool dense = shape && !mask_extra(m);
@@ -1379,12 +1313,13 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     const int keys_wg = 32 * NW_DKV;
     const int n_kblocks = (a.S + keys_wg - 1) / keys_wg;
     const dim3 kgrid((unsigned)(a.B * a.K * n_kblocks));
-    if constexpr (GQA_BWD_DKV2 && H <= 128 && NW_DKV == 4) {
+    if constexpr (H <= 128 && NW_DKV == 4) {
+        // no segment ids: the wave-pair kernel (8 waves, 128 keys per workgroup)
         if (a.q_seg == nullptr) {
             if (a.causal)
-                hipLaunchKernelGGL((attn_bwd_dkv2_kernel<H, true>), kgrid, dim3(256), 0, stream, a, n_kblocks);
+                hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, true>), kgrid, dim3(512), 0, stream, a);
             else
-                hipLaunchKernelGGL((attn_bwd_dkv2_kernel<H, false>), kgrid, dim3(256), 0, stream, a, n_kblocks);
+                hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, false>), kgrid, dim3(512), 0, stream, a);
             return hipGetLastError();
         }
     }

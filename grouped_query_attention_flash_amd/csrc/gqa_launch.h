@@ -82,6 +82,7 @@ struct BwdArgs {
     const float *lse;
     float *dq, *dk, *dv;
     float *delta;                    // workspace: D = rowsum(P * dP) in fp32, [B,K,G,T]
+    float *lse2;                     // workspace: lse * log2(e) per row, +inf for a row that sees no key
     const int32_t *q_seg, *kv_seg;
     int B, K, G, T, S;
     int causal, coff, wl, wr, prefix;  // the resolved mask, as in FwdArgs

@@ -202,9 +202,10 @@ int attn_check_fwd_mask(const void *q, const void *k, const void *v, const void 
                         int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                         int prefix, const void *workspace, size_t workspace_bytes);
 
-/* Bytes of device workspace attn_bwd needs for these sizes (the per-row
- * D = sum_s P[t,s] dP[t,s] vector, fp32 [B,K,G,T], rounded up to 256 bytes).
- * Returns 0 for invalid sizes. The pages give no backward; D is the row
+/* Bytes of device workspace attn_bwd needs for these sizes: the per-row
+ * D = sum_s P[t,s] dP[t,s] vector, fp32 [B,K,G,T], then lse * log2(e) in the
+ * same layout (the form the dK/dV kernel consumes), each rounded up to 256
+ * bytes. Returns 0 for invalid sizes. The pages give no backward; D is the row
  * quantity of the softmax derivative, kept beside the lse residual that
  * splash attention's save_residuals returns (danielwatson6.github.io/fa,
  * "Our first kernel"). */

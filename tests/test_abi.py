@@ -77,8 +77,9 @@ def test_check_fwd_codes():
 
 
 def test_check_bwd_codes_and_workspace():
-    assert gqa.attn_bwd_workspace_bytes(1, 8, 4, 8192, 8192, 128) == 4 * 8 * 4 * 8192
-    assert gqa.attn_bwd_workspace_bytes(1, 1, 1, 3, 3, 128) == 256
+    # D and lse * log2(e): one fp32 per query row each, each rounded up to 256 bytes
+    assert gqa.attn_bwd_workspace_bytes(1, 8, 4, 8192, 8192, 128) == 2 * 4 * 8 * 4 * 8192
+    assert gqa.attn_bwd_workspace_bytes(1, 1, 1, 3, 3, 128) == 512
     assert gqa.attn_bwd_workspace_bytes(0, 1, 1, 3, 3, 128) == 0
     assert check_bwd() == gqa.GQA_ATTN_OK
     assert check_bwd(lse=None) == gqa.GQA_ATTN_ERR_NULL
