@@ -34,6 +34,7 @@ GQA_ATTN_ERR_SEGMENTS = 5
 GQA_ATTN_ERR_WORKSPACE = 6
 GQA_ATTN_ERR_HIP = 7
 GQA_ATTN_ERR_MASK = 8
+GQA_ATTN_ERR_TUNING = 9
 
 CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_END = 0, 1, 2
 
@@ -41,7 +42,8 @@ EXPORTED_SYMBOLS = (
     "attn_fwd", "attn_check_fwd", "attn_fwd_ws", "attn_check_fwd_ws", "attn_fwd_workspace_bytes",
     "attn_fwd_split_count", "attn_fwd_local", "attn_check_fwd_local", "attn_fwd_mask", "attn_check_fwd_mask",
     "attn_bwd_workspace_bytes", "attn_bwd", "attn_check_bwd", "attn_bwd_local", "attn_check_bwd_local",
-    "attn_bwd_mask", "attn_check_bwd_mask", "attn_fwd_noalloc", "attn_strerror", "attn_last_hip_error",
+    "attn_bwd_mask", "attn_check_bwd_mask", "attn_fwd_noalloc", "attn_fwd_tuned", "attn_fwd_tuned_workspace_bytes",
+    "attn_fwd_tuning", "attn_strerror", "attn_last_hip_error",
 )
 
 _lib = None
@@ -92,6 +94,12 @@ def load_library():
     lib.attn_bwd_mask.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, SZ, P]
     lib.attn_check_bwd_mask.restype = I
     lib.attn_check_bwd_mask.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, SZ]
+    lib.attn_fwd_tuned.restype = I
+    lib.attn_fwd_tuned.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, I, P, SZ, P]
+    lib.attn_fwd_tuned_workspace_bytes.restype = SZ
+    lib.attn_fwd_tuned_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.attn_fwd_tuning.restype = I
+    lib.attn_fwd_tuning.argtypes = [I, I, I, I, I, I, I, I, I, I, I, P, P]
     lib.attn_fwd_noalloc.restype = I
     lib.attn_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P]
     lib.attn_fwd_workspace_bytes.restype = SZ
@@ -130,6 +138,22 @@ def attn_fwd_workspace_bytes(B: int, K: int, G: int, T: int, S: int, H: int) -> 
 
 def attn_fwd_split_count(B: int, K: int, G: int, T: int, S: int, H: int) -> int:
     return int(load_library().attn_fwd_split_count(B, K, G, T, S, H))
+
+
+def attn_fwd_tuning(B: int, K: int, G: int, T: int, S: int, H: int, causal=False, window=None, prefix: int = 0,
+                    segments: bool = False) -> Tuple[int, int]:
+    """The tuning table's (load_placement, split_target) for a call (host only)."""
+    lp, st = ctypes.c_int(-2), ctypes.c_int(-2)
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    rc = load_library().attn_fwd_tuning(B, K, G, T, S, H, causal_mode(causal), wl, wr, int(prefix), int(bool(segments)),
+                                        ctypes.byref(lp), ctypes.byref(st))
+    if rc != GQA_ATTN_OK:
+        raise GqaAttnError(rc, "attn_fwd_tuning")
+    return lp.value, st.value
+
+
+def attn_fwd_tuned_workspace_bytes(B: int, K: int, G: int, T: int, S: int, H: int, split_target: int = -1) -> int:
+    return int(load_library().attn_fwd_tuned_workspace_bytes(B, K, G, T, S, H, int(split_target)))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -246,6 +270,38 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False,
                                  B, K, G, T, S, H, cm, _stream_handle(dev))
     if rc != GQA_ATTN_OK:
         raise GqaAttnError(rc, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_tuned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, load_placement: int = -1,
+                   split_target: int = -1, causal=False, q_seg: Optional[torch.Tensor] = None,
+                   kv_seg: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, window: Optional[Tuple[int, int]] = None, prefix: int = 0,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """attn_fwd_mask with an explicit schedule (attn_fwd_tuned): load_placement
+    (0, 1, 2) and split_target (0 .. 2^20); -1 takes the tuning table's choice."""
+    B, K, G, T, S, H = _dims(q, k)
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16)
+    _check_tensor("k", k, torch.bfloat16, None, dev)
+    _check_tensor("v", v, torch.bfloat16, k.shape, dev)
+    cm = causal_mode(causal)
+    _check_segments(q_seg, kv_seg, B, T, S, dev, "attn_fwd_tuned")
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, torch.bfloat16, q.shape, dev)
+    lse = torch.empty(B, K, G, T, dtype=torch.float32, device=dev) if lse is None else lse
+    _check_tensor("lse", lse, torch.float32, (B, K, G, T), dev)
+    wsb = attn_fwd_tuned_workspace_bytes(B, K, G, T, S, H, split_target)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    rc = load_library().attn_fwd_tuned(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg), _ptr(kv_seg),
+                                       B, K, G, T, S, H, cm, wl, wr, int(prefix), int(load_placement),
+                                       int(split_target), _ptr(workspace),
+                                       0 if workspace is None else workspace.numel(), _stream_handle(dev))
+    if rc != GQA_ATTN_OK:
+        raise GqaAttnError(rc, "attn_fwd_tuned")
     return out, lse
 
 

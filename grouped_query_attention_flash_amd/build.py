@@ -23,6 +23,9 @@ HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
 
 
 def build(verbose: bool = False) -> str:
+    # the runtime tuning table, generated from tuning/mi355x.json
+    from grouped_query_attention_flash_amd.tuning import gen_table
+    gen_table.generate()
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objs = []
     procs = []

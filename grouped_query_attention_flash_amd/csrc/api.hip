@@ -90,12 +90,13 @@ int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, c
     return GQA_ATTN_OK;
 }
 
-// Forward with an optional split-KV plan (plan.n_splits > 1 needs the
-// workspace: partial outputs first, then partial lse).
+// Forward with a schedule (tuning) and an optional split-KV plan
+// (plan.n_splits > 1 needs the workspace: partial outputs first, then
+// partial lse).
 static int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, const gqa::MaskSpec &m,
-                   gqa::SplitPlan plan, void *workspace, void *stream) {
+                   gqa::FwdTuning tune, gqa::SplitPlan plan, void *workspace, void *stream) {
     const gqa::FwdConfig cfg =
         plan.n_splits > 1 ? gqa::fwd_config_split(G, T, H)
         : (H == 256 && gqa::fwd_pp256_applies(G, T, S, m, q_seg != nullptr)) ? gqa::fwd_config_pp256()
@@ -114,6 +115,7 @@ static int run_fwd(const void *q, const void *k, const void *v, void *o, float *
     a.wl = m.wl;
     a.wr = m.wr;
     a.prefix = m.prefix;
+    a.load_placement = tune.load_placement;
     a.gw = cfg.gw;
     a.bq = cfg.bq;
     a.n_gsplit = G / cfg.gw;
@@ -138,14 +140,15 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int K, int G, int T, int S, int H, int causal, void *stream) {
     int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal);
     if (rc) return rc;
-    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, resolve_mask(causal, -1, -1, 0, T, S),
-                   gqa::SplitPlan{1, 0}, nullptr, stream);
+    const gqa::MaskSpec m = resolve_mask(causal, -1, -1, 0, T, S);
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, m,
+                   gqa::fwd_tuning(G, T, S, H, m, q_seg != nullptr), gqa::SplitPlan{1, 0}, nullptr, stream);
 }
 
 size_t attn_fwd_workspace_bytes(int B, int K, int G, int T, int S, int H) {
     if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return 0;
     if (H != 64 && H != 128 && H != 256) return 0;
-    const gqa::SplitPlan plan = gqa::fwd_split_plan(B, K, G, T, S, H);
+    const gqa::SplitPlan plan = gqa::fwd_split_plan(B, K, G, T, S, H, gqa::fwd_split_target(T, S, H));
     if (plan.n_splits <= 1) return 0;
     const size_t rows = (size_t)B * K * G * T;
     return round256(sizeof(float) * (size_t)plan.n_splits * rows * (H + 1));
@@ -170,8 +173,10 @@ int attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse
                 void *workspace, size_t workspace_bytes, void *stream) {
     int rc = attn_check_fwd_ws(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace, workspace_bytes);
     if (rc) return rc;
-    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, resolve_mask(causal, -1, -1, 0, T, S),
-                   gqa::fwd_split_plan(B, K, G, T, S, H), workspace, stream);
+    const gqa::MaskSpec m = resolve_mask(causal, -1, -1, 0, T, S);
+    const gqa::FwdTuning tune = gqa::fwd_tuning(G, T, S, H, m, q_seg != nullptr);
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, m, tune,
+                   gqa::fwd_split_plan(B, K, G, T, S, H, tune.split_target), workspace, stream);
 }
 
 int attn_check_fwd_mask(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -190,9 +195,56 @@ int attn_fwd_mask(const void *q, const void *k, const void *v, void *o, float *l
     int rc = attn_check_fwd_mask(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left,
                                  window_right, prefix, workspace, workspace_bytes);
     if (rc) return rc;
-    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H,
-                   resolve_mask(causal, window_left, window_right, prefix, T, S),
-                   gqa::fwd_split_plan(B, K, G, T, S, H), workspace, stream);
+    const gqa::MaskSpec m = resolve_mask(causal, window_left, window_right, prefix, T, S);
+    const gqa::FwdTuning tune = gqa::fwd_tuning(G, T, S, H, m, q_seg != nullptr);
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, m, tune,
+                   gqa::fwd_split_plan(B, K, G, T, S, H, tune.split_target), workspace, stream);
+}
+
+size_t attn_fwd_tuned_workspace_bytes(int B, int K, int G, int T, int S, int H, int split_target) {
+    if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return 0;
+    if (H != 64 && H != 128 && H != 256) return 0;
+    if (split_target < -1 || split_target > (1 << 20)) return 0;
+    const int target = split_target < 0 ? gqa::fwd_split_target(T, S, H) : split_target;
+    const gqa::SplitPlan plan = gqa::fwd_split_plan(B, K, G, T, S, H, target);
+    if (plan.n_splits <= 1) return 0;
+    const size_t rows = (size_t)B * K * G * T;
+    return round256(sizeof(float) * (size_t)plan.n_splits * rows * (H + 1));
+}
+
+int attn_fwd_tuning(int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                    int prefix, int segments, int *load_placement, int *split_target) {
+    if (!load_placement || !split_target) return GQA_ATTN_ERR_NULL;
+    if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return GQA_ATTN_ERR_SHAPE;
+    if (H != 64 && H != 128 && H != 256) return GQA_ATTN_ERR_HEADDIM;
+    int rc = check_mask(causal, window_left, window_right, prefix);
+    if (rc) return rc;
+    const gqa::FwdTuning t =
+        gqa::fwd_tuning(G, T, S, H, resolve_mask(causal, window_left, window_right, prefix, T, S), segments != 0);
+    *load_placement = t.load_placement;
+    *split_target = t.split_target;
+    return GQA_ATTN_OK;
+}
+
+int attn_fwd_tuned(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right, int prefix,
+                   int load_placement, int split_target, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, 0);
+    if (rc) return rc;
+    rc = check_mask(causal, window_left, window_right, prefix);
+    if (rc) return rc;
+    if (load_placement < -1 || load_placement > 2 || split_target < -1 || split_target > (1 << 20))
+        return GQA_ATTN_ERR_TUNING;
+    const size_t need = attn_fwd_tuned_workspace_bytes(B, K, G, T, S, H, split_target);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GQA_ATTN_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return GQA_ATTN_ERR_ALIGN;
+    const gqa::MaskSpec m = resolve_mask(causal, window_left, window_right, prefix, T, S);
+    gqa::FwdTuning tune = gqa::fwd_tuning(G, T, S, H, m, q_seg != nullptr);
+    if (load_placement >= 0) tune.load_placement = load_placement;
+    if (split_target >= 0) tune.split_target = split_target;
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, m, tune,
+                   gqa::fwd_split_plan(B, K, G, T, S, H, tune.split_target), workspace, stream);
 }
 
 int attn_check_fwd_local(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -214,7 +266,7 @@ int attn_fwd_local(const void *q, const void *k, const void *v, void *o, float *
 int attn_fwd_split_count(int B, int K, int G, int T, int S, int H) {
     if (B < 1 || K < 1 || G < 1 || T < 1 || S < 1) return 0;
     if (H != 64 && H != 128 && H != 256) return 0;
-    return gqa::fwd_split_plan(B, K, G, T, S, H).n_splits;
+    return gqa::fwd_split_plan(B, K, G, T, S, H, gqa::fwd_split_target(T, S, H)).n_splits;
 }
 
 size_t attn_bwd_workspace_bytes(int B, int K, int G, int T, int S, int H) {
@@ -379,9 +431,10 @@ int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float
         rc = scratch_on_current_device(&ws);
         if (rc) return rc;
     }
-    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H,
-                   resolve_mask(causal, window_left, window_right, prefix, T, S),
-                   gqa::fwd_split_plan(B, K, G, T, S, H), ws, stream);
+    const gqa::MaskSpec m = resolve_mask(causal, window_left, window_right, prefix, T, S);
+    const gqa::FwdTuning tune = gqa::fwd_tuning(G, T, S, H, m, q_seg != nullptr);
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, m, tune,
+                   gqa::fwd_split_plan(B, K, G, T, S, H, tune.split_target), ws, stream);
 }
 
 const char *attn_strerror(int code) {
@@ -398,6 +451,9 @@ const char *attn_strerror(int code) {
             return "workspace is NULL or smaller than the call's attn_fwd_workspace_bytes() / "
                    "attn_bwd_workspace_bytes()";
         case GQA_ATTN_ERR_HIP: return "a HIP launch failed (see attn_last_hip_error)";
+        case GQA_ATTN_ERR_TUNING:
+            return "invalid schedule: load_placement must be -1 (table), 0, 1 or 2 and split_target -1 (table) or "
+                   "0 .. 2^20";
         case GQA_ATTN_ERR_MASK:
             return "invalid mask: causal must be 0, 1 (top-left) or 2 (end-aligned), window sides -1 or >= 0, "
                    "prefix >= 0";

@@ -32,61 +32,9 @@
 #include <type_traits>
 #include <utility>
 
-// Build-time switches of the forward schedule (defaults are the tuned ones).
-#ifndef GQA_FWD_FASTPATH
-#define GQA_FWD_FASTPATH 1
-#endif
-#ifndef GQA_FWD_SCHED
-#define GQA_FWD_SCHED 0
-#endif
-// interleave pattern for the dense loop (MFMA / operand reads / VALU)
-#ifndef GQA_FWD_DSCHED
-#define GQA_FWD_DSCHED 1
-#endif
-// LDS operand reads run this many MFMAs ahead in the dense loop
-#ifndef GQA_FWD_PREF
-#define GQA_FWD_PREF 2
-#endif
-// issue the global-to-LDS loads inside the dense loop's MFMA stream
-#ifndef GQA_FWD_DMASPREAD
-#define GQA_FWD_DMASPREAD 1
-#endif
-// dense shapes run the ping-pong kernel (H <= 128, and H = 256 when G is a
-// multiple of 8; at H <= 128 also shapes with segment ids and S <= 8192)
-#ifndef GQA_FWD_PINGPONG
-#define GQA_FWD_PINGPONG 1
-#endif
-// ping-pong M phase: pinned MFMA / operand-read pattern, reads this many steps ahead
-#ifndef GQA_PP_MSCHED
-#define GQA_PP_MSCHED 1
-#endif
-// ping-pong: O leaves through LDS in coalesced 1 KiB stores
-// split-KV: workgroups the split plan aims for
-#ifndef GQA_SPLIT_TARGET
-#define GQA_SPLIT_TARGET 1024
-#endif
-#ifndef GQA_PP_OSTAGE
-#define GQA_PP_OSTAGE 1
-#endif
-#ifndef GQA_PP_MPREF
-#define GQA_PP_MPREF 2
-#endif
-#ifndef GQA_FWD_BKV128
-#define GQA_FWD_BKV128 64
-#endif
-// waves per workgroup at H = 128 (8: one workgroup per CU; 4: two per CU)
-#ifndef GQA_FWD_NW128
-#define GQA_FWD_NW128 8
-#endif
-// 0: no scheduling fences; 1: fences between pipeline phases; 2: also inside
-// the QK^T and PV loops
-#ifndef GQA_FWD_FENCE
-#define GQA_FWD_FENCE 0
-#endif
-// raise the wave's issue priority while it feeds the matrix pipe
-#ifndef GQA_FWD_PRIO
-#define GQA_FWD_PRIO 1
-#endif
+// LDS operand reads run this many MFMAs ahead of their use: in the general
+// kernel's dense loop, and in the ping-pong kernel's M phase (in steps)
+constexpr int kFwdPrefetch = 2;
 
 namespace gqa {
 
@@ -123,11 +71,6 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     constexpr int HB = H / 32;        // 32-wide h blocks of O^T
     constexpr int PK = BKV / 16;      // k-steps of the PV contraction
     using L = TileLayout<H, BKV>;
-#if GQA_FWD_SCHED
-    // VALU instructions (exp, fma, convert, add) per lane per tile, spread over the
-    // QK^T MFMAs of the next tile
-    constexpr int kValuPerMfma = (MB * 16 * 3 + MB * 8 + MB * KSTEPS - 1) / (MB * KSTEPS);
-#endif
 
     // K and V tiles, two buffers each (see the pipeline below), in padded-row
     // layouts that make every MFMA operand read bank-conflict free.
@@ -359,7 +302,6 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
             for (int ks = 0; ks < KSTEPS; ks++) {
                 const bf16x8 kf = *(const bf16x8 *)(kt + k_lane + mb * 32 * L::KRS * 8 + ks * 16);
                 sacc[mb] = mfma32x32x16(kf, qf[ks], sacc[mb]);
-                if (GQA_FWD_FENCE >= 2 && ks % 4 == 3) sched_fence();  // at most 4 operand reads in flight
             }
         }
     };
@@ -452,7 +394,6 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
                 const s16x4 hi = lds_read_tr16(vp + 8 * L::VRS * 8);
                 oacc[hb] = mfma32x32x16(join_bf16x8(lo, hi), pf[kk], oacc[hb]);
             }
-            if (GQA_FWD_FENCE >= 2) sched_fence();
         }
     };
     auto softmax_pv = [&](f32x16 (&sacc)[MB], const __bf16 *vt) {
@@ -497,30 +438,22 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
                        const __bf16 *v_ld, int i) {
             wait_lds_loads();
             __syncthreads();
-#if GQA_FWD_DMASPREAD
             // the loads every wave issues go into the MFMA stream below (the
             // scheduler spreads them); K(i+2) past the last tile is a dead load,
             // or a bounds-checked zero read past the end of K
             if (i + 2 < n_t) issue_k_part(i + 2, k_ld, first_waves_t{});
             issue_v_part(i, v_ld, first_waves_t{});
-            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+            __builtin_amdgcn_s_setprio(1);
             issue_k_part(i + 2, k_ld, all_waves_t{});
             issue_v_part(i, v_ld, all_waves_t{});
-#else
-            if (i + 2 < n_t) issue_k(i + 2, k_ld);
-            issue_v(i, v_ld);
-            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
-#endif
             qk(k_rd, s_nxt);
             if constexpr (decltype(with_pv)::value) pv(p_prev, v_rd);
             float ls = weights(s_cur, m_run, p_cur);
-#if GQA_FWD_DSCHED
             constexpr int n_qk = MB * KSTEPS;
             constexpr int n_mfma = n_qk + (decltype(with_pv)::value ? PK * HB : 0);
             constexpr int valu_per = (3 * MB * 16 + n_mfma - 1) / n_mfma;
-            dense_schedule<n_qk, n_mfma, GQA_FWD_PREF, valu_per>(std::make_integer_sequence<int, GQA_FWD_PREF>(),
+            dense_schedule<n_qk, n_mfma, kFwdPrefetch, valu_per>(std::make_integer_sequence<int, kFwdPrefetch>(),
                                                                         std::make_integer_sequence<int, n_mfma>());
-#endif
             // a rescale in here multiplies O after the PV above has been added:
             // P(i-1) was taken against the old reference
             if (__any(!(ls <= kRescaleBound))) {
@@ -528,7 +461,7 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
                 ls = weights(s_cur, m_run, p_cur);
             }
             l_run += ls;
-            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_s_setprio(0);
         };
         using no_pv = std::integral_constant<bool, false>;
         using do_pv = std::integral_constant<bool, true>;
@@ -558,12 +491,12 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
             wait_lds_loads();
             __syncthreads();
             issue_v(n_t - 1, vA);
-            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+            __builtin_amdgcn_s_setprio(1);
             pv(pb, vB);
             if (CAUSAL) mask_tile(sa, (n_t - 1) * BKV);
             const float m_use = rowmax_rescale(sa);
             l_run += weights(sa, m_use, pa);
-            if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_s_setprio(0);
             wait_lds_loads();
             __syncthreads();
             pv(pa, vA);
@@ -598,7 +531,6 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
 
         auto iteration = [&](f32x16 (&s_cur)[MB], f32x16 (&s_nxt)[MB], __bf16 *k_cur, __bf16 *k_nxt,
                              __bf16 *v_cur, __bf16 *v_nxt) {
-            if (GQA_FWD_FENCE >= 1) sched_fence();
             const int j_nn = j_nxt < j_end ? next_tile(j_nxt + 1) : j_end;
             wait_lds_loads();
             __syncthreads();
@@ -607,38 +539,20 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
             bool run_nxt, mask_nxt;
             tile_flags(j_nxt, run_nxt, mask_nxt);
             if (run_cur && mask_cur) mask_tile(s_cur, j_cur * BKV);
-            if (GQA_FWD_FASTPATH && run_cur && run_nxt) {
+            if (run_cur && run_nxt) {
                 // common case, one basic block: the QK^T MFMAs of the next tile are
                 // interleaved with the exponentials of this one, so the matrix pipe
                 // and the VALU work at the same time
                 const float m_use = rowmax_rescale(s_cur);
                 bf16x8 pf[PK];
-                if (GQA_FWD_FENCE >= 1) sched_fence();
-                if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+                    __builtin_amdgcn_s_setprio(1);
                 qk(k_nxt, s_nxt);
                 l_run += weights(s_cur, m_use, pf);
-                if (GQA_FWD_FENCE >= 1) sched_fence();
-                pv(pf, v_cur);
-                if (GQA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
-                if (GQA_FWD_FENCE >= 1) sched_fence();
-                // schedule: K operand reads run two MFMAs ahead; each QK^T MFMA is
+                    pv(pf, v_cur);
+                __builtin_amdgcn_s_setprio(0);
+                    // schedule: K operand reads run two MFMAs ahead; each QK^T MFMA is
                 // followed by a share of the weight computation; then the PV MFMAs
                 // with their V transpose reads two MFMAs ahead
-    #if GQA_FWD_SCHED
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    #pragma unroll
-                for (int i = 0; i < MB * KSTEPS; i++) {
-                    if (i + 2 < MB * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    #pragma unroll
-                for (int i = 0; i < PK * HB; i++) {
-                    if (i + 2 < PK * HB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                }
-    #endif
             } else {
                 if (run_nxt) qk(k_nxt, s_nxt);
                 if (run_cur) softmax_pv(s_cur, v_cur);
@@ -968,12 +882,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
             if constexpr (MLD == 2 && decltype(loads)::value)
                 if (x % LSTEP == LSTEP / 2 && x / LSTEP < NL) issue_one(x / LSTEP, ld);
         }
-#if GQA_PP_MSCHED
         constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
-        constexpr int D = GQA_PP_MPREF < NQK ? GQA_PP_MPREF : NQK;
+        constexpr int D = kFwdPrefetch < NQK ? kFwdPrefetch : NQK;
         m_phase_schedule<NQK, (QK ? 1 : 0) + (PV ? 1 : 0), (QK ? 1 : 0) + (PV ? 2 : 0), D>(
             std::make_integer_sequence<int, D>(), std::make_integer_sequence<int, NQK>());
-#endif
         __builtin_amdgcn_s_setprio(0);
         if constexpr (MLD == 0) wait_lds_loads();
     };
@@ -1207,7 +1119,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     // and all loads have landed (each M phase ends with a wait). At H = 256
     // the rows do not fit and O leaves straight from registers.
     constexpr int OROW = H * 2 + 16;
-    constexpr bool kStage = GQA_PP_OSTAGE && 2 * 32 * OROW <= L::K_ELEMS * 2 && 2 * 32 * OROW <= L::V_ELEMS * 2;
+    constexpr bool kStage = 2 * 32 * OROW <= L::K_ELEMS * 2 && 2 * 32 * OROW <= L::V_ELEMS * 2;
     if constexpr (kStage) {
         char *stage = (wave < 6 ? (char *)sk[wave >> 1] : (char *)sv[n_t % NSLOT]) + (wave & 1) * 32 * OROW;
 #pragma unroll
@@ -1250,6 +1162,17 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     }
 }
 
+// The ping-pong kernel with the call's load placement (a runtime choice; the
+// three variants compute bitwise the same outputs).
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG>
+static void launch_pp(const FwdArgs &a, unsigned grid, hipStream_t stream) {
+    switch (a.load_placement) {
+        case 1: hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, CAUSAL, WIN, SEG, 1>), dim3(grid), dim3(512), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, CAUSAL, WIN, SEG, 2>), dim3(grid), dim3(512), 0, stream, a); break;
+        default: hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, CAUSAL, WIN, SEG, 0>), dim3(grid), dim3(512), 0, stream, a); break;
+    }
+}
+
 template <int H, int BKV, int NW, int WPS>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks * (a.o_part ? a.n_splits : 1));
@@ -1260,16 +1183,12 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     const bool diag_tiles = !a.causal || (a.coff >= 0 && a.coff % BKV == 0 && a.T + a.coff == a.S && a.bq == BKV);
     const bool dense = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 && !mask_extra(m) &&
                        diag_tiles;
-    if constexpr (GQA_FWD_PINGPONG && H <= 128 && NW == 8) {
+    if constexpr (H <= 128 && NW == 8) {
         if (dense) {
-            // H = 64: the loads go into the M phase, which is the shorter one
-            constexpr int MLD = H == 64 ? 1 : 0;
             if (a.causal)
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false, false, MLD>), dim3(grid), dim3(NW * 64), 0,
-                                   stream, a);
+                launch_pp<H, BKV, true, false, false>(a, grid, stream);
             else
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false, false, false, MLD>), dim3(grid), dim3(NW * 64), 0,
-                                   stream, a);
+                launch_pp<H, BKV, false, false, false>(a, grid, stream);
             return hipGetLastError();
         }
         // segment ids on an otherwise dense shape with at most 8192 keys: the
@@ -1278,9 +1197,9 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
                                a.S <= 8192 && !mask_extra(m) && diag_tiles;
         if (dense_seg) {
             if (a.causal)
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, false, true, 2>), dim3(grid), dim3(NW * 64), 0, stream, a);
+                launch_pp<H, BKV, true, false, true>(a, grid, stream);
             else
-                hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, false, false, true, 2>), dim3(grid), dim3(NW * 64), 0, stream, a);
+                launch_pp<H, BKV, false, false, true>(a, grid, stream);
             return hipGetLastError();
         }
         // a causal left window on an otherwise dense shape: the ping-pong kernel
@@ -1288,7 +1207,7 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
         const bool dense_win = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
                                mask_left_window_only(m) && diag_tiles;
         if (dense_win) {
-            hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, true, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+            launch_pp<H, BKV, true, true, false>(a, grid, stream);
             return hipGetLastError();
         }
     }
@@ -1336,7 +1255,7 @@ FwdConfig fwd_config(int G, int T, int H) {
     // (1 per SIMD, up to 512 registers). gw query heads (the largest divisor of
     // G that is <= the wave count) share each K/V tile.
     FwdConfig cfg;
-    cfg.nw = (H == 256) ? 4 : (H == 128 ? GQA_FWD_NW128 : 8);
+    cfg.nw = (H == 256) ? 4 : 8;
     cfg.bkv = (H == 256) ? 32 : 64;
     int gw = 1;
     for (int d = 1; d <= cfg.nw && d <= G; d++)
@@ -1396,10 +1315,10 @@ hipError_t launch_fwd_merge(const FwdArgs &a, int H, hipStream_t stream) {
 
 // Split-KV pays when the usual grid leaves the GPU idle (few (b, kv head)
 // units and query blocks, as in decoding with T << S): the key range is then
-// cut into splits of whole tiles until the grid has about kTargetBlocks
+// cut into splits of whole tiles until the grid has about split_target
 // workgroups, keeping at least kMinSplitTiles tiles per split.
-SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H) {
-    constexpr long long kTargetBlocks = GQA_SPLIT_TARGET;
+SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H, int split_target) {
+    const long long kTargetBlocks = split_target;
     constexpr int kMinSplitTiles = 4;
     const FwdConfig full = fwd_config(G, T, H);
     const long long base_full = (long long)B * K * (G / full.gw) * ((T + full.bq - 1) / full.bq);
@@ -1407,7 +1326,7 @@ SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H) {
     const long long base = (long long)B * K * (G / cfg.gw) * ((T + cfg.bq - 1) / cfg.bq);
     const int n_tiles = (S + cfg.bkv - 1) / cfg.bkv;
     SplitPlan p{1, n_tiles};
-    if (base_full >= kTargetBlocks / 2 || n_tiles < 2 * kMinSplitTiles) return p;
+    if (split_target <= 0 || base_full >= kTargetBlocks / 2 || n_tiles < 2 * kMinSplitTiles) return p;
     int want = (int)((kTargetBlocks + base - 1) / base);
     want = min(want, n_tiles / kMinSplitTiles);
     if (want < 2) return p;
@@ -1416,13 +1335,48 @@ SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H) {
     return p;
 }
 
+// ---------------------------------------------------------------------------
+// The runtime tuning table (tuning/mi355x.json, via the generated
+// tuning_table.inc): the first row that matches a call gives its choice.
+namespace {
+struct LoadPlacementRow {
+    int H, causal, segments, window, g8, t_min, t_max, s_min, s_max, value;
+};
+struct SplitTargetRow {
+    int H, t_min, t_max, s_min, s_max, value;
+};
+#include "tuning_table.inc"
+inline bool hit(int want, int have) { return want < 0 || want == have; }
+}  // namespace
+
+int fwd_split_target(int T, int S, int H) {
+    for (const SplitTargetRow &r : kSplitTargetRows)
+        if (hit(r.H, H) && T >= r.t_min && T <= r.t_max && S >= r.s_min && S <= r.s_max) return r.value;
+    return 1024;
+}
+
+FwdTuning fwd_tuning(int G, int T, int S, int H, const MaskSpec &m, bool segments) {
+    FwdTuning t{0, fwd_split_target(T, S, H)};
+    // the window column: 0 nothing beyond the causal diagonal, 1 a causal left
+    // window only, 2 anything else (prefix keys, right windows)
+    const int window = !mask_extra(m) ? 0 : (mask_left_window_only(m) ? 1 : 2);
+    for (const LoadPlacementRow &r : kLoadPlacementRows) {
+        if (hit(r.H, H) && hit(r.causal, m.causal) && hit(r.segments, segments ? 1 : 0) && hit(r.window, window) &&
+            hit(r.g8, G % 8 == 0 ? 1 : 0) && T >= r.t_min && T <= r.t_max && S >= r.s_min && S <= r.s_max) {
+            t.load_placement = r.value;
+            break;
+        }
+    }
+    return t;
+}
+
 // H = 256 on the ping-pong kernel: 8 waves of 32 query rows (gw = 8 heads by
 // bq = 32 queries) over 32-key tiles, for dense shapes: no segment ids, no
 // window or prefix, whole key tiles, and when causal T + coff == S with the
 // diagonal offset coff a whole number of tiles (the diagonal tile is then
 // each block's last).
 bool fwd_pp256_applies(int G, int T, int S, const MaskSpec &m, bool segments) {
-    return GQA_FWD_PINGPONG && G % 8 == 0 && !segments && S % 32 == 0 && !mask_extra(m) &&
+    return G % 8 == 0 && !segments && S % 32 == 0 && !mask_extra(m) &&
            (!m.causal || (m.coff >= 0 && m.coff % 32 == 0 && T + m.coff == S));
 }
 
@@ -1438,9 +1392,9 @@ FwdConfig fwd_config_pp256() {
 static hipError_t launch_fwd_pp256(const FwdArgs &a, hipStream_t stream) {
     const unsigned grid = (unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks);
     if (a.causal)
-        hipLaunchKernelGGL((attn_fwd_pp_kernel<256, 32, true, false>), dim3(grid), dim3(512), 0, stream, a);
+        launch_pp<256, 32, true, false, false>(a, grid, stream);
     else
-        hipLaunchKernelGGL((attn_fwd_pp_kernel<256, 32, false, false>), dim3(grid), dim3(512), 0, stream, a);
+        launch_pp<256, 32, false, false, false>(a, grid, stream);
     return hipGetLastError();
 }
 
@@ -1455,7 +1409,7 @@ hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
     }
     switch (H) {
         case 64: return launch_fwd_t<64, 64, 8, 2>(a, stream);
-        case 128: return launch_fwd_t<128, GQA_FWD_BKV128, GQA_FWD_NW128, 2>(a, stream);
+        case 128: return launch_fwd_t<128, 64, 8, 2>(a, stream);
         case 256:
             // a configuration from fwd_config_pp256 (all 8 waves hold rows)
             if (a.gw * a.bq == 256) return launch_fwd_pp256(a, stream);

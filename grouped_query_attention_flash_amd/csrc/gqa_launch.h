@@ -42,6 +42,7 @@ struct FwdArgs {
     int coff;
     int wl, wr;
     int prefix;
+    int load_placement;  // ping-pong kernel: where a wave issues its tile loads (FwdTuning)
     int gw;         // query heads per workgroup (divides G)
     int bq;         // queries per workgroup; gw * bq is a multiple of 32
     int n_gsplit;   // G / gw
@@ -58,10 +59,24 @@ struct FwdArgs {
 };
 
 // Split-KV plan of a shape (pure host function): n_splits == 1 means none.
+// split_target: the workgroups the plan aims for (0 never splits).
 struct SplitPlan {
     int n_splits, split_tiles;
 };
-SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H);
+SplitPlan fwd_split_plan(int B, int K, int G, int T, int S, int H, int split_target);
+
+// Schedule choices of the forward that leave its arithmetic unchanged (the
+// outputs are bitwise equal across them), chosen per call from the tuning
+// table compiled in from tuning/mi355x.json, or given by the caller.
+//   load_placement  ping-pong kernel: a wave issues its K/V tile loads in its
+//                   softmax phase (0), at the start of its MFMA phase (1) or
+//                   spread over its MFMA phase (2)
+//   split_target    split-KV: workgroups the split plan aims for (0: none)
+struct FwdTuning {
+    int load_placement, split_target;
+};
+FwdTuning fwd_tuning(int G, int T, int S, int H, const MaskSpec &m, bool segments);
+int fwd_split_target(int T, int S, int H);
 hipError_t launch_fwd_merge(const FwdArgs &a, int H, hipStream_t stream);
 
 struct FwdConfig {

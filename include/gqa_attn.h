@@ -71,8 +71,9 @@ enum {
     GQA_ATTN_ERR_SEGMENTS = 5,  /* exactly one of q_seg / kv_seg given           */
     GQA_ATTN_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required       */
     GQA_ATTN_ERR_HIP = 7,       /* a HIP launch failed: see attn_last_hip_error  */
-    GQA_ATTN_ERR_MASK = 8       /* causal not 0/1/2, a window side below -1, or a
+    GQA_ATTN_ERR_MASK = 8,      /* causal not 0/1/2, a window side below -1, or a
                                    negative prefix                               */
+    GQA_ATTN_ERR_TUNING = 9     /* an explicit schedule choice out of range      */
 };
 
 /* Forward pass (danielwatson6.github.io/fa, "Optimizing the kernel": the fused
@@ -201,6 +202,41 @@ int attn_check_fwd_mask(const void *q, const void *k, const void *v, const void 
                         const int32_t *q_seg, const int32_t *kv_seg,
                         int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
                         int prefix, const void *workspace, size_t workspace_bytes);
+
+/* Forward pass with an explicit schedule: attn_fwd_mask with the caller's
+ * choice of the two schedule parameters the library otherwise takes from its
+ * tuning table (attn_fwd_tuning). The pages' kernels take their block sizes
+ * from the caller, with a default getter whose heuristic is left as a TODO
+ * (fjformer page, "BlockSizes dataclass": BlockSizes and get_default; the
+ * block-size sweep of danielwatson6.github.io/fa, "Optimizing the kernel").
+ * Here the tile shapes are fixed per head size and kernel; what varies per
+ * shape is:
+ *   load_placement  where a ping-pong forward wave issues its K/V tile loads:
+ *                   0 in its softmax phase, 1 at the start of its MFMA phase,
+ *                   2 spread over its MFMA phase; -1 = the table's choice
+ *   split_target    the workgroups the split-KV plan aims for when the grid is
+ *                   small (0 = never split, at most 2^20); -1 = the table's
+ * Neither changes the arithmetic: every choice gives bitwise the same O and
+ * lse. The workspace must hold attn_fwd_tuned_workspace_bytes(...,
+ * split_target). Errors as attn_fwd_mask, plus ERR_TUNING for a choice out of
+ * range. */
+int attn_fwd_tuned(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int32_t *q_seg, const int32_t *kv_seg,
+                   int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right, int prefix,
+                   int load_placement, int split_target, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of attn_fwd_tuned for a split target (-1: the table's, the
+ * same as attn_fwd_workspace_bytes). 0 when the plan does not split or for
+ * invalid arguments. Library convention (no passage). */
+size_t attn_fwd_tuned_workspace_bytes(int B, int K, int G, int T, int S, int H, int split_target);
+
+/* The tuning table's schedule for a call (host only): the role of get_default
+ * in fjformer's BlockSizes dataclass, filled from measured sweeps on MI355X
+ * instead of a fixed default. segments: nonzero when segment ids are given.
+ * Writes load_placement and split_target; returns 0, or ERR_NULL / ERR_SHAPE /
+ * ERR_HEADDIM / ERR_MASK for invalid arguments. */
+int attn_fwd_tuning(int B, int K, int G, int T, int S, int H, int causal, int window_left, int window_right,
+                    int prefix, int segments, int *load_placement, int *split_target);
 
 /* Bytes of device workspace attn_bwd needs for these sizes: the per-row
  * D = sum_s P[t,s] dP[t,s] vector, fp32 [B,K,G,T], then lse * log2(e) in the

@@ -198,3 +198,64 @@ def test_python_binding_rejects_before_calling():
     k = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         gqa.attn_fwd(q, k, k)  # CPU tensors are refused; nothing is launched
+
+
+def _json_choice(table, key, H, G, T, S, causal, segments, window_col):
+    """The first row of the committed tuning JSON that matches (the same
+    first-match rule the library compiles in)."""
+    def hit(row, name, have):
+        return row.get(name, -1) in (-1, have)
+    for r in table[key]:
+        if not hit(r, "H", H):
+            continue
+        if key == "load_placement" and not (hit(r, "causal", causal) and hit(r, "segments", segments)
+                                             and hit(r, "window", window_col) and hit(r, "g8", int(G % 8 == 0))):
+            continue
+        if not (r.get("t_min", 0) <= T <= r.get("t_max", 2 ** 31 - 1)
+                and r.get("s_min", 0) <= S <= r.get("s_max", 2 ** 31 - 1)):
+            continue
+        return r[key]
+    raise AssertionError("no catch-all row")
+
+
+def test_tuning_table_matches_the_committed_json():
+    """attn_fwd_tuning returns, for every shape class, the first matching row of
+    tuning/mi355x.json: the runtime selection reads the committed sweep table."""
+    import json
+    table = json.load(open(os.path.join(ROOT, "grouped_query_attention_flash_amd", "tuning", "mi355x.json")))
+    shapes = [
+        # B, K, G, T, S, H, causal, window, prefix, segments, window column (0 none, 1 causal left, 2 other)
+        (1, 8, 4, 8192, 8192, 128, 1, None, 0, False, 0),
+        (2, 8, 4, 4096, 4096, 128, 1, None, 0, False, 0),
+        (4, 8, 4, 2048, 2048, 128, 1, None, 0, True, 0),
+        (1, 2, 8, 32768, 32768, 256, 1, None, 0, False, 0),
+        (1, 1, 4, 256, 256, 128, 0, None, 0, False, 0),
+        (1, 8, 4, 8192, 8192, 64, 1, None, 0, False, 0),
+        (1, 8, 4, 8192, 8192, 128, 1, (1023, -1), 0, False, 1),
+        (1, 8, 4, 8192, 8192, 64, 1, (1023, -1), 0, False, 1),
+        (1, 8, 4, 4096, 4096, 128, 1, None, 100, False, 2),
+        (16, 8, 4, 1, 32768, 128, 0, None, 0, False, 0),
+        (1, 8, 4, 512, 8192, 128, 2, None, 0, False, 0),
+    ]
+    for B, K, G, T, S, H, causal, win, pfx, seg, wcol in shapes:
+        lp, st = gqa.attn_fwd_tuning(B, K, G, T, S, H, causal=causal, window=win, prefix=pfx, segments=seg)
+        assert lp == _json_choice(table, "load_placement", H, G, T, S, int(causal != 0), int(seg), wcol), (T, S, H)
+        assert st == _json_choice(table, "split_target", H, G, T, S, causal, seg, wcol), (T, S, H)
+        # the workspace of the table's split target is the plain call's
+        assert gqa.attn_fwd_tuned_workspace_bytes(B, K, G, T, S, H, -1) == gqa.attn_fwd_workspace_bytes(B, K, G, T, S, H)
+    # a split target of 0 never splits; invalid arguments are refused
+    assert gqa.attn_fwd_tuned_workspace_bytes(16, 8, 4, 1, 32768, 128, 0) == 0
+    assert gqa.attn_fwd_tuned_workspace_bytes(16, 8, 4, 1, 32768, 128, -7) == 0
+    with pytest.raises(ValueError):
+        gqa.attn_fwd_tuning(1, 1, 4, 64, 64, 96)
+    with pytest.raises(ValueError):
+        gqa.attn_fwd_tuning(1, 1, 4, 64, 64, 128, causal=3)
+
+
+def test_generated_table_is_current():
+    """csrc/tuning_table.inc is what gen_table.py writes from the JSON."""
+    from grouped_query_attention_flash_amd.tuning import gen_table
+    import json
+    table = json.load(open(gen_table.JSON_PATH))
+    gen_table.check(table)
+    assert open(gen_table.INC_PATH).read() == gen_table.render(table)
