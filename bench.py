@@ -365,8 +365,10 @@ def decode_bench(args):
         # the oracle's rate in the metric's unit: each sampled row stands for
         # its share of the launch's algorithmic bytes
         total_rows = w.B * w.K * w.G * w.T
-        cb["value_tflops"] = cb["value"]
+        to_gbps = (hbm_bytes / flops) * 1e3  # TFLOP/s -> GB/s at the launch's bytes per FLOP
+        cb["value_tflops"], cb["fp64_value_tflops"] = cb["value"], cb["fp64_value"]
         cb["value"] = cb["rows"] / total_rows * hbm_bytes / cb["elapsed_s"] / 1e9
+        cb["fp64_value"] = cb["fp64_value"] * to_gbps
         cb["unit"] = "GB/s"
         result["cpu_baseline"] = cb
     finish(result)
