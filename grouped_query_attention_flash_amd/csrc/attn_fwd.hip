@@ -694,10 +694,48 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     const size_t bk = (size_t)b * a.K + kh;
     const size_t qrow_off = ((bk * a.G + g) * (size_t)T + t) * H;
 
-    bf16x8 qf[KSTEPS];
+    // SEG: every segment id the prologue needs (the lane's query, the block's
+    // queries, the keys of the tiles this wave stages) is loaded before Q and
+    // before any of them is used, so that the loads' latencies overlap
+    // instead of adding up.
+    constexpr int KV_CAP = SEG ? 8192 : 1;
+    constexpr int NT_CAP = SEG ? KV_CAP / BKV : 1;
+    constexpr int KV_PW = SEG ? NT_CAP / 8 : 1;  // key tiles a wave stages, at most
+    [[maybe_unused]] const int nt_all = CAUSAL ? qb + 1 + a.coff / BKV : S / BKV;
+    int pre_q = 0, pre_qb[4] = {}, pre_kv[KV_PW] = {};
+    if constexpr (SEG) {
+        const int32_t *qs = a.q_seg + (size_t)b * T;
+        const int32_t *kvs = a.kv_seg + (size_t)b * S;
+        // (loads from clamped in-range indices; the validity tests come at
+        // the uses, so that no select waits on a load here)
+        pre_q = qs[min(t, T - 1)];
+        // the block's queries t0 .. t0 + bq - 1 (bq <= 256: gw * bq == 256)
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ks++)
-        qf[ks] = q_valid ? *(const bf16x8 *)(a.q + qrow_off + 16 * ks + 8 * c) : bf16x8{};
+        for (int m = 0; m < 4; m++) pre_qb[m] = qs[min(t0 + lane + 64 * m, T - 1)];
+        // key tiles wave, wave + 8, ... (whole tiles: jj * BKV + lane < S)
+#pragma unroll
+        for (int m = 0; m < KV_PW; m++) {
+            const int jj = wave + 8 * m;
+            if (jj < nt_all) pre_kv[m] = kvs[jj * BKV + lane];
+        }
+    }
+
+    // Q^T. SEG: a row past T (a ragged last block) reads row T - 1 instead;
+    // its query column is computed but never stored, and no other column
+    // depends on it. Unconditional loads keep the compiler's waits exact, so
+    // that the id loads above and these are all in flight before the first
+    // use.
+    bf16x8 qf[KSTEPS];
+    if constexpr (SEG) {
+        const size_t qload_off = ((bk * a.G + g) * (size_t)T + min(t, T - 1)) * H;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++) qf[ks] = *(const bf16x8 *)(a.q + qload_off + 16 * ks + 8 * c);
+        sched_fence();
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++)
+            qf[ks] = q_valid ? *(const bf16x8 *)(a.q + qrow_off + 16 * ks + 8 * c) : bf16x8{};
+    }
 
     const buffer_rsrc krs = make_rsrc(a.k + bk * (size_t)S * H, S * H * 2);
     const buffer_rsrc vrs = make_rsrc(a.v + bk * (size_t)S * H, S * H * 2);
@@ -707,39 +745,39 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     // range meets the block's query-id range (in increasing order; the others
     // hold no visible pair). The loop walks that list; it is the same for
     // every wave, so both groups stay in step.
-    constexpr int KV_CAP = SEG ? 8192 : 1;
-    constexpr int NT_CAP = SEG ? KV_CAP / BKV : 1;
     __shared__ __attribute__((aligned(16))) int s_kvid[KV_CAP];
     __shared__ int s_tmin[NT_CAP], s_tmax[NT_CAP], s_jlist[NT_CAP];
     __shared__ int s_nvis;
     int my_qid = 0, w_qmin = 0, w_qmax = 0, n_vis = 0;
     if constexpr (SEG) {
-        const int32_t *qs = a.q_seg + (size_t)b * T;
-        const int32_t *kvs = a.kv_seg + (size_t)b * S;
-        my_qid = q_valid ? qs[t] : 0;
+        my_qid = q_valid ? pre_q : 0;
         w_qmin = wave_min_i(q_valid ? my_qid : INT_MAX);
         w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
         // id range of the block's queries t0 .. t0 + bq - 1 (bq may exceed
         // the wave's 64 lanes: 128 or 256 queries when a unit holds one or
         // two heads)
         int qlo = INT_MAX, qhi = INT_MIN;
-        for (int i = lane; i < a.bq; i += 64) {
-            if (t0 + i < T) {
-                const int id = qs[t0 + i];
-                qlo = min(qlo, id);
-                qhi = max(qhi, id);
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const int i = lane + 64 * m;
+            if (i < a.bq && t0 + i < T) {
+                qlo = min(qlo, pre_qb[m]);
+                qhi = max(qhi, pre_qb[m]);
             }
         }
         const int wg_qmin = wave_min_i(qlo), wg_qmax = wave_max_i(qhi);
-        const int nt_all = CAUSAL ? qb + 1 + a.coff / BKV : S / BKV;
-        for (int jj = wave; jj < nt_all; jj += 8) {
-            const bool ok = lane < BKV;  // whole tiles: jj * BKV + lane < S
-            const int id = ok ? kvs[jj * BKV + lane] : 0;
-            if (ok) s_kvid[jj * BKV + lane] = id;
-            const int lo = wave_min_i(ok ? id : INT_MAX), hi = wave_max_i(ok ? id : INT_MIN);
-            if (lane == 0) {
-                s_tmin[jj] = lo;
-                s_tmax[jj] = hi;
+        static_assert(!SEG || BKV == 64, "one key per lane");
+#pragma unroll
+        for (int m = 0; m < KV_PW; m++) {
+            const int jj = wave + 8 * m;
+            if (jj < nt_all) {
+                const int id = pre_kv[m];
+                s_kvid[jj * BKV + lane] = id;
+                const int lo = wave_min_i(id), hi = wave_max_i(id);
+                if (lane == 0) {
+                    s_tmin[jj] = lo;
+                    s_tmax[jj] = hi;
+                }
             }
         }
         __syncthreads();
