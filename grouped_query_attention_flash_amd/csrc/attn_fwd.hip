@@ -27,6 +27,8 @@
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
+#include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <type_traits>
@@ -657,8 +659,8 @@ __device__ __forceinline__ void m_phase_schedule(std::integer_sequence<int, P...
 // (V(i-1)), which both groups have finished. The V phase is the longer one
 // when the MFMAs per tile are few (H = 64) or the blocks short (segment ids),
 // and there moving the loads out of it pays.
-template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG = false, int MLD = 0>
-__global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG, int MLD>
+__device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid) {
     constexpr int NG = 4;  // waves per group (8 per workgroup)
     constexpr int CPR = H / 8;
     constexpr int KSTEPS = H / 16;
@@ -679,9 +681,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
 
     // ---- work unit (causal: heaviest query block first) and this lane's row
     const int units = a.B * a.K * a.n_gsplit;
-    int qb = blockIdx.x / units;
+    int qb = bid / units;
     if (CAUSAL) qb = a.n_qblocks - 1 - qb;
-    const int u = blockIdx.x % units;
+    const int u = bid % units;
     const int gs = u % a.n_gsplit;
     const int kh = (u / a.n_gsplit) % a.K;
     const int b = u / (a.n_gsplit * a.K);
@@ -1200,10 +1202,62 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     }
 }
 
+// The kernel: one query block per workgroup, or (PERSIST: H <= 128 without
+// segment ids, more blocks than compute units) a persistent grid of one
+// workgroup per compute unit walking the blocks in snake order (w, 2G - 1 -
+// w, 2G + w, ... for a grid of G): each round of G blocks is covered once,
+// and the heaviest causal blocks (first in the numbering) pair with the
+// lightest. This saves the dispatch of a new workgroup per block. With
+// segment ids the blocks' costs are unknown in advance and the hardware's
+// dynamic dispatch balances them better.
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG = false, int MLD = 0, bool PERSIST = false>
+__global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
+    if constexpr (PERSIST) {
+        const int total = a.B * a.K * a.n_gsplit * a.n_qblocks;
+        const int g2 = 2 * (int)gridDim.x;
+        for (int r = 0;; r++) {
+            const int bid = (r / 2) * g2 + ((r & 1) ? g2 - 1 - (int)blockIdx.x : (int)blockIdx.x);
+            if (bid >= total) break;
+            pp_block<H, BKV, CAUSAL, WIN, SEG, MLD>(a, bid);
+            __syncthreads();  // the next block's loads reuse the LDS slots
+        }
+    } else {
+        pp_block<H, BKV, CAUSAL, WIN, SEG, MLD>(a, blockIdx.x);
+    }
+}
+
 // The ping-pong kernel with the call's load placement (a runtime choice; the
 // three variants compute bitwise the same outputs).
+// Compute units of the current device, read once per device (1 if the query
+// fails, which leaves a persistent grid correct, only serial).
+static unsigned device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 1;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return (unsigned)n;
+}
+
 template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG>
 static void launch_pp(const FwdArgs &a, unsigned grid, hipStream_t stream) {
+    // H <= 128 without segment ids and more blocks than compute units: the
+    // persistent grid, one workgroup per CU (the kernel's LDS and registers
+    // allow one per CU)
+    if constexpr (H <= 128 && !SEG) {
+        const unsigned cus = device_cu_count();
+        if (grid > cus) {
+            switch (a.load_placement) {
+                case 1: hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, CAUSAL, WIN, SEG, 1, true>), dim3(cus), dim3(512), 0, stream, a); break;
+                case 2: hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, CAUSAL, WIN, SEG, 2, true>), dim3(cus), dim3(512), 0, stream, a); break;
+                default: hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, CAUSAL, WIN, SEG, 0, true>), dim3(cus), dim3(512), 0, stream, a); break;
+            }
+            return;
+        }
+    }
     switch (a.load_placement) {
         case 1: hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, CAUSAL, WIN, SEG, 1>), dim3(grid), dim3(512), 0, stream, a); break;
         case 2: hipLaunchKernelGGL((attn_fwd_pp_kernel<H, BKV, CAUSAL, WIN, SEG, 2>), dim3(grid), dim3(512), 0, stream, a); break;
