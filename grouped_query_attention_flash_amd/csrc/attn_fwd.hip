@@ -1314,6 +1314,222 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Split-KV decoding: few query rows per (b, kv head), R = G * T <= 16 (one new
+// token of each of the G query heads, say), against a long context. At T = 1
+// the work per byte is about G FLOP, so the call is bound by reading K and V.
+// The R rows of a unit all read the same K and V, so they are folded into the
+// 16 columns of one 16 x 16 MFMA tile: with 32 x 32 tiles and one wave per
+// head, each key would cost 32 times the MFMA work it needs.
+//
+// One workgroup per (b, kv head, split), 4 waves (one per SIMD). The split's
+// keys are cut into 16-key tiles; wave w takes tiles w, w + 4, ... and streams
+// them through its own ring of NST LDS stages (a K and a V tile per stage,
+// unpadded, 16-byte chunks XOR-swizzled by row), NST - 1 tiles ahead of its
+// compute. A wave reads only what it loaded, so it waits for its own loads
+// and the loop has no barrier.
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16: A = K rows, B = Q^T (registers)
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16: A = V^T (LDS transpose read),
+//                   B = P^T, which is the S^T accumulator's own layout
+// Lane l holds keys 4 (l / 16) + i (i < 4) of query column l % 16 of S^T, and
+// rows h = 16 hb + 4 (l / 16) + i of that column of O^T. The online softmax is
+// the forward's (exp2 domain, lazy rescale). At the end the 4 waves' running
+// max, sum and O merge through LDS into the split's normalised O and lse
+// (o_part, lse_part), which attn_fwd_merge_kernel combines across splits.
+template <int H, int NST>
+__global__ __launch_bounds__(256, 1) void attn_fwd_decode_kernel(FwdArgs a) {
+    constexpr int NW = 4, TK = 16;   // waves, keys per tile
+    constexpr int CPR = H / 8;       // 16-byte chunks per row
+    constexpr int TILE = TK * H;     // elements per K or V tile
+    constexpr int NLD = TILE / 512;  // 1 KiB loads per K or V tile
+    constexpr int KS = H / 32;       // k-steps of S^T = K Q^T
+    constexpr int HB = H / 16;       // 16-row blocks of O^T
+    constexpr int RPB = 128 / H;     // rows per 256 bytes (64 banks)
+    static_assert(NLD >= 1 && TILE % 512 == 0, "whole 1 KiB loads");
+    // K: chunk slot p of row r holds chunk p ^ kswz(r), so that a row read
+    // (16 lanes: 16 rows, one chunk) meets 16 distinct slots of 16 bytes mod
+    // 256. V: 32-byte pair slot p holds pair p ^ vswz(r), so that a transpose
+    // read (32 lanes: 8 rows of 32 bytes) meets 8 distinct 32-byte slots.
+    auto kswz = [](int r) { return (r / RPB) & (CPR - 1); };
+    auto vswz = [](int r) { return (r / RPB) & (CPR / 2 - 1); };
+    __shared__ __attribute__((aligned(1024))) __bf16 sk[NW][NST][TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 sv[NW][NST][TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp4 = lane >> 4;  // query column, key / h quad
+    const int R = a.G * a.T;                       // query rows of the unit
+    const int split = (int)blockIdx.x % a.n_splits;
+    const int unit = (int)blockIdx.x / a.n_splits;  // b * K + kv head
+    const int S = a.S;
+    const size_t rows_total = (size_t)a.B * a.K * R;
+
+    // the split's keys [k_begin, k_end) and this wave's 16-key tiles
+    const int k_begin = split * a.split_tiles * 64;
+    const int k_end = min(S, k_begin + a.split_tiles * 64);
+    const int n16 = max(0, (k_end - k_begin + TK - 1) / TK);
+    const int n_mine = n16 > wave ? (n16 - wave + NW - 1) / NW : 0;
+
+    // Q^T: column col is query row col of the unit (rows g T + t are
+    // contiguous in q); columns past R are zero and never stored
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+        qf[ks] = col < R ? *(const bf16x8 *)(a.q + ((size_t)unit * R + col) * H + 32 * ks + 8 * grp4) : bf16x8{};
+
+    const buffer_rsrc krs = make_rsrc(a.k + (size_t)unit * S * H, S * H * 2);
+    const buffer_rsrc vrs = make_rsrc(a.v + (size_t)unit * S * H, S * H * 2);
+    // per-lane byte offsets within a tile of the loads (load j: chunk slots
+    // 64 j + lane of the tile), and element offsets of the operand reads
+    int ld_k[NLD], ld_v[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; j++) {
+        const int p = 64 * j + lane, r = p / CPR, slot = p % CPR;
+        ld_k[j] = (r * H + 8 * (slot ^ kswz(r))) * 2;
+        const int pair = (slot >> 1) ^ vswz(r);
+        ld_v[j] = (r * H + 8 * (2 * pair + (slot & 1))) * 2;
+    }
+    int k_rd[KS], v_rd[HB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) k_rd[ks] = col * H + 8 * ((4 * ks + grp4) ^ kswz(col));
+    {
+        // transpose read: lane 16 g + m addresses key 4 g + m / 4, columns
+        // 16 hb + 4 (m % 4) .. + 3, and receives V[4 g + i][16 hb + m], i < 4
+        const int r = 4 * grp4 + col / 4;
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++)
+            v_rd[hb] = r * H + 16 * (hb ^ vswz(r)) + 8 * ((col & 3) >> 1) + 4 * (col & 1);
+    }
+    auto issue = [&](int i) {  // this wave's tile i into stage i % NST
+        const int key0 = k_begin + (wave + NW * i) * TK;
+        const int st = i % NST;
+#pragma unroll
+        for (int j = 0; j < NLD; j++) lds_load16_to(krs, (char *)sk[wave][st] + j * 1024, key0 * H * 2 + ld_k[j]);
+#pragma unroll
+        for (int j = 0; j < NLD; j++) lds_load16_to(vrs, (char *)sv[wave][st] + j * 1024, key0 * H * 2 + ld_v[j]);
+    };
+    // wait until tile i has landed: the loads of the k tiles issued after it
+    // may stay in flight
+    auto wait_tile = [&](int k) {
+        switch (k) {
+            case 0: wait_lds_loads(); break;
+            case 1: wait_lds_loads_but<2 * NLD>(); break;
+            case 2: wait_lds_loads_but<4 * NLD>(); break;
+            case 3: wait_lds_loads_but<6 * NLD>(); break;
+            default: wait_lds_loads_but<8 * NLD>(); break;
+        }
+    };
+    static_assert(NST <= 5 && 8 * NLD < 64, "wait_tile covers the ring");
+
+    f32x4 oacc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++) oacc[hb] = f32x4{};
+    float m_run = -INFINITY;  // reference max of column col, log2 units (same in its 4 lanes)
+    float l_run = 0.f;        // sum over this lane's keys of the column
+
+    for (int i = 0; i < min(NST - 1, n_mine); i++) issue(i);
+    for (int i = 0; i < n_mine; i++) {
+        if (i + NST - 1 < n_mine) {
+            // stage (i - 1) % NST: tile i - 1's reads are done (its MFMAs
+            // consumed them); make sure before the loads overwrite it
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            issue(i + NST - 1);
+        }
+        wait_tile(min(NST - 1, n_mine - 1 - i));
+        const int st = i % NST;
+        const __bf16 *kt = sk[wave][st];
+        const __bf16 *vt = sv[wave][st];
+        f32x4 s = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8 *)(kt + k_rd[ks]), qf[ks], s, 0, 0, 0);
+        const int key0 = k_begin + (wave + NW * i) * TK + 4 * grp4;
+        if (key0 + 3 >= k_end) {  // keys past the split (or past S) in the tile
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                if (key0 + e >= k_end) s[e] = -INFINITY;
+        }
+        float p[4];
+        auto weights = [&](float m_use) {
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                p[e] = exp2_fast(__builtin_fmaf(s[e], kLog2e, -m_use));
+                sum += p[e];
+            }
+            return sum;
+        };
+        float ls = weights(m_run);
+        if (__any(!(ls <= kRescaleBound))) {
+            // the tile's max per column (its 16 keys are in lanes col + 16 j)
+            float mx = max_nan(max_nan(s[0], s[1]), max_nan(s[2], s[3]));
+            mx = max_nan(mx, __shfl_xor(mx, 16));
+            mx = max_nan(mx, __shfl_xor(mx, 32));
+            const float m_new = max_nan(m_run, mx * kLog2e);
+            const float corr = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
+            l_run *= corr;
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++) oacc[hb] *= corr;
+            m_run = m_new;
+            ls = weights(m_run == -INFINITY ? 0.f : m_run);
+        }
+        l_run += ls;
+        s16x4 pt;
+#pragma unroll
+        for (int e = 0; e < 4; e++) pt[e] = __builtin_bit_cast(short, (__bf16)p[e]);
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++)
+            oacc[hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(vt + v_rd[hb]), pt, oacc[hb], 0, 0, 0);
+    }
+
+    // ---- merge the 4 waves: column sums, then (m, l, O) of every wave in LDS
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    __syncthreads();  // every wave is done with its ring (and its loads have landed)
+    float *mo = (float *)&sk[0][0][0];         // [NW][16][H] partial O^T columns
+    float *ml = mo + NW * 16 * H;              // [NW][16] max, then [NW][16] sum
+    static_assert((NW * 16 * H + 2 * NW * 16) * 4 <= (int)sizeof(sk), "merge buffer fits");
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++)
+        *(f32x4 *)(mo + (wave * 16 + col) * H + 16 * hb + 4 * grp4) = oacc[hb];
+    if (grp4 == 0) {
+        ml[wave * 16 + col] = m_run;
+        ml[NW * 16 + wave * 16 + col] = l_run;
+    }
+    __syncthreads();
+    // thread t: column t / 16, h = (t % 16) * H / 16 .. + H / 16
+    constexpr int HPT = H / 16;
+    const int q = tid >> 4, h0 = (tid & 15) * HPT;
+    if (q < R) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; w++) m = max_nan(m, ml[w * 16 + q]);
+        float wt[NW], L = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) {
+            wt[w] = m == -INFINITY ? 0.f : exp2_fast(ml[w * 16 + q] - m);
+            L += wt[w] * ml[NW * 16 + w * 16 + q];
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const size_t row = (size_t)unit * R + q;
+        float *orow = a.o_part + ((size_t)split * rows_total + row) * H + h0;
+#pragma unroll
+        for (int e = 0; e < HPT; e += 4) {
+            f32x4 v = f32x4{};
+#pragma unroll
+            for (int w = 0; w < NW; w++) v += wt[w] * *(const f32x4 *)(mo + (w * 16 + q) * H + h0 + e);
+            *(f32x4 *)(orow + e) = v * inv;
+        }
+        if (h0 == 0) a.lse_part[(size_t)split * rows_total + row] = L > 0.f ? (m + log2f(L)) * kLn2 : -INFINITY;
+    }
+}
+
+// Whether a split-KV call runs attn_fwd_decode_kernel: H = 64 or 128, at most
+// 16 query rows per (b, kv head), no segment ids and no mask.
+static bool fwd_decode_applies(int G, int T, int H, const MaskSpec &m, bool segments) {
+    return (H == 64 || H == 128) && G * T <= 16 && !segments && !m.causal && !mask_extra(m);
+}
+
 // Split-KV copies of the general kernel run 4 waves per workgroup at every
 // head size, so that at H <= 128 two workgroups share a CU (a decoding
 // workgroup has few query rows, and two of them keep twice the K/V bytes in
@@ -1492,6 +1708,15 @@ static hipError_t launch_fwd_pp256(const FwdArgs &a, hipStream_t stream) {
 
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
     if (a.o_part) {
+        const MaskSpec m{a.causal, a.coff, a.wl, a.wr, a.prefix};
+        if (fwd_decode_applies(a.G, a.T, H, m, a.q_seg != nullptr)) {
+            const unsigned grid = (unsigned)(a.B * a.K * a.n_splits);
+            if (H == 64)
+                hipLaunchKernelGGL((attn_fwd_decode_kernel<64, 5>), dim3(grid), dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((attn_fwd_decode_kernel<128, 4>), dim3(grid), dim3(256), 0, stream, a);
+            return hipGetLastError();
+        }
         switch (H) {
             case 64: return launch_fwd_split_t<64, 64, 2>(a, stream);
             case 128: return launch_fwd_split_t<128, 64, 2>(a, stream);

@@ -24,7 +24,11 @@ def run_split(q, k, v, causal, q_seg=None, kv_seg=None, workspace=None):
 
 
 # (B, K, G, T, S, H, causal, seg_len_range): decode and short-query shapes,
-# ragged S, every head size, causal (top-left: most splits see no key), segments
+# ragged S, every head size, causal (top-left: most splits see no key), segments.
+# Up to 16 query rows per (b, kv head) without a mask take the decoding kernel
+# (the rows of all heads in one 16-column tile, 16-key tiles per wave): R = 1,
+# 4, 8, 12 and 16, H = 64 and 128, a last split of 9 keys (its other waves
+# see none).
 CASES = [
     (1, 2, 4, 1, 4096, 128, False, None),
     (2, 2, 4, 3, 3000, 128, False, None),
@@ -34,6 +38,9 @@ CASES = [
     (1, 2, 4, 4, 4096, 128, False, (100, 900)),
     (1, 1, 1, 1, 2048, 128, False, None),
     (1, 1, 4, 40, 8000, 128, False, None),
+    (2, 2, 8, 2, 5000, 128, False, None),
+    (1, 2, 4, 4, 3000, 64, False, None),
+    (3, 1, 2, 1, 1289, 128, False, None),
 ]
 
 
