@@ -346,7 +346,7 @@ def decode_bench(args):
         "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
                    "causal": w.causal, "n_splits": n_splits},
         "roofline": {
-            "kernel": "attn_fwd_kernel split-KV + attn_fwd_merge_kernel (whole call)",
+            "kernel": "attn_fwd_decode_kernel<128,4> split-KV + attn_fwd_merge_kernel (whole call)",
             "bound": "hbm",
             "achieved": gbps,
             "peak": MI355X_HBM_GBPS,
