@@ -1344,14 +1344,15 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_decode_kernel(FwdArgs a) {
     constexpr int NLD = TILE / 512;  // 1 KiB loads per K or V tile
     constexpr int KS = H / 32;       // k-steps of S^T = K Q^T
     constexpr int HB = H / 16;       // 16-row blocks of O^T
-    constexpr int RPB = 128 / H;     // rows per 256 bytes (64 banks)
+    constexpr int RPB = H <= 128 ? 128 / H : 1;  // rows per 256 bytes (64 banks), at least 1
+    constexpr int KSW = CPR < 16 ? CPR - 1 : 15, VSW = CPR / 2 < 8 ? CPR / 2 - 1 : 7;
     static_assert(NLD >= 1 && TILE % 512 == 0, "whole 1 KiB loads");
     // K: chunk slot p of row r holds chunk p ^ kswz(r), so that a row read
     // (16 lanes: 16 rows, one chunk) meets 16 distinct slots of 16 bytes mod
     // 256. V: 32-byte pair slot p holds pair p ^ vswz(r), so that a transpose
     // read (32 lanes: 8 rows of 32 bytes) meets 8 distinct 32-byte slots.
-    auto kswz = [](int r) { return (r / RPB) & (CPR - 1); };
-    auto vswz = [](int r) { return (r / RPB) & (CPR / 2 - 1); };
+    auto kswz = [](int r) { return (r / RPB) & KSW; };
+    auto vswz = [](int r) { return (r / RPB) & VSW; };
     __shared__ __attribute__((aligned(1024))) __bf16 sk[NW][NST][TILE];
     __shared__ __attribute__((aligned(1024))) __bf16 sv[NW][NST][TILE];
 
@@ -1365,8 +1366,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_decode_kernel(FwdArgs a) {
     const size_t rows_total = (size_t)a.B * a.K * R;
 
     // the split's keys [k_begin, k_end) and this wave's 16-key tiles
-    const int k_begin = split * a.split_tiles * 64;
-    const int k_end = min(S, k_begin + a.split_tiles * 64);
+    // (split_tiles counts the split plan's key tiles: fwd_config_split's bkv)
+    constexpr int PLAN_BKV = H == 256 ? 32 : 64;
+    const int k_begin = split * a.split_tiles * PLAN_BKV;
+    const int k_end = min(S, k_begin + a.split_tiles * PLAN_BKV);
     const int n16 = max(0, (k_end - k_begin + TK - 1) / TK);
     const int n_mine = n16 > wave ? (n16 - wave + NW - 1) / NW : 0;
 
@@ -1410,16 +1413,18 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_decode_kernel(FwdArgs a) {
     };
     // wait until tile i has landed: the loads of the k tiles issued after it
     // may stay in flight
+    // (k < NST; the counts of k >= NST, never used, are clamped to compile)
+    constexpr auto cnt = [](int k) { return 2 * NLD * k < 64 ? 2 * NLD * k : 63; };
     auto wait_tile = [&](int k) {
         switch (k) {
             case 0: wait_lds_loads(); break;
-            case 1: wait_lds_loads_but<2 * NLD>(); break;
-            case 2: wait_lds_loads_but<4 * NLD>(); break;
-            case 3: wait_lds_loads_but<6 * NLD>(); break;
-            default: wait_lds_loads_but<8 * NLD>(); break;
+            case 1: wait_lds_loads_but<cnt(1)>(); break;
+            case 2: wait_lds_loads_but<cnt(2)>(); break;
+            case 3: wait_lds_loads_but<cnt(3)>(); break;
+            default: wait_lds_loads_but<cnt(4)>(); break;
         }
     };
-    static_assert(NST <= 5 && 8 * NLD < 64, "wait_tile covers the ring");
+    static_assert(NST <= 5 && 2 * NLD * (NST - 1) < 64, "wait_tile covers the ring within vmcnt");
 
     f32x4 oacc[HB];
 #pragma unroll
@@ -1486,9 +1491,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_decode_kernel(FwdArgs a) {
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     __syncthreads();  // every wave is done with its ring (and its loads have landed)
-    float *mo = (float *)&sk[0][0][0];         // [NW][16][H] partial O^T columns
-    float *ml = mo + NW * 16 * H;              // [NW][16] max, then [NW][16] sum
-    static_assert((NW * 16 * H + 2 * NW * 16) * 4 <= (int)sizeof(sk), "merge buffer fits");
+    float *mo = (float *)&sk[0][0][0];  // [NW][16][H] partial O^T columns
+    float *ml = (float *)&sv[0][0][0];  // [NW][16] max, then [NW][16] sum
+    static_assert(NW * 16 * H * 4 <= (int)sizeof(sk) && 2 * NW * 16 * 4 <= (int)sizeof(sv), "merge buffers fit");
 #pragma unroll
     for (int hb = 0; hb < HB; hb++)
         *(f32x4 *)(mo + (wave * 16 + col) * H + 16 * hb + 4 * grp4) = oacc[hb];
@@ -1524,10 +1529,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_decode_kernel(FwdArgs a) {
     }
 }
 
-// Whether a split-KV call runs attn_fwd_decode_kernel: H = 64 or 128, at most
-// 16 query rows per (b, kv head), no segment ids and no mask.
+// Whether a split-KV call runs attn_fwd_decode_kernel: at most 16 query rows
+// per (b, kv head), no segment ids and no mask.
 static bool fwd_decode_applies(int G, int T, int H, const MaskSpec &m, bool segments) {
-    return (H == 64 || H == 128) && G * T <= 16 && !segments && !m.causal && !mask_extra(m);
+    return (H == 64 || H == 128 || H == 256) && G * T <= 16 && !segments && !m.causal && !mask_extra(m);
 }
 
 // Split-KV copies of the general kernel run 4 waves per workgroup at every
@@ -1713,8 +1718,10 @@ hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
             const unsigned grid = (unsigned)(a.B * a.K * a.n_splits);
             if (H == 64)
                 hipLaunchKernelGGL((attn_fwd_decode_kernel<64, 5>), dim3(grid), dim3(256), 0, stream, a);
-            else
+            else if (H == 128)
                 hipLaunchKernelGGL((attn_fwd_decode_kernel<128, 4>), dim3(grid), dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((attn_fwd_decode_kernel<256, 2>), dim3(grid), dim3(256), 0, stream, a);
             return hipGetLastError();
         }
         switch (H) {

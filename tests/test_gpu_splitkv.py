@@ -27,8 +27,8 @@ def run_split(q, k, v, causal, q_seg=None, kv_seg=None, workspace=None):
 # ragged S, every head size, causal (top-left: most splits see no key), segments.
 # Up to 16 query rows per (b, kv head) without a mask take the decoding kernel
 # (the rows of all heads in one 16-column tile, 16-key tiles per wave): R = 1,
-# 4, 8, 12 and 16, H = 64 and 128, a last split of 9 keys (its other waves
-# see none).
+# 4, 8, 12 and 16, H = 64, 128 and 256, a last split of 9 keys (its other
+# waves see none).
 CASES = [
     (1, 2, 4, 1, 4096, 128, False, None),
     (2, 2, 4, 3, 3000, 128, False, None),
@@ -41,6 +41,8 @@ CASES = [
     (2, 2, 8, 2, 5000, 128, False, None),
     (1, 2, 4, 4, 3000, 64, False, None),
     (3, 1, 2, 1, 1289, 128, False, None),
+    (1, 2, 8, 1, 3000, 256, False, None),
+    (2, 1, 4, 4, 2000, 256, False, None),
 ]
 
 
