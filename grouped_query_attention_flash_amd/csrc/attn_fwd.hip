@@ -659,8 +659,20 @@ __device__ __forceinline__ void m_phase_schedule(std::integer_sequence<int, P...
 // (V(i-1)), which both groups have finished. The V phase is the longer one
 // when the MFMAs per tile are few (H = 64) or the blocks short (segment ids),
 // and there moving the loads out of it pays.
-template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG, int MLD>
-__device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid) {
+//
+// PF (a persistent grid without segment ids, loads in the V phase): the next
+// block's Q and first tiles are loaded during this block's last V phase
+// (next_bid >= 0), and this block's came from the previous one (prefetched).
+// The blocks of a workgroup rotate the slots: a block starts at slot base and
+// leaves base + n_t (mod 3) to the next. In the last V phases the phases still
+// to run read K slot base + n_t - 2 (group B's M(n_t - 2)) and V slots
+// base + n_t - 2 and base + n_t - 1, so the next block's K(0) (K slot
+// base + n_t - 1), K(1) and V(0) (slot base + n_t) are free. Q's registers
+// are dead after each group's last QK^T.
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG, int MLD, bool PF>
+__device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const int next_bid, int &base,
+                                         bf16x8 (&qf)[H / 16], const bool prefetched) {
+    static_assert(!PF || (MLD == 0 && !SEG), "prefetch: loads in the V phase, no segment ids");
     constexpr int NG = 4;  // waves per group (8 per workgroup)
     constexpr int CPR = H / 8;
     constexpr int KSTEPS = H / 16;
@@ -727,13 +739,12 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid) {
     // depends on it. Unconditional loads keep the compiler's waits exact, so
     // that the id loads above and these are all in flight before the first
     // use.
-    bf16x8 qf[KSTEPS];
     if constexpr (SEG) {
         const size_t qload_off = ((bk * a.G + g) * (size_t)T + min(t, T - 1)) * H;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ks++) qf[ks] = *(const bf16x8 *)(a.q + qload_off + 16 * ks + 8 * c);
         sched_fence();
-    } else {
+    } else if (!(PF && prefetched)) {
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ks++)
             qf[ks] = q_valid ? *(const bf16x8 *)(a.q + qrow_off + 16 * ks + 8 * c) : bf16x8{};
@@ -834,20 +845,21 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid) {
     // Tiles j < n_t lie wholly inside K and V (S % BKV == 0, rows < BKV), so
     // the tile offset may go in the scalar offset, which the range check does
     // not cover.
-    auto issue_tile = [&](int j, int slot) {
-        const int tile = __builtin_amdgcn_readfirstlane(tile_of(j) * BKV * H * 2);
+    auto issue_tile_from = [&](const buffer_rsrc &kr, const buffer_rsrc &vr, int jt, int slot) {
+        const int tile = __builtin_amdgcn_readfirstlane(jt * BKV * H * 2);
         if (grp == 0) {
 #pragma unroll
             for (int i = 0; i < KL; i++)
                 if (gwv + i * NG < L::K_BLOCKS)
-                    lds_load16_to(krs, (char *)sk[slot] + (gwv + i * NG) * 1024, ld_off[i], tile);
+                    lds_load16_to(kr, (char *)sk[slot] + (gwv + i * NG) * 1024, ld_off[i], tile);
         } else {
 #pragma unroll
             for (int i = 0; i < VL; i++)
                 if (gwv + i * NG < L::V_BLOCKS)
-                    lds_load16_to(vrs, (char *)sv[slot] + (gwv + i * NG) * 1024, ld_off[i], tile);
+                    lds_load16_to(vr, (char *)sv[slot] + (gwv + i * NG) * 1024, ld_off[i], tile);
         }
     };
+    auto issue_tile = [&](int j, int slot) { issue_tile_from(krs, vrs, tile_of(j), slot); };
     // the tile load an M phase issues (slot < 0: none)
     struct MLd {
         int bytes, slot;
@@ -1025,22 +1037,27 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid) {
         return MLD > 0 && i + 2 < n_t ? MLd{tile_of(i + 2) * BKV * H * 2, grp == 0 ? nslot : nnslot} : MLd{0, -1};
     };
 
-    // ---- prologue: K(0) -> slot 2, K(1) and V(0) -> slot 0 (MLD > 0: K(1)
-    // and V(1) come from M(-1))
-    issue_tile(0, grp == 0 ? 2 : 0);
-    if (MLD == 0 && grp == 0 && n_t > 1) issue_tile(1, 0);
-    wait_lds_loads();
+    // ---- prologue: K(0) -> slot base - 1, K(1) and V(0) -> slot base (MLD >
+    // 0: K(1) and V(1) come from M(-1)); base is 0 without PF. A prefetched
+    // block's loads have landed: each wave waited for its own at the end of
+    // the previous block's last M phase.
+    const int slot_m1 = base == 0 ? NSLOT - 1 : base - 1;
+    if (!(PF && prefetched)) {
+        issue_tile(0, grp == 0 ? slot_m1 : base);
+        if (MLD == 0 && grp == 0 && n_t > 1) issue_tile(1, base);
+        wait_lds_loads();
+    }
     barrier_no_drain();
 
     if (grp == 1) barrier_no_drain();  // group B runs one phase behind
     {                                  // M(-1): S^T of tile 0
-        const MLd ld = mload(-1, 0);
+        const MLd ld = mload(-1, base);
         if (MLD == 2 && ld.slot >= 0)
-            m_phase(yes{}, no{}, 2, 0, ld, yes{});
+            m_phase(yes{}, no{}, slot_m1, base, ld, yes{});
         else
-            m_phase(yes{}, no{}, 2, 0, ld, no{});
+            m_phase(yes{}, no{}, slot_m1, base, ld, no{});
     }
-    int slot = 0;                      // slot of tile set i: K(i+1), V(i)
+    int slot = base;                   // slot of tile set i: K(i+1), V(i)
     // MLD > 0: round i = V(i), the wait for the loads of M(i-1), M(i) with
     // its loads (rounds 0 .. n_t - 3; MLD 2 keeps the branch out of M by
     // peeling the last round). VK: how V(i) masks (0: no element mask, 1: the
@@ -1136,8 +1153,39 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid) {
     }
     // the last tile (the diagonal one when causal): nothing left to load or to
     // multiply with K. SEG masks it always (its ids and, when causal, the
-    // diagonal).
+    // diagonal). PF: the next block's loads go out first.
+    const int base_next = (base + n_t) % NSLOT;
     barrier_no_drain();
+    if constexpr (PF) {
+        if (next_bid >= 0) {
+            const int qb_n = CAUSAL ? a.n_qblocks - 1 - next_bid / units : next_bid / units;
+            const int u_n = next_bid % units;
+            const int kh_n = (u_n / a.n_gsplit) % a.K;
+            const int b_n = u_n / (a.n_gsplit * a.K);
+            const int t0_n = qb_n * a.bq;
+            const size_t bk_n = (size_t)b_n * a.K + kh_n;
+            // Q^T of the lane's next row, through a descriptor over its head's
+            // rows (wave-uniform: a wave's 32 rows belong to one head); a row
+            // past T reads zeros without a select
+            const int g_n = (u_n % a.n_gsplit) * a.gw + rho / a.bq;
+            const int t_n = t0_n + rho % a.bq;
+            const buffer_rsrc qrs = make_rsrc(a.q + (bk_n * a.G + g_n) * (size_t)T * H, T * H * 2);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ks++)
+                qf[ks] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, (t_n * H + 16 * ks + 8 * c) * 2, 0, 0));
+            const int j0_n = WIN && t0_n - WL > 0 ? (t0_n - WL) / BKV : 0;
+            const int n_t_n = (CAUSAL ? qb_n + 1 + a.coff / BKV : S / BKV) - j0_n;
+            const buffer_rsrc krs_n = make_rsrc(a.k + bk_n * (size_t)S * H, S * H * 2);
+            const buffer_rsrc vrs_n = make_rsrc(a.v + bk_n * (size_t)S * H, S * H * 2);
+            if (grp == 0) {
+                issue_tile_from(krs_n, vrs_n, j0_n, base_next == 0 ? NSLOT - 1 : base_next - 1);
+                if (n_t_n > 1) issue_tile_from(krs_n, vrs_n, j0_n + 1, base_next);
+            } else {
+                issue_tile_from(krs_n, vrs_n, j0_n, base_next);
+            }
+        }
+    }
     if (CAUSAL || SEG)
         v_phase_masked(tile_of(n_t - 1) * BKV);
     else
@@ -1157,11 +1205,22 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid) {
     // V slot. Every K slot and V slot n_t % 3 are dead here: the only phase
     // still running is group B's last PV, which reads V slot (n_t - 1) % 3,
     // and all loads have landed (each M phase ends with a wait). At H = 256
-    // the rows do not fit and O leaves straight from registers.
+    // the rows do not fit and O leaves straight from registers. PF: the next
+    // block's tiles hold K slots base + n_t - 1 and base + n_t and V slot
+    // base + n_t, so group A stages in K and V slot base + n_t + 1 (dead since
+    // group B's M(n_t - 2)) and group B in a region of its own.
     constexpr int OROW = H * 2 + 16;
     constexpr bool kStage = 2 * 32 * OROW <= L::K_ELEMS * 2 && 2 * 32 * OROW <= L::V_ELEMS * 2;
+    __shared__ __attribute__((aligned(16))) char s_ostage[PF && kStage ? 4 * 32 * OROW : 16];
     if constexpr (kStage) {
-        char *stage = (wave < 6 ? (char *)sk[wave >> 1] : (char *)sv[n_t % NSLOT]) + (wave & 1) * 32 * OROW;
+        char *stage;
+        if constexpr (PF) {
+            const int fs = base_next == NSLOT - 1 ? 0 : base_next + 1;
+            stage = grp == 1 ? s_ostage + (wave - 4) * 32 * OROW
+                             : (wave < 2 ? (char *)sk[fs] : (char *)sv[fs]) + (wave & 1) * 32 * OROW;
+        } else {
+            stage = (wave < 6 ? (char *)sk[wave >> 1] : (char *)sv[n_t % NSLOT]) + (wave & 1) * 32 * OROW;
+        }
 #pragma unroll
         for (int hb = 0; hb < HB; hb++)
 #pragma unroll
@@ -1200,6 +1259,7 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid) {
                 a.lse[(bk * a.G + g) * (size_t)T + t] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
         }
     }
+    if constexpr (PF) base = base_next;
 }
 
 // The kernel: one query block per workgroup, or (PERSIST: H <= 128 without
@@ -1212,17 +1272,25 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid) {
 // dynamic dispatch balances them better.
 template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG = false, int MLD = 0, bool PERSIST = false>
 __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
+    bf16x8 qf[H / 16];
+    int base = 0;
     if constexpr (PERSIST) {
         const int total = a.B * a.K * a.n_gsplit * a.n_qblocks;
         const int g2 = 2 * (int)gridDim.x;
+        auto bid_of = [&](int r) { return (r / 2) * g2 + ((r & 1) ? g2 - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+        // loads in the V phase, no segment ids: each block prefetches the next
+        constexpr bool PF = MLD == 0 && !SEG;
         for (int r = 0;; r++) {
-            const int bid = (r / 2) * g2 + ((r & 1) ? g2 - 1 - (int)blockIdx.x : (int)blockIdx.x);
+            const int bid = bid_of(r);
             if (bid >= total) break;
-            pp_block<H, BKV, CAUSAL, WIN, SEG, MLD>(a, bid);
-            __syncthreads();  // the next block's loads reuse the LDS slots
+            const int next = bid_of(r + 1) < total ? bid_of(r + 1) : -1;
+            pp_block<H, BKV, CAUSAL, WIN, SEG, MLD, PF>(a, bid, next, base, qf, r > 0);
+            // without the prefetch the next block's prologue reuses the LDS
+            // slots; with it the prologue's barrier orders the blocks
+            if constexpr (!PF) __syncthreads();
         }
     } else {
-        pp_block<H, BKV, CAUSAL, WIN, SEG, MLD>(a, blockIdx.x);
+        pp_block<H, BKV, CAUSAL, WIN, SEG, MLD, false>(a, blockIdx.x, -1, base, qf, false);
     }
 }
 
