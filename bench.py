@@ -173,7 +173,7 @@ def measured_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
-HEADLINE_KERNEL = "attn_fwd_pp_kernel<128, 64, true, false, false, 0>"
+HEADLINE_KERNEL = "attn_fwd_pp_kernel<128, 64, true, false, false, 0, true>"
 
 
 def write_traffic(fetch_csv, write_csv, calib_mib, out_path=TRAFFIC_FILE):
@@ -413,7 +413,7 @@ def window_bench(args):
         "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
                    "causal": True, "window_left": WINDOW_LEFT, "window_right": -1},
         "roofline": {
-            "kernel": "attn_fwd_pp_kernel<128,64,true,true,false,0> (ping-pong, windowed)",
+            "kernel": "attn_fwd_pp_kernel<128,64,true,true,false,0,true> (ping-pong, windowed, persistent grid)",
             "bound": "mfma",
             "achieved": tflops,
             "peak": MI355X_BF16_DENSE_TFLOPS,
@@ -528,18 +528,18 @@ def main():
         window_bench(args)
         return
     w = HEADLINE
-    kernel = "attn_fwd_pp_kernel<128,64,true,false,false,0> (ping-pong, dense causal)"
-    kernel_substr = "attn_fwd_pp_kernel<128, 64, true, false, false, 0>"
+    kernel = "attn_fwd_pp_kernel<128,64,true,false,false,0,true> (ping-pong, dense causal, persistent grid)"
+    kernel_substr = "attn_fwd_pp_kernel<128, 64, true, false, false, 0, true>"
     seg = None
     if args.workload == "long":
         w = WORKLOADS["causal_b1_k2_g8_t32768_h256"]
-        kernel = "attn_fwd_pp_kernel<256,32,true,false,false,0> (ping-pong, dense causal)"
-        kernel_substr = "attn_fwd_pp_kernel<256, 32, true, false, false, 0>"
+        kernel = "attn_fwd_pp_kernel<256,32,true,false,false,0,false> (ping-pong, dense causal)"
+        kernel_substr = "attn_fwd_pp_kernel<256, 32, true, false, false, 0, false>"
         args.no_backward = True
     elif args.workload == "segments":
         w = WORKLOADS["segments_causal_b4_k8_g4_t2048_h128"]
-        kernel = "attn_fwd_pp_kernel<128,64,true,false,true,2> (ping-pong, causal with segment ids; loads spread over the MFMA phase)"
-        kernel_substr = "attn_fwd_pp_kernel<128, 64, true, false, true, 2>"
+        kernel = "attn_fwd_pp_kernel<128,64,true,false,true,2,false> (ping-pong, causal with segment ids; loads spread over the MFMA phase)"
+        kernel_substr = "attn_fwd_pp_kernel<128, 64, true, false, true, 2, false>"
         args.no_backward = True
         seg = make_segment_ids(w.B, w.T, w.seed)
     t = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=not args.no_backward)
