@@ -345,8 +345,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
     constexpr int CPR = H / 8;
     constexpr int KSTEPS = H / 16;
     constexpr int HB = H / 32;
-    constexpr int RS = CPR + 3;                 // padded Q / dO rows, as in the kernel above
-    constexpr int TBLK = (BQ * RS + 63) / 64;   // 1 KiB wave loads per tile
+    // Q / dO tile layout (16-byte chunks): rows RS = CPR + 4 chunks apart,
+    // one more chunk after every 4 rows (group stride GS). The row reads (16
+    // lanes: 16 rows, one chunk each) and the transposed reads (32 lanes: 4
+    // rows, 4 chunks each) then both meet 16 distinct 4-bank groups of the
+    // 64 banks, so neither has bank conflicts, and every read's offset is a
+    // constant added to one base address per lane.
+    constexpr int RS = CPR + 4;
+    constexpr int GS = 4 * RS + 1;
+    constexpr int TBLK = (BQ / 4 * GS + 63) / 64;  // 1 KiB wave loads per tile
     constexpr int TILE = TBLK * 512;
     constexpr int TBW = (TBLK + NP - 1) / NP;   // tile loads per wave and step
     constexpr int NLD = TBW + 1;                // + lse (wave 0) or D (wave 4)
@@ -403,8 +410,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
     int t_off[TBW];
 #pragma unroll
     for (int i = 0; i < TBW; i++) {
+        // chunk p of the tile: row 4 (p / GS) + (p % GS) / RS; padding chunks
+        // (and those past the last row) re-read an in-range chunk
         const int p = (pair + i * NP) * 64 + lane;
-        t_off[i] = ((p / RS) * H + min(p % RS, CPR - 1) * 8) * 2;
+        const int rem = p % GS;
+        const int row = min(4 * (p / GS) + min(rem / RS, 3), BQ - 1);
+        t_off[i] = (row * H + min(rem % RS, CPR - 1) * 8) * 2;
     }
     const unsigned t_dst0 = (is_a ? lds_addr(sq[0]) : lds_addr(sdo[0])) + pair * 1024;
     const unsigned l_dst0 = lds_addr(sld[0][is_a ? 0 : 1]), dummy = lds_addr(sdummy);
@@ -438,9 +449,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
 #pragma unroll
     for (int hb = 0; hb < HB; hb++) acc[hb] = f32x16{};
 
-    const int row_lane = n * RS * 8 + c * 8;  // row n, chunk c
+    const int row_lane = ((n >> 2) * GS + (n & 3) * RS) * 8 + c * 8;  // row n, chunk c
     const int gi = lane & 15, hh = (lane >> 4) & 1;
-    const int tr_lane = (4 * c + (gi >> 2)) * RS * 8 + 16 * hh + 4 * (gi & 3);
+    // row 4 c + gi / 4 (group c, row gi / 4 of it), column 16 hh + 4 (gi & 3)
+    const int tr_lane = c * GS * 8 + (gi >> 2) * RS * 8 + 16 * hh + 4 * (gi & 3);
     // S (A) or dP (B) of the step in `stage`: 32 queries x the pair's 32 keys
     auto sdp = [&](int stage, f32x16 &x) {
         const __bf16 *rowp = (is_a ? sq[stage] : sdo[stage]) + row_lane;
@@ -522,8 +534,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         for (int xs = 0; xs < KSTEPS; xs++) {
             x = mfma32x32x16(*(const bf16x8 *)(rowp + 16 * xs), kv[xs], xs == 0 ? f32x16{} : x);
             const int kk = xs / HB, hb = xs % HB;
-            const __bf16 *base = trp + 16 * kk * RS * 8 + 32 * hb;
-            acc[hb] = mfma32x32x16(join_bf16x8(lds_read_tr16(base), lds_read_tr16(base + 8 * RS * 8)), w[kk], acc[hb]);
+            // rows 16 kk + ... (4 groups per 16 rows) and 8 rows (2 groups) further
+            const __bf16 *base = trp + kk * 4 * GS * 8 + 32 * hb;
+            acc[hb] = mfma32x32x16(join_bf16x8(lds_read_tr16(base), lds_read_tr16(base + 2 * GS * 8)), w[kk], acc[hb]);
         }
         pp_schedule<KSTEPS, 2, 3, 2>(std::make_integer_sequence<int, 2>(), std::make_integer_sequence<int, KSTEPS>());
         // the row product is read only in the next phase: keep the compiler
