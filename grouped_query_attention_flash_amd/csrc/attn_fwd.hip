@@ -669,10 +669,17 @@ __device__ __forceinline__ void m_phase_schedule(std::integer_sequence<int, P...
 // base + n_t - 2 and base + n_t - 1, so the next block's K(0) (K slot
 // base + n_t - 1), K(1) and V(0) (slot base + n_t) are free. Q's registers
 // are dead after each group's last QK^T.
-template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG, int MLD, bool PF>
+//
+// RAG: S is not a multiple of BKV. The last key tile is partial: every tile
+// then loads with its whole offset per lane, so that the range check reads
+// zeros past S, and the partial tile's keys at or past S are masked. Loads in
+// the V phase only (the M-phase placements put the tile offset in the scalar
+// offset, which the range check does not cover).
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG, int MLD, bool PF, bool RAG = false>
 __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const int next_bid, int &base,
                                          bf16x8 (&qf)[H / 16], const bool prefetched) {
     static_assert(!PF || (MLD == 0 && !SEG), "prefetch: loads in the V phase, no segment ids");
+    static_assert(!RAG || (MLD == 0 && !SEG), "partial key tiles: loads in the V phase, no segment ids");
     constexpr int NG = 4;  // waves per group (8 per workgroup)
     constexpr int CPR = H / 8;
     constexpr int KSTEPS = H / 16;
@@ -824,7 +831,7 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const 
     const int WL = a.wl;
     const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
     // causal: the block's diagonal tile qb + coff / BKV comes last
-    const int n_t = SEG ? n_vis : (CAUSAL ? qb + 1 + a.coff / BKV : S / BKV) - j0;
+    const int n_t = SEG ? n_vis : (CAUSAL ? qb + 1 + a.coff / BKV : (RAG ? (S + BKV - 1) / BKV : S / BKV)) - j0;
     // key tile of loop step i
     auto tile_of = [&](int i) { return SEG ? __builtin_amdgcn_readfirstlane(s_jlist[i]) : j0 + i; };
 
@@ -842,21 +849,25 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const 
         // re-read row BKV - 1 into the slot's tail
         ld_off[i] = (min(pslot / rs, BKV - 1) * H + min(pslot % rs, CPR - 1) * 8) * 2;
     }
-    // Tiles j < n_t lie wholly inside K and V (S % BKV == 0, rows < BKV), so
-    // the tile offset may go in the scalar offset, which the range check does
-    // not cover.
+    // Without RAG, tiles j < n_t lie wholly inside K and V (S % BKV == 0,
+    // rows < BKV), so the tile offset may go in the scalar offset, which the
+    // range check does not cover. With RAG it goes into each lane's offset.
     auto issue_tile_from = [&](const buffer_rsrc &kr, const buffer_rsrc &vr, int jt, int slot) {
         const int tile = __builtin_amdgcn_readfirstlane(jt * BKV * H * 2);
+        auto load = [&](const buffer_rsrc &r, char *dst, int off) {
+            if constexpr (RAG)
+                lds_load16_to(r, dst, off + tile);
+            else
+                lds_load16_to(r, dst, off, tile);
+        };
         if (grp == 0) {
 #pragma unroll
             for (int i = 0; i < KL; i++)
-                if (gwv + i * NG < L::K_BLOCKS)
-                    lds_load16_to(kr, (char *)sk[slot] + (gwv + i * NG) * 1024, ld_off[i], tile);
+                if (gwv + i * NG < L::K_BLOCKS) load(kr, (char *)sk[slot] + (gwv + i * NG) * 1024, ld_off[i]);
         } else {
 #pragma unroll
             for (int i = 0; i < VL; i++)
-                if (gwv + i * NG < L::V_BLOCKS)
-                    lds_load16_to(vr, (char *)sv[slot] + (gwv + i * NG) * 1024, ld_off[i], tile);
+                if (gwv + i * NG < L::V_BLOCKS) load(vr, (char *)sv[slot] + (gwv + i * NG) * 1024, ld_off[i]);
         }
     };
     auto issue_tile = [&](int j, int slot) { issue_tile_from(krs, vrs, tile_of(j), slot); };
@@ -1175,7 +1186,7 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const 
                 qf[ks] = __builtin_bit_cast(
                     bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, (t_n * H + 16 * ks + 8 * c) * 2, 0, 0));
             const int j0_n = WIN && t0_n - WL > 0 ? (t0_n - WL) / BKV : 0;
-            const int n_t_n = (CAUSAL ? qb_n + 1 + a.coff / BKV : S / BKV) - j0_n;
+            const int n_t_n = (CAUSAL ? qb_n + 1 + a.coff / BKV : (RAG ? (S + BKV - 1) / BKV : S / BKV)) - j0_n;
             const buffer_rsrc krs_n = make_rsrc(a.k + bk_n * (size_t)S * H, S * H * 2);
             const buffer_rsrc vrs_n = make_rsrc(a.v + bk_n * (size_t)S * H, S * H * 2);
             if (grp == 0) {
@@ -1186,10 +1197,14 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const 
             }
         }
     }
-    if (CAUSAL || SEG)
+    if constexpr (CAUSAL || SEG) {
         v_phase_masked(tile_of(n_t - 1) * BKV);
-    else
+    } else {
+        // a partial last tile: its keys at or past S out, then the usual
+        // weights (a lane whose keys are all out sums zero)
+        if constexpr (RAG) mask_tile(tile_of(n_t - 1) * BKV);
         v_phase_open();
+    }
     if (MLD > 0) wait_lds_loads();
     barrier_no_drain();
     m_phase(no{}, yes{}, slot, slot, MLd{0, -1}, no{});
@@ -1270,8 +1285,8 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const 
 // lightest. This saves the dispatch of a new workgroup per block. With
 // segment ids the blocks' costs are unknown in advance and the hardware's
 // dynamic dispatch balances them better.
-template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG = false, int MLD = 0, bool PERSIST = false>
-__global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG, int MLD, bool PERSIST, bool RAG>
+__device__ __forceinline__ void pp_run(const FwdArgs &a) {
     bf16x8 qf[H / 16];
     int base = 0;
     if constexpr (PERSIST) {
@@ -1284,14 +1299,26 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
             const int bid = bid_of(r);
             if (bid >= total) break;
             const int next = bid_of(r + 1) < total ? bid_of(r + 1) : -1;
-            pp_block<H, BKV, CAUSAL, WIN, SEG, MLD, PF>(a, bid, next, base, qf, r > 0);
+            pp_block<H, BKV, CAUSAL, WIN, SEG, MLD, PF, RAG>(a, bid, next, base, qf, r > 0);
             // without the prefetch the next block's prologue reuses the LDS
             // slots; with it the prologue's barrier orders the blocks
             if constexpr (!PF) __syncthreads();
         }
     } else {
-        pp_block<H, BKV, CAUSAL, WIN, SEG, MLD, false>(a, blockIdx.x, -1, base, qf, false);
+        pp_block<H, BKV, CAUSAL, WIN, SEG, MLD, false, RAG>(a, blockIdx.x, -1, base, qf, false);
     }
+}
+
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG = false, int MLD = 0, bool PERSIST = false>
+__global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
+    pp_run<H, BKV, CAUSAL, WIN, SEG, MLD, PERSIST, false>(a);
+}
+
+// The same with a partial last key tile (S not a multiple of BKV): loads in
+// the V phase, no segment ids.
+template <int H, int BKV, bool CAUSAL, bool WIN, bool PERSIST>
+__global__ __launch_bounds__(512, 2) void attn_fwd_pp_ragged_kernel(FwdArgs a) {
+    pp_run<H, BKV, CAUSAL, WIN, false, 0, PERSIST, true>(a);
 }
 
 // The ping-pong kernel with the call's load placement (a runtime choice; the
@@ -1312,6 +1339,23 @@ static unsigned device_cu_count() {
 
 template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG>
 static void launch_pp(const FwdArgs &a, unsigned grid, hipStream_t stream) {
+    // a partial last key tile: the ragged kernel (loads in the V phase, the
+    // same arithmetic as every placement)
+    if constexpr (!SEG) {
+        if (a.S % BKV != 0) {
+            if constexpr (H <= 128) {
+                const unsigned cus = device_cu_count();
+                if (grid > cus) {
+                    hipLaunchKernelGGL((attn_fwd_pp_ragged_kernel<H, BKV, CAUSAL, WIN, true>), dim3(cus), dim3(512),
+                                       0, stream, a);
+                    return;
+                }
+            }
+            hipLaunchKernelGGL((attn_fwd_pp_ragged_kernel<H, BKV, CAUSAL, WIN, false>), dim3(grid), dim3(512), 0,
+                               stream, a);
+            return;
+        }
+    }
     // H <= 128 without segment ids and more blocks than compute units: the
     // persistent grid, one workgroup per CU (the kernel's LDS and registers
     // allow one per CU)
@@ -1344,7 +1388,9 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     const bool dense = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 && !mask_extra(m) &&
                        diag_tiles;
     if constexpr (H <= 128 && NW == 8) {
-        if (dense) {
+        // the ping-pong kernel, also with a partial last key tile
+        const bool pp_dense = a.o_part == nullptr && a.q_seg == nullptr && all_waves && !mask_extra(m) && diag_tiles;
+        if (pp_dense) {
             if (a.causal)
                 launch_pp<H, BKV, true, false, false>(a, grid, stream);
             else
@@ -1364,8 +1410,8 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
         }
         // a causal left window on an otherwise dense shape: the ping-pong kernel
         // starting at each block's first visible tile
-        const bool dense_win = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
-                               mask_left_window_only(m) && diag_tiles;
+        const bool dense_win =
+            a.o_part == nullptr && a.q_seg == nullptr && all_waves && mask_left_window_only(m) && diag_tiles;
         if (dense_win) {
             launch_pp<H, BKV, true, true, false>(a, grid, stream);
             return hipGetLastError();
@@ -1757,7 +1803,7 @@ FwdTuning fwd_tuning(int G, int T, int S, int H, const MaskSpec &m, bool segment
 // diagonal offset coff a whole number of tiles (the diagonal tile is then
 // each block's last).
 bool fwd_pp256_applies(int G, int T, int S, const MaskSpec &m, bool segments) {
-    return G % 8 == 0 && !segments && S % 32 == 0 && !mask_extra(m) &&
+    return G % 8 == 0 && !segments && !mask_extra(m) &&
            (!m.causal || (m.coff >= 0 && m.coff % 32 == 0 && T + m.coff == S));
 }
 

@@ -26,6 +26,8 @@ CASES = [
     (8, 8, 4, 1024, 1024, 128, 1, 100),  # causal left window
     (8, 8, 4, 1024, 1024, 64, 1, -1),
     (3, 8, 4, 704, 704, 128, 1, -1),
+    (8, 8, 4, 1000, 1000, 128, 0, -1),  # partial last key tile
+    (8, 8, 4, 1000, 1000, 128, 1, -1),
 ]
 
 
