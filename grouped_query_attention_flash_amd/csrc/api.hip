@@ -97,10 +97,13 @@ static int run_fwd(const void *q, const void *k, const void *v, void *o, float *
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, const gqa::MaskSpec &m,
                    gqa::FwdTuning tune, gqa::SplitPlan plan, void *workspace, void *stream) {
+    const bool segments = q_seg != nullptr;
     const gqa::FwdConfig cfg =
-        plan.n_splits > 1 ? gqa::fwd_config_split(G, T, H)
-        : (H == 256 && gqa::fwd_pp256_applies(G, T, S, m, q_seg != nullptr)) ? gqa::fwd_config_pp256()
-                                                                             : gqa::fwd_config(G, T, H);
+        plan.n_splits > 1
+            ? (gqa::fwd_pp_split_applies(G, T, S, H, m, segments) ? gqa::fwd_config(G, T, H)
+                                                                  : gqa::fwd_config_split(G, T, H))
+        : (H == 256 && gqa::fwd_pp256_applies(G, T, S, m, segments)) ? gqa::fwd_config_pp256()
+                                                                     : gqa::fwd_config(G, T, H);
     gqa::FwdArgs a;
     a.q = (const __bf16 *)q;
     a.k = (const __bf16 *)k;

@@ -675,9 +675,16 @@ __device__ __forceinline__ void m_phase_schedule(std::integer_sequence<int, P...
 // zeros past S, and the partial tile's keys at or past S are masked. Loads in
 // the V phase only (the M-phase placements put the tile offset in the scalar
 // offset, which the range check does not cover).
-template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG, int MLD, bool PF, bool RAG = false>
+//
+// SPL: split-KV. The grid is n_splits copies of the blocks; copy j covers the
+// key tiles [j split_tiles, (j + 1) split_tiles) of each block's range and
+// writes its normalised fp32 O and lse to o_part[j] and lse_part[j], which the
+// merge kernel combines. Only the copy holding a block's diagonal tile masks
+// it; a copy whose range misses the block's keys writes O = 0, lse = -inf.
+template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG, int MLD, bool PF, bool RAG = false, bool SPL = false>
 __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const int next_bid, int &base,
                                          bf16x8 (&qf)[H / 16], const bool prefetched) {
+    static_assert(!SPL || (!PF && !SEG && !WIN && MLD == 0), "split-KV: dense shapes, loads in the V phase");
     static_assert(!PF || (MLD == 0 && !SEG), "prefetch: loads in the V phase, no segment ids");
     static_assert(!RAG || (MLD == 0 && !SEG), "partial key tiles: loads in the V phase, no segment ids");
     constexpr int NG = 4;  // waves per group (8 per workgroup)
@@ -700,9 +707,12 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const 
 
     // ---- work unit (causal: heaviest query block first) and this lane's row
     const int units = a.B * a.K * a.n_gsplit;
-    int qb = bid / units;
+    const int per_split = units * a.n_qblocks;
+    const int split = SPL ? bid / per_split : 0;
+    const int bidb = SPL ? bid % per_split : bid;
+    int qb = bidb / units;
     if (CAUSAL) qb = a.n_qblocks - 1 - qb;
-    const int u = bid % units;
+    const int u = bidb % units;
     const int gs = u % a.n_gsplit;
     const int kh = (u / a.n_gsplit) % a.K;
     const int b = u / (a.n_gsplit * a.K);
@@ -829,9 +839,31 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const 
     // window (causal only, WIN) starts the block's range at the first tile its
     // first query can see
     const int WL = a.wl;
-    const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
-    // causal: the block's diagonal tile qb + coff / BKV comes last
-    const int n_t = SEG ? n_vis : (CAUSAL ? qb + 1 + a.coff / BKV : (RAG ? (S + BKV - 1) / BKV : S / BKV)) - j0;
+    // causal: the block's diagonal tile qb + coff / BKV comes last (j_end is
+    // one past it); SPL: the copy's part of the range
+    const int j_end = CAUSAL ? qb + 1 + a.coff / BKV : (RAG ? (S + BKV - 1) / BKV : S / BKV);
+    const int j0_blk = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
+    const int j0 = SPL ? max(j0_blk, split * a.split_tiles) : j0_blk;
+    const int n_t = SEG ? n_vis : (SPL ? min(j_end, (split + 1) * a.split_tiles) : j_end) - j0;
+    // SPL: does the copy hold the block's last tile (the diagonal, or the
+    // partial one)?
+    const bool holds_last = !SPL || j0 + n_t == j_end;
+    if constexpr (SPL) {
+        if (n_t <= 0) {
+            // none of the block's keys: O = 0, lse = -inf
+            if (q_valid) {
+                const size_t row = (bk * a.G + g) * (size_t)T + t;
+                const size_t rows = (size_t)a.B * a.K * a.G * T;
+                float *orow = a.o_part + ((size_t)split * rows + row) * H;
+#pragma unroll
+                for (int hb = 0; hb < H / 32; hb++)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; q4++) *(f32x4 *)(orow + 32 * hb + 8 * q4 + 4 * c) = f32x4{};
+                if (c == 0) a.lse_part[(size_t)split * rows + row] = -INFINITY;
+            }
+            return;
+        }
+    }
     // key tile of loop step i
     auto tile_of = [&](int i) { return SEG ? __builtin_amdgcn_readfirstlane(s_jlist[i]) : j0 + i; };
 
@@ -1198,11 +1230,15 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const 
         }
     }
     if constexpr (CAUSAL || SEG) {
-        v_phase_masked(tile_of(n_t - 1) * BKV);
+        if (holds_last)
+            v_phase_masked(tile_of(n_t - 1) * BKV);
+        else
+            v_phase_open();  // SPL: a tile before the diagonal one
     } else {
         // a partial last tile: its keys at or past S out, then the usual
         // weights (a lane whose keys are all out sums zero)
-        if constexpr (RAG) mask_tile(tile_of(n_t - 1) * BKV);
+        if constexpr (RAG)
+            if (holds_last) mask_tile(tile_of(n_t - 1) * BKV);
         v_phase_open();
     }
     if (MLD > 0) wait_lds_loads();
@@ -1227,7 +1263,23 @@ __device__ __forceinline__ void pp_block(const FwdArgs &a, const int bid, const 
     constexpr int OROW = H * 2 + 16;
     constexpr bool kStage = 2 * 32 * OROW <= L::K_ELEMS * 2 && 2 * 32 * OROW <= L::V_ELEMS * 2;
     __shared__ __attribute__((aligned(16))) char s_ostage[PF && kStage ? 4 * 32 * OROW : 16];
-    if constexpr (kStage) {
+    if constexpr (SPL) {
+        // the copy's normalised O in fp32 and its lse, straight from registers
+        if (q_valid) {
+            const size_t row = (bk * a.G + g) * (size_t)T + t;
+            const size_t rows = (size_t)a.B * a.K * a.G * T;
+            float *orow = a.o_part + ((size_t)split * rows + row) * H;
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++)
+                    *(f32x4 *)(orow + 32 * hb + 8 * q4 + 4 * c) =
+                        f32x4{oacc[hb][4 * q4] * inv, oacc[hb][4 * q4 + 1] * inv, oacc[hb][4 * q4 + 2] * inv,
+                              oacc[hb][4 * q4 + 3] * inv};
+            if (c == 0)
+                a.lse_part[(size_t)split * rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+        }
+    } else if constexpr (kStage) {
         char *stage;
         if constexpr (PF) {
             const int fs = base_next == NSLOT - 1 ? 0 : base_next + 1;
@@ -1312,6 +1364,15 @@ __device__ __forceinline__ void pp_run(const FwdArgs &a) {
 template <int H, int BKV, bool CAUSAL, bool WIN, bool SEG = false, int MLD = 0, bool PERSIST = false>
 __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(FwdArgs a) {
     pp_run<H, BKV, CAUSAL, WIN, SEG, MLD, PERSIST, false>(a);
+}
+
+// Split-KV on the ping-pong kernel (dense shapes without a window; RAG: a
+// partial last key tile): one workgroup per (split, block).
+template <int H, int BKV, bool CAUSAL, bool RAG>
+__global__ __launch_bounds__(512, 2) void attn_fwd_pp_split_kernel(FwdArgs a) {
+    bf16x8 qf[H / 16];
+    int base = 0;
+    pp_block<H, BKV, CAUSAL, false, false, 0, false, RAG, true>(a, blockIdx.x, -1, base, qf, false);
 }
 
 // The same with a partial last key tile (S not a multiple of BKV): loads in
@@ -1825,6 +1886,31 @@ static hipError_t launch_fwd_pp256(const FwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Split-KV on the ping-pong kernel: H <= 128, no segment ids, no window or
+// prefix, and when causal the dense kernel's diagonal structure (one query
+// block per key tile, the diagonal offset a whole number of tiles). The call
+// then uses fwd_config's 8-wave blocks.
+bool fwd_pp_split_applies(int G, int T, int S, int H, const MaskSpec &m, bool segments) {
+    if (H > 128 || segments || mask_extra(m)) return false;
+    const FwdConfig cfg = fwd_config(G, T, H);
+    return !m.causal || (m.coff >= 0 && m.coff % cfg.bkv == 0 && T + m.coff == S && cfg.bq == cfg.bkv);
+}
+
+template <int H>
+static hipError_t launch_fwd_pp_split(const FwdArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.B * a.K * a.n_gsplit * a.n_qblocks * a.n_splits));
+    const bool rag = a.S % 64 != 0;
+    if (a.causal && rag)
+        hipLaunchKernelGGL((attn_fwd_pp_split_kernel<H, 64, true, true>), grid, dim3(512), 0, stream, a);
+    else if (a.causal)
+        hipLaunchKernelGGL((attn_fwd_pp_split_kernel<H, 64, true, false>), grid, dim3(512), 0, stream, a);
+    else if (rag)
+        hipLaunchKernelGGL((attn_fwd_pp_split_kernel<H, 64, false, true>), grid, dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_fwd_pp_split_kernel<H, 64, false, false>), grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
     if (a.o_part) {
         const MaskSpec m{a.causal, a.coff, a.wl, a.wr, a.prefix};
@@ -1837,6 +1923,11 @@ hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream) {
             else
                 hipLaunchKernelGGL((attn_fwd_decode_kernel<256, 2>), dim3(grid), dim3(256), 0, stream, a);
             return hipGetLastError();
+        }
+        // the ping-pong kernel's blocks (the call's configuration is fwd_config's)
+        if (a.gw * a.bq == 256 && fwd_pp_split_applies(a.G, a.T, a.S, H, m, a.q_seg != nullptr)) {
+            if (H == 64) return launch_fwd_pp_split<64>(a, stream);
+            if (H == 128) return launch_fwd_pp_split<128>(a, stream);
         }
         switch (H) {
             case 64: return launch_fwd_split_t<64, 64, 2>(a, stream);

@@ -89,6 +89,8 @@ FwdConfig fwd_config(int G, int T, int H);
 FwdConfig fwd_config_split(int G, int T, int H);
 // H = 256 dense shapes that run the ping-pong kernel, and its configuration.
 bool fwd_pp256_applies(int G, int T, int S, const MaskSpec &m, bool segments);
+// split-KV on the ping-pong kernel (with fwd_config's blocks)
+bool fwd_pp_split_applies(int G, int T, int S, int H, const MaskSpec &m, bool segments);
 FwdConfig fwd_config_pp256();
 hipError_t launch_fwd(const FwdArgs &a, int H, hipStream_t stream);
 

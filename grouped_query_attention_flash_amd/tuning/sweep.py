@@ -43,6 +43,13 @@ SPLIT_CLASSES = [
      [(16, 8, 4, 1, 32768, 128, 0, -1), (4, 8, 4, 1, 8192, 128, 0, -1), (16, 8, 4, 4, 8192, 128, 2, -1)]),
     ("decode_h256", {"H": 256, "t_max": 64}, [(8, 2, 8, 1, 32768, 256, 0, -1)]),
     ("decode_h64", {"H": 64, "t_max": 64}, [(16, 8, 4, 1, 16384, 64, 0, -1)]),
+    # chunked prefill: a chunk of queries after a long context (few query
+    # blocks), split on the ping-pong kernel
+    ("prefill_h128", {"H": 128, "t_min": 65},
+     [(1, 8, 4, 1024, 8192, 128, 2, -1), (1, 8, 4, 512, 8192, 128, 2, -1), (2, 8, 4, 1024, 8192, 128, 2, -1),
+      (1, 8, 4, 256, 8192, 128, 2, -1), (1, 8, 4, 512, 4096, 128, 0, -1)]),
+    ("prefill_h64", {"H": 64, "t_min": 65},
+     [(1, 8, 4, 1024, 8192, 64, 2, -1), (1, 8, 4, 512, 8192, 64, 2, -1)]),
 ]
 SPLIT_CANDIDATES = [0, 256, 512, 1024, 2048, 4096]
 
