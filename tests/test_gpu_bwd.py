@@ -68,6 +68,21 @@ def test_bwd_small_vs_oracle_all_elements(case):
     assert_close_all([("dQ", dq, ref["dq"]), ("dK", dk, ref["dk"]), ("dV", dv, ref["dv"])])
 
 
+def test_bwd_dq_with_and_without_the_ds_lo_part():
+    """Causal T = S = 2048 at H = 128 (the ping-pong dQ kernel): waves of the
+    early rows see |dS| above the bound for adding dS's bf16 lo part into dQ,
+    waves of the later rows stay under it and drop it. Every element of dQ,
+    dK and dV against the oracle."""
+    q, k, v, do = make_qkv(1, 1, 4, 2048, 2048, 128, seed=2048, with_do=True)
+    dq, dk, dv = run_gpu(q, k, v, do, True)
+    ref = oracle.bwd(q, k, v, do, causal=True)
+    assert_close_all([("dQ", dq, ref["dq"]), ("dK", dk, ref["dk"]), ("dV", dv, ref["dv"])])
+    # the first and last 256 rows of every head separately: both paths pass
+    dq4, ref4 = dq.reshape(4, 2048, 128), ref["dq"].reshape(4, 2048, 128)
+    assert_close_all([("dQ rows 0-255", dq4[:, :256], ref4[:, :256]),
+                      ("dQ rows 1792-2047", dq4[:, -256:], ref4[:, -256:])])
+
+
 def test_bwd_fwdbwd_workload_sampled_rows():
     """B=1, K=8, G=4, T=S=8192, H=128, causal: sampled dQ rows and dK/dV rows of two kv heads."""
     w = WORKLOADS["causal_fwdbwd_b1_k8_g4_t8192_h128"]
