@@ -27,6 +27,10 @@ H=128 (causal and segment ids, segments of 64-1024 tokens) in the same
 format; value and the roofline fraction count only the visible (t, s) pairs
 (the work the kernel executes), with the causal-half rate beside them.
 
+--workload prefill times a chunk of T=1024 new queries at the end of an
+S=8192 context (B=1, K=8, G=4, H=128, end-aligned causal) through the tuned
+split-KV forward, FLOPs counted on visible pairs, with the single pass beside it.
+
 --write-traffic FETCH_CSV WRITE_CSV turns two rocprofv3 --pmc runs (FETCH_SIZE,
 then WRITE_SIZE, each with --copy-calibration-mib) into the HBM bytes per
 launch of the headline forward kernel, scaled by what the same counters read
@@ -450,6 +454,80 @@ def window_bench(args):
     finish(result)
 
 
+def prefill_bench(args):
+    """A chunk of new queries at the end of a cached context (end-aligned
+    causal) through the tuned split-KV forward: MFMA-bound, FLOPs counted on
+    the visible pairs, the single pass timed beside it."""
+    import torch
+    import grouped_query_attention_flash_amd as gqa
+    from workloads import PREFILL, PREFILL_CAUSAL, end_aligned_pairs, make_qkv
+
+    w = PREFILL
+    q, k, v = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(w.B, w.K, w.G, w.T, dtype=torch.float32, device=dev)
+    n_splits = gqa.attn_fwd_split_count(w.B, w.K, w.G, w.T, w.S, w.H)
+    ws = torch.empty(max(1, gqa.attn_fwd_workspace_bytes(w.B, w.K, w.G, w.T, w.S, w.H)), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        gqa.attn_fwd(qd, kd, vd, causal=PREFILL_CAUSAL, out=o, lse=lse, split_kv=True, workspace=ws)
+
+    def step_single():
+        gqa.attn_fwd(qd, kd, vd, causal=PREFILL_CAUSAL, out=o, lse=lse)
+
+    ms_single = time_launches(step_single, max(5, args.steps // 2), max(2, args.warmup // 2), args.settle_seconds)
+    ms = time_launches(step, args.steps, args.warmup, args.settle_seconds)
+    pairs = end_aligned_pairs(w.T, w.S) * w.B * w.K * w.G
+    flops = 4.0 * w.H * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    hbm_bytes = 2 * (qd.numel() + kd.numel() + vd.numel() + o.numel()) + 4 * lse.numel()
+    result = {
+        "metric": "chunked-prefill attention TFLOP/s (fwd, end-aligned causal, T=1024 after 7168 cached keys) "
+                  "at 1 GPU; % of bf16 MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, q pre-scaled by H^-1/2)",
+        "config": {"workload": w.name, "B": w.B, "K": w.K, "G": w.G, "T": w.T, "S": w.S, "H": w.H,
+                   "causal": "end-aligned", "n_splits": n_splits},
+        "roofline": {
+            "kernel": "attn_fwd_pp_split_kernel<128,64,true,false> + attn_fwd_merge_kernel (whole call)",
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MI355X_BF16_DENSE_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_hbm_bytes_per_launch": hbm_bytes,
+            "visible_pairs": pairs,
+        },
+        "single_pass": {"ms": ms_single, "tflops": flops / (ms_single * 1e-3) / 1e12},
+    }
+    if not args.no_cpu_baseline:
+        step()
+        torch.cuda.synchronize()
+
+        def row_flops(rows):
+            t = rows % w.T
+            return float(4.0 * w.H * (t + w.S - w.T + 1).sum())
+
+        result["cpu_baseline"] = cpu_baseline({"q": q, "k": k, "v": v}, w, o, row_flops=row_flops,
+                                              oracle_kw={"causal": PREFILL_CAUSAL}, total_flops=flops)
+    finish(result)
+
+
 def finish(result):
     """Print the one JSON line; a sampled parity miss exits with status 3."""
     print(json.dumps(result), flush=True)
@@ -485,9 +563,11 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed launches before the warm-up steps, for the clock to settle")
-    ap.add_argument("--workload", choices=["headline", "decode", "window", "long", "segments"], default="headline",
+    ap.add_argument("--workload", choices=["headline", "decode", "window", "prefill", "long", "segments"],
+                    default="headline",
                     help="headline: the causal T=S=8192 forward (default); decode: T=1 against S=32768; "
                          "window: the headline shape with a causal 1024-key sliding window; "
+                         "prefill: 1024 end-aligned causal queries against S=8192 through the split-KV forward; "
                          "long: the causal T=S=32768 H=256 forward; "
                          "segments: the packed-sequence T=S=2048 forward with segment ids")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -526,6 +606,9 @@ def main():
         return
     if args.workload == "window":
         window_bench(args)
+        return
+    if args.workload == "prefill":
+        prefill_bench(args)
         return
     w = HEADLINE
     kernel = "attn_fwd_pp_kernel<128,64,true,false,false,0,true> (ping-pong, dense causal, persistent grid)"

@@ -103,3 +103,16 @@ def test_finish_exits_3_on_a_parity_miss(capsys):
     with pytest.raises(SystemExit) as e:
         bench.finish({"value": 1.0, "cpu_baseline": {"parity_ok": False}})
     assert e.value.code == 3
+
+
+def test_pair_counts_match_a_brute_force_mask():
+    """The visible-pair counts behind the window and prefill FLOP figures,
+    against counting a dense boolean mask."""
+    import numpy as np
+    from workloads import end_aligned_pairs, window_pairs
+    for T, S in [(1, 1), (5, 9), (9, 5), (16, 16), (7, 40)]:
+        t, s = np.arange(T)[:, None], np.arange(S)[None, :]
+        assert end_aligned_pairs(T, S) == int((s <= t + S - T).sum()), (T, S)
+        for wl in (0, 3, 100):
+            band = (s <= t) & (s >= t - wl)
+            assert window_pairs(T, S, wl) == int(band.sum()), (T, S, wl)

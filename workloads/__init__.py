@@ -76,9 +76,17 @@ WINDOW = Workload("window1024_causal_b1_k8_g4_t8192_h128", 1, 8, 4, 8192, 8192, 
 WINDOW_LEFT = 1023
 
 
+# Chunked prefill: a chunk of 1024 new queries at the end of an 8192-token
+# context (7168 cached keys), end-aligned causal (query t sees keys
+# s <= t + S - T). One workgroup per 256 query rows gives only 128 blocks, so
+# the call splits the key range. bench.py --workload prefill.
+PREFILL = Workload("prefill_endcausal_b1_k8_g4_t1024_s8192_h128", 1, 8, 4, 1024, 8192, 128, True, False, False, 8)
+PREFILL_CAUSAL = 2  # the end-aligned form of the causal argument
+
+
 def workload_by_bench_name(name: str) -> Workload:
     """The workload bench.py's --workload option names."""
-    return {"headline": HEADLINE, "decode": DECODE, "window": WINDOW,
+    return {"headline": HEADLINE, "decode": DECODE, "window": WINDOW, "prefill": PREFILL,
             "long": WORKLOADS["causal_b1_k2_g8_t32768_h256"],
             "segments": WORKLOADS["segments_causal_b4_k8_g4_t2048_h128"]}[name]
 
@@ -87,6 +95,11 @@ def window_pairs(T: int, S: int, wl: int, causal: bool = True) -> int:
     """Visible (t, s) pairs per head of a causal band t - wl <= s <= t."""
     assert causal
     return sum(min(t, S - 1) - max(0, t - wl) + 1 for t in range(T) if t - wl <= S - 1)
+
+
+def end_aligned_pairs(T: int, S: int) -> int:
+    """Visible (t, s) pairs per head when query t sees keys s <= t + S - T."""
+    return sum(max(0, min(S, t + S - T + 1)) for t in range(T))
 
 
 def make_qkv(B: int, K: int, G: int, T: int, S: int, H: int, seed: int,
