@@ -1760,38 +1760,73 @@ FwdConfig fwd_config(int G, int T, int H) {
 //   lse = ln sum_j exp(lse_j),   O = sum_j exp(lse_j - lse) O_j,
 // which is the online-softmax combination applied across the splits. A split
 // that sees no key has lse_j = -inf and weight 0; a row that sees none gets
-// O = 0 and lse = -inf. One wave per row, each lane H / 64 elements.
+// O = 0 and lse = -inf. One pass over the splits with a running maximum, so
+// that no load waits on another (the kernel is bound by the latency of its
+// loads, not their bytes); each wave takes kMergeRows rows, each lane H / 64
+// elements of a row.
+constexpr int kMergeRows = 2;
 template <int H>
 __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(FwdArgs a, int rows) {
     constexpr int EPL = H / 64;  // elements per lane
+    constexpr int RPW = kMergeRows;
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    float m = -INFINITY;
-    for (int j = 0; j < a.n_splits; j++) m = max_nan(m, a.lse_part[(size_t)j * rows + row]);
-    float acc[EPL];
+    const int row0 = ((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * RPW;
+    if (row0 >= rows) return;
+    float m[RPW], wsum[RPW], acc[RPW][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; e++) acc[e] = 0.f;
-    float wsum = 0.f;
-    if (m != -INFINITY) {
-        for (int j = 0; j < a.n_splits; j++) {
-            const float w = exp2_fast((a.lse_part[(size_t)j * rows + row] - m) * kLog2e);
-            wsum += w;
-            const float *op = a.o_part + ((size_t)j * rows + row) * H + lane * EPL;
+    for (int r = 0; r < RPW; r++) {
+        m[r] = -INFINITY;
+        wsum[r] = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; e++) acc[e] += w * op[e];
-        }
+        for (int e = 0; e < EPL; e++) acc[r][e] = 0.f;
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    __bf16 *orow = a.o + (size_t)row * H + lane * EPL;
+    // splits in groups of four, all loads of a group issued before any use
+    // (a split past n_splits reads the last one again and counts as -inf)
+    constexpr int NJ = 4;
+    for (int j0 = 0; j0 < a.n_splits; j0 += NJ) {
+        float lj[NJ][RPW], oj[NJ][RPW][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; e++) orow[e] = (__bf16)(acc[e] * inv);
-    if (lane == 0 && a.lse) a.lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+        for (int q = 0; q < NJ; q++)
+#pragma unroll
+            for (int r = 0; r < RPW; r++) {
+                const size_t pr = (size_t)min(j0 + q, a.n_splits - 1) * rows + min(row0 + r, rows - 1);
+                lj[q][r] = a.lse_part[pr];
+                const float *op = a.o_part + pr * H + lane * EPL;
+#pragma unroll
+                for (int e = 0; e < EPL; e++) oj[q][r][e] = op[e];
+            }
+#pragma unroll
+        for (int q = 0; q < NJ; q++)
+#pragma unroll
+            for (int r = 0; r < RPW; r++) {
+                const float l = j0 + q < a.n_splits ? lj[q][r] : -INFINITY;
+                // running maximum; what was summed is rescaled to it (by 0
+                // while the maximum was -inf), without a branch
+                const float m_new = max_nan(m[r], l);
+                const float corr = m_new == -INFINITY ? 1.f : exp2_fast((m[r] - m_new) * kLog2e);
+                const float w = l == -INFINITY ? 0.f : exp2_fast((l - m_new) * kLog2e);
+                wsum[r] = wsum[r] * corr + w;
+#pragma unroll
+                for (int e = 0; e < EPL; e++) acc[r][e] = acc[r][e] * corr + w * oj[q][r][e];
+                m[r] = m_new;
+            }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; r++) {
+        const int row = row0 + r;
+        if (row >= rows) break;
+        const float inv = wsum[r] > 0.f ? 1.f / wsum[r] : 0.f;
+        __bf16 *orow = a.o + (size_t)row * H + lane * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; e++) orow[e] = (__bf16)(acc[r][e] * inv);
+        if (lane == 0 && a.lse) a.lse[row] = wsum[r] > 0.f ? m[r] + logf(wsum[r]) : -INFINITY;
+    }
 }
 
 hipError_t launch_fwd_merge(const FwdArgs &a, int H, hipStream_t stream) {
     const int rows = a.B * a.K * a.G * a.T;
-    const dim3 grid((unsigned)((rows + 3) / 4));
+    const int waves = (rows + kMergeRows - 1) / kMergeRows;
+    const dim3 grid((unsigned)((waves + 3) / 4));
     switch (H) {
         case 64: hipLaunchKernelGGL((attn_fwd_merge_kernel<64>), grid, dim3(256), 0, stream, a, rows); break;
         case 128: hipLaunchKernelGGL((attn_fwd_merge_kernel<128>), grid, dim3(256), 0, stream, a, rows); break;
