@@ -1086,8 +1086,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
 // last read by M(i-2), over for both groups by then; the M phases running
 // beside V(i) read slots i % 4 and (i +- 1) % 4. Each wave waits for its own
 // loads at the end of its next M phase, one barrier before M(i+1) reads them.
-// K rows are padded to CPR + 3 chunks (its b128 row reads conflict-free and
-// its transpose reads 2-way), V rows to CPR + 1.
+// The K tile takes the dK/dV kernel's Q / dO layout: rows CPR + 4 chunks
+// apart and one more chunk after every 4 rows, so that its b128 row reads and
+// its transpose reads are both free of bank conflicts. V rows are padded to
+// CPR + 1 chunks (row reads only).
 template <int H, bool CAUSAL, bool WIN = false>
 __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
                                                                 int n_qblocks) {
@@ -1098,8 +1100,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     constexpr int PK = BKV / 16;     // 16-key chunks of a tile
     static_assert(PK * HB == KSTEPS, "one dQ step per S / dP step");
     constexpr int CPR = H / 8;
-    constexpr int KRS = CPR + 3, VRS = CPR + 1;
-    constexpr int KBLK = (BKV * KRS + 63) / 64, VBLK = (BKV * VRS + 63) / 64;
+    constexpr int KRS = CPR + 4, KGS = 4 * KRS + 1, VRS = CPR + 1;
+    constexpr int KBLK = (BKV / 4 * KGS + 63) / 64, VBLK = (BKV * VRS + 63) / 64;
     constexpr int NL = ((KBLK > VBLK ? KBLK : VBLK) + NG - 1) / NG;
     constexpr int NSLOT = 4;
     __shared__ __attribute__((aligned(1024))) __bf16 sk[NSLOT][KBLK * 512];
@@ -1147,15 +1149,21 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     const int n_t = (CAUSAL ? (t0 + bq + a.coff) / BKV : S / BKV) - j0;
 
     // global -> LDS: group A loads K tiles, group B V tiles; wave gwv of a group
-    // issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat the row's
-    // last chunk; slots past the last padded row re-read row BKV - 1)
-    const int rs = grp == 0 ? KRS : VRS;
+    // issues 1 KiB blocks gwv, gwv + NG, ... Chunk p of a K tile holds row
+    // 4 (p / KGS) + (p % KGS) / KRS; padding chunks repeat an in-range chunk,
+    // as do slots past the last row
     const int nblk = grp == 0 ? KBLK : VBLK;
     int ld_off[NL];
 #pragma unroll
     for (int i = 0; i < NL; i++) {
         const int pslot = (gwv + i * NG) * 64 + lane;
-        ld_off[i] = (min(pslot / rs, BKV - 1) * H + min(pslot % rs, CPR - 1) * 8) * 2;
+        if (grp == 0) {
+            const int rem = pslot % KGS;
+            const int row = min(4 * (pslot / KGS) + min(rem / KRS, 3), BKV - 1);
+            ld_off[i] = (row * H + min(rem % KRS, CPR - 1) * 8) * 2;
+        } else {
+            ld_off[i] = (min(pslot / VRS, BKV - 1) * H + min(pslot % VRS, CPR - 1) * 8) * 2;
+        }
     }
     // tiles j < n_t lie wholly inside K and V (S % BKV == 0), so the tile
     // offset may go in the scalar offset
@@ -1172,10 +1180,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
 #pragma unroll
     for (int hb = 0; hb < HB; hb++) dq_acc[hb] = f32x16{};
     bf16x8 dsh[PK], dsl[PK];
-    const int k_lane = n * KRS * 8 + c * 8, v_lane = n * VRS * 8 + c * 8;
+    const int k_lane = ((n >> 2) * KGS + (n & 3) * KRS) * 8 + c * 8, v_lane = n * VRS * 8 + c * 8;
     // transpose read of K^T: lane (gi, hh) of 16-lane group c addresses key
     // 16 kk + 4 c + gi / 4 (+ 8 for the upper half) at h = 32 hb + 16 hh + 4 (gi % 4)
-    const int tr_lane = (4 * c + ((lane & 15) >> 2)) * KRS * 8 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int tr_lane = c * KGS * 8 + ((lane & 15) >> 2) * KRS * 8 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     // M phase: S / dP of the tile in slot `cur` (SD) and dQ of the tile in
     // slot `prev` (DQ) from the hi part of dS, interleaved S, dQ, dP
@@ -1189,8 +1197,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
             const int kk = x / HB, hb = x % HB;
             bf16x8 kt;
             if constexpr (decltype(dq)::value) {
-                const __bf16 *p = kp + tr_lane + kk * 16 * KRS * 8 + hb * 32;
-                kt = join_bf16x8(lds_read_tr16(p), lds_read_tr16(p + 8 * KRS * 8));
+                const __bf16 *p = kp + tr_lane + kk * 4 * KGS * 8 + hb * 32;
+                kt = join_bf16x8(lds_read_tr16(p), lds_read_tr16(p + 2 * KGS * 8));
             }
             if constexpr (decltype(sd)::value) {
                 const bf16x8 kf = *(const bf16x8 *)(kc + k_lane + x * 16);
@@ -1219,8 +1227,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
 #pragma unroll
         for (int x = 0; x < KSTEPS; x++) {
             const int kk = x / HB, hb = x % HB;
-            const __bf16 *p = kp + tr_lane + kk * 16 * KRS * 8 + hb * 32;
-            const bf16x8 kt = join_bf16x8(lds_read_tr16(p), lds_read_tr16(p + 8 * KRS * 8));
+            const __bf16 *p = kp + tr_lane + kk * 4 * KGS * 8 + hb * 32;
+            const bf16x8 kt = join_bf16x8(lds_read_tr16(p), lds_read_tr16(p + 2 * KGS * 8));
             dq_acc[hb] = mfma32x32x16(kt, dsl[kk], dq_acc[hb]);
         }
         __builtin_amdgcn_s_setprio(0);
