@@ -43,7 +43,8 @@ EXPORTED_SYMBOLS = (
     "attn_fwd_split_count", "attn_fwd_local", "attn_check_fwd_local", "attn_fwd_mask", "attn_check_fwd_mask",
     "attn_bwd_workspace_bytes", "attn_bwd", "attn_check_bwd", "attn_bwd_local", "attn_check_bwd_local",
     "attn_bwd_mask", "attn_check_bwd_mask", "attn_fwd_noalloc", "attn_fwd_tuned", "attn_fwd_tuned_workspace_bytes",
-    "attn_fwd_tuning", "attn_strerror", "attn_last_hip_error",
+    "attn_fwd_tuning", "attn_fwd_head_masks", "attn_check_fwd_head_masks", "attn_bwd_head_masks",
+    "attn_check_bwd_head_masks", "attn_strerror", "attn_last_hip_error",
 )
 
 _lib = None
@@ -112,6 +113,14 @@ def load_library():
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, SZ, P]
     lib.attn_check_bwd.restype = I
     lib.attn_check_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, SZ]
+    lib.attn_fwd_head_masks.restype = I
+    lib.attn_fwd_head_masks.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
+    lib.attn_check_fwd_head_masks.restype = I
+    lib.attn_check_fwd_head_masks.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.attn_bwd_head_masks.restype = I
+    lib.attn_bwd_head_masks.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, SZ, P]
+    lib.attn_check_bwd_head_masks.restype = I
+    lib.attn_check_bwd_head_masks.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, SZ]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_strerror.argtypes = [I]
     lib.attn_last_hip_error.restype = I
@@ -215,13 +224,17 @@ def _check_workspace(workspace, device):
             raise ValueError("workspace must be a 1-D uint8 tensor")
 
 
+def _check_head_mask(head_mask, K, G, device):
+    _check_tensor("head_mask", head_mask, torch.int32, (K, G, 3), device)
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False,
              q_seg: Optional[torch.Tensor] = None, kv_seg: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
              want_lse: bool = True, split_kv: bool = False,
              workspace: Optional[torch.Tensor] = None,
              window: Optional[Tuple[int, int]] = None,
-             prefix: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+             prefix: int = 0, head_mask: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Forward pass on the current stream. Returns (o, lse).
 
     causal: see causal_mode(). split_kv=True calls attn_fwd_ws, which splits
@@ -230,7 +243,10 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False,
     allocated when not given. window=(left, right) and / or prefix=p call
     attn_fwd_mask: key s is visible to query t when s < p or t - left <= s <=
     t + right (-1: unbounded side) and the causal rule holds; it splits like
-    split_kv."""
+    split_kv. head_mask (int32 [K, G, 3] on the device: window left, window
+    right, prefix per query head) calls attn_fwd_head_masks instead: each
+    query head takes its own window and prefix; it excludes window, prefix
+    and split_kv."""
     B, K, G, T, S, H = _dims(q, k)
     dev = q.device
     _check_tensor("q", q, torch.bfloat16)
@@ -245,6 +261,16 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False,
         lse = torch.empty(B, K, G, T, dtype=torch.float32, device=dev)
     if lse is not None:
         _check_tensor("lse", lse, torch.float32, (B, K, G, T), dev)
+    if head_mask is not None:
+        if window is not None or prefix != 0 or split_kv:
+            raise ValueError("head_mask excludes window, prefix and split_kv")
+        _check_head_mask(head_mask, K, G, dev)
+        rc = load_library().attn_fwd_head_masks(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(q_seg),
+                                                _ptr(kv_seg), B, K, G, T, S, H, cm, _ptr(head_mask),
+                                                _stream_handle(dev))
+        if rc != GQA_ATTN_OK:
+            raise GqaAttnError(rc, "attn_fwd_head_masks")
+        return out, lse
     masked = window is not None or prefix != 0
     if masked or split_kv:
         wsb = attn_fwd_workspace_bytes(B, K, G, T, S, H)
@@ -337,11 +363,12 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torc
              kv_seg: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
              dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, window: Optional[Tuple[int, int]] = None,
-             prefix: int = 0):
+             prefix: int = 0, head_mask: Optional[torch.Tensor] = None):
     """Backward pass on the current stream. Returns (dq, dk, dv) in fp32.
 
     `o` (the forward output) may be None: the library does not read it.
-    window / prefix call attn_bwd_mask with the forward's mask. Every tensor
+    window / prefix call attn_bwd_mask with the forward's mask; head_mask
+    (as in attn_fwd) calls attn_bwd_head_masks. Every tensor
     is checked (device, dtype, shape, contiguity) before anything is
     launched."""
     B, K, G, T, S, H = _dims(q, k)
@@ -365,6 +392,17 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torc
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     _check_workspace(workspace, dev)
+    if head_mask is not None:
+        if window is not None or prefix != 0:
+            raise ValueError("head_mask excludes window and prefix")
+        _check_head_mask(head_mask, K, G, dev)
+        rc = load_library().attn_bwd_head_masks(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                                _ptr(dk), _ptr(dv), _ptr(q_seg), _ptr(kv_seg), B, K, G, T, S, H, cm,
+                                                _ptr(head_mask), _ptr(workspace), workspace.numel(),
+                                                _stream_handle(dev))
+        if rc != GQA_ATTN_OK:
+            raise GqaAttnError(rc, "attn_bwd_head_masks")
+        return dq, dk, dv
     if window is not None or prefix != 0:
         wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
         rc = load_library().attn_bwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),

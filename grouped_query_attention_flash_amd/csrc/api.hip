@@ -96,10 +96,12 @@ int attn_check_fwd(const void *q, const void *k, const void *v, const void *o, c
 static int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, const gqa::MaskSpec &m,
-                   gqa::FwdTuning tune, gqa::SplitPlan plan, void *workspace, void *stream) {
+                   gqa::FwdTuning tune, gqa::SplitPlan plan, void *workspace, void *stream,
+                   const int32_t *head_mask = nullptr) {
     const bool segments = q_seg != nullptr;
     const gqa::FwdConfig cfg =
-        plan.n_splits > 1
+        head_mask ? gqa::fwd_config(G, T, H)  // per-head masks: the general kernel, one pass
+        : plan.n_splits > 1
             ? (gqa::fwd_pp_split_applies(G, T, S, H, m, segments) ? gqa::fwd_config(G, T, H)
                                                                   : gqa::fwd_config_split(G, T, H))
         : (H == 256 && gqa::fwd_pp256_applies(G, T, S, m, segments)) ? gqa::fwd_config_pp256()
@@ -127,6 +129,7 @@ static int run_fwd(const void *q, const void *k, const void *v, void *o, float *
     a.split_tiles = plan.split_tiles;
     a.o_part = nullptr;
     a.lse_part = nullptr;
+    a.head_mask = head_mask;
     if (plan.n_splits > 1) {
         const size_t rows = (size_t)B * K * G * T;
         a.o_part = (float *)workspace;
@@ -301,7 +304,7 @@ static int run_bwd(const void *q, const void *k, const void *v, const void *o, c
                    const void *dO, float *dq, float *dk, float *dv,
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, const gqa::MaskSpec &m,
-                   void *workspace, void *stream) {
+                   void *workspace, void *stream, const int32_t *head_mask = nullptr) {
     gqa::BwdArgs a;
     a.q = (const __bf16 *)q;
     a.k = (const __bf16 *)k;
@@ -322,6 +325,7 @@ static int run_bwd(const void *q, const void *k, const void *v, const void *o, c
     a.wl = m.wl;
     a.wr = m.wr;
     a.prefix = m.prefix;
+    a.head_mask = head_mask;
     hipError_t e = gqa::launch_bwd(a, H, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return GQA_ATTN_OK;
@@ -378,6 +382,58 @@ int attn_bwd_local(const void *q, const void *k, const void *v, const void *o, c
                    void *workspace, size_t workspace_bytes, void *stream) {
     return attn_bwd_mask(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, window_left,
                          window_right, 0, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Per-head masks: head_mask is a device int32 array [K][G][3] holding, for
+// query head (k, g), its window left side, window right side and prefix
+// length; causal masking applies to every head. The kernels normalise each
+// entry as resolve_mask does a call's (head_mask_of), so every value is a
+// valid mask; the host checks only the pointer.
+int attn_check_fwd_head_masks(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                              const int32_t *q_seg, const int32_t *kv_seg,
+                              int B, int K, int G, int T, int S, int H, int causal, const int32_t *head_mask) {
+    int rc = attn_check_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal);
+    if (rc) return rc;
+    if (!head_mask) return GQA_ATTN_ERR_NULL;
+    if (!aligned(head_mask, 4)) return GQA_ATTN_ERR_ALIGN;
+    return GQA_ATTN_OK;
+}
+
+int attn_fwd_head_masks(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *q_seg, const int32_t *kv_seg,
+                        int B, int K, int G, int T, int S, int H, int causal, const int32_t *head_mask,
+                        void *stream) {
+    int rc = attn_check_fwd_head_masks(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, causal, head_mask);
+    if (rc) return rc;
+    const gqa::MaskSpec m = resolve_mask(causal, -1, -1, 0, T, S);
+    return run_fwd(q, k, v, o, lse, q_seg, kv_seg, B, K, G, T, S, H, m, gqa::FwdTuning{0, 0}, gqa::SplitPlan{1, 0},
+                   nullptr, stream, head_mask);
+}
+
+int attn_check_bwd_head_masks(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                              const void *dO, const float *dq, const float *dk, const float *dv,
+                              const int32_t *q_seg, const int32_t *kv_seg,
+                              int B, int K, int G, int T, int S, int H, int causal, const int32_t *head_mask,
+                              const void *workspace, size_t workspace_bytes) {
+    int rc = attn_check_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal, workspace,
+                            workspace_bytes);
+    if (rc) return rc;
+    if (!head_mask) return GQA_ATTN_ERR_NULL;
+    if (!aligned(head_mask, 4)) return GQA_ATTN_ERR_ALIGN;
+    return GQA_ATTN_OK;
+}
+
+int attn_bwd_head_masks(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const void *dO, float *dq, float *dk, float *dv,
+                        const int32_t *q_seg, const int32_t *kv_seg,
+                        int B, int K, int G, int T, int S, int H, int causal, const int32_t *head_mask,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = attn_check_bwd_head_masks(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H, causal,
+                                       head_mask, workspace, workspace_bytes);
+    if (rc) return rc;
+    return run_bwd(q, k, v, o, lse, dO, dq, dk, dv, q_seg, kv_seg, B, K, G, T, S, H,
+                   resolve_mask(causal, -1, -1, 0, T, S), workspace, stream, head_mask);
 }
 
 // ---------------------------------------------------------------------------

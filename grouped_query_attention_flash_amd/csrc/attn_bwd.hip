@@ -141,13 +141,33 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
     }
 
     // query tiles that can see the block's keys: t in [s - R, s + L] for the
-    // band sides L, R, or every query for a block that starts in the prefix
-    const int WL = a.wl, WR = a.wr, PFX = a.prefix;
+    // band sides L, R, or every query for a block that starts in the prefix.
+    // Per-head masks: the range of the union over the kv head's G heads, and
+    // each step takes its own head's sides (head_sides).
+    int WLu = a.wl, WRu = a.wr, PFXu = a.prefix;
+    if (a.head_mask) {
+        WLu = WRu = INT_MIN;
+        PFXu = 0;
+        for (int i = 0; i < G; i++) {
+            const HeadMask h = head_mask_of(a.head_mask, kh, G, i, T, S, a.causal, a.coff);
+            WLu = max(WLu, h.wl);
+            WRu = max(WRu, h.wr);
+            PFXu = max(PFXu, h.pfx);
+        }
+    }
+    auto head_sides = [&](int g, int &wl, int &wr, int &pfx) {
+        if (a.head_mask) {
+            const HeadMask h = head_mask_of(a.head_mask, kh, G, g, T, S, a.causal, a.coff);
+            wl = h.wl, wr = h.wr, pfx = h.pfx;
+        } else {
+            wl = a.wl, wr = a.wr, pfx = a.prefix;
+        }
+    };
     const int n_qt_all = (T + BQ - 1) / BQ;
-    const bool blk_pfx = s0_wg < PFX;
-    const int qt_begin = blk_pfx ? 0 : min(n_qt_all, max(0, s0_wg - WR) / BQ);
+    const bool blk_pfx = s0_wg < PFXu;
+    const int qt_begin = blk_pfx ? 0 : min(n_qt_all, max(0, s0_wg - WRu) / BQ);
     const int n_qt = blk_pfx ? n_qt_all
-                             : max(qt_begin, min(n_qt_all, (s0_wg + 32 * NW - 1 + WL) / BQ + 1));  // end of the tile range
+                             : max(qt_begin, min(n_qt_all, (s0_wg + 32 * NW - 1 + WLu) / BQ + 1));  // end of the tile range
     const int n_steps = G * (n_qt - qt_begin);  // (g, query tile) pairs, g outer
 
     auto q_ids = [&](int qt, int &qmin, int &qmax) {
@@ -158,11 +178,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
         qmax = wave_max_i(ok ? id : INT_MIN);
     };
     auto next_step = [&](int st) {
-        if (!segs) return st;
+        if (!segs && !a.head_mask) return st;
         for (; st < n_steps; st++) {
-            int qmin, qmax;
-            q_ids(qt_begin + st % (n_qt - qt_begin), qmin, qmax);
-            if (!(qmax < wg_kmin || qmin > wg_kmax)) break;
+            const int qt = qt_begin + st % (n_qt - qt_begin);
+            if (a.head_mask) {
+                // the step's head sees none of the block's keys from this tile
+                int wl, wr, pfx;
+                head_sides(st / (n_qt - qt_begin), wl, wr, pfx);
+                const int t0 = qt * BQ;
+                if (!(s0_wg < pfx || (t0 + BQ - 1 >= s0_wg - wr && t0 <= s0_wg + 32 * NW - 1 + wl))) continue;
+            }
+            if (segs) {
+                int qmin, qmax;
+                q_ids(qt, qmin, qmax);
+                if (qmax < wg_kmin || qmin > wg_kmax) continue;
+            }
+            break;
         }
         return st;
     };
@@ -231,6 +262,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
         if (st_next < n_steps) load_step(st_next);
 
         const int t0 = (qt_begin + st % (n_qt - qt_begin)) * BQ;
+        int WL, WR, PFX;  // the step's head
+        head_sides(st / (n_qt - qt_begin), WL, WR, PFX);
         bool run = wave_active && (s_w < PFX || (t0 + BQ - 1 >= s_w - WR && t0 <= s_w + 31 + WL));
         bool seg_mask = false;
         if (run && segs) {
@@ -733,14 +766,32 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
         w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
     }
 
+    // mask sides: WL, WR, PFX of this wave's head (its 32 rows are one head),
+    // WLu, WRu, PFXu of the union over the block's heads (the call's own
+    // without per-head masks)
+    int WL = a.wl, WR = a.wr, PFX = a.prefix;
+    int WLu = WL, WRu = WR, PFXu = PFX;
+    if (a.head_mask) {
+        const HeadMask hw = head_mask_of(a.head_mask, kh, a.G, __builtin_amdgcn_readfirstlane(g), T, S, a.causal,
+                                         a.coff);
+        WL = hw.wl, WR = hw.wr, PFX = hw.pfx;
+        WLu = WRu = INT_MIN;
+        PFXu = 0;
+        for (int i = 0; i < gw; i++) {
+            const HeadMask h = head_mask_of(a.head_mask, kh, a.G, gs * gw + i, T, S, a.causal, a.coff);
+            WLu = max(WLu, h.wl);
+            WRu = max(WRu, h.wr);
+            PFXu = max(PFXu, h.pfx);
+        }
+    }
+
     // key tiles: the band of the block's first and last query, and the
-    // prefix keys s < PFX
-    const int WL = a.wl, WR = a.wr, PFX = a.prefix;
+    // prefix keys s < PFXu
     const int n_tiles = (S + BKV - 1) / BKV;
     const int t_last = min(t0 + bq, T) - 1;
-    const int s_last = max(min(t_last + WR, S - 1), PFX - 1);
+    const int s_last = max(min(t_last + WRu, S - 1), PFXu - 1);
     const int j_end = s_last < 0 ? 0 : min(n_tiles, s_last / BKV + 1);
-    const int j_begin = (PFX > 0 || t0 - WL <= 0) ? 0 : (t0 - WL) / BKV;
+    const int j_begin = (PFXu > 0 || t0 - WLu <= 0) ? 0 : (t0 - WLu) / BKV;
 
     auto tile_ids = [&](int j, int &kmin, int &kmax) {
         const int ss = j * BKV + lane;
@@ -752,10 +803,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
     // next tile at or after j inside the prefix or the block's band, and
     // (segment ids) sharing an id range with the block
     auto next_tile = [&](int j) {
-        if (!segs && PFX == 0) return j;
+        if (!segs && PFXu == 0) return j;
         for (; j < j_end; j++) {
             const int s0 = j * BKV;
-            if (!(s0 < PFX || (s0 + BKV - 1 >= t0 - WL && s0 <= t_last + WR))) continue;
+            if (!(s0 < PFXu || (s0 + BKV - 1 >= t0 - WLu && s0 <= t_last + WRu))) continue;
             if (segs) {
                 int kmin, kmax;
                 tile_ids(j, kmin, kmax);
@@ -1314,8 +1365,8 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     if constexpr (H <= 128 && NW_DQ == 8) {
         // dense shapes: the ping-pong D pass (query blocks of 64 rows x gw heads)
         constexpr int BKV_PP = 64;
-        const bool shape = a.q_seg == nullptr && gw * bq == 256 && a.T % bq == 0 && a.S % BKV_PP == 0 &&
-                           diag_tiles(BKV_PP) && (!a.causal || bq == BKV_PP);
+        const bool shape = a.q_seg == nullptr && a.head_mask == nullptr && gw * bq == 256 && a.T % bq == 0 &&
+                           a.S % BKV_PP == 0 && diag_tiles(BKV_PP) && (!a.causal || bq == BKV_PP);
         const bool dense = shape && !mask_extra(m);
         // a causal left window on an otherwise dense shape
         const bool dense_win = shape && mask_left_window_only(m);
@@ -1341,7 +1392,8 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     bool dq_done = false;
     if constexpr (H <= 128 && NW_DQ == 8) {
         // dense shapes: dQ on the ping-pong kernel (32-key tiles)
-        const bool shape = a.q_seg == nullptr && gw * bq == 256 && a.T % bq == 0 && a.S % 32 == 0 && diag_tiles(32);
+        const bool shape = a.q_seg == nullptr && a.head_mask == nullptr && gw * bq == 256 && a.T % bq == 0 &&
+                           a.S % 32 == 0 && diag_tiles(32);
         const bool dense = shape && !mask_extra(m);
         // a causal left window on an otherwise dense shape
         const bool dense_win = shape && mask_left_window_only(m);
@@ -1368,8 +1420,9 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     const int n_kblocks = (a.S + keys_wg - 1) / keys_wg;
     const dim3 kgrid((unsigned)(a.B * a.K * n_kblocks));
     if constexpr (H <= 128 && NW_DKV == 4) {
-        // no segment ids: the wave-pair kernel (8 waves, 128 keys per workgroup)
-        if (a.q_seg == nullptr) {
+        // no segment ids or per-head masks: the wave-pair kernel (8 waves, 128
+        // keys per workgroup)
+        if (a.q_seg == nullptr && a.head_mask == nullptr) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, true>), kgrid, dim3(512), 0, stream, a);
             else

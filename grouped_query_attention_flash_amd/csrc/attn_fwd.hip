@@ -149,14 +149,33 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
         w_qmax = wave_max_i(q_valid ? my_qid : INT_MIN);
     }
 
-    // ---- key-tile range: the band [t - WL, t + WR] of the block's first and
-    // last query, and the prefix keys s < PFX; a split covers its own range
-    const int WL = a.wl, WR = a.wr, PFX = a.prefix;
+    // ---- the mask sides: WL, WR, PFX of this wave's head (its 32 rows are one
+    // head: bq is a multiple of 32), and WLu, WRu, PFXu of the union over the
+    // block's heads, which bound its key range. Without per-head masks all are
+    // the call's.
+    int WL = a.wl, WR = a.wr, PFX = a.prefix;
+    int WLu = WL, WRu = WR, PFXu = PFX;
+    if (!DENSE && a.head_mask) {
+        const HeadMask hw = head_mask_of(a.head_mask, kh, a.G, __builtin_amdgcn_readfirstlane(g), T, S, a.causal,
+                                         a.coff);
+        WL = hw.wl, WR = hw.wr, PFX = hw.pfx;
+        WLu = WRu = INT_MIN;
+        PFXu = 0;
+        for (int i = 0; i < a.gw; i++) {
+            const HeadMask h = head_mask_of(a.head_mask, kh, a.G, gs * a.gw + i, T, S, a.causal, a.coff);
+            WLu = max(WLu, h.wl);
+            WRu = max(WRu, h.wr);
+            PFXu = max(PFXu, h.pfx);
+        }
+    }
+
+    // ---- key-tile range: the band [t - WLu, t + WRu] of the block's first and
+    // last query, and the prefix keys s < PFXu; a split covers its own range
     const int n_tiles = (S + BKV - 1) / BKV;
     const int t_last = min(t0 + a.bq, T) - 1;  // the block's last query
-    const int s_last = max(min(t_last + WR, S - 1), PFX - 1);
+    const int s_last = max(min(t_last + WRu, S - 1), PFXu - 1);
     int j_end = s_last < 0 ? 0 : min(n_tiles, s_last / BKV + 1);
-    int j_begin = (PFX > 0 || t0 - WL <= 0) ? 0 : (t0 - WL) / BKV;
+    int j_begin = (PFXu > 0 || t0 - WLu <= 0) ? 0 : (t0 - WLu) / BKV;
     if (!DENSE && a.o_part) {
         j_begin = max(j_begin, split * a.split_tiles);
         j_end = min(j_end, split * a.split_tiles + a.split_tiles);
@@ -205,10 +224,10 @@ __global__ __launch_bounds__(NW * 64, WAVES_PER_SIMD) void attn_fwd_kernel(FwdAr
     // next tile at or after j that some query of the workgroup can see: inside
     // the prefix or the block's band, and (segment ids) sharing an id range
     auto next_tile = [&](int j) {
-        if (!segs && PFX == 0) return j;
+        if (!segs && PFXu == 0) return j;
         for (; j < j_end; j++) {
             const int s0 = j * BKV;
-            if (!(s0 < PFX || (s0 + BKV - 1 >= t0 - WL && s0 <= t_last + WR))) continue;
+            if (!(s0 < PFXu || (s0 + BKV - 1 >= t0 - WLu && s0 <= t_last + WRu))) continue;
             if (segs) {
                 int kmin, kmax;
                 tile_ids(j, kmin, kmax);
@@ -1446,11 +1465,14 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     // causal: every block's diagonal lies in its last key tile (one query
     // block per key tile, the diagonal offset a whole number of tiles)
     const bool diag_tiles = !a.causal || (a.coff >= 0 && a.coff % BKV == 0 && a.T + a.coff == a.S && a.bq == BKV);
-    const bool dense = a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 && !mask_extra(m) &&
-                       diag_tiles;
+    // per-head masks: the general kernel (it alone reads the table)
+    const bool uniform = a.head_mask == nullptr;
+    const bool dense = uniform && a.o_part == nullptr && a.q_seg == nullptr && all_waves && a.S % BKV == 0 &&
+                       !mask_extra(m) && diag_tiles;
     if constexpr (H <= 128 && NW == 8) {
         // the ping-pong kernel, also with a partial last key tile
-        const bool pp_dense = a.o_part == nullptr && a.q_seg == nullptr && all_waves && !mask_extra(m) && diag_tiles;
+        const bool pp_dense =
+            uniform && a.o_part == nullptr && a.q_seg == nullptr && all_waves && !mask_extra(m) && diag_tiles;
         if (pp_dense) {
             if (a.causal)
                 launch_pp<H, BKV, true, false, false>(a, grid, stream);
@@ -1460,7 +1482,7 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
         }
         // segment ids on an otherwise dense shape with at most 8192 keys: the
         // ping-pong kernel over each block's list of tiles that share an id
-        const bool dense_seg = a.o_part == nullptr && a.q_seg != nullptr && all_waves && a.S % BKV == 0 &&
+        const bool dense_seg = uniform && a.o_part == nullptr && a.q_seg != nullptr && all_waves && a.S % BKV == 0 &&
                                a.S <= 8192 && !mask_extra(m) && diag_tiles;
         if (dense_seg) {
             if (a.causal)
@@ -1471,8 +1493,8 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
         }
         // a causal left window on an otherwise dense shape: the ping-pong kernel
         // starting at each block's first visible tile
-        const bool dense_win =
-            a.o_part == nullptr && a.q_seg == nullptr && all_waves && mask_left_window_only(m) && diag_tiles;
+        const bool dense_win = uniform && a.o_part == nullptr && a.q_seg == nullptr && all_waves &&
+                               mask_left_window_only(m) && diag_tiles;
         if (dense_win) {
             launch_pp<H, BKV, true, true, false>(a, grid, stream);
             return hipGetLastError();

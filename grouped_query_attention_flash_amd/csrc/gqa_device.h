@@ -29,6 +29,26 @@ constexpr float kRescaleBound = 256.0f;  // 2^kRescaleLog2
 // wr may be negative (a causal diagonal below the first query).
 constexpr int kNoWindow = 1 << 29;
 
+// The mask sides of query head (kh, g) from a per-head table int32 [K][G][3]
+// (window left, window right, prefix), normalised as the host normalises a
+// call's single mask: a negative side, or one that bounds nothing for these
+// sizes, is kNoWindow; a causal diagonal s <= t + coff caps the right side;
+// the prefix is clamped to [0, S]. Every table value is thus accepted.
+struct HeadMask {
+    int wl, wr, pfx;
+};
+__device__ __forceinline__ HeadMask head_mask_of(const int32_t *tab, int kh, int G, int g, int T, int S, int causal,
+                                                 int coff) {
+    const int32_t *e = tab + ((size_t)kh * G + g) * 3;
+    const int wl = e[0], wr = e[1], pf = e[2];
+    HeadMask h;
+    h.wl = (wl < 0 || wl >= T - 1) ? kNoWindow : wl;
+    h.wr = (wr < 0 || wr >= S - 1) ? kNoWindow : wr;
+    if (causal) h.wr = h.wr < coff ? h.wr : coff;
+    h.pfx = pf < 0 ? 0 : (pf < S ? pf : S);
+    return h;
+}
+
 // D = A * B + C on a 32x32 fp32 tile, A 32x16 and B 16x32 in bf16.
 // Operand layout (64-wide wave): lane l holds A[l%32][8*(l/32) .. +7] and
 // B[8*(l/32) .. +7][l%32]; result register r of lane l is

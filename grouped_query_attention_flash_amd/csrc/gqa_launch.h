@@ -56,6 +56,11 @@ struct FwdArgs {
     int split_tiles;
     float *o_part;
     float *lse_part;
+    // Per-head masks (null: every head takes wl, wr, prefix above): int32
+    // [K][G][3] in device memory, window left, window right and prefix of
+    // query head (k, g), normalised in the kernels by head_mask_of. Only the
+    // general kernel reads it; such a call never splits.
+    const int32_t *head_mask;
 };
 
 // Split-KV plan of a shape (pure host function): n_splits == 1 means none.
@@ -103,6 +108,7 @@ struct BwdArgs {
     const int32_t *q_seg, *kv_seg;
     int B, K, G, T, S;
     int causal, coff, wl, wr, prefix;  // the resolved mask, as in FwdArgs
+    const int32_t *head_mask;          // per-head masks, as in FwdArgs (general kernels only)
 };
 
 hipError_t launch_bwd(const BwdArgs &a, int H, hipStream_t stream);

@@ -29,7 +29,8 @@
  *        first T - S queries see no key.
  *   segments (fjformer Pallas flash-attention docs, SegmentIds): key s visible
  *     to query t iff q_seg[b,t] == kv_seg[b,s]; combined with the rest by AND.
- *   window and prefix (attn_fwd_mask / attn_bwd_mask below).
+ *   window and prefix (attn_fwd_mask / attn_bwd_mask below), also per query
+ *     head (attn_fwd_head_masks / attn_bwd_head_masks).
  * A query row that sees no key gets O = 0 and lse = -inf.
  *
  * Conventions for every call:
@@ -319,6 +320,48 @@ int attn_check_bwd(const void *q, const void *k, const void *v, const void *o, c
                    const int32_t *q_seg, const int32_t *kv_seg,
                    int B, int K, int G, int T, int S, int H, int causal,
                    const void *workspace, size_t workspace_bytes);
+
+/* Forward pass with a mask per query head: the splash baseline's
+ * MultiHeadMask (danielwatson6.github.io/fa, "Our first kernel") holds one
+ * mask per head, so that local and global heads, or heads with different
+ * prefixes, share one call. Query head (k, g) takes the mask of attn_fwd_mask
+ * with its own window sides and prefix from the table; the causal mode and
+ * segment ids apply to every head.
+ *   head_mask   device int32 [K][G][3], 4-byte aligned, owned by the caller:
+ *               head_mask[(k G + g) 3 + 0] window_left, + 1 window_right,
+ *               + 2 prefix. A negative side is unbounded; a prefix is
+ *               clamped to [0, S]. Every value is accepted (the host cannot
+ *               read device memory), normalised in the kernels as the
+ *               single-mask calls normalise theirs.
+ * Runs the general kernel, one pass (no split, no workspace): it visits a
+ * block's key tiles inside the union of its heads' bands and prefixes, and
+ * each wave masks with its own head's. Errors as attn_fwd, plus ERR_NULL /
+ * ERR_ALIGN for head_mask. */
+int attn_fwd_head_masks(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *q_seg, const int32_t *kv_seg,
+                        int B, int K, int G, int T, int S, int H, int causal, const int32_t *head_mask,
+                        void *stream);
+
+/* Host-only validation of attn_fwd_head_masks' arguments. Same return codes. */
+int attn_check_fwd_head_masks(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                              const int32_t *q_seg, const int32_t *kv_seg,
+                              int B, int K, int G, int T, int S, int H, int causal, const int32_t *head_mask);
+
+/* Backward pass of attn_fwd_head_masks: every recomputed weight of head
+ * (k, g) takes that head's mask. Otherwise as attn_bwd (its workspace
+ * included); it runs the general dQ and dK / dV kernels. */
+int attn_bwd_head_masks(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const void *dO, float *dq, float *dk, float *dv,
+                        const int32_t *q_seg, const int32_t *kv_seg,
+                        int B, int K, int G, int T, int S, int H, int causal, const int32_t *head_mask,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only validation of attn_bwd_head_masks' arguments. Same return codes. */
+int attn_check_bwd_head_masks(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                              const void *dO, const float *dq, const float *dk, const float *dv,
+                              const int32_t *q_seg, const int32_t *kv_seg,
+                              int B, int K, int G, int T, int S, int H, int causal, const int32_t *head_mask,
+                              const void *workspace, size_t workspace_bytes);
 
 /* Forward pass that allocates nothing, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, and

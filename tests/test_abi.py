@@ -175,6 +175,26 @@ def test_check_mask_codes():
         gqa.GQA_ATTN_ERR_SHAPE
 
 
+def test_check_head_mask_codes():
+    """The per-head mask calls check the table pointer (NULL -> ERR_NULL, not
+    4-byte aligned -> ERR_ALIGN) after the checks of attn_fwd / attn_bwd; its
+    contents live on the device and every value is a valid mask."""
+    P = ctypes.c_void_p
+    lib = gqa.load_library()
+    fargs = (P(A16), P(A16), P(A16), P(A16), P(A16), None, None, 1, 2, 4, 64, 128, 128)
+    assert lib.attn_check_fwd_head_masks(*fargs, 1, P(A16)) == gqa.GQA_ATTN_OK
+    assert lib.attn_check_fwd_head_masks(*fargs, 2, P(A16 + 4)) == gqa.GQA_ATTN_OK
+    assert lib.attn_check_fwd_head_masks(*fargs, 1, None) == gqa.GQA_ATTN_ERR_NULL
+    assert lib.attn_check_fwd_head_masks(*fargs, 1, P(A16 + 2)) == gqa.GQA_ATTN_ERR_ALIGN
+    assert lib.attn_check_fwd_head_masks(*fargs, 3, P(A16)) == gqa.GQA_ATTN_ERR_MASK
+    assert lib.attn_check_fwd_head_masks(*(fargs[:12] + (96,)), 1, P(A16)) == gqa.GQA_ATTN_ERR_HEADDIM
+    wsb = gqa.attn_bwd_workspace_bytes(1, 2, 4, 64, 128, 128)
+    bargs = (P(A16),) * 9 + (None, None, 1, 2, 4, 64, 128, 128)
+    assert lib.attn_check_bwd_head_masks(*bargs, 2, P(A16), P(A16), wsb) == gqa.GQA_ATTN_OK
+    assert lib.attn_check_bwd_head_masks(*bargs, 2, None, P(A16), wsb) == gqa.GQA_ATTN_ERR_NULL
+    assert lib.attn_check_bwd_head_masks(*bargs, 2, P(A16), P(A16), wsb - 1) == gqa.GQA_ATTN_ERR_WORKSPACE
+
+
 def test_causal_mode_mapping():
     assert gqa.causal_mode(False) == 0 and gqa.causal_mode(True) == 1
     assert gqa.causal_mode("top_left") == 1 and gqa.causal_mode("end") == 2 and gqa.causal_mode(2) == 2
