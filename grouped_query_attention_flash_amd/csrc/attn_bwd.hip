@@ -77,8 +77,12 @@ __device__ __forceinline__ void pp_schedule(std::integer_sequence<int, P...>, st
 //   lane (n, c) holds key n and the 16 queries acc_row(r, c) of S, P, dP, dS
 //   dV^T += dO^T P   A: dO^T (LDS transpose read)   B: P  (registers, bf16)
 //   dK^T += Q^T dS   A: Q^T  (LDS transpose read)   B: dS (registers, bf16)
-template <int H, int NW>
+// PART: 0 computes dK and dV; 1 only dV (S, P, dV^T); 2 only dK (S, dP, dS,
+// dK^T). At H = 256 the two accumulators of one pass would fill a wave's
+// registers, so two passes run, one per part.
+template <int H, int NW, int PART>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_kblocks) {
+    constexpr bool DO_DV = PART != 2, DO_DK = PART != 1;
     constexpr int BQ = 32;
     constexpr int CPR = H / 8;
     constexpr int KSTEPS = H / 16;
@@ -108,15 +112,25 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
     const bool wave_active = s_w < S;
     const size_t bk = (size_t)b * a.K + kh;
 
-    // K^T and V^T operands (B operands): lane (n, c), k-step ks holds row s, h = 16ks + 8c .. +7
-    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    // K^T and V^T operands (B operands): lane (n, c), k-step ks holds row s, h = 16ks + 8c .. +7.
+    // VLDS (H = 256): the V^T operands wait in LDS, in the wave's 32 rows of
+    // svw (swizzled as the Q / dO tiles), and are read back per k-step: K^T,
+    // V^T and both accumulators do not fit in one wave's registers together.
+    constexpr bool VLDS = H > 128 && DO_DK;
+    __shared__ __attribute__((aligned(16))) __bf16 svw[VLDS ? NW * 32 * H : 8];
+    const int vrow_l = 32 * wave + n;  // the lane's row of svw
+    bf16x8 kf[KSTEPS], vf[VLDS ? 1 : KSTEPS];
     {
         const __bf16 *krow = a.k + (bk * S + s) * H;
         const __bf16 *vrow = a.v + (bk * S + s) * H;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ks++) {
             kf[ks] = k_valid ? *(const bf16x8 *)(krow + 16 * ks + 8 * c) : bf16x8{};
-            vf[ks] = k_valid ? *(const bf16x8 *)(vrow + 16 * ks + 8 * c) : bf16x8{};
+            const bf16x8 vv = k_valid ? *(const bf16x8 *)(vrow + 16 * ks + 8 * c) : bf16x8{};
+            if constexpr (VLDS)
+                *(bf16x8 *)(svw + vrow_l * H + (((2 * ks + c) ^ swz<CPR>(vrow_l)) << 3)) = vv;
+            else
+                vf[ks] = vv;
         }
     }
 
@@ -283,7 +297,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
                 for (int ks = 0; ks < KSTEPS; ks++) {
                     const int off = ((2 * ks + c) ^ sw) << 3;
                     sacc = mfma32x32x16(*(const bf16x8 *)(qrow + off), kf[ks], sacc);
-                    pacc = mfma32x32x16(*(const bf16x8 *)(drow + off), vf[ks], pacc);
+                    if constexpr (DO_DK) {
+                        bf16x8 vk;
+                        if constexpr (VLDS)
+                            vk = *(const bf16x8 *)(svw + vrow_l * H + (((2 * ks + c) ^ swz<CPR>(vrow_l)) << 3));
+                        else
+                            vk = vf[ks];
+                        pacc = mfma32x32x16(*(const bf16x8 *)(drow + off), vk, pacc);
+                    }
                 }
             }
             // keys wholly inside the prefix need no band mask
@@ -307,7 +328,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
                     }
                     const float p = exp2_fast(__builtin_fmaf(x, kLog2e, -l4[e]));
                     sacc[r] = p;
-                    pacc[r] = p * (pacc[r] - d4[e]);
+                    if constexpr (DO_DK) pacc[r] = p * (pacc[r] - d4[e]);
                 }
             }
             // dV^T += dO^T P ; dK^T += Q^T dS   (k = queries, 2 k-steps of 16)
@@ -329,10 +350,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
                     const int ch = hcol >> 3, within = hcol & 7;
                     const int o0 = r0 * H + ((ch ^ sw0) << 3) + within;
                     const int o1 = r1 * H + ((ch ^ sw1) << 3) + within;
-                    const bf16x8 dot = join_bf16x8(lds_read_tr16(sdo + o0), lds_read_tr16(sdo + o1));
-                    dv_acc[hb] = mfma32x32x16(dot, pf, dv_acc[hb]);
-                    const bf16x8 qt = join_bf16x8(lds_read_tr16(sq + o0), lds_read_tr16(sq + o1));
-                    dk_acc[hb] = mfma32x32x16(qt, sf, dk_acc[hb]);
+                    if constexpr (DO_DV) {
+                        const bf16x8 dot = join_bf16x8(lds_read_tr16(sdo + o0), lds_read_tr16(sdo + o1));
+                        dv_acc[hb] = mfma32x32x16(dot, pf, dv_acc[hb]);
+                    }
+                    if constexpr (DO_DK) {
+                        const bf16x8 qt = join_bf16x8(lds_read_tr16(sq + o0), lds_read_tr16(sq + o1));
+                        dk_acc[hb] = mfma32x32x16(qt, sf, dk_acc[hb]);
+                    }
                 }
             }
         }
@@ -348,10 +373,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++) {
                 const int h = 32 * hb + 8 * q4 + 4 * c;
-                *(f32x4 *)(dkrow + h) = f32x4{dk_acc[hb][4 * q4], dk_acc[hb][4 * q4 + 1], dk_acc[hb][4 * q4 + 2],
-                                              dk_acc[hb][4 * q4 + 3]};
-                *(f32x4 *)(dvrow + h) = f32x4{dv_acc[hb][4 * q4], dv_acc[hb][4 * q4 + 1], dv_acc[hb][4 * q4 + 2],
-                                              dv_acc[hb][4 * q4 + 3]};
+                if constexpr (DO_DK)
+                    *(f32x4 *)(dkrow + h) = f32x4{dk_acc[hb][4 * q4], dk_acc[hb][4 * q4 + 1], dk_acc[hb][4 * q4 + 2],
+                                                  dk_acc[hb][4 * q4 + 3]};
+                if constexpr (DO_DV)
+                    *(f32x4 *)(dvrow + h) = f32x4{dv_acc[hb][4 * q4], dv_acc[hb][4 * q4 + 1], dv_acc[hb][4 * q4 + 2],
+                                                  dv_acc[hb][4 * q4 + 3]};
             }
     }
     (void)n_kblocks;
@@ -1430,7 +1457,15 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<H, NW_DKV>), kgrid, dim3(NW_DKV * 64), 0, stream, a, n_kblocks);
+    if constexpr (H > 128) {
+        // one pass for dV, one for dK (the two accumulators do not fit one wave together)
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<H, NW_DKV, 1>), kgrid, dim3(NW_DKV * 64), 0, stream, a, n_kblocks);
+        hipError_t e2 = hipGetLastError();
+        if (e2 != hipSuccess) return e2;
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<H, NW_DKV, 2>), kgrid, dim3(NW_DKV * 64), 0, stream, a, n_kblocks);
+    } else {
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<H, NW_DKV, 0>), kgrid, dim3(NW_DKV * 64), 0, stream, a, n_kblocks);
+    }
     return hipGetLastError();
 }
 
