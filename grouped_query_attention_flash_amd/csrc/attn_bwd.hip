@@ -409,7 +409,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
 // and D. Iteration i reads steps i .. i+2 and loads step i+4 into the stage of
 // step i-1, whose last readers finished in iteration i-1; every wave waits for
 // its own loads one iteration later, a barrier before anyone reads them.
-template <int H, bool CAUSAL>
+//
+// SEG (segment ids, T <= 8192): the walk covers only the query tiles whose id
+// range meets the ids of the block's keys (a list built at the start, the
+// same for every wave), and a step whose ids are not all one value takes the
+// element mask, which compares the lane's key id with the step's query ids
+// (loaded beside lse, lanes 0-7 of one A wave).
+template <int H, bool CAUSAL, bool SEG = false>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
     constexpr int NP = 4, BQ = 32;  // wave pairs, queries per step
     constexpr int CPR = H / 8;
@@ -430,7 +436,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
     constexpr int NSTAGE = 5;
     __shared__ __attribute__((aligned(1024))) __bf16 sq[NSTAGE][TILE];
     __shared__ __attribute__((aligned(1024))) __bf16 sdo[NSTAGE][TILE];
-    __shared__ __attribute__((aligned(1024))) float sld[NSTAGE][2][256];  // lse, D (32 used)
+    __shared__ __attribute__((aligned(1024))) float sld[NSTAGE][2][256];  // lse (SEG: + query ids), D (32 used)
     __shared__ __attribute__((aligned(1024))) f32x4 sp[2][NP][4][64];      // P exchange: [buf][pair][q4][lane]
     __shared__ __attribute__((aligned(1024))) char sdummy[1024];
 
@@ -466,7 +472,74 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
     const bool blk_pfx = s0_wg < a.prefix;
     const int qt_begin = blk_pfx ? 0 : min(n_qt, max(0, s0_wg - WR) / BQ);
     const int qt_end = blk_pfx ? n_qt : max(qt_begin, min(n_qt, (s0_wg + 32 * NP - 1 + WL) / BQ + 1));
-    const int n_steps = G * (qt_end - qt_begin);
+
+    // SEG: the key's id, the pair's id range, and the list of the query tiles
+    // in [qt_begin, qt_end) whose id range meets the block's (s_qtl[0 ..
+    // n_vis)); otherwise the walk is [qt_begin, qt_end)
+    constexpr int QT_CAP = SEG ? 8192 / BQ : 1;
+    __shared__ int s_tmin[QT_CAP], s_tmax[QT_CAP], s_qtl[QT_CAP];
+    __shared__ int s_krange[2 * NP + 1];
+    int my_kid = 0, p_kmin = 0, p_kmax = 0;
+    int q_lo = qt_begin, q_hi = qt_end;
+    if constexpr (SEG) {
+        const int32_t *qs = a.q_seg + (size_t)b * T;
+        const int32_t *kvs = a.kv_seg + (size_t)b * S;
+        // ids of the query tiles qt_begin + 2 wave + (lane >> 5) + 16 m, all
+        // loads in flight before the first use (clamped in-range indices)
+        constexpr int QM = QT_CAP / 16;
+        int qid[QM];
+#pragma unroll
+        for (int m = 0; m < QM; m++) {
+            const int qt = qt_begin + 2 * wave + (lane >> 5) + 16 * m;
+            qid[m] = qs[min(qt * BQ + n, T - 1)];
+        }
+        my_kid = kvs[min(s, S - 1)];
+        p_kmin = wave_min_i(k_valid ? my_kid : INT_MAX);
+        p_kmax = wave_max_i(k_valid ? my_kid : INT_MIN);
+        if (is_a && lane == 0) {
+            s_krange[2 * pair] = p_kmin;
+            s_krange[2 * pair + 1] = p_kmax;
+        }
+#pragma unroll
+        for (int m = 0; m < QM; m++) {
+            const int qt = qt_begin + 2 * wave + (lane >> 5) + 16 * m;
+            if (qt < qt_end) {  // wave-uniform per half: both halves' tiles below qt_end, or one
+                const bool ok = qt * BQ + n < T;
+                int lo = ok ? qid[m] : INT_MAX, hi = ok ? qid[m] : INT_MIN;
+#pragma unroll
+                for (int o = 16; o >= 1; o >>= 1) {
+                    lo = min(lo, __shfl_xor(lo, o));
+                    hi = max(hi, __shfl_xor(hi, o));
+                }
+                if (n == 0) {
+                    s_tmin[qt] = lo;
+                    s_tmax[qt] = hi;
+                }
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            int bmin = INT_MAX, bmax = INT_MIN;
+#pragma unroll
+            for (int p = 0; p < NP; p++) {
+                bmin = min(bmin, s_krange[2 * p]);
+                bmax = max(bmax, s_krange[2 * p + 1]);
+            }
+            int cnt = 0;
+            for (int jb = qt_begin; jb < qt_end; jb += 64) {
+                const int qt = jb + lane;
+                const bool vis = qt < qt_end && !(s_tmax[qt] < bmin || s_tmin[qt] > bmax);
+                const unsigned long long m = __ballot(vis);
+                if (vis) s_qtl[cnt + __popcll(m & ((1ull << lane) - 1))] = qt;
+                cnt += __popcll(m);
+            }
+            if (lane == 0) s_krange[2 * NP] = cnt;
+        }
+        __syncthreads();
+        q_lo = 0;
+        q_hi = __builtin_amdgcn_readfirstlane(s_krange[2 * NP]);
+    }
+    const int n_steps = G * (q_hi - q_lo);
 
     // loads: A waves the Q tile (blocks pair, pair + 4, ...) and, wave 0, lse;
     // B waves the dO tile and, wave 4, D. Every wave issues NLD loads per step
@@ -474,8 +547,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
     // offset (reads nothing) and the dummy destination.
     const i32x4 trs = is_a ? make_rsrc_words(a.q + bk * G * (size_t)T * H, G * T * H * 2)
                            : make_rsrc_words(a.dout + bk * G * (size_t)T * H, G * T * H * 2);
-    const i32x4 lrs = is_a ? make_rsrc_words(a.lse2 + bk * G * (size_t)T, G * T * 4)
-                           : make_rsrc_words(a.delta + bk * G * (size_t)T, G * T * 4);
+    // SEG: wave 1 (an A wave) loads the step's query ids instead of nothing
+    const bool ids_wave = SEG && is_a && pair == 1;
+    const i32x4 lrs = ids_wave ? make_rsrc_words(a.q_seg + (size_t)b * T, T * 4)
+                      : is_a   ? make_rsrc_words(a.lse2 + bk * G * (size_t)T, G * T * 4)
+                               : make_rsrc_words(a.delta + bk * G * (size_t)T, G * T * 4);
     constexpr unsigned kOutOfRange = 0x80000000u;
     int t_off[TBW];
 #pragma unroll
@@ -488,13 +564,21 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         t_off[i] = (row * H + min(rem % RS, CPR - 1) * 8) * 2;
     }
     const unsigned t_dst0 = (is_a ? lds_addr(sq[0]) : lds_addr(sdo[0])) + pair * 1024;
-    const unsigned l_dst0 = lds_addr(sld[0][is_a ? 0 : 1]), dummy = lds_addr(sdummy);
-    auto issue_load = [&](int j, int row0, int stage) {
+    const unsigned l_dst0 = lds_addr(ids_wave ? &sld[0][0][32] : sld[0][is_a ? 0 : 1]), dummy = lds_addr(sdummy);
+    // row0: the step's first row g T + t (-1: none); t_row: its first query t
+    auto issue_load = [&](int j, int row0, int t_row, int stage) {
         if (j < TBW) {
             const bool ok = row0 >= 0 && pair + j * NP < TBLK;
             const unsigned voff = ok ? (unsigned)(row0 * H * 2 + t_off[j]) : kOutOfRange;
             const unsigned dst = ok ? t_dst0 + stage * (TILE * 2) + j * NP * 1024 : dummy;
             lds_dma16(trs, __builtin_amdgcn_readfirstlane(dst), voff);
+        } else if constexpr (SEG) {
+            // 32 values, lanes 0-7 only: lse (wave 0) into sld[stage][0][0
+            // .. 31], the query ids (wave 1) into [32 .. 63], D (wave 4)
+            const bool ok = row0 >= 0 && (pair == 0 || ids_wave);
+            const unsigned voff = ok ? (unsigned)((ids_wave ? t_row : row0) * 4 + (lane & 7) * 16) : kOutOfRange;
+            const unsigned dst = ok ? l_dst0 + stage * (2 * 256 * 4) : dummy;
+            if (lane < 8) lds_dma16(lrs, __builtin_amdgcn_readfirstlane(dst), voff);
         } else {
             // 32 floats: lanes 0-7 fetch them, the others repeat in-range
             // addresses into slots that are not read
@@ -503,17 +587,25 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
             const unsigned dst = ok ? l_dst0 + stage * (2 * 256 * 4) : dummy;
             lds_dma16(lrs, __builtin_amdgcn_readfirstlane(dst), voff);
         }
+        (void)t_row;
     };
+    // (g, qi): head g, query tile qi (SEG: entry qi of the list)
     struct Cursor {
-        int g, qt;
+        int g, qi;
     };
     auto advance = [&](Cursor &cu) {
-        if (++cu.qt == qt_end) {
-            cu.qt = qt_begin;
+        if (++cu.qi == q_hi) {
+            cu.qi = q_lo;
             ++cu.g;
         }
     };
-    auto row_of = [&](const Cursor &cu) { return cu.g < G ? cu.g * T + cu.qt * BQ : -1; };
+    auto qt_of = [&](const Cursor &cu) {
+        if constexpr (SEG)
+            return __builtin_amdgcn_readfirstlane(s_qtl[cu.g < G ? cu.qi : 0]);
+        else
+            return cu.qi;
+    };
+    auto row_of = [&](const Cursor &cu) { return cu.g < G ? cu.g * T + qt_of(cu) * BQ : -1; };
 
     f32x16 acc[HB];  // A: dV^T, B: dK^T
 #pragma unroll
@@ -545,17 +637,26 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
     // one of the wave's loads after each group of four weights (ld(j)). The
     // lane's 16 rows are t0 + 4 c + {0..3, 8..11, 16..19, 24..27}; a step where
     // every lane sees all of them skips the mask.
-    auto weights_a = [&](const f32x4 (&l4s)[4], int t0, const f32x16 &sx, bf16x8 (&pf)[2], int buf, auto ld) {
+    // SEG: st_ids is the stage holding the step's query ids.
+    auto weights_a = [&](const f32x4 (&l4s)[4], int t0, const f32x16 &sx, bf16x8 (&pf)[2], int buf, auto ld,
+                         int st_ids) {
         const int tb = t0 + 4 * c - s + RR;
         auto body = [&](auto masked) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++) {
                 f32x4 p4;
+                i32x4 qi4{};
+                if constexpr (SEG && decltype(masked)::value)
+                    qi4 = *(const i32x4 *)(&sld[st_ids][0][32 + 8 * q4 + 4 * c]);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = 4 * q4 + e;
                     float p = exp2_fast(__builtin_fmaf(sx[r], kLog2e, -l4s[q4][e]));
-                    if constexpr (decltype(masked)::value) p = (unsigned)(tb + 8 * q4 + e) < vis_bound ? p : 0.f;
+                    if constexpr (decltype(masked)::value) {
+                        bool vis = (unsigned)(tb + 8 * q4 + e) < vis_bound;
+                        if constexpr (SEG) vis = vis && qi4[e] == my_kid;
+                        p = vis ? p : 0.f;
+                    }
                     p4[e] = p;
                     pf[r >> 3][r & 7] = (__bf16)p;
                 }
@@ -563,7 +664,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
                 if (q4 < NLD) ld(q4);
             }
         };
-        if (__all(tb >= 0 && tb + 27 < (int)vis_bound))
+        // SEG: the step's ids and the pair's keys' ids all one value
+        bool seg_open = true;
+        if constexpr (SEG) {
+            const int qt = t0 / BQ;
+            const int qmn = __builtin_amdgcn_readfirstlane(s_tmin[qt]), qmx = __builtin_amdgcn_readfirstlane(s_tmax[qt]);
+            seg_open = qmn == qmx && p_kmin == p_kmax && qmn == p_kmin;
+        }
+        (void)st_ids;
+        if (seg_open && __all(tb >= 0 && tb + 27 < (int)vis_bound))
             body(std::integral_constant<bool, false>{});
         else
             body(std::integral_constant<bool, true>{});
@@ -621,11 +730,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         constexpr bool ROLE_A = decltype(role)::value;
         // prologue: steps 0 .. 3 into stages 0 .. 3; A: P(0) (exchange buffer
         // 0) and S(1); B: dP(0)
-        Cursor c_ld{0, qt_begin};
+        Cursor c_ld{0, q_lo};
 #pragma unroll
         for (int st = 0; st < 4; st++) {
+            const int row_p = row_of(c_ld), t_p = qt_of(c_ld) * BQ;
 #pragma unroll
-            for (int j = 0; j < NLD; j++) issue_load(j, row_of(c_ld), st);
+            for (int j = 0; j < NLD; j++) issue_load(j, row_p, t_p, st);
             advance(c_ld);
         }
         wait_lds_loads();
@@ -638,13 +748,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         if constexpr (ROLE_A) {
             sdp(0, sb);
             read_rows(0, r4);
-            weights_a(r4, qt_begin * BQ, sb, w, 0, no_load);
+            weights_a(r4, qt_of(Cursor{0, q_lo}) * BQ, sb, w, 0, no_load, 0);
             sdp(1, sa);
         } else {
             sdp(0, sa);
             read_rows(0, r4);
         }
-        Cursor c_w{0, qt_begin};  // A: step i+1 in iteration i
+        Cursor c_w{0, q_lo};  // A: step i+1 in iteration i
         advance(c_w);
         int st0 = 0, st1 = 1, st2 = 2, st4 = 4;  // stages of steps i, i+1, i+2, i+4
         // Two phases per iteration, separated by workgroup barriers, so that
@@ -655,11 +765,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         // Each wave issues its loads of step i+4 in its VALU phase and then
         // waits for those of step i+3, one barrier before their first reader.
         for (int i = 0; i < n_steps; i++) {
-            const int row_ld = row_of(c_ld);
+            const int row_ld = row_of(c_ld), t_ld = qt_of(c_ld) * BQ;
             advance(c_ld);
-            const int t1 = c_w.qt * BQ;
+            const int t1 = qt_of(c_w) * BQ;
             advance(c_w);
-            auto ld = [&](int j) { issue_load(j, row_ld, st4); };
+            auto ld = [&](int j) { issue_load(j, row_ld, t_ld, st4); };
             barrier_no_drain();
             if constexpr (ROLE_A) {
                 m_phase(st2, st0, sb, w, st1, r4);  // and lse of step i+1
@@ -671,7 +781,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
             barrier_no_drain();
             if constexpr (ROLE_A) {
                 pin_value(sa);  // no weight work hoisted above the barrier
-                weights_a(r4, t1, sa, w, (i + 1) & 1, ld);
+                weights_a(r4, t1, sa, w, (i + 1) & 1, ld, st1);
                 wait_lds_loads_but<NLD>();
                 sa = sb;
             } else {
@@ -1447,13 +1557,20 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     const int n_kblocks = (a.S + keys_wg - 1) / keys_wg;
     const dim3 kgrid((unsigned)(a.B * a.K * n_kblocks));
     if constexpr (H <= 128 && NW_DKV == 4) {
-        // no segment ids or per-head masks: the wave-pair kernel (8 waves, 128
-        // keys per workgroup)
+        // no per-head masks: the wave-pair kernel (8 waves, 128 keys per
+        // workgroup), with segment ids up to 8192 queries
         if (a.q_seg == nullptr && a.head_mask == nullptr) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, true>), kgrid, dim3(512), 0, stream, a);
             else
                 hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, false>), kgrid, dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
+        if (a.q_seg != nullptr && a.head_mask == nullptr && a.T <= 8192) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, true, true>), kgrid, dim3(512), 0, stream, a);
+            else
+                hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, false, true>), kgrid, dim3(512), 0, stream, a);
             return hipGetLastError();
         }
     }
