@@ -64,6 +64,70 @@ __device__ __forceinline__ void pp_schedule(std::integer_sequence<int, P...>, st
     (pp_sched_step<X, NX, NM, R, D>(), ...);
 }
 
+// Segment ids for the ping-pong D and dQ kernels (512 threads, at most 8192
+// keys): stages the kv ids of key tiles 0 .. nt - 1 (BKV keys each) in s_kvid
+// with each tile's id range, and lists in s_jlist, in increasing order, the
+// tiles whose range meets the id range of the block's queries t0 .. t0 + bq
+// - 1 (the others hold no visible pair). Returns the list's length, the same
+// in every wave. Every id load is in flight before the first use.
+constexpr int kSegKeyCap = 8192;
+template <int BKV>
+__device__ __forceinline__ int seg_tile_list(const int32_t *qs, const int32_t *kvs, int t0, int bq, int T, int nt,
+                                             int *s_kvid, int *s_tmin, int *s_tmax, int *s_jlist, int *s_cnt) {
+    static_assert(BKV == 32 || BKV == 64, "a tile is one wave or half of one");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int PER = kSegKeyCap / 512;
+    const int nkeys = nt * BKV;  // >= BKV
+    int id[PER], qb_id[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++) qb_id[m] = qs[min(t0 + lane + 64 * m, T - 1)];
+#pragma unroll
+    for (int m = 0; m < PER; m++) id[m] = kvs[min(tid + 512 * m, nkeys - 1)];
+    int qlo = INT_MAX, qhi = INT_MIN;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const int i = lane + 64 * m;
+        if (i < bq && t0 + i < T) {
+            qlo = min(qlo, qb_id[m]);
+            qhi = max(qhi, qb_id[m]);
+        }
+    }
+    qlo = wave_min_i(qlo);
+    qhi = wave_max_i(qhi);
+#pragma unroll
+    for (int m = 0; m < PER; m++) {
+        const int k = tid + 512 * m;
+        if (512 * m + 64 * wave < nkeys) {  // wave-uniform; whole tiles below nkeys
+            const bool ok = k < nkeys;
+            if (ok) s_kvid[k] = id[m];
+            int lo = ok ? id[m] : INT_MAX, hi = ok ? id[m] : INT_MIN;
+#pragma unroll
+            for (int o = BKV / 2; o >= 1; o >>= 1) {
+                lo = min(lo, __shfl_xor(lo, o));
+                hi = max(hi, __shfl_xor(hi, o));
+            }
+            if (ok && (lane & (BKV - 1)) == 0) {
+                s_tmin[k / BKV] = lo;
+                s_tmax[k / BKV] = hi;
+            }
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int cnt = 0;
+        for (int jb = 0; jb < nt; jb += 64) {
+            const int j = jb + lane;
+            const bool vis = j < nt && !(s_tmax[j] < qlo || s_tmin[j] > qhi);
+            const unsigned long long m = __ballot(vis);
+            if (vis) s_jlist[cnt + __popcll(m & ((1ull << lane) - 1))] = j;
+            cnt += __popcll(m);
+        }
+        if (lane == 0) *s_cnt = cnt;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*s_cnt);
+}
+
 
 // ---------------------------------------------------------------------------
 // dK, dV. One workgroup per (b, kv head, block of 32*NW keys); wave w owns
@@ -1105,7 +1169,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
 // into the slot that M(i-1) of both groups has finished reading; every wave
 // waits for its own loads at the end of its next M phase, a barrier before
 // any wave reads them.
-template <int H, int BKV, bool CAUSAL, bool WIN = false>
+//
+// SEG (segment ids, S <= 8192): the tiles are those of the block's list
+// (seg_tile_list); a tile whose ids and the wave's query ids are not all one
+// value takes the element mask, and so does the list's last tile.
+template <int H, int BKV, bool CAUSAL, bool WIN = false, bool SEG = false>
 __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
                                                                    int n_qblocks) {
     constexpr int NG = 4;  // waves per group
@@ -1157,7 +1225,35 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     const int WL = a.wl;
     const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
     // causal: the block's diagonal tile qb + coff / BKV comes last
-    const int n_t = (CAUSAL ? qb + 1 + a.coff / BKV : S / BKV) - j0;
+    const int nt_all = CAUSAL ? qb + 1 + a.coff / BKV : S / BKV;
+    // SEG: the block's list of tiles and the lane's and wave's query ids
+    constexpr int KV_CAP = SEG ? kSegKeyCap : 1, NT_CAP = SEG ? kSegKeyCap / BKV : 1;
+    __shared__ __attribute__((aligned(16))) int s_kvid[KV_CAP];
+    __shared__ int s_tmin[NT_CAP], s_tmax[NT_CAP], s_jlist[NT_CAP], s_nvis;
+    int my_qid = 0, w_qmin = 0, w_qmax = 0, n_vis = 0;
+    if constexpr (SEG) {
+        const int32_t *qs = a.q_seg + (size_t)b * T;
+        my_qid = qs[t];
+        w_qmin = wave_min_i(my_qid);
+        w_qmax = wave_max_i(my_qid);
+        n_vis = seg_tile_list<BKV>(qs, a.kv_seg + (size_t)b * S, t0, bq, T, nt_all, s_kvid, s_tmin, s_tmax, s_jlist,
+                                   &s_nvis);
+        if (n_vis == 0) {
+            // no query of the block shares an id with a key it may see
+            if (c == 0) {
+                a.delta[row] = 0.f;
+                a.lse2[row] = lse2;
+            }
+            return;
+        }
+    }
+    const int n_t = SEG ? n_vis : nt_all - j0;
+    auto tile_of = [&](int i) { return SEG ? __builtin_amdgcn_readfirstlane(s_jlist[i]) : j0 + i; };
+    // SEG: tile j needs the element mask for this wave's rows
+    auto seg_mask = [&](int j) {
+        const int kmin = __builtin_amdgcn_readfirstlane(s_tmin[j]), kmax = __builtin_amdgcn_readfirstlane(s_tmax[j]);
+        return !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
+    };
 
     // global -> LDS: group A loads K tiles, group B V tiles; wave gwv of a group
     // issues 1 KiB blocks gwv, gwv + NG, ... (padding slots repeat the row's
@@ -1172,7 +1268,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     // tiles j < n_t lie wholly inside K and V (S % BKV == 0), so the tile
     // offset may go in the scalar offset
     auto issue_tile = [&](int j, int slot) {
-        const int tile = __builtin_amdgcn_readfirstlane((j0 + j) * BKV * H * 2);
+        const int tile = __builtin_amdgcn_readfirstlane(tile_of(j) * BKV * H * 2);
         __bf16 *dst = grp == 0 ? sk[slot] : sv[slot];
         const buffer_rsrc &rs = grp == 0 ? krs : vrs;
 #pragma unroll
@@ -1203,18 +1299,27 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     };
     // V phase: lane (n, c) holds keys s0 + 32 mb + acc_row(r, c) of query t
     auto v_phase = [&](int s0, auto masked) {
-        const int lim = t + a.coff - s0 - 4 * c;                // last visible key offset (causal)
-        const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;  // first visible key offset (window)
+        const int lim = CAUSAL ? t + a.coff - s0 - 4 * c : INT_MAX;  // last visible key offset (causal)
+        const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;       // first visible key offset (window)
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                float p = exp2_fast(__builtin_fmaf(sacc[mb][r], kLog2e, -lse2));
-                if constexpr (decltype(masked)::value) {
-                    const int off = 32 * mb + 8 * (r >> 2) + (r & 3);
-                    if (off > lim || off < first) p = 0.f;
+            for (int q4 = 0; q4 < 4; q4++) {
+                // SEG: the ids of keys s0 + 32 mb + 8 q4 + 4 c + 0..3
+                i32x4 ids{};
+                if constexpr (SEG && decltype(masked)::value) ids = *(const i32x4 *)&s_kvid[s0 + 32 * mb + 8 * q4 + 4 * c];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = 4 * q4 + e;
+                    float p = exp2_fast(__builtin_fmaf(sacc[mb][r], kLog2e, -lse2));
+                    if constexpr (decltype(masked)::value) {
+                        const int off = 32 * mb + 8 * q4 + e;
+                        bool hide = off > lim || off < first;
+                        if constexpr (SEG) hide = hide || ids[e] != my_qid;
+                        if (hide) p = 0.f;
+                    }
+                    d_acc = __builtin_fmaf(p, pacc[mb][r], d_acc);
                 }
-                d_acc = __builtin_fmaf(p, pacc[mb][r], d_acc);
             }
     };
     using yes = std::integral_constant<bool, true>;
@@ -1235,19 +1340,24 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
         if (i + 2 < n_t) issue_tile(i + 2, lslot);
         // WIN: the window's left edge, t - WL over the block's BKV queries,
         // cuts at most the block's first two tiles
-        if (WIN && i < 2 && (j0 + i) * BKV < t0 + BKV - 1 - WL)
-            v_phase((j0 + i) * BKV, yes{});
+        bool mk;
+        if constexpr (SEG)
+            mk = seg_mask(tile_of(i));
         else
-            v_phase((j0 + i) * BKV, no{});
+            mk = WIN && i < 2 && (j0 + i) * BKV < t0 + BKV - 1 - WL;
+        if (mk)
+            v_phase(tile_of(i) * BKV, yes{});
+        else
+            v_phase(tile_of(i) * BKV, no{});
         barrier_no_drain();
         m_phase(nslot);
         slot = nslot;
     }
     barrier_no_drain();
-    if (CAUSAL)
-        v_phase((j0 + n_t - 1) * BKV, yes{});
+    if (CAUSAL || SEG)
+        v_phase(tile_of(n_t - 1) * BKV, yes{});
     else
-        v_phase((j0 + n_t - 1) * BKV, no{});
+        v_phase(tile_of(n_t - 1) * BKV, no{});
     if (grp == 0) barrier_no_drain();  // group A's trailing phase
 
     d_acc += __shfl_xor(d_acc, 32);
@@ -1278,7 +1388,11 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
 // apart and one more chunk after every 4 rows, so that its b128 row reads and
 // its transpose reads are both free of bank conflicts. V rows are padded to
 // CPR + 1 chunks (row reads only).
-template <int H, bool CAUSAL, bool WIN = false>
+//
+// SEG (segment ids, S <= 8192): the tiles are those of the block's list
+// (seg_tile_list); a tile whose ids and the wave's query ids are not all one
+// value takes the element mask.
+template <int H, bool CAUSAL, bool WIN = false, bool SEG = false>
 __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
                                                                 int n_qblocks) {
     constexpr int BKV = 32;
@@ -1334,7 +1448,31 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     const int WL = a.wl;
     const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
     // causal: up to the tile of the block's last query's diagonal
-    const int n_t = (CAUSAL ? (t0 + bq + a.coff) / BKV : S / BKV) - j0;
+    const int nt_all = CAUSAL ? (t0 + bq + a.coff) / BKV : S / BKV;
+    // SEG: the block's list of tiles and the lane's and wave's query ids
+    constexpr int KV_CAP = SEG ? kSegKeyCap : 1, NT_CAP = SEG ? kSegKeyCap / BKV : 1;
+    __shared__ __attribute__((aligned(16))) int s_kvid[KV_CAP];
+    __shared__ int s_tmin[NT_CAP], s_tmax[NT_CAP], s_jlist[NT_CAP], s_nvis;
+    int my_qid = 0, w_qmin = 0, w_qmax = 0, n_vis = 0;
+    if constexpr (SEG) {
+        const int32_t *qs = a.q_seg + (size_t)b * T;
+        my_qid = qs[t];
+        w_qmin = wave_min_i(my_qid);
+        w_qmax = wave_max_i(my_qid);
+        n_vis = seg_tile_list<BKV>(qs, a.kv_seg + (size_t)b * S, t0, bq, T, nt_all, s_kvid, s_tmin, s_tmax, s_jlist,
+                                   &s_nvis);
+        if (n_vis == 0) {
+            // no query of the block shares an id with a key it may see: dQ = 0
+            float *dqrow = a.dq + row * H;
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++) *(f32x4 *)(dqrow + 32 * hb + 8 * q4 + 4 * c) = f32x4{};
+            return;
+        }
+    }
+    const int n_t = SEG ? n_vis : nt_all - j0;
+    auto tile_of = [&](int i) { return SEG ? __builtin_amdgcn_readfirstlane(s_jlist[i]) : j0 + i; };
 
     // global -> LDS: group A loads K tiles, group B V tiles; wave gwv of a group
     // issues 1 KiB blocks gwv, gwv + NG, ... Chunk p of a K tile holds row
@@ -1356,7 +1494,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     // tiles j < n_t lie wholly inside K and V (S % BKV == 0), so the tile
     // offset may go in the scalar offset
     auto issue_tile = [&](int j, int slot) {
-        const int tile = __builtin_amdgcn_readfirstlane((j0 + j) * BKV * H * 2);
+        const int tile = __builtin_amdgcn_readfirstlane(tile_of(j) * BKV * H * 2);
         char *dst = grp == 0 ? (char *)sk[slot] : (char *)sv[slot];
         const buffer_rsrc &rsrc = grp == 0 ? krs : vrs;
 #pragma unroll
@@ -1428,16 +1566,32 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     bool need_lo = true;
     auto v_phase = [&](int s0) {
         // some key after some query of the wave, or (WIN) before some query's
-        // first visible key t - WL
-        const bool masked = (CAUSAL && s0 + BKV - 1 > t_w + a.coff) || (WIN && s0 < t_w + 31 - WL);
-        const int lim = t + a.coff - s0 - 4 * c;                // last visible key offset (causal)
-        const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;  // first visible key offset (window)
+        // first visible key t - WL; SEG: ids not all one value
+        bool masked = (CAUSAL && s0 + BKV - 1 > t_w + a.coff) || (WIN && s0 < t_w + 31 - WL);
+        if constexpr (SEG) {
+            const int j = s0 / BKV;
+            const int kmin = __builtin_amdgcn_readfirstlane(s_tmin[j]);
+            const int kmax = __builtin_amdgcn_readfirstlane(s_tmax[j]);
+            masked = masked || !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
+        }
+        const int lim = CAUSAL ? t + a.coff - s0 - 4 * c : INT_MAX;  // last visible key offset (causal)
+        const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;       // first visible key offset (window)
         float amax = 0.f;
+        // SEG: the ids of keys s0 + 8 q4 + 4 c + 0..3 (read on masked tiles only)
+        i32x4 ids[4] = {};
+        if constexpr (SEG) {
+            if (masked) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++) ids[q4] = *(const i32x4 *)&s_kvid[s0 + 8 * q4 + 4 * c];
+            }
+        }
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             float p = exp2_fast(__builtin_fmaf(sacc[r], kLog2e, -lse2));
             const int off = 8 * (r >> 2) + (r & 3);
-            if (masked && (off > lim || off < first)) p = 0.f;
+            bool hide = off > lim || off < first;
+            if constexpr (SEG) hide = hide || ids[r >> 2][r & 3] != my_qid;
+            if (masked && hide) p = 0.f;
             const float ds = p * (pacc[r] - dlt);
             amax = fmaxf(amax, fabsf(ds));
             const __bf16 hi = (__bf16)ds;
@@ -1459,13 +1613,13 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     for (int i = 0; i < n_t - 1; i++) {
         barrier_no_drain();
         if (i + 2 < n_t) issue_tile(i + 2, (i + 2) % NSLOT);
-        v_phase((j0 + i) * BKV);
+        v_phase(tile_of(i) * BKV);
         barrier_no_drain();
         m_phase(yes{}, yes{}, (i + 1) % NSLOT, i % NSLOT);
         if (need_lo) lo_phase(i % NSLOT);
     }
     barrier_no_drain();
-    v_phase((j0 + n_t - 1) * BKV);
+    v_phase(tile_of(n_t - 1) * BKV);
     barrier_no_drain();
     m_phase(no{}, yes{}, 0, (n_t - 1) % NSLOT);
     if (need_lo) lo_phase((n_t - 1) % NSLOT);
@@ -1507,7 +1661,19 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
         const bool dense = shape && !mask_extra(m);
         // a causal left window on an otherwise dense shape
         const bool dense_win = shape && mask_left_window_only(m);
-        if (dense) {
+        // segment ids on an otherwise dense shape with at most 8192 keys
+        const bool seg_shape = a.q_seg != nullptr && a.head_mask == nullptr && gw * bq == 256 && a.T % bq == 0 &&
+                               a.S % BKV_PP == 0 && a.S <= kSegKeyCap && diag_tiles(BKV_PP) &&
+                               (!a.causal || bq == BKV_PP) && !mask_extra(m);
+        if (seg_shape) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, true, false, true>), qgrid, dim3(512), 0,
+                                   stream, a, gw, bq, n_gsplit, n_qblocks);
+            else
+                hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, false, false, true>), qgrid, dim3(512), 0,
+                                   stream, a, gw, bq, n_gsplit, n_qblocks);
+            delta_done = true;
+        } else if (dense) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, true>), qgrid, dim3(512), 0, stream, a, gw,
                                    bq, n_gsplit, n_qblocks);
@@ -1534,7 +1700,18 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
         const bool dense = shape && !mask_extra(m);
         // a causal left window on an otherwise dense shape
         const bool dense_win = shape && mask_left_window_only(m);
-        if (dense) {
+        // segment ids on an otherwise dense shape with at most 8192 keys
+        const bool seg_shape = a.q_seg != nullptr && a.head_mask == nullptr && gw * bq == 256 && a.T % bq == 0 &&
+                               a.S % 32 == 0 && a.S <= kSegKeyCap && diag_tiles(32) && !mask_extra(m);
+        if (seg_shape) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, true, false, true>), qgrid, dim3(512), 0, stream, a, gw,
+                                   bq, n_gsplit, n_qblocks);
+            else
+                hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, false, false, true>), qgrid, dim3(512), 0, stream, a, gw,
+                                   bq, n_gsplit, n_qblocks);
+            dq_done = true;
+        } else if (dense) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, true>), qgrid, dim3(512), 0, stream, a, gw, bq, n_gsplit,
                                    n_qblocks);

@@ -1,9 +1,12 @@
 """GPU parity of the backward with segment ids (SegmentIds of the fjformer
 page; the FA page's splash kernel takes them too): the wave-pair dK/dV
-kernel walks only the query tiles whose ids meet its keys' ids and masks
-pairs of different ids element by element. Every element of dQ, dK and dV
-against the fp64 oracle, with ids packed in order, ids in no order at all,
-and each mask form the ids combine with."""
+kernel walks only the query tiles whose ids meet its keys' ids, the
+ping-pong D and dQ kernels only the key tiles whose ids meet their queries',
+and all three mask pairs of different ids element by element. Every element
+of dQ, dK and dV against the fp64 oracle, with ids packed in order, ids in
+no order at all, blocks that meet no id, and each mask form the ids combine
+with (the shapes that the ping-pong kernels do not take run the general
+ones)."""
 import numpy as np
 import pytest
 import torch
@@ -100,3 +103,25 @@ def test_bwd_segments_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(r1, r2):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_bwd_segments_query_block_without_keys(causal):
+    """A whole query block (and a key block) whose ids appear on no key (no
+    query): its list of tiles is empty, dQ of its rows is zero, and the
+    other rows match the oracle."""
+    B, K, G, T, H = 1, 2, 4, 512, 128
+    q, k, v, do = make_qkv(B, K, G, T, T, H, seed=21, with_do=True)
+    q_seg = make_segment_ids(B, T, seed=4, lo=60, hi=200)
+    kv_seg = q_seg.clone()
+    q_seg[:, 128:192] = 1000  # one 64-query block: no key has this id
+    kv_seg[:, 320:448] = 2000  # one 128-key block: no query has it
+    qd, kd, vd, dod, qs, ks = to_dev(q, k, v, do, q_seg, kv_seg)
+    o, lse = gqa.attn_fwd(qd, kd, vd, causal=causal, q_seg=qs, kv_seg=ks)
+    dq, dk, dv = gqa.attn_bwd(qd, kd, vd, o, lse, dod, causal=causal, q_seg=qs, kv_seg=ks)
+    torch.cuda.synchronize()
+    dq, dk, dv = f32(dq), f32(dk), f32(dv)
+    assert np.all(dq[:, :, :, 128:192] == 0)
+    assert np.all(dk[:, :, 320:448] == 0) and np.all(dv[:, :, 320:448] == 0)
+    ref = oracle.bwd(q, k, v, do, causal=causal, q_seg=q_seg, kv_seg=kv_seg)
+    assert_close_all([("dQ", dq, ref["dq"]), ("dK", dk, ref["dk"]), ("dV", dv, ref["dv"])])
