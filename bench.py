@@ -25,7 +25,8 @@ tensors and reports it under "backward".
 --workload segments times the packed-sequence shape B=4, K=8, G=4, T=S=2048,
 H=128 (causal and segment ids, segments of 64-1024 tokens) in the same
 format; value and the roofline fraction count only the visible (t, s) pairs
-(the work the kernel executes), with the causal-half rate beside them.
+(the work the kernel executes), with the causal-half rate beside them. Its
+backward leg, with the same segment ids, counts the visible pairs too.
 
 --workload prefill times a chunk of T=1024 new queries at the end of an
 S=8192 context (B=1, K=8, G=4, H=128, end-aligned causal) through the tuned
@@ -623,7 +624,6 @@ def main():
         w = WORKLOADS["segments_causal_b4_k8_g4_t2048_h128"]
         kernel = "attn_fwd_pp_kernel<128,64,true,false,true,2,false> (ping-pong, causal with segment ids; loads spread over the MFMA phase)"
         kernel_substr = "attn_fwd_pp_kernel<128, 64, true, false, true, 2, false>"
-        args.no_backward = True
         seg = make_segment_ids(w.B, w.T, w.seed)
     t = make_qkv(w.B, w.K, w.G, w.T, w.S, w.H, w.seed, with_do=not args.no_backward)
     q, k, v = t[:3]
@@ -694,7 +694,8 @@ def main():
         step()
 
         def bstep():
-            gqa.attn_bwd(qd, kd, vd, o, lse, dod, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+            gqa.attn_bwd(qd, kd, vd, o, lse, dod, causal=w.causal, q_seg=segd, kv_seg=segd, dq=dq, dk=dk, dv=dv,
+                         workspace=ws)
 
         try:
             bms = time_launches(bstep, max(5, args.steps // 2), max(2, args.warmup // 2), args.settle_seconds)

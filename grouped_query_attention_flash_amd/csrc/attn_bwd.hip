@@ -628,7 +628,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         t_off[i] = (row * H + min(rem % RS, CPR - 1) * 8) * 2;
     }
     const unsigned t_dst0 = (is_a ? lds_addr(sq[0]) : lds_addr(sdo[0])) + pair * 1024;
-    const unsigned l_dst0 = lds_addr(ids_wave ? &sld[0][0][32] : sld[0][is_a ? 0 : 1]), dummy = lds_addr(sdummy);
+    // (offsets from sld's base as wave-uniform integers: lse at 0, the ids 32
+    // floats on, D one row of 256 on)
+    const unsigned l_dst0 =
+        __builtin_amdgcn_readfirstlane(lds_addr(sld[0][0]) + (ids_wave ? 32u * 4u : is_a ? 0u : 256u * 4u));
+    const unsigned dummy = lds_addr(sdummy);
     // row0: the step's first row g T + t (-1: none); t_row: its first query t
     auto issue_load = [&](int j, int row0, int t_row, int stage) {
         if (j < TBW) {
@@ -641,8 +645,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
             // .. 31], the query ids (wave 1) into [32 .. 63], D (wave 4)
             const bool ok = row0 >= 0 && (pair == 0 || ids_wave);
             const unsigned voff = ok ? (unsigned)((ids_wave ? t_row : row0) * 4 + (lane & 7) * 16) : kOutOfRange;
-            const unsigned dst = ok ? l_dst0 + stage * (2 * 256 * 4) : dummy;
-            if (lane < 8) lds_dma16(lrs, __builtin_amdgcn_readfirstlane(dst), voff);
+            const unsigned dst = __builtin_amdgcn_readfirstlane(ok ? l_dst0 + stage * (2 * 256 * 4) : dummy);
+            if (lane < 8) lds_dma16(lrs, dst, voff);
         } else {
             // 32 floats: lanes 0-7 fetch them, the others repeat in-range
             // addresses into slots that are not read
