@@ -479,8 +479,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a, int n_
 // same for every wave), and a step whose ids are not all one value takes the
 // element mask, which compares the lane's key id with the step's query ids
 // (loaded beside lse, lanes 0-7 of one A wave).
-template <int H, bool CAUSAL, bool SEG = false>
+//
+// HM (per-head masks, G <= 64): each head walks its own query tile range,
+// from its window sides and prefix (head_mask_of), and masks with them.
+template <int H, bool CAUSAL, bool SEG = false, bool HM = false>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
+    static_assert(!(SEG && HM), "segment ids or per-head masks");
     constexpr int NP = 4, BQ = 32;  // wave pairs, queries per step
     constexpr int CPR = H / 8;
     constexpr int KSTEPS = H / 16;
@@ -536,6 +540,32 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
     const bool blk_pfx = s0_wg < a.prefix;
     const int qt_begin = blk_pfx ? 0 : min(n_qt, max(0, s0_wg - WR) / BQ);
     const int qt_end = blk_pfx ? n_qt : max(qt_begin, min(n_qt, (s0_wg + 32 * NP - 1 + WL) / BQ + 1));
+
+    // HM: each head's window sides, prefix and query tile range, and the
+    // number of steps over all heads, from wave 0 (one lane per head)
+    constexpr int HM_CAP = HM ? 64 : 1;
+    __shared__ int s_hwl[HM_CAP], s_hwr[HM_CAP], s_hpf[HM_CAP], s_hlo[HM_CAP], s_hhi[HM_CAP], s_hsteps;
+    if constexpr (HM) {
+        if (wave == 0) {
+            int cnt = 0;
+            if (lane < G) {
+                const HeadMask h = head_mask_of(a.head_mask, kh, G, lane, T, S, a.causal, a.coff);
+                const bool bp = s0_wg < h.pfx;
+                const int lo = bp ? 0 : min(n_qt, max(0, s0_wg - h.wr) / BQ);
+                const int hi = bp ? n_qt : max(lo, min(n_qt, (s0_wg + 32 * NP - 1 + h.wl) / BQ + 1));
+                s_hwl[lane] = h.wl;
+                s_hwr[lane] = h.wr;
+                s_hpf[lane] = h.pfx;
+                s_hlo[lane] = lo;
+                s_hhi[lane] = hi;
+                cnt = hi - lo;
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+            if (lane == 0) s_hsteps = cnt;
+        }
+        __syncthreads();
+    }
 
     // SEG: the key's id, the pair's id range, and the list of the query tiles
     // in [qt_begin, qt_end) whose id range meets the block's (s_qtl[0 ..
@@ -603,7 +633,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         q_lo = 0;
         q_hi = __builtin_amdgcn_readfirstlane(s_krange[2 * NP]);
     }
-    const int n_steps = G * (q_hi - q_lo);
+    const int n_steps = HM ? __builtin_amdgcn_readfirstlane(s_hsteps) : G * (q_hi - q_lo);
 
     // loads: A waves the Q tile (blocks pair, pair + 4, ...) and, wave 0, lse;
     // B waves the dO tile and, wave 4, D. Every wave issues NLD loads per step
@@ -657,12 +687,28 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         }
         (void)t_row;
     };
-    // (g, qi): head g, query tile qi (SEG: entry qi of the list)
+    // (g, qi): head g, query tile qi (SEG: entry qi of the list; HM: hi is
+    // the end of head g's range, and heads with an empty range are skipped)
     struct Cursor {
-        int g, qi;
+        int g, qi, hi;
+    };
+    auto hm_lo = [&](int g) { return __builtin_amdgcn_readfirstlane(s_hlo[g]); };
+    auto hm_hi = [&](int g) { return __builtin_amdgcn_readfirstlane(s_hhi[g]); };
+    // HM: the cursor at the first step of head g or the next head with steps
+    auto hm_seek = [&](int g) {
+        while (g < G && hm_lo(g) == hm_hi(g)) ++g;
+        return g < G ? Cursor{g, hm_lo(g), hm_hi(g)} : Cursor{G, 0, 0};
+    };
+    auto first_cursor = [&]() {
+        if constexpr (HM)
+            return hm_seek(0);
+        else
+            return Cursor{0, q_lo, 0};
     };
     auto advance = [&](Cursor &cu) {
-        if (++cu.qi == q_hi) {
+        if constexpr (HM) {
+            if (++cu.qi >= cu.hi) cu = hm_seek(cu.g + 1);
+        } else if (++cu.qi == q_hi) {
             cu.qi = q_lo;
             ++cu.g;
         }
@@ -706,9 +752,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
     // lane's 16 rows are t0 + 4 c + {0..3, 8..11, 16..19, 24..27}; a step where
     // every lane sees all of them skips the mask.
     // SEG: st_ids is the stage holding the step's query ids.
+    // HM: g_step is the step's head, whose sides and prefix replace the
+    // call's.
     auto weights_a = [&](const f32x4 (&l4s)[4], int t0, const f32x16 &sx, bf16x8 (&pf)[2], int buf, auto ld,
-                         int st_ids) {
-        const int tb = t0 + 4 * c - s + RR;
+                         int st_ids, int g_step) {
+        int rr = RR;
+        unsigned vbound = vis_bound;
+        if constexpr (HM) {
+            const int hpf = __builtin_amdgcn_readfirstlane(s_hpf[g_step]);
+            const int hwl = __builtin_amdgcn_readfirstlane(s_hwl[g_step]);
+            const int hwr = __builtin_amdgcn_readfirstlane(s_hwr[g_step]);
+            const bool kp = s < hpf;
+            const int l2 = kp ? kNoWindow : hwl;
+            rr = kp ? kNoWindow : hwr;
+            vbound = k_valid ? (unsigned)max(0, min(l2 + rr + 1, T - s + rr)) : 0u;
+        }
+        (void)g_step;
+        const int tb = t0 + 4 * c - s + rr;
         auto body = [&](auto masked) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++) {
@@ -721,7 +781,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
                     const int r = 4 * q4 + e;
                     float p = exp2_fast(__builtin_fmaf(sx[r], kLog2e, -l4s[q4][e]));
                     if constexpr (decltype(masked)::value) {
-                        bool vis = (unsigned)(tb + 8 * q4 + e) < vis_bound;
+                        bool vis = (unsigned)(tb + 8 * q4 + e) < vbound;
                         if constexpr (SEG) vis = vis && qi4[e] == my_kid;
                         p = vis ? p : 0.f;
                     }
@@ -740,7 +800,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
             seg_open = qmn == qmx && p_kmin == p_kmax && qmn == p_kmin;
         }
         (void)st_ids;
-        if (seg_open && __all(tb >= 0 && tb + 27 < (int)vis_bound))
+        if (seg_open && __all(tb >= 0 && tb + 27 < (int)vbound))
             body(std::integral_constant<bool, false>{});
         else
             body(std::integral_constant<bool, true>{});
@@ -798,7 +858,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         constexpr bool ROLE_A = decltype(role)::value;
         // prologue: steps 0 .. 3 into stages 0 .. 3; A: P(0) (exchange buffer
         // 0) and S(1); B: dP(0)
-        Cursor c_ld{0, q_lo};
+        Cursor c_ld = first_cursor();
 #pragma unroll
         for (int st = 0; st < 4; st++) {
             const int row_p = row_of(c_ld), t_p = qt_of(c_ld) * BQ;
@@ -816,13 +876,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         if constexpr (ROLE_A) {
             sdp(0, sb);
             read_rows(0, r4);
-            weights_a(r4, qt_of(Cursor{0, q_lo}) * BQ, sb, w, 0, no_load, 0);
+            const Cursor c0 = first_cursor();
+            weights_a(r4, qt_of(c0) * BQ, sb, w, 0, no_load, 0, c0.g);
             sdp(1, sa);
         } else {
             sdp(0, sa);
             read_rows(0, r4);
         }
-        Cursor c_w{0, q_lo};  // A: step i+1 in iteration i
+        Cursor c_w = first_cursor();  // A: step i+1 in iteration i
         advance(c_w);
         int st0 = 0, st1 = 1, st2 = 2, st4 = 4;  // stages of steps i, i+1, i+2, i+4
         // Two phases per iteration, separated by workgroup barriers, so that
@@ -835,7 +896,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
         for (int i = 0; i < n_steps; i++) {
             const int row_ld = row_of(c_ld), t_ld = qt_of(c_ld) * BQ;
             advance(c_ld);
-            const int t1 = qt_of(c_w) * BQ;
+            const int t1 = qt_of(c_w) * BQ, g1 = c_w.g;
             advance(c_w);
             auto ld = [&](int j) { issue_load(j, row_ld, t_ld, st4); };
             barrier_no_drain();
@@ -849,7 +910,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv3_kernel(BwdArgs a) {
             barrier_no_drain();
             if constexpr (ROLE_A) {
                 pin_value(sa);  // no weight work hoisted above the barrier
-                weights_a(r4, t1, sa, w, (i + 1) & 1, ld, st1);
+                weights_a(r4, t1, sa, w, (i + 1) & 1, ld, st1, g1);
                 wait_lds_loads_but<NLD>();
                 sa = sb;
             } else {
@@ -1752,6 +1813,14 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
                 hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, true, true>), kgrid, dim3(512), 0, stream, a);
             else
                 hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, false, true>), kgrid, dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
+        // per-head masks without segment ids, up to 64 query heads per kv head
+        if (a.q_seg == nullptr && a.head_mask != nullptr && a.G <= 64) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, true, false, true>), kgrid, dim3(512), 0, stream, a);
+            else
+                hipLaunchKernelGGL((attn_bwd_dkv3_kernel<H, false, false, true>), kgrid, dim3(512), 0, stream, a);
             return hipGetLastError();
         }
     }
