@@ -128,6 +128,35 @@ __device__ __forceinline__ int seg_tile_list(const int32_t *qs, const int32_t *k
     return __builtin_amdgcn_readfirstlane(*s_cnt);
 }
 
+// Per-head masks on the ping-pong D and dQ kernels: the block's key tiles are
+// the union of its gw heads' ranges, [first, last] of BKV-key tiles (each
+// wave computes it from the table, one lane per head), and a wave masks with
+// its own head's sides and prefix. Whole tiles (S % BKV == 0).
+template <int BKV>
+struct HmRange {
+    int first, last;
+};
+template <int BKV>
+__device__ __forceinline__ HmRange<BKV> hm_union(const BwdArgs &a, int kh, int g0, int gw, int t0, int bq) {
+    const int lane = threadIdx.x & 63;
+    int f = INT_MAX, l = INT_MIN;
+    if (lane < gw) {
+        const HeadMask h = head_mask_of(a.head_mask, kh, a.G, g0 + lane, a.T, a.S, a.causal, a.coff);
+        f = h.pfx > 0 ? 0 : max(0, t0 - h.wl) / BKV;
+        l = min(a.S / BKV - 1, max(h.pfx - 1, t0 + bq - 1 + h.wr) / BKV);
+    }
+    return HmRange<BKV>{wave_min_i(f), wave_max_i(l)};
+}
+// Does key tile j hold a pair that head mask hw hides from the wave's rows
+// t_w .. t_w + 31?
+template <int BKV>
+__device__ __forceinline__ bool hm_tile_masked(const HeadMask &hw, int j, int t_w) {
+    const int s0 = j * BKV;
+    const bool all_pfx = s0 + BKV - 1 < hw.pfx;
+    const bool all_band = s0 >= t_w + 31 - hw.wl && s0 + BKV - 1 <= t_w + hw.wr;
+    return !(all_pfx || all_band);
+}
+
 
 // ---------------------------------------------------------------------------
 // dK, dV. One workgroup per (b, kv head, block of 32*NW keys); wave w owns
@@ -1238,9 +1267,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a, int gw,
 // SEG (segment ids, S <= 8192): the tiles are those of the block's list
 // (seg_tile_list); a tile whose ids and the wave's query ids are not all one
 // value takes the element mask, and so does the list's last tile.
-template <int H, int BKV, bool CAUSAL, bool WIN = false, bool SEG = false>
+//
+// HM (per-head masks): the block walks the union of its heads' tile ranges
+// (hm_union) and each wave masks with its own head's sides and prefix.
+template <int H, int BKV, bool CAUSAL, bool WIN = false, bool SEG = false, bool HM = false>
 __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
                                                                    int n_qblocks) {
+    static_assert(!(HM && (WIN || SEG)), "per-head masks alone");
     constexpr int NG = 4;  // waves per group
     constexpr int KSTEPS = H / 16;
     constexpr int MB = BKV / 32;
@@ -1288,9 +1321,17 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     // key tiles j0 .. j0 + n_t - 1: a left window (causal only, WIN) starts the
     // block at the tile holding its first query's first visible key
     const int WL = a.wl;
-    const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
+    // HM: the wave's head mask and the block's union of tile ranges
+    HeadMask hw{kNoWindow, kNoWindow, 0};
+    HmRange<BKV> hr{0, 0};
+    const int t_w = t - n;  // the wave's first query
+    if constexpr (HM) {
+        hw = head_mask_of(a.head_mask, kh, a.G, __builtin_amdgcn_readfirstlane(g), T, S, a.causal, a.coff);
+        hr = hm_union<BKV>(a, kh, gs * gw, gw, t0, bq);
+    }
+    const int j0 = HM ? hr.first : (WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0);
     // causal: the block's diagonal tile qb + coff / BKV comes last
-    const int nt_all = CAUSAL ? qb + 1 + a.coff / BKV : S / BKV;
+    const int nt_all = HM ? hr.last + 1 : (CAUSAL ? qb + 1 + a.coff / BKV : S / BKV);
     // SEG: the block's list of tiles and the lane's and wave's query ids
     constexpr int KV_CAP = SEG ? kSegKeyCap : 1, NT_CAP = SEG ? kSegKeyCap / BKV : 1;
     __shared__ __attribute__((aligned(16))) int s_kvid[KV_CAP];
@@ -1364,8 +1405,9 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
     };
     // V phase: lane (n, c) holds keys s0 + 32 mb + acc_row(r, c) of query t
     auto v_phase = [&](int s0, auto masked) {
-        const int lim = CAUSAL ? t + a.coff - s0 - 4 * c : INT_MAX;  // last visible key offset (causal)
-        const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;       // first visible key offset (window)
+        // last and first visible key offsets (causal, window; HM: the head's)
+        const int lim = HM ? t + hw.wr - s0 - 4 * c : CAUSAL ? t + a.coff - s0 - 4 * c : INT_MAX;
+        const int first = HM ? t - hw.wl - s0 - 4 * c : WIN ? t - WL - s0 - 4 * c : INT_MIN;
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
@@ -1381,6 +1423,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
                         const int off = 32 * mb + 8 * q4 + e;
                         bool hide = off > lim || off < first;
                         if constexpr (SEG) hide = hide || ids[e] != my_qid;
+                        if constexpr (HM) hide = hide && s0 + off + 4 * c >= hw.pfx;  // prefix keys stay
                         if (hide) p = 0.f;
                     }
                     d_acc = __builtin_fmaf(p, pacc[mb][r], d_acc);
@@ -1408,6 +1451,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
         bool mk;
         if constexpr (SEG)
             mk = seg_mask(tile_of(i));
+        else if constexpr (HM)
+            mk = hm_tile_masked<BKV>(hw, j0 + i, t_w);
         else
             mk = WIN && i < 2 && (j0 + i) * BKV < t0 + BKV - 1 - WL;
         if (mk)
@@ -1419,7 +1464,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
         slot = nslot;
     }
     barrier_no_drain();
-    if (CAUSAL || SEG)
+    if (HM ? hm_tile_masked<BKV>(hw, j0 + n_t - 1, t_w) : (CAUSAL || SEG))
         v_phase(tile_of(n_t - 1) * BKV, yes{});
     else
         v_phase(tile_of(n_t - 1) * BKV, no{});
@@ -1457,9 +1502,13 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_delta_pp_kernel(BwdArgs a, in
 // SEG (segment ids, S <= 8192): the tiles are those of the block's list
 // (seg_tile_list); a tile whose ids and the wave's query ids are not all one
 // value takes the element mask.
-template <int H, bool CAUSAL, bool WIN = false, bool SEG = false>
+//
+// HM (per-head masks): the block walks the union of its heads' tile ranges
+// (hm_union) and each wave masks with its own head's sides and prefix.
+template <int H, bool CAUSAL, bool WIN = false, bool SEG = false, bool HM = false>
 __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int gw, int bq, int n_gsplit,
                                                                 int n_qblocks) {
+    static_assert(!(HM && (WIN || SEG)), "per-head masks alone");
     constexpr int BKV = 32;
     constexpr int NG = 4;            // waves per group
     constexpr int KSTEPS = H / 16;   // S and dP MFMAs per tile
@@ -1511,9 +1560,16 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     // key tiles j0 .. j0 + n_t - 1: a left window (causal only, WIN) starts the
     // block at the tile holding its first query's first visible key
     const int WL = a.wl;
-    const int j0 = WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0;
+    // HM: the wave's head mask and the block's union of tile ranges
+    HeadMask hw{kNoWindow, kNoWindow, 0};
+    HmRange<BKV> hr{0, 0};
+    if constexpr (HM) {
+        hw = head_mask_of(a.head_mask, kh, a.G, __builtin_amdgcn_readfirstlane(g), T, S, a.causal, a.coff);
+        hr = hm_union<BKV>(a, kh, gs * gw, gw, t0, bq);
+    }
+    const int j0 = HM ? hr.first : (WIN && t0 - WL > 0 ? (t0 - WL) / BKV : 0);
     // causal: up to the tile of the block's last query's diagonal
-    const int nt_all = CAUSAL ? (t0 + bq + a.coff) / BKV : S / BKV;
+    const int nt_all = HM ? hr.last + 1 : (CAUSAL ? (t0 + bq + a.coff) / BKV : S / BKV);
     // SEG: the block's list of tiles and the lane's and wave's query ids
     constexpr int KV_CAP = SEG ? kSegKeyCap : 1, NT_CAP = SEG ? kSegKeyCap / BKV : 1;
     __shared__ __attribute__((aligned(16))) int s_kvid[KV_CAP];
@@ -1632,15 +1688,17 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
     auto v_phase = [&](int s0) {
         // some key after some query of the wave, or (WIN) before some query's
         // first visible key t - WL; SEG: ids not all one value
-        bool masked = (CAUSAL && s0 + BKV - 1 > t_w + a.coff) || (WIN && s0 < t_w + 31 - WL);
+        bool masked = HM ? hm_tile_masked<BKV>(hw, s0 / BKV, t_w)
+                         : (CAUSAL && s0 + BKV - 1 > t_w + a.coff) || (WIN && s0 < t_w + 31 - WL);
         if constexpr (SEG) {
             const int j = s0 / BKV;
             const int kmin = __builtin_amdgcn_readfirstlane(s_tmin[j]);
             const int kmax = __builtin_amdgcn_readfirstlane(s_tmax[j]);
             masked = masked || !(w_qmin == w_qmax && kmin == kmax && kmin == w_qmin);
         }
-        const int lim = CAUSAL ? t + a.coff - s0 - 4 * c : INT_MAX;  // last visible key offset (causal)
-        const int first = WIN ? t - WL - s0 - 4 * c : INT_MIN;       // first visible key offset (window)
+        // last and first visible key offsets (causal, window; HM: the head's)
+        const int lim = HM ? t + hw.wr - s0 - 4 * c : CAUSAL ? t + a.coff - s0 - 4 * c : INT_MAX;
+        const int first = HM ? t - hw.wl - s0 - 4 * c : WIN ? t - WL - s0 - 4 * c : INT_MIN;
         float amax = 0.f;
         // SEG: the ids of keys s0 + 8 q4 + 4 c + 0..3 (read on masked tiles only)
         i32x4 ids[4] = {};
@@ -1656,6 +1714,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_pp_kernel(BwdArgs a, int g
             const int off = 8 * (r >> 2) + (r & 3);
             bool hide = off > lim || off < first;
             if constexpr (SEG) hide = hide || ids[r >> 2][r & 3] != my_qid;
+            if constexpr (HM) hide = hide && s0 + off + 4 * c >= hw.pfx;  // prefix keys stay
             if (masked && hide) p = 0.f;
             const float ds = p * (pacc[r] - dlt);
             amax = fmaxf(amax, fabsf(ds));
@@ -1730,6 +1789,10 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
         const bool seg_shape = a.q_seg != nullptr && a.head_mask == nullptr && gw * bq == 256 && a.T % bq == 0 &&
                                a.S % BKV_PP == 0 && a.S <= kSegKeyCap && diag_tiles(BKV_PP) &&
                                (!a.causal || bq == BKV_PP) && !mask_extra(m);
+        // per-head masks on an otherwise dense shape
+        const bool hm_shape = a.q_seg == nullptr && a.head_mask != nullptr && gw * bq == 256 && a.T % bq == 0 &&
+                              a.S % BKV_PP == 0 && diag_tiles(BKV_PP) && (!a.causal || bq == BKV_PP) &&
+                              !mask_extra(m);
         if (seg_shape) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, true, false, true>), qgrid, dim3(512), 0,
@@ -1737,6 +1800,14 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
             else
                 hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, false, false, true>), qgrid, dim3(512), 0,
                                    stream, a, gw, bq, n_gsplit, n_qblocks);
+            delta_done = true;
+        } else if (hm_shape) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, true, false, false, true>), qgrid, dim3(512),
+                                   0, stream, a, gw, bq, n_gsplit, n_qblocks);
+            else
+                hipLaunchKernelGGL((attn_bwd_delta_pp_kernel<H, BKV_PP, false, false, false, true>), qgrid, dim3(512),
+                                   0, stream, a, gw, bq, n_gsplit, n_qblocks);
             delta_done = true;
         } else if (dense) {
             if (a.causal)
@@ -1768,6 +1839,9 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
         // segment ids on an otherwise dense shape with at most 8192 keys
         const bool seg_shape = a.q_seg != nullptr && a.head_mask == nullptr && gw * bq == 256 && a.T % bq == 0 &&
                                a.S % 32 == 0 && a.S <= kSegKeyCap && diag_tiles(32) && !mask_extra(m);
+        // per-head masks on an otherwise dense shape
+        const bool hm_shape = a.q_seg == nullptr && a.head_mask != nullptr && gw * bq == 256 && a.T % bq == 0 &&
+                              a.S % 32 == 0 && diag_tiles(32) && !mask_extra(m);
         if (seg_shape) {
             if (a.causal)
                 hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, true, false, true>), qgrid, dim3(512), 0, stream, a, gw,
@@ -1775,6 +1849,14 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
             else
                 hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, false, false, true>), qgrid, dim3(512), 0, stream, a, gw,
                                    bq, n_gsplit, n_qblocks);
+            dq_done = true;
+        } else if (hm_shape) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, true, false, false, true>), qgrid, dim3(512), 0, stream,
+                                   a, gw, bq, n_gsplit, n_qblocks);
+            else
+                hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<H, false, false, false, true>), qgrid, dim3(512), 0, stream,
+                                   a, gw, bq, n_gsplit, n_qblocks);
             dq_done = true;
         } else if (dense) {
             if (a.causal)

@@ -29,6 +29,18 @@ CASES = [
     # S, sides past the sequence
     (1, 2, 2, 130, 130, 128, 1, False, [(-7, -3, 0), (10, -1, 1000), (5000, 5000, 0), (3, 4, -9)]),
     (1, 1, 3, 64, 64, 64, 0, False, [(0, 0, 0), GLOBAL, (5, 0, 8)]),
+    # shapes of the ping-pong D and dQ kernels and the wave-pair dK/dV kernel
+    # (whole tiles, causal T = S): per-wave masks over the union of a block's heads
+    (1, 2, 4, 512, 512, 128, 1, False, [GLOBAL, (255, -1, 0), (63, -1, 32), DIAG]),
+    (1, 1, 4, 384, 384, 64, 0, False, [TWO_SIDED, PREFIX_ONLY, BAND, (100, 30, 20)]),
+    # (a prefix of only 3 keys under a 5-key window would gather about 1500 of
+    # the eight heads' bf16-rounded weights on each of those keys: that
+    # rounding alone, which the kernels share with the pages' fused kernel,
+    # moves dV there by 2.1e-2, past the absolute bar; with 40 prefix keys it
+    # is 1.3e-2, as a CPU simulation of bf16 weights in fp64 shows)
+    (2, 1, 8, 256, 256, 128, 1, False, [GLOBAL, (31, -1, 0), (127, -1, 64), DIAG, (0, -1, 200), LOCAL64,
+                                        GLOBAL, (5, -1, 40)]),
+    (1, 1, 2, 256, 320, 128, 0, False, [(50, 50, 0), (-1, -1, 100)]),
 ]
 
 
