@@ -147,15 +147,6 @@ __device__ __forceinline__ HmRange<BKV> hm_union(const BwdArgs &a, int kh, int g
     }
     return HmRange<BKV>{wave_min_i(f), wave_max_i(l)};
 }
-// Does key tile j hold a pair that head mask hw hides from the wave's rows
-// t_w .. t_w + 31?
-template <int BKV>
-__device__ __forceinline__ bool hm_tile_masked(const HeadMask &hw, int j, int t_w) {
-    const int s0 = j * BKV;
-    const bool all_pfx = s0 + BKV - 1 < hw.pfx;
-    const bool all_band = s0 >= t_w + 31 - hw.wl && s0 + BKV - 1 <= t_w + hw.wr;
-    return !(all_pfx || all_band);
-}
 
 
 // ---------------------------------------------------------------------------

@@ -48,6 +48,15 @@ __device__ __forceinline__ HeadMask head_mask_of(const int32_t *tab, int kh, int
     h.pfx = pf < 0 ? 0 : (pf < S ? pf : S);
     return h;
 }
+// Does key tile j (BKV keys) hold a pair that head mask hw hides from a
+// wave's query rows t_w .. t_w + 31?
+template <int BKV>
+__device__ __forceinline__ bool hm_tile_masked(const HeadMask &hw, int j, int t_w) {
+    const int s0 = j * BKV;
+    const bool all_pfx = s0 + BKV - 1 < hw.pfx;
+    const bool all_band = s0 >= t_w + 31 - hw.wl && s0 + BKV - 1 <= t_w + hw.wr;
+    return !(all_pfx || all_band);
+}
 
 // D = A * B + C on a 32x32 fp32 tile, A 32x16 and B 16x32 in bf16.
 // Operand layout (64-wide wave): lane l holds A[l%32][8*(l/32) .. +7] and
