@@ -591,7 +591,7 @@ def main():
         write_counters(args.write_counters, workload_by_bench_name(args.workload).name)
         return
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (--gpus %d refused)"
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path (--gpus %d refused)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
